@@ -1,0 +1,191 @@
+"""Benchmark of one GPU's trainable MoE layer (forward + backward) on MI355X.
+
+    python bench.py [--gpus 1] [--steps 15] [--warmup 5] [--config 30b]
+
+A step is one forward and one backward pass of the whole layer (routing,
+dispatch, both expert GEMMs with fused SwiGLU, combine; dy dispatch, the four
+backward GEMMs with fused SwiGLU-backward and routing-weight gradient,
+un-permute reduction) over one batch of synthetic inputs already resident in
+HBM.  The default workload is the Qwen3-30B-A3B-shaped layer (T=16384 tokens,
+D=2048, F=768, 128 experts, top-8, uniform random routing, bf16).  Timing
+follows the pages' averaging rule (mean over steps after a warm-up: Prime Mega
+MoE news item, "How fast is Prime Mega MoE?").
+
+Prints one JSON line.  `value` is achieved TFLOP/s of the algorithmic fwd+bwd
+FLOPs (18 * T * K * D * F).  `roofline` covers the kernel with the largest
+share of the step, timed with HIP events on the stream it is launched on;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd+bwd ms and TFLOP/s (% MFMA peak), Qwen3-30B/235B shapes"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp32": 157.3}
+HBM_PEAK_GBS = 8000.0
+
+
+def gemm_flops(cfg) -> dict:
+    """Algorithmic FLOPs per launch of each GEMM kernel (2 per multiply-add)."""
+    ndf = float(cfg.N) * cfg.D * cfg.F
+    return {"gemm_w1_swiglu": 4 * ndf, "gemm_w2": 2 * ndf, "gemm_w2_dgrad_dswiglu": 2 * ndf,
+            "gemm_w2_wgrad": 2 * ndf, "gemm_w1_dgrad": 4 * ndf, "gemm_w1_wgrad": 4 * ndf}
+
+
+def row_bytes(cfg, b=2) -> dict:
+    """Algorithmic HBM bytes per launch of the row movers."""
+    T, N, D = cfg.T, cfg.N, cfg.D
+    return {"dispatch": T * D * b + N * D * b + 2 * N * 4 + N * 4,
+            "combine": N * D * b + T * D * b + N * 8,
+            "unpermute": N * D * b + T * D * b + N * 4}
+
+
+def cpu_baseline(cfg, inp, budget_s: float) -> dict:
+    """Times the CPU oracle's fwd+bwd on the first S tokens of the workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import moe_oracle as orc
+
+    cores = len(os.sched_getaffinity(0))
+
+    def run(S):
+        sl = slice(0, S)
+        t0 = time.perf_counter()
+        f = orc.forward(inp["x"][sl], inp["topk_idx"][sl], inp["topk_w"][sl], inp["w1"], inp["w2"])
+        orc.backward(inp["dy"][sl], inp["x"][sl], inp["topk_idx"][sl], inp["topk_w"][sl],
+                     inp["w1"], inp["w2"], f)
+        return time.perf_counter() - t0
+
+    with threadpool_limits(limits=cores):
+        t_small = run(2)
+        S = int(max(2, min(cfg.T, 2 * budget_s / max(t_small, 1e-3))))
+        S = min(S, 512)
+        t = run(S)
+    flops = 18.0 * S * cfg.K * cfg.D * cfg.F
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fwd+bwd of the first {S} of {cfg.T} tokens (all {cfg.K} routed pairs each), "
+                      f"numpy float64, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=15)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="30b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-profile", action="store_true",
+                    help="time without per-kernel events (no roofline entry)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's layer only: the expert-parallel exchange between "
+              "GPUs is outside this build, so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_layer_31_amd as moe
+    import moe_inputs as mi
+    from tests.layer_harness import Layer
+
+    cfg = mi.CONFIGS[args.config]
+    t0 = time.perf_counter()
+    inp = mi.make_inputs(cfg, threads=16)
+    gen_s = time.perf_counter() - t0
+    L = Layer(cfg, inp, device="cuda:0")
+    L.prepare()
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        L.fwd()
+        L.bwd()
+    torch.cuda.synchronize()
+    status = L.check()
+    if status != moe.MOE_OK:
+        raise RuntimeError(moe.strerror(status))
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    if not args.no_profile:
+        moe.moe_profile_reset()
+        moe.moe_profile_enable(True)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for a, b, c in ev:
+        a.record(stream)
+        L.fwd()
+        b.record(stream)
+        L.bwd()
+        c.record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(False)
+    kernels = {} if args.no_profile else moe.moe_profile_collect()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
+    status = L.check()
+    if status != moe.MOE_OK:
+        raise RuntimeError(moe.strerror(status))
+
+    flops = cfg.fwd_flops() + cfg.bwd_flops()
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    dtype = "bf16" if cfg.io_is_bf16 else "fp32"
+    peak = PEAK_TFLOPS["bf16"]
+
+    roof = None
+    per_kernel = {}
+    if kernels:
+        gf = gemm_flops(cfg)
+        rb = row_bytes(cfg)
+        for name, (ms, n) in kernels.items():
+            avg = ms / n
+            entry = {"avg_ms": round(avg, 4), "launches": n}
+            if name in gf:
+                entry["tflops"] = round(gf[name] / (avg * 1e-3) / 1e12, 1)
+                entry["frac_peak"] = round(gf[name] / (avg * 1e-3) / 1e12 / peak, 3)
+            if name in rb:
+                entry["gbs"] = round(rb[name] / (avg * 1e-3) / 1e9, 1)
+                entry["frac_hbm"] = round(rb[name] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)
+            per_kernel[name] = entry
+        dom = max((k for k in kernels if k in gf), key=lambda k: kernels[k][0])
+        avg = kernels[dom][0] / kernels[dom][1]
+        ach = gf[dom] / (avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                "flops_per_launch": gf[dom], "avg_ms": round(avg, 4)}
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: Qwen3 MoE layer T={cfg.T} D={cfg.D} F={cfg.F} "
+                               f"E={cfg.E} top-{cfg.K}, {cfg.routing} routing",
+                   "T": cfg.T, "D": cfg.D, "F": cfg.F, "E": cfg.E, "K": cfg.K, "mode": cfg.mode},
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "fwd_tflops": round(cfg.fwd_flops() / (fwd_ms * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(cfg.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1),
+        "frac_mfma_peak": round(tflops / peak, 4),
+        "roofline": roof,
+        "kernels": per_kernel,
+        "input_gen_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

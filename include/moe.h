@@ -1,0 +1,184 @@
+/*
+ * moe.h - C ABI of one GPU's trainable mixture-of-experts layer on MI355X (gfx950).
+ *
+ * The layer is the one described on the Prime Mega MoE pages (news item,
+ * section "How does the fused kernel work?"): tokens are dispatched to their
+ * top-k experts, each expert applies two linear layers with SwiGLU in between,
+ * and the expert outputs are combined with the routing weights; the same
+ * section adds the training (backward) pass.  Section "How do developers use
+ * it?" lists the precisions bf16, mxfp8, fp8 and fp8_bwd.
+ *
+ * Shapes (all row-major):
+ *   x, y, dy, dx   [T, D]         tokens x model dim
+ *   topk_idx       [T, K] int32   expert id of each (token, slot); p = t*K + k
+ *   topk_w         [T, K] fp32    routing weight of each (token, slot)
+ *   w1, dw1        [E, 2F, D]     expert linear 1; rows 0..F-1 gate, F..2F-1 up
+ *   w2, dw2        [E, D, F]      expert linear 2 (down)
+ *   dtopk_w        [T, K] fp32    gradient of the loss wrt topk_w
+ * Forward:  h = W1[e] x_t, a = silu(h[:F]) * h[F:], o = W2[e] a, y_t = sum_k w o.
+ * Backward of a loss L with dL/dy = dy: dx, dW1, dW2 and dtopk_w = <dy_t, o>.
+ *
+ * Element types by mode:
+ *   MOE_FP32            x y dy dx w1 w2 dw1 dw2 fp32; fp32 GEMMs       (not built yet)
+ *   MOE_FP32_BF16GEMM   fp32 storage, GEMM operands rounded to bf16, fp32 accumulate
+ *   MOE_BF16            bf16 storage (raw 16-bit bfloat16), bf16 GEMMs, fp32 accumulate
+ *   MOE_FP8_BWD         bf16 storage, bf16 forward, blockwise-FP8 backward GEMMs (not built yet)
+ *   MOE_MXFP8           bf16 storage, MXFP8 GEMMs forward and backward           (not built yet)
+ *   MOE_FP8             bf16 storage, blockwise-FP8 GEMMs forward and backward   (not built yet)
+ * Intermediates are kept in bf16 (fp32 accumulators, rounded once when stored);
+ * SwiGLU, its backward, the routing-weight products and all row sums are fp32.
+ *
+ * Ownership and threading:
+ *   - Every pointer is a device pointer unless noted.  The caller allocates and
+ *     owns every buffer, including `scratch` and `wprep`; the library never
+ *     allocates or frees device memory.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work
+ *     asynchronously and return without synchronizing, except moe_check and
+ *     moe_profile_collect.
+ *   - Inputs are never modified.  Calls on distinct scratch buffers are
+ *     independent; the library keeps no state except the opt-in profiler.
+ *   - Buffers must be 16-byte aligned and must not overlap.
+ *
+ * Errors: every call returns MOE_OK (0) or a negative MOE_E* code found on the
+ * host before anything is enqueued.  Errors found by the GPU (an expert id out
+ * of range) are latched in a word inside `scratch` and returned by moe_check.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+enum moe_mode {
+  MOE_FP32 = 0,
+  MOE_FP32_BF16GEMM = 1,
+  MOE_BF16 = 2,
+  MOE_FP8_BWD = 3,
+  MOE_MXFP8 = 4,
+  MOE_FP8 = 5
+};
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* null pointer, non-positive or inconsistent sizes, bad mode */
+  MOE_ESCRATCH = -2,     /* scratch_bytes / wprep_bytes smaller than required */
+  MOE_EALIGN = -3,       /* a buffer is not 16-byte aligned */
+  MOE_EUNSUPPORTED = -4, /* valid request this build cannot run (mode or shape) */
+  MOE_EHIP = -5,         /* a HIP launch or runtime call failed */
+  MOE_EINDEX = -6,       /* (device) a topk_idx entry was outside [0, E) */
+  MOE_ETIMEOUT = -7      /* (device) a bounded wait in a persistent kernel expired */
+};
+
+/* Flags (moe_desc.flags). */
+#define MOE_FLAG_NO_QUEUE 0x1u  /* forward: separate kernels instead of the persistent overlap kernel */
+
+/* Layer descriptor, passed by host pointer.  Requirements: T, E, K >= 1;
+ * K <= E; E <= 1024; D % 64 == 0 and F % 64 == 0; T * K < 2^31. */
+typedef struct moe_desc {
+  int32_t T, D, F, E, K;
+  int32_t mode;  /* enum moe_mode */
+  int32_t flags; /* MOE_FLAG_* */
+} moe_desc;
+
+/* Size in bytes of the scratch buffer for `d` (host call; 0 if `d` is invalid).
+ * The scratch holds the routing metadata (the stable by-expert sort of the
+ * routed pairs, the pages' "GPU sorts tokens" in "Why is MoE training
+ * communication-bound?") and the intermediates kept between forward and
+ * backward (the pages' "GPU-only scratch buffers" instead of intermediate
+ * tensors, "How does the fused kernel work?").  Its layout is private. */
+size_t moe_scratch_bytes(const moe_desc* d);
+
+/* Size in bytes of the prepared-weight buffer (quantised weight copies for the
+ * FP8 modes; 0 for the bf16/fp32 modes, where `wprep` may be NULL). */
+size_t moe_wprep_bytes(const moe_desc* d);
+
+/* Fill `wprep` from w1/w2 for the FP8 modes (a no-op returning MOE_OK for the
+ * other modes).  Must be called again whenever the weights change. */
+int moe_prepare_weights(const moe_desc* d, const void* w1, const void* w2,
+                        void* wprep, size_t wprep_bytes, void* stream);
+
+/* Routing metadata only (moe_fwd runs it itself).  For the flat pair index
+ * p = t*K + k with expert e = topk_idx[p]:
+ *   counts[e] = #{p : idx_p = e}; offsets = exclusive prefix sum, offsets[E]
+ *   = number of valid pairs; pos[p] = offsets[e] + #{p' < p : idx_p' = e}
+ *   (stable by p; -1 for an id outside [0, E), which also latches MOE_EINDEX);
+ *   src[pos[p]] = p.  All int32, in scratch; see moe_routing_view. */
+int moe_route(const moe_desc* d, const int32_t* topk_idx, void* scratch,
+              size_t scratch_bytes, void* stream);
+
+/* Device pointers into `scratch` for counts [E], offsets [E+1], pos [T*K] and
+ * src [T*K] (src entries past offsets[E] are unspecified).  Host arithmetic
+ * only; any output pointer may be NULL. */
+int moe_routing_view(const moe_desc* d, const void* scratch, size_t scratch_bytes,
+                     int32_t** counts, int32_t** offsets, int32_t** pos, int32_t** src);
+
+/* Intermediates in scratch, for tests and tools (row r is the r-th routed pair
+ * in expert order, i.e. pair src[r]):
+ *   MOE_VIEW_XPERM  [T*K, D]   dispatched tokens (bf16; fp32 in MOE_FP32)
+ *   MOE_VIEW_H      [T*K, 2F]  linear-1 output: gate | up
+ *   MOE_VIEW_A      [T*K, F]   SwiGLU output
+ *   MOE_VIEW_O      [T*K, D]   linear-2 output (unweighted)
+ *   MOE_VIEW_DYPERM [T*K, D]   dispatched upstream gradient (unweighted)
+ *   MOE_VIEW_DH     [T*K, 2F]  gradient wrt linear-1 output
+ *   MOE_VIEW_DXPERM [T*K, D]   gradient wrt dispatched tokens
+ *   MOE_VIEW_WPERM  [T*K] fp32 routing weight of each routed pair */
+enum moe_view {
+  MOE_VIEW_XPERM = 0, MOE_VIEW_H = 1, MOE_VIEW_A = 2, MOE_VIEW_O = 3,
+  MOE_VIEW_DYPERM = 4, MOE_VIEW_DH = 5, MOE_VIEW_DXPERM = 6, MOE_VIEW_WPERM = 7
+};
+int moe_scratch_view(const moe_desc* d, const void* scratch, size_t scratch_bytes,
+                     int which, void** ptr, size_t* bytes);
+
+/* Forward pass.  Runs the routing step, the dispatch (x -> expert-contiguous
+ * rows), expert linear 1 with SwiGLU fused into its epilogue, expert linear 2,
+ * and the weighted combine y_t = sum_k w[t,k] o_{t,k} (an fp32 gather-reduce in
+ * ascending k, rounded once).  Writes `y`; leaves the routing metadata and the
+ * intermediates needed by moe_bwd in `scratch`.  `wprep` is ignored in the
+ * bf16/fp32 modes. */
+int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const float* topk_w,
+            const void* w1, const void* w2, const void* wprep, void* y,
+            void* scratch, size_t scratch_bytes, void* stream);
+
+/* Backward pass of the forward that last used `scratch` (which must be passed
+ * back unmodified, with the same descriptor, topk_w and weights).  Runs the
+ * combine-backward dispatch of dy, the W2 dgrad with SwiGLU-backward, the
+ * routing-weight product and the partial <dy, o> sums fused into its epilogue,
+ * the W2 and W1 wgrads (per-expert reductions over that expert's tokens, no
+ * atomics), the W1 dgrad and the un-permute reduction of dx (fp32 sum over k).
+ * Overwrites dx, dw1, dw2 (experts with no tokens get zeros) and dtopk_w. */
+int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w,
+            const void* w1, const void* w2, const void* wprep,
+            void* dx, void* dw1, void* dw2, float* dtopk_w,
+            void* scratch, size_t scratch_bytes, void* stream);
+
+/* Synchronizes `stream`, returns the latched device error (MOE_OK, MOE_EINDEX
+ * or MOE_ETIMEOUT) of `scratch` and clears it. */
+int moe_check(const moe_desc* d, void* scratch, size_t scratch_bytes, void* stream);
+
+/* Text of a status code (static string, host). */
+const char* moe_strerror(int status);
+
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+/* Opt-in kernel profiler (process-wide, for benchmarks).  While enabled, every
+ * kernel the library launches is bracketed by HIP events recorded on the
+ * stream it is launched on.  moe_profile_collect synchronizes those events,
+ * adds their durations to per-kernel totals and returns the number of distinct
+ * kernels; moe_profile_get reads entry i (name valid until the next reset);
+ * moe_profile_reset clears the totals. */
+int moe_profile_enable(int on);
+int moe_profile_collect(void);
+int moe_profile_get(int i, const char** name, double* total_ms, int64_t* launches);
+int moe_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

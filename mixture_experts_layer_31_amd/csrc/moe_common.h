@@ -1,0 +1,95 @@
+// Internal definitions shared by the MI355X MoE layer's host code and kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Bits of the device error word kept in scratch.
+enum : uint32_t { kErrIndex = 1u, kErrTimeout = 2u };
+
+// Routing processes the flat pair list in chunks of this many pairs per block.
+constexpr int kRouteChunk = 2048;
+constexpr int kRouteThreads = 256;
+
+// Byte offsets of the regions of the caller's scratch buffer.  Every region
+// starts on a 256-byte boundary.  The layout depends only on the descriptor.
+struct Layout {
+  size_t err, counts, offsets, tiles[3], chunk_cnt, pos, src, wperm;
+  size_t xperm, h, a, o, dyperm, dh, dxperm, dprob_part, queue, total;
+  int nchunks;      // routing chunks
+  int nparts_max;   // capacity of per-row partial <dy, o> sums
+  int act_bytes;    // bytes per intermediate element
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline Layout make_layout(const moe_desc& d) {
+  Layout L{};
+  const size_t N = size_t(d.T) * d.K, E = d.E, D = d.D, F = d.F;
+  L.act_bytes = d.mode == MOE_FP32 ? 4 : 2;
+  L.nchunks = int((N + kRouteChunk - 1) / kRouteChunk);
+  L.nparts_max = 2 * int(F / 64);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
+  L.err = take(256);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  for (int i = 0; i < 3; ++i) L.tiles[i] = take((E + 1) * 4);
+  L.chunk_cnt = take(size_t(L.nchunks) * E * 4);
+  L.pos = take(N * 4);
+  L.src = take(N * 4);
+  L.wperm = take(N * 4);
+  const size_t ab = L.act_bytes;
+  L.xperm = take(N * D * ab);
+  L.h = take(N * 2 * F * ab);
+  L.a = take(N * F * ab);
+  L.o = take(N * D * ab);
+  L.dyperm = take(N * D * ab);
+  L.dh = take(N * 2 * F * ab);
+  L.dxperm = take(N * D * ab);
+  L.dprob_part = take(N * size_t(L.nparts_max) * 4);
+  L.queue = take(4096);
+  L.total = o;
+  return L;
+}
+
+// Tile heights for which the routing step writes per-expert m-tile prefix sums.
+constexpr int kTileRows[3] = {64, 128, 256};
+
+// ---- launch helpers (host), implemented in moe_api.hip ----
+// Every kernel launch goes through these so the opt-in profiler can bracket it.
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(hipStream_t s);
+
+// ---- kernel launchers (host) ----
+int launch_route(const moe_desc& d, const Layout& L, const int32_t* idx, char* scratch,
+                 hipStream_t s);
+int launch_clear_err(char* scratch, const Layout& L, hipStream_t s);
+
+// Row gathers/scatters: dispatch (x -> expert-contiguous rows), combine and the
+// un-permute reduction.  `in_f32`/`out_f32` select fp32 instead of bf16 I/O.
+int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool in_f32,
+                    const float* topk_w, char* scratch, size_t dst_off, hipStream_t s);
+int launch_combine(const moe_desc& d, const Layout& L, const float* topk_w, void* y,
+                   bool out_f32, const char* scratch, hipStream_t s);
+int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
+                     float* dtopk_w, int nparts, const char* scratch, hipStream_t s);
+int launch_convert_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
+
+// Grouped GEMMs (MFMA).  See moe_gemm.hip.
+int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
+                     char* scratch, hipStream_t s);
+int launch_bwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
+                     void* dw1, void* dw2, bool dw_f32, int* nparts, char* scratch,
+                     hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,187 @@
+"""Parity of the HIP layer (through the C ABI) against the CPU oracle.
+
+Integer routing arrays must be bit-exact; floating-point outputs and
+intermediates must meet max|err| / max|ref| <= 1e-2 (bf16 GEMM operands and
+bf16 storage, fp32 accumulation) against the fp64 oracle on the same inputs.
+Dispatch copies (x_perm, dY_perm) and the permuted routing weights are
+bit-exact copies.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_31_amd as moe
+import moe_inputs as mi
+from oracle import moe_oracle as orc
+from tests.layer_harness import Layer, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 1e-2
+
+SMALL = ["tiny_bf16gemm", "small_bf16", "dead_bf16", "mid_bf16", "wide_bf16"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    moe.lib()
+
+
+def _run(cfg, inp):
+    L = Layer(cfg, inp)
+    L.prepare()
+    L.fwd()
+    L.bwd()
+    assert L.check() == moe.MOE_OK
+    torch.cuda.synchronize()
+    return L
+
+
+def _routing_bitexact(L, idx):
+    got = L.routing()
+    ref = orc.route(idx, L.cfg.E)
+    np.testing.assert_array_equal(got["counts"], ref["counts"])
+    np.testing.assert_array_equal(got["offsets"], ref["offsets"])
+    np.testing.assert_array_equal(got["pos"], ref["pos"])
+    nv = int(ref["offsets"][-1])
+    np.testing.assert_array_equal(got["src"][:nv], ref["src"])
+    return ref
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_layer_matches_oracle(name):
+    cfg = mi.CONFIGS[name]
+    inp = mi.make_inputs(cfg)
+    print(f"[case] {name} T={cfg.T} D={cfg.D} F={cfg.F} E={cfg.E} K={cfg.K} mode={cfg.mode}",
+          flush=True)
+    L = _run(cfg, inp)
+    r = _routing_bitexact(L, inp["topk_idx"])
+    f = orc.forward(inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"], inp["w2"])
+    b = orc.backward(inp["dy"], inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"], inp["w2"], f)
+    out = L.outputs()
+    errs = {k: rel_err(out[k], ref) for k, ref in
+            (("y", f["y"]), ("dx", b["dx"]), ("dw1", b["dw1"]), ("dw2", b["dw2"]),
+             ("dprob", b["dprob"]))}
+    print(name, errs, flush=True)
+    for k, e in errs.items():
+        assert e <= TOL_BF16, (k, e)
+
+    # intermediates, row r of a view is pair src[r]
+    K, F, D = cfg.K, cfg.F, cfg.D
+    src = r["src"]
+    t_of, k_of = src // K, src % K
+    xp = L.view(moe.MOE_VIEW_XPERM, D)
+    dyp = L.view(moe.MOE_VIEW_DYPERM, D)
+    wp = L.view(moe.MOE_VIEW_WPERM, 0, torch.float32)
+    if cfg.io_is_bf16:
+        np.testing.assert_array_equal(xp, inp["x"][t_of])
+        np.testing.assert_array_equal(dyp, inp["dy"][t_of])
+    else:
+        assert rel_err(xp, inp["x"][t_of]) <= 2 ** -8
+        assert rel_err(dyp, inp["dy"][t_of]) <= 2 ** -8
+    np.testing.assert_array_equal(wp[:len(src)], inp["topk_w"][t_of, k_of])
+    for which, cols, ref in ((moe.MOE_VIEW_H, 2 * F, f["h"]), (moe.MOE_VIEW_A, F, f["a"]),
+                             (moe.MOE_VIEW_O, D, f["o"]), (moe.MOE_VIEW_DH, 2 * F, b["dh"])):
+        got = L.view(which, cols)[:len(src)]
+        e = rel_err(got, ref[t_of, k_of])
+        assert e <= TOL_BF16, (which, e)
+
+
+def test_zero_token_experts_get_zero_wgrad():
+    cfg = mi.CONFIGS["dead_bf16"]
+    inp = mi.make_inputs(cfg)
+    L = _run(cfg, inp)
+    counts = np.bincount(inp["topk_idx"].ravel(), minlength=cfg.E)
+    dead = np.nonzero(counts == 0)[0]
+    assert len(dead) == 4
+    out = L.outputs()
+    for e in dead:
+        assert np.all(out["dw1"][e] == 0) and np.all(out["dw2"][e] == 0)
+
+
+def test_run_to_run_bitwise_determinism():
+    cfg = mi.CONFIGS["mid_bf16"]
+    inp = mi.make_inputs(cfg)
+    L = _run(cfg, inp)
+    first = L.outputs()
+    for _ in range(3):
+        L.fwd()
+        L.bwd()
+        torch.cuda.synchronize()
+        again = L.outputs()
+        for k in first:
+            np.testing.assert_array_equal(again[k], first[k], err_msg=k)
+
+
+def test_out_of_range_index_is_reported_and_skipped():
+    cfg = mi.CONFIGS["small_bf16"]
+    inp = mi.make_inputs(cfg)
+    idx = inp["topk_idx"].copy()
+    idx[3, 1] = cfg.E + 5
+    idx[150, 0] = -2
+    L = Layer(cfg, dict(inp, topk_idx=idx))
+    moe.check(moe.moe_route(L.desc, L.idx, L.scratch), "route")
+    assert L.check() == moe.MOE_EINDEX
+    assert L.check() == moe.MOE_OK  # cleared
+    got = L.routing()
+    ref = orc.route(idx, cfg.E)
+    assert ref["invalid"] == 2
+    np.testing.assert_array_equal(got["pos"], ref["pos"])
+    np.testing.assert_array_equal(got["counts"], ref["counts"])
+    nv = int(ref["offsets"][-1])
+    np.testing.assert_array_equal(got["src"][:nv], ref["src"])
+
+
+@pytest.mark.parametrize("name", ["30b", "30b_mxfp8"])
+def test_routing_full_size_bitexact(name):
+    cfg = mi.CONFIGS[name]
+    idx, w = mi.make_routing(cfg)
+    d = moe.make_desc(cfg.T, cfg.D, cfg.F, cfg.E, cfg.K, mi.MODE_BF16)
+    scratch = torch.empty(moe.moe_scratch_bytes(d), dtype=torch.uint8, device="cuda")
+    tidx = torch.from_numpy(idx).cuda()
+    moe.check(moe.moe_route(d, tidx, scratch), "route")
+    assert moe.moe_check(d, scratch) == moe.MOE_OK
+
+    L = Layer.__new__(Layer)
+    L.cfg, L.desc, L.scratch = cfg, d, scratch
+    _routing_bitexact(L, idx)
+
+
+def _full_size(name, ntok, nexp):
+    cfg = mi.CONFIGS[name]
+    print(f"[case] full-size {name}", flush=True)
+    inp = mi.make_inputs(cfg, threads=16)
+    L = _run(cfg, inp)
+    _routing_bitexact(L, inp["topk_idx"])
+    rng = np.random.default_rng(0)
+    tok = np.sort(rng.choice(cfg.T, size=ntok, replace=False))
+    tok[0], tok[-1] = 0, cfg.T - 1
+    ref = orc.backward_tokens(inp["dy"], inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"],
+                              inp["w2"], tok)
+    tt = torch.from_numpy(tok).cuda()
+    out = dict(y=L.y[tt], dx=L.dx[tt], dprob=L.dprob[tt])
+    from tests.layer_harness import to_host
+    errs = {k: rel_err(to_host(v), ref[k]) for k, v in out.items()}
+    counts = np.bincount(inp["topk_idx"].ravel(), minlength=cfg.E)
+    for e in rng.choice(np.nonzero(counts)[0], size=nexp, replace=False):
+        r1 = np.sort(rng.choice(2 * cfg.F, size=6, replace=False))
+        r2 = np.sort(rng.choice(cfg.D, size=6, replace=False))
+        wr = orc.wgrad_rows(inp["dy"], inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"],
+                            inp["w2"], int(e), r1, r2)
+        errs[f"dw1[{e}]"] = rel_err(to_host(L.dw1[int(e)][torch.from_numpy(r1).cuda()]), wr["dw1"])
+        errs[f"dw2[{e}]"] = rel_err(to_host(L.dw2[int(e)][torch.from_numpy(r2).cuda()]), wr["dw2"])
+    print(name, errs, flush=True)
+    for k, e in errs.items():
+        assert e <= TOL_BF16, (k, e)
+
+
+@pytest.mark.timeout(600)
+def test_full_size_30b_sampled():
+    _full_size("30b", ntok=24, nexp=2)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_235b_sampled():
+    _full_size("235b", ntok=12, nexp=1)
