@@ -41,7 +41,8 @@
  *
  * Errors: every call returns MOE_OK (0) or a negative MOE_E* code found on the
  * host before anything is enqueued.  Errors found by the GPU (an expert id out
- * of range) are latched in a word inside `scratch` and returned by moe_check.
+ * of range) are latched in a word inside `scratch`, which moe_route and moe_fwd
+ * clear when they start; moe_check returns and clears it.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

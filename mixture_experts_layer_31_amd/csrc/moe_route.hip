@@ -156,6 +156,10 @@ int launch_route(const moe_desc& d, const Layout& L, const int32_t* idx, char* s
   while ((1 << nbits) < E) ++nbits;
   auto* err = reinterpret_cast<uint32_t*>(scratch + L.err);
   auto* chunk = reinterpret_cast<int32_t*>(scratch + L.chunk_cnt);
+  // the caller's scratch may hold anything: start the error word from zero
+  prof_begin("clear_err", s);
+  clear_err_kernel<<<1, 64, 0, s>>>(err);
+  prof_end(s);
   prof_begin("route_count", s);
   route_count_kernel<<<L.nchunks, kRouteThreads, 0, s>>>(idx, N, E, chunk, err);
   prof_end(s);
