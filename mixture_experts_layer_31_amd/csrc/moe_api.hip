@@ -251,10 +251,9 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
   char* sc = static_cast<char*>(scratch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool io_f32 = d->mode == MOE_FP32_BF16GEMM;
-  if ((rc = launch_dispatch(*d, L, dy, io_f32, topk_w, sc, L.dyperm, s))) return rc;
-  int nparts = 0;
-  if ((rc = launch_bwd_gemms(*d, L, g1, g2, dw1, dw2, io_f32, &nparts, sc, s))) return rc;
-  return launch_unpermute(*d, L, dx, io_f32, dtopk_w, nparts, sc, s);
+  if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s))) return rc;
+  if ((rc = launch_bwd_gemms(*d, L, g1, g2, dw1, dw2, io_f32, sc, s))) return rc;
+  return launch_unpermute(*d, L, dx, io_f32, sc, s);
 }
 
 int moe_check(const moe_desc* d, void* scratch, size_t scratch_bytes, void* stream) {

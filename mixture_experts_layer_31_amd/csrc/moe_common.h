@@ -24,9 +24,8 @@ constexpr int kRouteThreads = 256;
 // starts on a 256-byte boundary.  The layout depends only on the descriptor.
 struct Layout {
   size_t err, counts, offsets, tiles[3], chunk_cnt, pos, src, wperm;
-  size_t xperm, h, a, o, dyperm, dh, dxperm, dprob_part, queue, total;
+  size_t xperm, h, a, o, dyperm, dh, dxperm, queue, total;
   int nchunks;      // routing chunks
-  int nparts_max;   // capacity of per-row partial <dy, o> sums
   int act_bytes;    // bytes per intermediate element
 };
 
@@ -37,7 +36,6 @@ inline Layout make_layout(const moe_desc& d) {
   const size_t N = size_t(d.T) * d.K, E = d.E, D = d.D, F = d.F;
   L.act_bytes = d.mode == MOE_FP32 ? 4 : 2;
   L.nchunks = int((N + kRouteChunk - 1) / kRouteChunk);
-  L.nparts_max = 2 * int(F / 64);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
   L.err = take(256);
@@ -56,7 +54,6 @@ inline Layout make_layout(const moe_desc& d) {
   L.dyperm = take(N * D * ab);
   L.dh = take(N * 2 * F * ab);
   L.dxperm = take(N * D * ab);
-  L.dprob_part = take(N * size_t(L.nparts_max) * 4);
   L.queue = take(4096);
   L.total = o;
   return L;
@@ -82,14 +79,16 @@ int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool i
 int launch_combine(const moe_desc& d, const Layout& L, const float* topk_w, void* y,
                    bool out_f32, const char* scratch, hipStream_t s);
 int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
-                     float* dtopk_w, int nparts, const char* scratch, hipStream_t s);
+                     const char* scratch, hipStream_t s);
+// Combine-backward: dYw_perm rows (w * dy, bf16) and dtopk_w = <dy, o>.
+int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool in_f32,
+                       const float* topk_w, float* dtopk_w, char* scratch, hipStream_t s);
 int launch_convert_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
 
 // Grouped GEMMs (MFMA).  See moe_gemm.hip.
 int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
                      char* scratch, hipStream_t s);
 int launch_bwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
-                     void* dw1, void* dw2, bool dw_f32, int* nparts, char* scratch,
-                     hipStream_t s);
+                     void* dw1, void* dw2, bool dw_f32, char* scratch, hipStream_t s);
 
 }  // namespace moe

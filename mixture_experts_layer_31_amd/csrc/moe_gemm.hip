@@ -5,27 +5,37 @@
 // work?").  On one GPU this file provides the six expert GEMMs of a training
 // step, with the element-wise work fused into their epilogues:
 //
-//   fwd  W1 + SwiGLU  H = x_perm W1[e]^T, A = silu(H_gate) * H_up   (token-grouped, NT)
-//   fwd  W2           O = A W2[e]^T                                 (token-grouped, NT)
-//   bwd  W2 dgrad     G = dY_perm W2[e]; dH = SwiGLU'(H, w G); partial <G, A>  (NN)
-//   bwd  W1 dgrad     dX_perm = dH W1[e]                            (token-grouped, NN)
-//   bwd  W2 wgrad     dW2[e] = sum_r (w_r dY_perm[r]) A[r]^T         (per-expert, TN)
-//   bwd  W1 wgrad     dW1[e] = sum_r dH[r] x_perm[r]^T               (per-expert, TN)
+//   fwd  W1 + SwiGLU  H = x_perm W1[e]^T, A = silu(H_gate) * H_up      (token-grouped, NT)
+//   fwd  W2           O = A W2[e]^T                                    (token-grouped, NT)
+//   bwd  W2 dgrad     dA = dYw_perm W2[e]; dH = SwiGLU'(H) applied to dA  (token-grouped, NN)
+//   bwd  W1 dgrad     dX_perm = dH W1[e]                               (token-grouped, NN)
+//   bwd  W2 wgrad     dW2[e] = sum_r dYw_perm[r] A[r]^T                 (per-expert, TN)
+//   bwd  W1 wgrad     dW1[e] = sum_r dH[r] x_perm[r]^T                  (per-expert, TN)
+// (dYw_perm holds the dispatched upstream gradient already multiplied by the
+// pair's routing weight.)
 //
 // Work decomposition: a 256-thread workgroup (four wave64s in a 2x2 grid) owns
 // one BM x BN output tile; each wave accumulates (BM/2) x (BN/2) with
-// v_mfma_f32_32x32x16_bf16.  K advances in steps of 64 through a double-buffered
-// LDS stage: the next step's global loads are issued into registers before the
-// current step's MFMAs and written to the other LDS buffer after them.
+// v_mfma_f32_32x32x16_bf16.  The contraction advances 64 at a time through a
+// ring of STAGES LDS buffers filled by direct-to-LDS buffer loads
+// (buffer_load_dwordx4 ... lds): a wave issues the loads for k-step kt+STAGES-1
+// and goes on to the MFMAs of k-step kt without holding the data in registers,
+// so STAGES-1 k-steps of global latency are in flight.  Loads past the end of
+// an expert's rows (or of its tokens, in the wgrads) fall outside the buffer
+// resource and land as zeros.
 //
-// LDS tiles hold R rows x 64 bf16 with the contraction index contiguous, so
-// every MFMA operand fragment (8 consecutive k of one row) is one 16-byte
-// ds_read.  The eight 16-byte chunks of a row are XOR-swizzled with (row & 7) so
-// those reads and the staging writes spread over all banks.  Operands whose
-// global layout has the contraction index outermost (weights in the dgrads,
-// both operands of the wgrads) are transposed in registers while staging: each
-// thread loads KB rows of 8 consecutive elements and writes 8 LDS rows of KB
-// elements.
+// LDS layouts.  An operand whose global rows run along the contraction index
+// ("k-contiguous": activations, and the weights in the forward) is staged as
+// R rows x 64 k, 128 bytes per row; an MFMA fragment (8 consecutive k of one
+// row) is one ds_read_b128.  An operand whose global rows run along the output
+// index ("k-outer": the weights in the dgrads and both operands of the wgrads)
+// is staged as 64 k-rows x R, exactly as it lies in memory, and its fragments
+// are read with ds_read_b64_tr_b16: a 16-lane group pointing at a 4 (k) x 16
+// (m) block gets one column of 4 consecutive k per lane, two reads give the 8
+// consecutive k of an MFMA fragment.  In both layouts the 16-byte chunks of a
+// row are XOR-swizzled so that each read instruction touches every LDS bank
+// once; the swizzle is applied on the load side by choosing which global chunk
+// each lane of the (contiguous) LDS write fetches.
 //
 // Token-grouped GEMMs walk a flat list of (expert, m-tile, n-tile) built from
 // the routing step's per-expert m-tile prefix sums; workgroups past the end
@@ -40,11 +50,11 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 64;
+constexpr int kBK = 64;  // contraction step (bf16 elements)
 
-__device__ __forceinline__ int lds_idx(int row, int chunk) {
-  return row * kBK + ((chunk ^ (row & 7)) << 3);
-}
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define AS3(p) ((__attribute__((address_space(3))) void*)(p))
 
 __device__ __forceinline__ int xcd_remap(int b, int G) {
   const int xcd = b & 7, local = b >> 3;
@@ -55,124 +65,203 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
-// ---------------------------------------------------------------------------
-// Staging of an operand whose rows are contiguous along k (R rows x 64 k).
+// Raw buffer resource over [base, base + bytes): loads at byte offsets >= bytes return 0.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(int(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from the buffer at `voff` into LDS at lds_base + 16 * lane.
+// Issued as inline asm so the compiler does not serialise on it; completion is
+// awaited explicitly with wait_vmcnt before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(AS3(p)));
+}
+
+// Chunk swizzles (chunk = 16 bytes = 8 bf16).
+__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
 template <int R>
-struct KRows {
-  static constexpr int CPT = R / 32;  // 16-byte chunks per thread
-  const uint16_t* rp[CPT];
-  uint4 v[CPT];
+__device__ __forceinline__ int swz_t(int krow) {
+  if constexpr (R >= 128) return (krow & 3) << 2;
+  else return ((krow >> 1) & 1) << 2;
+}
 
-  template <class RowPtr>
-  __device__ __forceinline__ void init(RowPtr rowptr) {
+// ---------------------------------------------------------------------------
+// Operand stagers.  Each knows, per lane, the byte offset (relative to its
+// buffer resource, at k-step 0) of the 16-byte chunk that lane fetches for each
+// of the wave's DMA instructions, and how far that offset moves per k-step.
+
+// k-contiguous operand, R rows: row r of the tile is at rowoff(r) bytes.
+template <int R>
+struct KStager {
+  static constexpr int NI = R / 32;  // DMA instructions per wave per k-step (1 KB each)
+  i32x4 rsrc;
+  int vb[NI];
+  template <class RowOff>
+  __device__ __forceinline__ void init(i32x4 r, RowOff rowoff, int wave, int lane) {
+    rsrc = r;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) rp[j] = rowptr((threadIdx.x + j * kThreads) >> 3);
-  }
-  __device__ __forceinline__ void load(int k0) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int ch = (threadIdx.x + j * kThreads) & 7;
-      v[j] = rp[j] ? *reinterpret_cast<const uint4*>(rp[j] + k0 + ch * 8) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < NI; ++j) {
+      const int q = wave * NI + j;
+      const int row = q * 8 + (lane >> 3);
+      const int logical = (lane & 7) ^ swz_k(row);
+      const int ro = rowoff(row);
+      vb[j] = ro < 0 ? int(0x80000000u) : ro + logical * 16;
     }
   }
-  __device__ __forceinline__ void store(uint16_t* lds) const {
+  __device__ __forceinline__ void issue(uint32_t lds, int wave, int kt) const {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int c = threadIdx.x + j * kThreads;
-      *reinterpret_cast<uint4*>(lds + lds_idx(c >> 3, c & 7)) = v[j];
-    }
+    for (int j = 0; j < NI; ++j)
+      dma16(rsrc, lds + uint32_t(wave * NI + j) * 1024u, vb[j] + kt * (kBK * 2));
   }
 };
 
-// Staging of an operand stored with k outermost: element (row, k) at
-// kptr(k)[row].  Each thread loads KB consecutive k of 8 consecutive rows and
-// transposes them in registers.  With SCALED, k-row k is multiplied by kscale(k)
-// (fp32) before rounding back to bf16.
-template <int R, bool SCALED>
-struct MNRows {
-  static constexpr int KB = R / 32;      // k per thread: 8, 4 or 2
-  static constexpr int KG = kBK / KB;    // threads along k
-  uint4 v[KB];
-  float sc[KB];
-  int kb, mg;
-
-  __device__ __forceinline__ void init() {
-    kb = threadIdx.x % KG;
-    mg = threadIdx.x / KG;
-  }
-  template <class KPtr, class KScale>
-  __device__ __forceinline__ void load(KPtr kptr, KScale kscale, int k0) {
+// k-outer operand, R output columns: k-row k of the tile is at k * ld_bytes,
+// column c at c * 2 (relative to the resource base, which includes the tile's
+// first column).
+template <int R>
+struct TStager {
+  static constexpr int NI = R / 32;
+  static constexpr int LPR = R / 8;      // lanes per k-row
+  static constexpr int RPI = 64 / LPR;   // k-rows per DMA instruction
+  i32x4 rsrc;
+  int vb[NI];
+  int step;  // bytes per k-step
+  __device__ __forceinline__ void init(i32x4 r, int ld_bytes, int wave, int lane) {
+    rsrc = r;
+    step = ld_bytes * kBK;
 #pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      const int k = k0 + kb * KB + i;
-      const uint16_t* p = kptr(k);
-      v[i] = p ? *reinterpret_cast<const uint4*>(p + mg * 8) : make_uint4(0, 0, 0, 0);
-      if constexpr (SCALED) sc[i] = p ? kscale(k) : 0.f;
+    for (int j = 0; j < NI; ++j) {
+      const int q = wave * NI + j;
+      const int krow = q * RPI + lane / LPR;
+      const int logical = (lane % LPR) ^ swz_t<R>(krow);
+      vb[j] = krow * ld_bytes + logical * 16;
     }
   }
-  __device__ __forceinline__ void store(uint16_t* lds) const {
-    uint32_t w[KB][4];
+  __device__ __forceinline__ void issue(uint32_t lds, int wave, int kt) const {
 #pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      const uint32_t in[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (SCALED) {
-          const float lo = __uint_as_float(in[q] << 16) * sc[i];
-          const float hi = __uint_as_float(in[q] & 0xffff0000u) * sc[i];
-          w[i][q] = uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
-        } else {
-          w[i][q] = in[q];
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = mg * 8 + j;
-      uint32_t o[KB / 2];
-#pragma unroll
-      for (int q = 0; q < KB / 2; ++q) {
-        const uint32_t a = w[2 * q][j >> 1], b = w[2 * q + 1][j >> 1];
-        o[q] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-      }
-      const int k = kb * KB;
-      uint16_t* dst = lds + row * kBK + (((k >> 3) ^ (row & 7)) << 3) + (k & 7);
-      if constexpr (KB == 8)
-        *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-      else if constexpr (KB == 4)
-        *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
-      else
-        *reinterpret_cast<uint32_t*>(dst) = o[0];
-    }
+    for (int j = 0; j < NI; ++j)
+      dma16(rsrc, lds + uint32_t(wave * NI + j) * 1024u, vb[j] + kt * step);
   }
 };
 
-// One 64-deep step of MFMAs for a wave's (WMT*32) x (WNT*32) sub-tile.
-template <int WMT, int WNT>
-__device__ __forceinline__ void mma_step(const uint16_t* la, const uint16_t* lb, int arow0,
-                                         int brow0, int lane, f32x16 (&acc)[WMT][WNT]) {
-  const int r = lane & 31, hi = lane >> 5;
+// Fragment reads (8 consecutive k of one row/column, k-step sub-block kk).
+__device__ __forceinline__ bf16x8 frag_k(const char* tile, int row, int kk, int lane) {
+  const int chunk = kk * 2 + (lane >> 5);
+  return *reinterpret_cast<const bf16x8*>(tile + row * 128 + ((chunk ^ swz_k(row)) << 4));
+}
+
+template <int R>
+__device__ __forceinline__ bf16x8 frag_t(const char* tile, int col0, int kk, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
+  i16x4 h[2];
 #pragma unroll
-  for (int kk = 0; kk < kBK / 16; ++kk) {
-    const int ch = kk * 2 + hi;
-    bf16x8 af[WMT], bfr[WNT];
+  for (int half = 0; half < 2; ++half) {
+    const int krow = kk * 16 + 8 * (g >> 1) + 4 * half + (s >> 2);
+    const char* p = tile + krow * (2 * R) + (((col >> 3) ^ swz_t<R>(krow)) << 4) + (col & 7) * 2;
+    h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)AS3(p));
+  }
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// The pipelined main loop: acc += A_tile * B_tile^T over ktiles k-steps.
+template <int BM, int BN, int STAGES, bool A_T, bool B_T, class SA, class SB>
+__device__ __forceinline__ void mainloop(char* smem, const SA& sa, const SB& sb, int ktiles,
+                                         f32x16 (&acc)[BM / 64][BN / 64], int wave, int lane) {
+  constexpr int WM = BM / 2, WN = BN / 2, WMT = WM / 32, WNT = WN / 32;
+  constexpr int A_BYTES = BM * kBK * 2, STAGE = (BM + BN) * kBK * 2;
+  constexpr int NI = BM / 32 + BN / 32;  // DMA instructions per wave per stage
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t base = lds_addr(smem);
+
 #pragma unroll
-    for (int i = 0; i < WMT; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(la + lds_idx(arow0 + i * 32 + r, ch));
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < ktiles) {
+      sa.issue(base + s * STAGE, wave, s);
+      sb.issue(base + s * STAGE + A_BYTES, wave, s);
+    }
+
+  for (int kt = 0; kt < ktiles; ++kt) {
+    // wait for this wave's loads of k-step kt (later stages may stay in flight)
+    const int ahead = min(ktiles - 1 - kt, STAGES - 2);
+    if constexpr (STAGES >= 4) {
+      if (ahead >= 2) wait_vmcnt<2 * NI>();
+      else if (ahead == 1) wait_vmcnt<NI>();
+      else wait_vmcnt<0>();
+    } else if constexpr (STAGES == 3) {
+      if (ahead >= 1) wait_vmcnt<NI>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    const int kn = kt + STAGES - 1;
+    if (kn < ktiles) {
+      const int sn = kn % STAGES;
+      sa.issue(base + sn * STAGE, wave, kn);
+      sb.issue(base + sn * STAGE + A_BYTES, wave, kn);
+    }
+    const char* ta = smem + (kt % STAGES) * STAGE;
+    const char* tb = ta + A_BYTES;
 #pragma unroll
-    for (int j = 0; j < WNT; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8*>(lb + lds_idx(brow0 + j * 32 + r, ch));
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      bf16x8 af[WMT], bfr[WNT];
 #pragma unroll
-    for (int i = 0; i < WMT; ++i)
+      for (int i = 0; i < WMT; ++i) {
+        const int r0 = wm * WM + i * 32;
+        if constexpr (A_T) af[i] = frag_t<BM>(ta, r0, kk, lane);
+        else af[i] = frag_k(ta, r0 + (lane & 31), kk, lane);
+      }
 #pragma unroll
-      for (int j = 0; j < WNT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < WNT; ++j) {
+        const int c0 = wn * WN + j * 32;
+        if constexpr (B_T) bfr[j] = frag_t<BN>(tb, c0, kk, lane);
+        else bfr[j] = frag_k(tb, c0 + (lane & 31), kk, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < WMT; ++i)
+#pragma unroll
+        for (int j = 0; j < WNT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
   }
 }
 
-// Row (within the wave's sub-tile) of accumulator element r of a 32x32 block.
+// Row (within a 32x32 block) of accumulator element r.
 __device__ __forceinline__ int acc_row(int r, int lane) {
   return (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void zero(f32x16 (&acc)[BM / 64][BN / 64]) {
+#pragma unroll
+  for (int i = 0; i < BM / 64; ++i)
+#pragma unroll
+    for (int j = 0; j < BN / 64; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
 
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
@@ -181,25 +270,24 @@ struct GroupedArgs {
   const int32_t* offsets;     // [E+1] first permuted row of each expert
   const int32_t* tile_start;  // [E+1] prefix sum of ceil(count/BM)
   int E, K, ntn, F;
-  const uint16_t* A;          // [rows, K] permuted activations
+  const uint16_t* A;          // [rows, K] permuted activations (k-contiguous)
   int lda;
   const uint16_t* B;          // weights of expert 0; expert e at B + e*bstride
-  int64_t ldb, bstride;
+  int64_t bstride;
+  int ldb;                    // row length of a weight matrix (elements)
+  int brows;                  // rows of a weight matrix
   uint16_t* out;              // STORE: [rows, ldo]; SWIGLU: H [rows, 2F]; DSWIGLU: dH [rows, 2F]
   int ldo;
   uint16_t* out2;             // SWIGLU: A [rows, F]
   const uint16_t* hsave;      // DSWIGLU: H [rows, 2F]
-  const uint16_t* asave;      // DSWIGLU: A [rows, F]
-  const float* wperm;         // DSWIGLU: routing weight per permuted row
-  float* part;                // DSWIGLU: [rows, pstride] partial <G, A> per n-tile half
-  int pstride;
 };
 
-template <int BM, int BN, bool B_MN, int EPI>
+// B_T = false: B[e] is [N, K] (row n holds the k-run); true: B[e] is [K, N].
+template <int BM, int BN, int STAGES, bool B_T, int EPI>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GroupedArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2, WMT = WM / 32, WNT = WN / 32;
-  static_assert(EPI != EPI_SWIGLU || WNT % 2 == 0, "SwiGLU pairs gate and up sub-tiles");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * kBK];
+  static_assert(EPI != EPI_SWIGLU || (WNT % 2 == 0 && !B_T), "SwiGLU pairs gate/up sub-tiles");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * (BM + BN) * kBK * 2];
 
   const int l = xcd_remap(blockIdx.x, gridDim.x);
   const int mt_g = l / p.ntn, nt = l - mt_g * p.ntn;
@@ -210,70 +298,47 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GroupedArgs p
     if (p.tile_start[mid] <= mt_g) lo = mid; else hi = mid;
   }
   const int e = lo;
-  const int row0 = p.offsets[e] + (mt_g - p.tile_start[e]) * BM;
-  const int rows_valid = min(BM, p.offsets[e + 1] - row0);
+  const int e0 = p.offsets[e];
+  const int ne = p.offsets[e + 1] - e0;
+  const int m0 = (mt_g - p.tile_start[e]) * BM;  // first row of the tile within the expert
+  const int rows_valid = min(BM, ne - m0);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+
+  KStager<BM> sa;
+  sa.init(make_rsrc(p.A + size_t(e0) * p.lda, uint32_t(ne) * p.lda * 2),
+          [&](int r) { return r < rows_valid ? (m0 + r) * p.lda * 2 : -1; }, wave, lane);
   const uint16_t* Be = p.B + size_t(e) * p.bstride;
-
-  KRows<BM> ga;
-  ga.init([&](int r) -> const uint16_t* {
-    return r < rows_valid ? p.A + size_t(row0 + r) * p.lda : nullptr;
-  });
-  KRows<BN> gbk;
-  MNRows<BN, false> gbm;
-  auto bk_ptr = [&](int k) -> const uint16_t* { return Be + size_t(k) * p.ldb + nt * BN; };
-  auto no_scale = [](int) { return 1.f; };
-  if constexpr (B_MN) {
-    gbm.init();
-  } else {
-    gbk.init([&](int n) -> const uint16_t* {
-      int row;
-      if constexpr (EPI == EPI_SWIGLU) {
-        const int w = n / WN, rem = n % WN;
-        const int half = rem / (WN / 2), c = rem % (WN / 2);
-        row = half * p.F + nt * (BN / 2) + w * (WN / 2) + c;
-      } else {
-        row = nt * BN + n;
-      }
-      return Be + size_t(row) * p.ldb;
-    });
-  }
-
+  const uint32_t bbytes = uint32_t(p.brows) * p.ldb * 2;
   f32x16 acc[WMT][WNT];
-#pragma unroll
-  for (int i = 0; i < WMT; ++i)
-#pragma unroll
-    for (int j = 0; j < WNT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
+  zero<BM, BN>(acc);
   const int ktiles = p.K / kBK;
-  constexpr int kStage = (BM + BN) * kBK;
-  ga.load(0);
-  if constexpr (B_MN) gbm.load(bk_ptr, no_scale, 0); else gbk.load(0);
-  ga.store(smem);
-  if constexpr (B_MN) gbm.store(smem + BM * kBK); else gbk.store(smem + BM * kBK);
-  __syncthreads();
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < ktiles;
-    if (more) {
-      ga.load((kt + 1) * kBK);
-      if constexpr (B_MN) gbm.load(bk_ptr, no_scale, (kt + 1) * kBK); else gbk.load((kt + 1) * kBK);
-    }
-    uint16_t* sc = smem + cur * kStage;
-    uint16_t* sn = smem + (cur ^ 1) * kStage;
-    mma_step<WMT, WNT>(sc, sc + BM * kBK, wm * WM, wn * WN, lane, acc);
-    if (more) {
-      ga.store(sn);
-      if constexpr (B_MN) gbm.store(sn + BM * kBK); else gbk.store(sn + BM * kBK);
-    }
-    __syncthreads();
+  if constexpr (B_T) {
+    TStager<BN> sb;
+    sb.init(make_rsrc(Be + nt * BN, bbytes - nt * BN * 2), p.ldb * 2, wave, lane);
+    mainloop<BM, BN, STAGES, false, true>(smem, sa, sb, ktiles, acc, wave, lane);
+  } else {
+    KStager<BN> sb;
+    sb.init(make_rsrc(Be, bbytes),
+            [&](int n) {
+              int row;
+              if constexpr (EPI == EPI_SWIGLU) {
+                const int w = n / WN, rem = n % WN;
+                const int half = rem / (WN / 2), c = rem % (WN / 2);
+                row = half * p.F + nt * (BN / 2) + w * (WN / 2) + c;
+              } else {
+                row = nt * BN + n;
+              }
+              return row * p.ldb * 2;
+            },
+            wave, lane);
+    mainloop<BM, BN, STAGES, false, false>(smem, sa, sb, ktiles, acc, wave, lane);
   }
 
   const int col = lane & 31;
+  const size_t grow0 = size_t(e0) + m0;
   if constexpr (EPI == EPI_STORE) {
 #pragma unroll
     for (int i = 0; i < WMT; ++i)
@@ -281,7 +346,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GroupedArgs p
       for (int r = 0; r < 16; ++r) {
         const int m = wm * WM + i * 32 + acc_row(r, lane);
         if (m < rows_valid) {
-          uint16_t* o = p.out + size_t(row0 + m) * p.ldo + nt * BN + wn * WN + col;
+          uint16_t* o = p.out + (grow0 + m) * p.ldo + nt * BN + wn * WN + col;
 #pragma unroll
           for (int j = 0; j < WNT; ++j) o[j * 32] = f2bf(acc[i][j][r]);
         }
@@ -294,7 +359,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GroupedArgs p
       for (int r = 0; r < 16; ++r) {
         const int m = wm * WM + i * 32 + acc_row(r, lane);
         if (m < rows_valid) {
-          const size_t row = size_t(row0 + m);
+          const size_t row = grow0 + m;
 #pragma unroll
           for (int j = 0; j < WNT / 2; ++j) {
             const int f = nt * (BN / 2) + wn * (WN / 2) + j * 32 + col;
@@ -306,34 +371,26 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GroupedArgs p
           }
         }
       }
-  } else {  // EPI_DSWIGLU
+  } else {  // EPI_DSWIGLU: acc holds dA = w * W2^T dy for the tile's F-columns
     const int F = p.F;
 #pragma unroll
     for (int i = 0; i < WMT; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = wm * WM + i * 32 + acc_row(r, lane);
-        float psum = 0.f;
         if (m < rows_valid) {
-          const size_t row = size_t(row0 + m);
-          const float w = p.wperm[row];
+          const size_t row = grow0 + m;
 #pragma unroll
           for (int j = 0; j < WNT; ++j) {
             const int f = nt * BN + wn * WN + j * 32 + col;
-            const float G = acc[i][j][r];
-            psum += G * bf2f(p.asave[row * F + f]);
+            const float dA = acc[i][j][r];
             const float g = bf2f(p.hsave[row * 2 * F + f]);
             const float u = bf2f(p.hsave[row * 2 * F + F + f]);
             const float s = 1.f / (1.f + __expf(-g));
-            const float dA = w * G;
             p.out[row * 2 * F + f] = f2bf(dA * u * s * (1.f + g * (1.f - s)));
             p.out[row * 2 * F + F + f] = f2bf(dA * g * s);
           }
         }
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) psum += __shfl_xor(psum, off, 64);
-        if (col == 0 && m < rows_valid)
-          p.part[size_t(row0 + m) * p.pstride + nt * 2 + wn] = psum;
       }
   }
 }
@@ -341,18 +398,15 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GroupedArgs p
 struct WgradArgs {
   const int32_t* offsets;  // [E+1]
   int E, M, N, tm, tn;
-  const uint16_t* A;       // [rows, lda]: element (m, k) of expert e at A[(off_e + k)*lda + m]
-  int lda;
-  const uint16_t* B;       // [rows, ldb]: element (n, k) at B[(off_e + k)*ldb + n]
-  int ldb;
-  const float* kscale;     // per permuted row, multiplies A (SCALED only)
+  const uint16_t* A;       // [rows, M]: element (m, k) of expert e at A[(off_e + k)*M + m]
+  const uint16_t* B;       // [rows, N]: element (n, k) at B[(off_e + k)*N + n]
   void* C;                 // [E, M, N] bf16 or fp32
 };
 
-template <int BM, int BN, bool SCALED, bool OUT_F32>
+template <int BM, int BN, int STAGES, bool OUT_F32>
 __global__ void __launch_bounds__(kThreads, 1) wgrad_gemm_kernel(WgradArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2, WMT = WM / 32, WNT = WN / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * kBK];
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * (BM + BN) * kBK * 2];
 
   const int l = xcd_remap(blockIdx.x, gridDim.x);
   const int per = p.tm * p.tn;
@@ -361,54 +415,22 @@ __global__ void __launch_bounds__(kThreads, 1) wgrad_gemm_kernel(WgradArgs p) {
   const int off = p.offsets[e];
   const int ne = p.offsets[e + 1] - off;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  MNRows<BM, SCALED> ga;
-  MNRows<BN, false> gb;
-  ga.init();
-  gb.init();
-  auto a_ptr = [&](int k) -> const uint16_t* {
-    return k < ne ? p.A + size_t(off + k) * p.lda + mt * BM : nullptr;
-  };
-  auto a_scale = [&](int k) -> float { return p.kscale[off + k]; };
-  auto b_ptr = [&](int k) -> const uint16_t* {
-    return k < ne ? p.B + size_t(off + k) * p.ldb + nt * BN : nullptr;
-  };
-  auto no_scale = [](int) { return 1.f; };
-
   f32x16 acc[WMT][WNT];
-#pragma unroll
-  for (int i = 0; i < WMT; ++i)
-#pragma unroll
-    for (int j = 0; j < WNT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
+  zero<BM, BN>(acc);
   const int ktiles = (ne + kBK - 1) / kBK;
   if (ktiles > 0) {
-    constexpr int kStage = (BM + BN) * kBK;
-    ga.load(a_ptr, a_scale, 0);
-    gb.load(b_ptr, no_scale, 0);
-    ga.store(smem);
-    gb.store(smem + BM * kBK);
-    __syncthreads();
-    for (int kt = 0; kt < ktiles; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < ktiles;
-      if (more) {
-        ga.load(a_ptr, a_scale, (kt + 1) * kBK);
-        gb.load(b_ptr, no_scale, (kt + 1) * kBK);
-      }
-      uint16_t* sc = smem + cur * kStage;
-      uint16_t* sn = smem + (cur ^ 1) * kStage;
-      mma_step<WMT, WNT>(sc, sc + BM * kBK, wm * WM, wn * WN, lane, acc);
-      if (more) {
-        ga.store(sn);
-        gb.store(sn + BM * kBK);
-      }
-      __syncthreads();
-    }
+    TStager<BM> sa;
+    TStager<BN> sb;
+    // tokens past the expert's last row fall outside the resources and read as zeros
+    sa.init(make_rsrc(p.A + size_t(off) * p.M + mt * BM, uint32_t(ne) * p.M * 2 - mt * BM * 2),
+            p.M * 2, wave, lane);
+    sb.init(make_rsrc(p.B + size_t(off) * p.N + nt * BN, uint32_t(ne) * p.N * 2 - nt * BN * 2),
+            p.N * 2, wave, lane);
+    mainloop<BM, BN, STAGES, true, true>(smem, sa, sb, ktiles, acc, wave, lane);
   }
 
   const int col = lane & 31;
@@ -438,7 +460,7 @@ inline int max_mtiles(const moe_desc& d, int bm) {
 
 inline int tile_index(int bm) { return bm == 64 ? 0 : (bm == 128 ? 1 : 2); }
 
-template <int BM, int BN, bool B_MN, int EPI>
+template <int BM, int BN, int STAGES, bool B_T, int EPI>
 int run_grouped(const moe_desc& d, const Layout& L, GroupedArgs a, const char* name,
                 char* scratch, hipStream_t s) {
   a.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
@@ -447,12 +469,12 @@ int run_grouped(const moe_desc& d, const Layout& L, GroupedArgs a, const char* n
   const long long grid = (long long)max_mtiles(d, BM) * a.ntn;
   if (grid <= 0) return MOE_OK;
   prof_begin(name, s);
-  grouped_gemm_kernel<BM, BN, B_MN, EPI><<<unsigned(grid), kThreads, 0, s>>>(a);
+  grouped_gemm_kernel<BM, BN, STAGES, B_T, EPI><<<unsigned(grid), kThreads, 0, s>>>(a);
   prof_end(s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-template <int BM, int BN, bool SCALED, bool OUT_F32>
+template <int BM, int BN, int STAGES, bool OUT_F32>
 int run_wgrad(const moe_desc& d, const Layout& L, WgradArgs a, const char* name, char* scratch,
               hipStream_t s) {
   a.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
@@ -461,19 +483,38 @@ int run_wgrad(const moe_desc& d, const Layout& L, WgradArgs a, const char* name,
   a.tn = a.N / BN;
   const long long grid = (long long)d.E * a.tm * a.tn;
   prof_begin(name, s);
-  wgrad_gemm_kernel<BM, BN, SCALED, OUT_F32><<<unsigned(grid), kThreads, 0, s>>>(a);
+  wgrad_gemm_kernel<BM, BN, STAGES, OUT_F32><<<unsigned(grid), kThreads, 0, s>>>(a);
   prof_end(s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-template <bool SCALED, bool OUT_F32>
+// Token-grouped GEMM with the widest n-tile dividing N.
+template <bool B_T, int EPI>
+int run_grouped_any(const moe_desc& d, const Layout& L, GroupedArgs a, int N, const char* name,
+                    char* scratch, hipStream_t s) {
+  if (N % 256 == 0) {
+    a.ntn = N / 256;
+    return run_grouped<128, 256, 3, B_T, EPI>(d, L, a, name, scratch, s);
+  }
+  if (N % 128 == 0) {
+    a.ntn = N / 128;
+    return run_grouped<128, 128, 4, B_T, EPI>(d, L, a, name, scratch, s);
+  }
+  if constexpr (EPI != EPI_SWIGLU) {
+    a.ntn = N / 64;
+    return run_grouped<128, 64, 4, B_T, EPI>(d, L, a, name, scratch, s);
+  }
+  return MOE_EUNSUPPORTED;
+}
+
+template <bool OUT_F32>
 int run_wgrad_any(const moe_desc& d, const Layout& L, WgradArgs a, const char* name,
                   char* scratch, hipStream_t s) {
-  const bool m128 = a.M % 128 == 0, n128 = a.N % 128 == 0;
-  if (m128 && n128) return run_wgrad<128, 128, SCALED, OUT_F32>(d, L, a, name, scratch, s);
-  if (m128) return run_wgrad<128, 64, SCALED, OUT_F32>(d, L, a, name, scratch, s);
-  if (n128) return run_wgrad<64, 128, SCALED, OUT_F32>(d, L, a, name, scratch, s);
-  return run_wgrad<64, 64, SCALED, OUT_F32>(d, L, a, name, scratch, s);
+  if (a.M % 256 == 0 && a.N % 128 == 0) return run_wgrad<256, 128, 3, OUT_F32>(d, L, a, name, scratch, s);
+  if (a.M % 128 == 0 && a.N % 128 == 0) return run_wgrad<128, 128, 4, OUT_F32>(d, L, a, name, scratch, s);
+  if (a.M % 128 == 0) return run_wgrad<128, 64, 4, OUT_F32>(d, L, a, name, scratch, s);
+  if (a.N % 128 == 0) return run_wgrad<64, 128, 4, OUT_F32>(d, L, a, name, scratch, s);
+  return run_wgrad<64, 64, 4, OUT_F32>(d, L, a, name, scratch, s);
 }
 
 }  // namespace
@@ -482,117 +523,82 @@ int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, con
                      char* scratch, hipStream_t s) {
   const int D = d.D, F = d.F;
   int rc;
-  {  // expert linear 1 with SwiGLU epilogue: H, A
+  {  // expert linear 1 with SwiGLU epilogue: H, A.  W1[e] is [2F, D].
     GroupedArgs a{};
     a.K = D;
     a.F = F;
     a.A = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
     a.lda = D;
     a.B = w1;
-    a.ldb = D;
     a.bstride = int64_t(2) * F * D;
+    a.ldb = D;
+    a.brows = 2 * F;
     a.out = reinterpret_cast<uint16_t*>(scratch + L.h);
     a.out2 = reinterpret_cast<uint16_t*>(scratch + L.a);
-    if (F % 128 == 0) {
-      a.ntn = 2 * F / 256;
-      rc = run_grouped<128, 256, false, EPI_SWIGLU>(d, L, a, "gemm_w1_swiglu", scratch, s);
-    } else {
-      a.ntn = 2 * F / 128;
-      rc = run_grouped<128, 128, false, EPI_SWIGLU>(d, L, a, "gemm_w1_swiglu", scratch, s);
-    }
+    rc = run_grouped_any<false, EPI_SWIGLU>(d, L, a, 2 * F, "gemm_w1_swiglu", scratch, s);
     if (rc) return rc;
   }
-  {  // expert linear 2: O
+  {  // expert linear 2: O.  W2[e] is [D, F].
     GroupedArgs a{};
     a.K = F;
     a.F = F;
     a.A = reinterpret_cast<const uint16_t*>(scratch + L.a);
     a.lda = F;
     a.B = w2;
-    a.ldb = F;
     a.bstride = int64_t(D) * F;
+    a.ldb = F;
+    a.brows = D;
     a.out = reinterpret_cast<uint16_t*>(scratch + L.o);
     a.ldo = D;
-    if (D % 256 == 0) {
-      a.ntn = D / 256;
-      rc = run_grouped<128, 256, false, EPI_STORE>(d, L, a, "gemm_w2", scratch, s);
-    } else if (D % 128 == 0) {
-      a.ntn = D / 128;
-      rc = run_grouped<128, 128, false, EPI_STORE>(d, L, a, "gemm_w2", scratch, s);
-    } else {
-      a.ntn = D / 64;
-      rc = run_grouped<128, 64, false, EPI_STORE>(d, L, a, "gemm_w2", scratch, s);
-    }
+    rc = run_grouped_any<false, EPI_STORE>(d, L, a, D, "gemm_w2", scratch, s);
     if (rc) return rc;
   }
   return MOE_OK;
 }
 
 int launch_bwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
-                     void* dw1, void* dw2, bool dw_f32, int* nparts, char* scratch,
-                     hipStream_t s) {
+                     void* dw1, void* dw2, bool dw_f32, char* scratch, hipStream_t s) {
   const int D = d.D, F = d.F;
   int rc;
-  {  // W2 dgrad with SwiGLU-backward, routing weight and partial <dy, o> in the epilogue
+  {  // W2 dgrad (dA = dYw W2[e], W2[e] is [D, F] = [K, N]) with SwiGLU-backward epilogue
     GroupedArgs a{};
     a.K = D;
     a.F = F;
     a.A = reinterpret_cast<const uint16_t*>(scratch + L.dyperm);
     a.lda = D;
     a.B = w2;
-    a.ldb = F;
     a.bstride = int64_t(D) * F;
+    a.ldb = F;
+    a.brows = D;
     a.out = reinterpret_cast<uint16_t*>(scratch + L.dh);
     a.hsave = reinterpret_cast<const uint16_t*>(scratch + L.h);
-    a.asave = reinterpret_cast<const uint16_t*>(scratch + L.a);
-    a.wperm = reinterpret_cast<const float*>(scratch + L.wperm);
-    a.part = reinterpret_cast<float*>(scratch + L.dprob_part);
-    a.pstride = L.nparts_max;
-    if (F % 128 == 0) {
-      a.ntn = F / 128;
-      rc = run_grouped<128, 128, true, EPI_DSWIGLU>(d, L, a, "gemm_w2_dgrad_dswiglu", scratch, s);
-    } else {
-      a.ntn = F / 64;
-      rc = run_grouped<128, 64, true, EPI_DSWIGLU>(d, L, a, "gemm_w2_dgrad_dswiglu", scratch, s);
-    }
-    *nparts = 2 * a.ntn;
+    rc = run_grouped_any<true, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s);
     if (rc) return rc;
   }
-  {  // W2 wgrad: dW2[e] = sum_r (w_r dY_perm[r]) A[r]^T
+  {  // W2 wgrad: dW2[e] = sum_r dYw_perm[r] A[r]^T
     WgradArgs a{};
     a.M = D;
     a.N = F;
     a.A = reinterpret_cast<const uint16_t*>(scratch + L.dyperm);
-    a.lda = D;
-    a.kscale = reinterpret_cast<const float*>(scratch + L.wperm);
     a.B = reinterpret_cast<const uint16_t*>(scratch + L.a);
-    a.ldb = F;
     a.C = dw2;
-    rc = dw_f32 ? run_wgrad_any<true, true>(d, L, a, "gemm_w2_wgrad", scratch, s)
-                : run_wgrad_any<true, false>(d, L, a, "gemm_w2_wgrad", scratch, s);
+    rc = dw_f32 ? run_wgrad_any<true>(d, L, a, "gemm_w2_wgrad", scratch, s)
+                : run_wgrad_any<false>(d, L, a, "gemm_w2_wgrad", scratch, s);
     if (rc) return rc;
   }
-  {  // W1 dgrad: dX_perm = dH W1[e]
+  {  // W1 dgrad: dX_perm = dH W1[e], W1[e] is [2F, D] = [K, N]
     GroupedArgs a{};
     a.K = 2 * F;
     a.F = F;
     a.A = reinterpret_cast<const uint16_t*>(scratch + L.dh);
     a.lda = 2 * F;
     a.B = w1;
-    a.ldb = D;
     a.bstride = int64_t(2) * F * D;
+    a.ldb = D;
+    a.brows = 2 * F;
     a.out = reinterpret_cast<uint16_t*>(scratch + L.dxperm);
     a.ldo = D;
-    if (D % 256 == 0) {
-      a.ntn = D / 256;
-      rc = run_grouped<128, 256, true, EPI_STORE>(d, L, a, "gemm_w1_dgrad", scratch, s);
-    } else if (D % 128 == 0) {
-      a.ntn = D / 128;
-      rc = run_grouped<128, 128, true, EPI_STORE>(d, L, a, "gemm_w1_dgrad", scratch, s);
-    } else {
-      a.ntn = D / 64;
-      rc = run_grouped<128, 64, true, EPI_STORE>(d, L, a, "gemm_w1_dgrad", scratch, s);
-    }
+    rc = run_grouped_any<true, EPI_STORE>(d, L, a, D, "gemm_w1_dgrad", scratch, s);
     if (rc) return rc;
   }
   {  // W1 wgrad: dW1[e] = sum_r dH[r] x_perm[r]^T
@@ -600,12 +606,10 @@ int launch_bwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, con
     a.M = 2 * F;
     a.N = D;
     a.A = reinterpret_cast<const uint16_t*>(scratch + L.dh);
-    a.lda = 2 * F;
     a.B = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
-    a.ldb = D;
     a.C = dw1;
-    rc = dw_f32 ? run_wgrad_any<false, true>(d, L, a, "gemm_w1_wgrad", scratch, s)
-                : run_wgrad_any<false, false>(d, L, a, "gemm_w1_wgrad", scratch, s);
+    rc = dw_f32 ? run_wgrad_any<true>(d, L, a, "gemm_w1_wgrad", scratch, s)
+                : run_wgrad_any<false>(d, L, a, "gemm_w1_wgrad", scratch, s);
     if (rc) return rc;
   }
   return MOE_OK;

@@ -1,4 +1,4 @@
-// HBM-bound row movers of the MoE layer: dispatch, combine, un-permute.
+// HBM-bound row movers of the MoE layer: dispatch, combine, combine-backward, un-permute.
 //
 // Dispatch copies every token row to the expert-contiguous row of each of its
 // routed pairs (the single-GPU form of the pages' expert-parallel dispatch,
@@ -110,19 +110,63 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_kernel(
   }
 }
 
-// dtopk_w[p] = sum of the per-tile partial <dy, o> sums of pair p, in tile order.
-__global__ void dprob_reduce_kernel(const int32_t* __restrict__ pos,
-                                    const float* __restrict__ part, int nparts, int stride,
-                                    int N, float* __restrict__ dprob) {
-  const int p = blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= N) return;
-  const int q = pos[p];
-  float s = 0.f;
-  if (q >= 0) {
-    const float* r = part + size_t(q) * stride;
-    for (int j = 0; j < nparts; ++j) s += r[j];
+// Combine-backward: for each routed pair p of token t (row q = pos[p]),
+//   dYw_perm[q] = w_p * dy_t          (rounded once to bf16)
+//   dtopk_w[p]  = <dy_t, O[q]>         (fp32, the routing-weight gradient)
+// One wavefront owns one token: its dy row stays in registers while the K
+// expert-output rows are streamed and dotted against it.  CPL = 16-byte chunks
+// per lane (D / 512, at least 1).
+template <bool IN_F32, int CPL>
+__global__ void __launch_bounds__(kRowThreads) dispatch_dy_kernel(
+    const void* __restrict__ dy, int T, int K, int D, const int32_t* __restrict__ pos,
+    const float* __restrict__ topk_w, const uint16_t* __restrict__ O, uint16_t* __restrict__ dst,
+    float* __restrict__ dprob) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int chunks = D / 8;
+  float v[CPL][8];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    if (c < chunks) {
+      if constexpr (IN_F32) {
+        const float4* src = reinterpret_cast<const float4*>(dy) + (size_t(t) * D + c * 8) / 4;
+        const float4 a = src[0], b = src[1];
+        v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
+        v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
+      } else {
+        unpack8(reinterpret_cast<const uint4*>(dy)[(size_t(t) * D) / 8 + c], v[j]);
+      }
+    }
   }
-  dprob[p] = s;
+  for (int k = 0; k < K; ++k) {
+    const int p = t * K + k;
+    const int q = pos[p];
+    if (q < 0) {
+      if (lane == 0) dprob[p] = 0.f;
+      continue;
+    }
+    const float w = topk_w[p];
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (c < chunks) {
+        float o[8], sc[8];
+        unpack8(reinterpret_cast<const uint4*>(O)[(size_t(q) * D) / 8 + c], o);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          dot = __builtin_fmaf(v[j][i], o[i], dot);
+          sc[i] = w * v[j][i];
+        }
+        reinterpret_cast<uint4*>(dst)[(size_t(q) * D) / 8 + c] = pack8(sc);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+    if (lane == 0) dprob[p] = dot;
+  }
 }
 
 __global__ void convert_bf16_kernel(const float* __restrict__ in, uint16_t* __restrict__ out,
@@ -176,8 +220,8 @@ int launch_combine(const moe_desc& d, const Layout& L, const float* topk_w, void
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32, float* dtopk_w,
-                     int nparts, const char* scratch, hipStream_t s) {
+int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
+                     const char* scratch, hipStream_t s) {
   const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
   const auto* rows = reinterpret_cast<const uint16_t*>(scratch + L.dxperm);
   prof_begin("unpermute", s);
@@ -188,12 +232,36 @@ int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
     gather_reduce_kernel<false, false><<<row_blocks(d), kRowThreads, 0, s>>>(rows, pos, nullptr,
                                                                               d.T, d.K, d.D, dx);
   prof_end(s);
-  const int N = d.T * d.K;
-  prof_begin("dprob_reduce", s);
-  dprob_reduce_kernel<<<(N + 255) / 256, 256, 0, s>>>(
-      pos, reinterpret_cast<const float*>(scratch + L.dprob_part), nparts, L.nparts_max, N,
-      dtopk_w);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+template <bool IN_F32>
+static int dispatch_dy_cpl(const moe_desc& d, const void* dy, const int32_t* pos,
+                           const float* topk_w, const uint16_t* o, uint16_t* dst, float* dprob,
+                           hipStream_t s) {
+  const unsigned blocks = unsigned((d.T + kRowThreads / 64 - 1) / (kRowThreads / 64));
+  const int cpl = (d.D / 8 + 63) / 64;
+#define MOE_DY(C) dispatch_dy_kernel<IN_F32, C><<<blocks, kRowThreads, 0, s>>>(dy, d.T, d.K, d.D, pos, topk_w, o, dst, dprob)
+  if (cpl <= 1) MOE_DY(1);
+  else if (cpl <= 2) MOE_DY(2);
+  else if (cpl <= 4) MOE_DY(4);
+  else if (cpl <= 8) MOE_DY(8);
+  else if (cpl <= 16) MOE_DY(16);
+  else return MOE_EUNSUPPORTED;
+#undef MOE_DY
+  return MOE_OK;
+}
+
+int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool in_f32,
+                       const float* topk_w, float* dtopk_w, char* scratch, hipStream_t s) {
+  const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
+  const auto* o = reinterpret_cast<const uint16_t*>(scratch + L.o);
+  auto* dst = reinterpret_cast<uint16_t*>(scratch + L.dyperm);
+  prof_begin("dispatch_dy", s);
+  const int rc = in_f32 ? dispatch_dy_cpl<true>(d, dy, pos, topk_w, o, dst, dtopk_w, s)
+                        : dispatch_dy_cpl<false>(d, dy, pos, topk_w, o, dst, dtopk_w, s);
   prof_end(s);
+  if (rc) return rc;
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
