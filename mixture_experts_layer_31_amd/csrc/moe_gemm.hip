@@ -49,7 +49,6 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kBK = 64;  // contraction step (bf16 elements)
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -110,9 +109,9 @@ __device__ __forceinline__ int swz_t(int krow) {
 // of the wave's DMA instructions, and how far that offset moves per k-step.
 
 // k-contiguous operand, R rows: row r of the tile is at rowoff(r) bytes.
-template <int R>
+template <int R, int WAVES>
 struct KStager {
-  static constexpr int NI = R / 32;  // DMA instructions per wave per k-step (1 KB each)
+  static constexpr int NI = R / (8 * WAVES);  // DMA instructions per wave per k-step (1 KB each)
   i32x4 rsrc;
   int vb[NI];
   template <class RowOff>
@@ -137,9 +136,9 @@ struct KStager {
 // k-outer operand, R output columns: k-row k of the tile is at k * ld_bytes,
 // column c at c * 2 (relative to the resource base, which includes the tile's
 // first column).
-template <int R>
+template <int R, int WAVES>
 struct TStager {
-  static constexpr int NI = R / 32;
+  static constexpr int NI = R / (8 * WAVES);
   static constexpr int LPR = R / 8;      // lanes per k-row
   static constexpr int RPI = 64 / LPR;   // k-rows per DMA instruction
   i32x4 rsrc;
@@ -186,14 +185,19 @@ __device__ __forceinline__ bf16x8 frag_t(const char* tile, int col0, int kk, int
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// The pipelined main loop: acc += A_tile * B_tile^T over ktiles k-steps.
-template <int BM, int BN, int STAGES, bool A_T, bool B_T, class SA, class SB>
+// The pipelined main loop: acc += A_tile * B_tile^T over ktiles k-steps.  The
+// workgroup's WGM x WGN waves each own a (BM/WGM) x (BN/WGN) sub-tile.  The
+// MFMA takes the B fragment as its first operand, so an accumulator register
+// block holds C^T: lane l owns output row (l & 31) of a 32 x 32 block and four
+// consecutive output columns per group of four registers (see acc_col).
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_T, bool B_T, class SA, class SB>
 __device__ __forceinline__ void mainloop(char* smem, const SA& sa, const SB& sb, int ktiles,
-                                         f32x16 (&acc)[BM / 64][BN / 64], int wave, int lane) {
-  constexpr int WM = BM / 2, WN = BN / 2, WMT = WM / 32, WNT = WN / 32;
+                                         f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int wave,
+                                         int lane) {
+  constexpr int WM = BM / WGM, WN = BN / WGN, WMT = WM / 32, WNT = WN / 32;
   constexpr int A_BYTES = BM * kBK * 2, STAGE = (BM + BN) * kBK * 2;
-  constexpr int NI = BM / 32 + BN / 32;  // DMA instructions per wave per stage
-  const int wm = wave >> 1, wn = wave & 1;
+  constexpr int NI = SA::NI + SB::NI;  // DMA instructions per wave per stage
+  const int wm = wave / WGN, wn = wave % WGN;
   const uint32_t base = lds_addr(smem);
 
 #pragma unroll
@@ -225,43 +229,60 @@ __device__ __forceinline__ void mainloop(char* smem, const SA& sa, const SB& sb,
     }
     const char* ta = smem + (kt % STAGES) * STAGE;
     const char* tb = ta + A_BYTES;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8 af[WMT], bfr[WNT];
+    // fragments of sub-step kk+1 are read while the MFMAs of sub-step kk run
+    bf16x8 af[2][WMT], bfr[2][WNT];
+    auto load = [&](int kk, bf16x8 (&a)[WMT], bf16x8 (&b)[WNT]) {
 #pragma unroll
       for (int i = 0; i < WMT; ++i) {
         const int r0 = wm * WM + i * 32;
-        if constexpr (A_T) af[i] = frag_t<BM>(ta, r0, kk, lane);
-        else af[i] = frag_k(ta, r0 + (lane & 31), kk, lane);
+        if constexpr (A_T) a[i] = frag_t<BM>(ta, r0, kk, lane);
+        else a[i] = frag_k(ta, r0 + (lane & 31), kk, lane);
       }
 #pragma unroll
       for (int j = 0; j < WNT; ++j) {
         const int c0 = wn * WN + j * 32;
-        if constexpr (B_T) bfr[j] = frag_t<BN>(tb, c0, kk, lane);
-        else bfr[j] = frag_k(tb, c0 + (lane & 31), kk, lane);
+        if constexpr (B_T) b[j] = frag_t<BN>(tb, c0, kk, lane);
+        else b[j] = frag_k(tb, c0 + (lane & 31), kk, lane);
       }
+    };
+    load(0, af[0], bfr[0]);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      if (kk + 1 < kBK / 16) load(kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < WMT; ++i)
 #pragma unroll
         for (int j = 0; j < WNT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk & 1][j], af[kk & 1][i],
+                                                              acc[i][j], 0, 0, 0);
     }
   }
 }
 
-// Row (within a 32x32 block) of accumulator element r.
-__device__ __forceinline__ int acc_row(int r, int lane) {
-  return (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
-}
+// Column (within a 32x32 block) of accumulator register 4*g (the first of four
+// consecutive columns); the row is lane & 31.
+__device__ __forceinline__ int acc_col(int g, int lane) { return 8 * g + 4 * (lane >> 5); }
 
-template <int BM, int BN>
-__device__ __forceinline__ void zero(f32x16 (&acc)[BM / 64][BN / 64]) {
+template <int A, int B>
+__device__ __forceinline__ void zero(f32x16 (&acc)[A][B]) {
 #pragma unroll
-  for (int i = 0; i < BM / 64; ++i)
+  for (int i = 0; i < A; ++i)
 #pragma unroll
-    for (int j = 0; j < BN / 64; ++j)
+    for (int j = 0; j < B; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  return make_uint2(uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16),
+                    uint32_t(f2bf(c)) | (uint32_t(f2bf(d)) << 16));
+}
+
+__device__ __forceinline__ void unpack4(uint2 v, float (&f)[4]) {
+  f[0] = __uint_as_float(v.x << 16);
+  f[1] = __uint_as_float(v.x & 0xffff0000u);
+  f[2] = __uint_as_float(v.y << 16);
+  f[3] = __uint_as_float(v.y & 0xffff0000u);
 }
 
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
@@ -282,12 +303,23 @@ struct GroupedArgs {
   const uint16_t* hsave;      // DSWIGLU: H [rows, 2F]
 };
 
+// Tile shape of a GEMM kernel: BM x BN outputs per workgroup of WGM x WGN waves.
+template <int BM_, int BN_, int WGM_, int WGN_, int STAGES_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, STAGES = STAGES_;
+  static constexpr int WAVES = WGM * WGN, THREADS = 64 * WAVES;
+  static constexpr int WM = BM / WGM, WN = BN / WGN, WMT = WM / 32, WNT = WN / 32;
+  static constexpr int LDS = STAGES * (BM + BN) * kBK * 2;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32x32");
+};
+
 // B_T = false: B[e] is [N, K] (row n holds the k-run); true: B[e] is [K, N].
-template <int BM, int BN, int STAGES, bool B_T, int EPI>
-__global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GroupedArgs p) {
-  constexpr int WM = BM / 2, WN = BN / 2, WMT = WM / 32, WNT = WN / 32;
+template <class TL, bool B_T, int EPI>
+__global__ void __launch_bounds__(TL::THREADS, 1) grouped_gemm_kernel(GroupedArgs p) {
+  constexpr int BM = TL::BM, BN = TL::BN, WM = TL::WM, WN = TL::WN;
+  constexpr int WMT = TL::WMT, WNT = TL::WNT, WAVES = TL::WAVES;
   static_assert(EPI != EPI_SWIGLU || (WNT % 2 == 0 && !B_T), "SwiGLU pairs gate/up sub-tiles");
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * (BM + BN) * kBK * 2];
+  __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
 
   const int l = xcd_remap(blockIdx.x, gridDim.x);
   const int mt_g = l / p.ntn, nt = l - mt_g * p.ntn;
@@ -305,22 +337,22 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GroupedArgs p
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
 
-  KStager<BM> sa;
+  KStager<BM, WAVES> sa;
   sa.init(make_rsrc(p.A + size_t(e0) * p.lda, uint32_t(ne) * p.lda * 2),
           [&](int r) { return r < rows_valid ? (m0 + r) * p.lda * 2 : -1; }, wave, lane);
   const uint16_t* Be = p.B + size_t(e) * p.bstride;
   const uint32_t bbytes = uint32_t(p.brows) * p.ldb * 2;
   f32x16 acc[WMT][WNT];
-  zero<BM, BN>(acc);
+  zero(acc);
   const int ktiles = p.K / kBK;
   if constexpr (B_T) {
-    TStager<BN> sb;
+    TStager<BN, WAVES> sb;
     sb.init(make_rsrc(Be + nt * BN, bbytes - nt * BN * 2), p.ldb * 2, wave, lane);
-    mainloop<BM, BN, STAGES, false, true>(smem, sa, sb, ktiles, acc, wave, lane);
+    mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, true>(smem, sa, sb, ktiles, acc, wave, lane);
   } else {
-    KStager<BN> sb;
+    KStager<BN, WAVES> sb;
     sb.init(make_rsrc(Be, bbytes),
             [&](int n) {
               int row;
@@ -334,64 +366,66 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GroupedArgs p
               return row * p.ldb * 2;
             },
             wave, lane);
-    mainloop<BM, BN, STAGES, false, false>(smem, sa, sb, ktiles, acc, wave, lane);
+    mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, false>(smem, sa, sb, ktiles, acc, wave, lane);
   }
 
-  const int col = lane & 31;
+  // Epilogue: lane owns row (lane & 31) of each 32-row block and, per group g
+  // of four registers, four consecutive columns starting at acc_col(g).
   const size_t grow0 = size_t(e0) + m0;
-  if constexpr (EPI == EPI_STORE) {
 #pragma unroll
-    for (int i = 0; i < WMT; ++i)
+  for (int i = 0; i < WMT; ++i) {
+    const int m = wm * WM + i * 32 + (lane & 31);
+    if (m >= rows_valid) continue;
+    const size_t row = grow0 + m;
+    if constexpr (EPI == EPI_STORE) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = wm * WM + i * 32 + acc_row(r, lane);
-        if (m < rows_valid) {
-          uint16_t* o = p.out + (grow0 + m) * p.ldo + nt * BN + wn * WN + col;
+      for (int j = 0; j < WNT; ++j)
 #pragma unroll
-          for (int j = 0; j < WNT; ++j) o[j * 32] = f2bf(acc[i][j][r]);
+        for (int g = 0; g < 4; ++g) {
+          const int n = nt * BN + wn * WN + j * 32 + acc_col(g, lane);
+          const f32x16& a = acc[i][j];
+          *reinterpret_cast<uint2*>(p.out + row * p.ldo + n) =
+              pack4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
         }
-      }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    const int F = p.F;
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      const int F = p.F;
 #pragma unroll
-    for (int i = 0; i < WMT; ++i)
+      for (int j = 0; j < WNT / 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = wm * WM + i * 32 + acc_row(r, lane);
-        if (m < rows_valid) {
-          const size_t row = grow0 + m;
+        for (int g = 0; g < 4; ++g) {
+          const int f = nt * (BN / 2) + wn * (WN / 2) + j * 32 + acc_col(g, lane);
+          float gv[4], uv[4], av[4];
 #pragma unroll
-          for (int j = 0; j < WNT / 2; ++j) {
-            const int f = nt * (BN / 2) + wn * (WN / 2) + j * 32 + col;
-            const float g = acc[i][j][r], u = acc[i][j + WNT / 2][r];
-            const float a = g / (1.f + __expf(-g)) * u;
-            p.out[row * 2 * F + f] = f2bf(g);
-            p.out[row * 2 * F + F + f] = f2bf(u);
-            p.out2[row * F + f] = f2bf(a);
+          for (int c = 0; c < 4; ++c) {
+            gv[c] = acc[i][j][4 * g + c];
+            uv[c] = acc[i][j + WNT / 2][4 * g + c];
+            av[c] = gv[c] / (1.f + __expf(-gv[c])) * uv[c];
           }
+          *reinterpret_cast<uint2*>(p.out + row * 2 * F + f) = pack4(gv[0], gv[1], gv[2], gv[3]);
+          *reinterpret_cast<uint2*>(p.out + row * 2 * F + F + f) = pack4(uv[0], uv[1], uv[2], uv[3]);
+          *reinterpret_cast<uint2*>(p.out2 + row * F + f) = pack4(av[0], av[1], av[2], av[3]);
         }
-      }
-  } else {  // EPI_DSWIGLU: acc holds dA = w * W2^T dy for the tile's F-columns
-    const int F = p.F;
+    } else {  // EPI_DSWIGLU: acc holds dA = (w dy) W2[e] for the tile's F-columns
+      const int F = p.F;
 #pragma unroll
-    for (int i = 0; i < WMT; ++i)
+      for (int j = 0; j < WNT; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = wm * WM + i * 32 + acc_row(r, lane);
-        if (m < rows_valid) {
-          const size_t row = grow0 + m;
+        for (int g = 0; g < 4; ++g) {
+          const int f = nt * BN + wn * WN + j * 32 + acc_col(g, lane);
+          float gv[4], uv[4], dg[4], du[4];
+          unpack4(*reinterpret_cast<const uint2*>(p.hsave + row * 2 * F + f), gv);
+          unpack4(*reinterpret_cast<const uint2*>(p.hsave + row * 2 * F + F + f), uv);
 #pragma unroll
-          for (int j = 0; j < WNT; ++j) {
-            const int f = nt * BN + wn * WN + j * 32 + col;
-            const float dA = acc[i][j][r];
-            const float g = bf2f(p.hsave[row * 2 * F + f]);
-            const float u = bf2f(p.hsave[row * 2 * F + F + f]);
-            const float s = 1.f / (1.f + __expf(-g));
-            p.out[row * 2 * F + f] = f2bf(dA * u * s * (1.f + g * (1.f - s)));
-            p.out[row * 2 * F + F + f] = f2bf(dA * g * s);
+          for (int c = 0; c < 4; ++c) {
+            const float dA = acc[i][j][4 * g + c];
+            const float sg = 1.f / (1.f + __expf(-gv[c]));
+            dg[c] = dA * uv[c] * sg * (1.f + gv[c] * (1.f - sg));
+            du[c] = dA * gv[c] * sg;
           }
+          *reinterpret_cast<uint2*>(p.out + row * 2 * F + f) = pack4(dg[0], dg[1], dg[2], dg[3]);
+          *reinterpret_cast<uint2*>(p.out + row * 2 * F + F + f) = pack4(du[0], du[1], du[2], du[3]);
         }
-      }
+    }
   }
 }
 
@@ -403,10 +437,11 @@ struct WgradArgs {
   void* C;                 // [E, M, N] bf16 or fp32
 };
 
-template <int BM, int BN, int STAGES, bool OUT_F32>
-__global__ void __launch_bounds__(kThreads, 1) wgrad_gemm_kernel(WgradArgs p) {
-  constexpr int WM = BM / 2, WN = BN / 2, WMT = WM / 32, WNT = WN / 32;
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * (BM + BN) * kBK * 2];
+template <class TL, bool OUT_F32>
+__global__ void __launch_bounds__(TL::THREADS, 1) wgrad_gemm_kernel(WgradArgs p) {
+  constexpr int BM = TL::BM, BN = TL::BN, WM = TL::WM, WN = TL::WN;
+  constexpr int WMT = TL::WMT, WNT = TL::WNT, WAVES = TL::WAVES;
+  __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
 
   const int l = xcd_remap(blockIdx.x, gridDim.x);
   const int per = p.tm * p.tn;
@@ -417,37 +452,40 @@ __global__ void __launch_bounds__(kThreads, 1) wgrad_gemm_kernel(WgradArgs p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
 
   f32x16 acc[WMT][WNT];
-  zero<BM, BN>(acc);
+  zero(acc);
   const int ktiles = (ne + kBK - 1) / kBK;
   if (ktiles > 0) {
-    TStager<BM> sa;
-    TStager<BN> sb;
+    TStager<BM, WAVES> sa;
+    TStager<BN, WAVES> sb;
     // tokens past the expert's last row fall outside the resources and read as zeros
     sa.init(make_rsrc(p.A + size_t(off) * p.M + mt * BM, uint32_t(ne) * p.M * 2 - mt * BM * 2),
             p.M * 2, wave, lane);
     sb.init(make_rsrc(p.B + size_t(off) * p.N + nt * BN, uint32_t(ne) * p.N * 2 - nt * BN * 2),
             p.N * 2, wave, lane);
-    mainloop<BM, BN, STAGES, true, true>(smem, sa, sb, ktiles, acc, wave, lane);
+    mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, true, true>(smem, sa, sb, ktiles, acc, wave, lane);
   }
 
-  const int col = lane & 31;
 #pragma unroll
-  for (int i = 0; i < WMT; ++i)
+  for (int i = 0; i < WMT; ++i) {
+    const int m = mt * BM + wm * WM + i * 32 + (lane & 31);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = mt * BM + wm * WM + i * 32 + acc_row(r, lane);
-      const size_t o = (size_t(e) * p.M + m) * p.N + nt * BN + wn * WN + col;
+    for (int j = 0; j < WNT; ++j)
 #pragma unroll
-      for (int j = 0; j < WNT; ++j) {
+      for (int g = 0; g < 4; ++g) {
+        const int n = nt * BN + wn * WN + j * 32 + acc_col(g, lane);
+        const size_t o = (size_t(e) * p.M + m) * p.N + n;
+        const f32x16& a = acc[i][j];
         if constexpr (OUT_F32)
-          reinterpret_cast<float*>(p.C)[o + j * 32] = acc[i][j][r];
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + o) =
+              make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
         else
-          reinterpret_cast<uint16_t*>(p.C)[o + j * 32] = f2bf(acc[i][j][r]);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + o) =
+              pack4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
       }
-    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -460,61 +498,61 @@ inline int max_mtiles(const moe_desc& d, int bm) {
 
 inline int tile_index(int bm) { return bm == 64 ? 0 : (bm == 128 ? 1 : 2); }
 
-template <int BM, int BN, int STAGES, bool B_T, int EPI>
-int run_grouped(const moe_desc& d, const Layout& L, GroupedArgs a, const char* name,
+template <class TL, bool B_T, int EPI>
+int run_grouped(const moe_desc& d, const Layout& L, GroupedArgs a, int N, const char* name,
                 char* scratch, hipStream_t s) {
   a.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
-  a.tile_start = reinterpret_cast<const int32_t*>(scratch + L.tiles[tile_index(BM)]);
+  a.tile_start = reinterpret_cast<const int32_t*>(scratch + L.tiles[tile_index(TL::BM)]);
   a.E = d.E;
-  const long long grid = (long long)max_mtiles(d, BM) * a.ntn;
+  a.ntn = N / TL::BN;
+  const long long grid = (long long)max_mtiles(d, TL::BM) * a.ntn;
   if (grid <= 0) return MOE_OK;
   prof_begin(name, s);
-  grouped_gemm_kernel<BM, BN, STAGES, B_T, EPI><<<unsigned(grid), kThreads, 0, s>>>(a);
+  grouped_gemm_kernel<TL, B_T, EPI><<<unsigned(grid), TL::THREADS, 0, s>>>(a);
   prof_end(s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-template <int BM, int BN, int STAGES, bool OUT_F32>
+template <class TL, bool OUT_F32>
 int run_wgrad(const moe_desc& d, const Layout& L, WgradArgs a, const char* name, char* scratch,
               hipStream_t s) {
   a.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
   a.E = d.E;
-  a.tm = a.M / BM;
-  a.tn = a.N / BN;
+  a.tm = a.M / TL::BM;
+  a.tn = a.N / TL::BN;
   const long long grid = (long long)d.E * a.tm * a.tn;
   prof_begin(name, s);
-  wgrad_gemm_kernel<BM, BN, STAGES, OUT_F32><<<unsigned(grid), kThreads, 0, s>>>(a);
+  wgrad_gemm_kernel<TL, OUT_F32><<<unsigned(grid), TL::THREADS, 0, s>>>(a);
   prof_end(s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-// Token-grouped GEMM with the widest n-tile dividing N.
+// Tile choices (measured on the 30B/235B shapes); narrower fallbacks keep small
+// shapes (D or F not a multiple of 256) working.
+using TileBig = Tile<256, 256, 2, 4, 2>;
+using TileMid = Tile<128, 128, 2, 2, 4>;
+using TileNarrow = Tile<128, 64, 2, 2, 4>;
+using TileWg128x64 = Tile<128, 64, 2, 2, 4>;
+using TileWg64x128 = Tile<64, 128, 2, 2, 4>;
+using TileWg64x64 = Tile<64, 64, 2, 2, 4>;
+
 template <bool B_T, int EPI>
 int run_grouped_any(const moe_desc& d, const Layout& L, GroupedArgs a, int N, const char* name,
                     char* scratch, hipStream_t s) {
-  if (N % 256 == 0) {
-    a.ntn = N / 256;
-    return run_grouped<128, 256, 3, B_T, EPI>(d, L, a, name, scratch, s);
-  }
-  if (N % 128 == 0) {
-    a.ntn = N / 128;
-    return run_grouped<128, 128, 4, B_T, EPI>(d, L, a, name, scratch, s);
-  }
-  if constexpr (EPI != EPI_SWIGLU) {
-    a.ntn = N / 64;
-    return run_grouped<128, 64, 4, B_T, EPI>(d, L, a, name, scratch, s);
-  }
+  if (N % 256 == 0) return run_grouped<TileBig, B_T, EPI>(d, L, a, N, name, scratch, s);
+  if (N % 128 == 0) return run_grouped<TileMid, B_T, EPI>(d, L, a, N, name, scratch, s);
+  if constexpr (EPI != EPI_SWIGLU) return run_grouped<TileNarrow, B_T, EPI>(d, L, a, N, name, scratch, s);
   return MOE_EUNSUPPORTED;
 }
 
 template <bool OUT_F32>
 int run_wgrad_any(const moe_desc& d, const Layout& L, WgradArgs a, const char* name,
                   char* scratch, hipStream_t s) {
-  if (a.M % 256 == 0 && a.N % 128 == 0) return run_wgrad<256, 128, 3, OUT_F32>(d, L, a, name, scratch, s);
-  if (a.M % 128 == 0 && a.N % 128 == 0) return run_wgrad<128, 128, 4, OUT_F32>(d, L, a, name, scratch, s);
-  if (a.M % 128 == 0) return run_wgrad<128, 64, 4, OUT_F32>(d, L, a, name, scratch, s);
-  if (a.N % 128 == 0) return run_wgrad<64, 128, 4, OUT_F32>(d, L, a, name, scratch, s);
-  return run_wgrad<64, 64, 4, OUT_F32>(d, L, a, name, scratch, s);
+  if (a.M % 256 == 0 && a.N % 256 == 0) return run_wgrad<TileBig, OUT_F32>(d, L, a, name, scratch, s);
+  if (a.M % 128 == 0 && a.N % 128 == 0) return run_wgrad<TileMid, OUT_F32>(d, L, a, name, scratch, s);
+  if (a.M % 128 == 0) return run_wgrad<TileWg128x64, OUT_F32>(d, L, a, name, scratch, s);
+  if (a.N % 128 == 0) return run_wgrad<TileWg64x128, OUT_F32>(d, L, a, name, scratch, s);
+  return run_wgrad<TileWg64x64, OUT_F32>(d, L, a, name, scratch, s);
 }
 
 }  // namespace
