@@ -47,6 +47,24 @@ def row_bytes(cfg, b=2) -> dict:
             "unpermute": N * D * b + T * D * b + N * 4}
 
 
+def measured_traffic(cfg, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary (already scaled by the copy-kernel calibration), or None when there is no
+    summary for this workload or the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}_bf16.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for p in rec["sources"]:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    if h.hexdigest()[:16] != rec["source_sha256_16"] or kernel not in rec["kernels"]:
+        return None
+    k = rec["kernels"][kernel]
+    return k["fetch_bytes"] + k["write_bytes"]
+
+
 def cpu_baseline(cfg, inp, budget_s: float) -> dict:
     """Times the CPU oracle's fwd+bwd on the first S tokens of the workload."""
     import numpy as np
@@ -83,6 +101,8 @@ def main():
     ap.add_argument("--config", default="30b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (reference for HBM counters)")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without per-kernel events (no roofline entry)")
     args = ap.parse_args()
@@ -104,6 +124,14 @@ def main():
     L = Layer(cfg, inp, device="cuda:0")
     L.prepare()
     stream = torch.cuda.current_stream()
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         L.fwd()
@@ -163,7 +191,8 @@ def main():
         avg = kernels[dom][0] / kernels[dom][1]
         ach = gf[dom] / (avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                "traffic": measured_traffic(cfg, dom),
                 "flops_per_launch": gf[dom], "avg_ms": round(avg, 4)}
 
     out = {

@@ -147,12 +147,14 @@ int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const flo
             void* scratch, size_t scratch_bytes, void* stream);
 
 /* Backward pass of the forward that last used `scratch` (which must be passed
- * back unmodified, with the same descriptor, topk_w and weights).  Runs the
- * combine-backward dispatch of dy, the W2 dgrad with SwiGLU-backward, the
- * routing-weight product and the partial <dy, o> sums fused into its epilogue,
- * the W2 and W1 wgrads (per-expert reductions over that expert's tokens, no
- * atomics), the W1 dgrad and the un-permute reduction of dx (fp32 sum over k).
- * Overwrites dx, dw1, dw2 (experts with no tokens get zeros) and dtopk_w. */
+ * back unmodified, with the same descriptor, topk_w and weights).  Steps:
+ * combine-backward (dispatch of w * dy to the expert rows, and the
+ * routing-weight gradient dtopk_w[t,k] = <dy_t, o_{t,k}> from the saved expert
+ * output, an fp32 dot product), the W2 dgrad with SwiGLU-backward fused into
+ * its epilogue, the W2 and W1 wgrads (per-expert reductions over that expert's
+ * tokens, no atomics), the W1 dgrad and the un-permute reduction of dx (fp32
+ * sum over k).  Overwrites dx, dw1, dw2 (experts with no tokens get zeros) and
+ * dtopk_w (0 for a slot whose expert id is out of range). */
 int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w,
             const void* w1, const void* w2, const void* wprep,
             void* dx, void* dw1, void* dw2, float* dtopk_w,
