@@ -22,9 +22,16 @@
  *   MOE_FP32            x y dy dx w1 w2 dw1 dw2 fp32; fp32 GEMMs       (not built yet)
  *   MOE_FP32_BF16GEMM   fp32 storage, GEMM operands rounded to bf16, fp32 accumulate
  *   MOE_BF16            bf16 storage (raw 16-bit bfloat16), bf16 GEMMs, fp32 accumulate
- *   MOE_FP8_BWD         bf16 storage, bf16 forward, blockwise-FP8 backward GEMMs (not built yet)
- *   MOE_MXFP8           bf16 storage, MXFP8 GEMMs forward and backward           (not built yet)
- *   MOE_FP8             bf16 storage, blockwise-FP8 GEMMs forward and backward   (not built yet)
+ *   MOE_FP8_BWD         bf16 storage, bf16 forward, blockwise-FP8 backward GEMMs
+ *   MOE_MXFP8           bf16 storage, MXFP8 GEMMs forward and backward
+ *   MOE_FP8             bf16 storage, blockwise-FP8 GEMMs forward and backward
+ * FP8 operands are OCP e4m3 (round to nearest even, saturating at 448).  Blockwise
+ * FP8: one fp32 scale amax/448 per 1x128 activation tile along the GEMM's
+ * contraction axis (for the weight gradients: 128 consecutive tokens of one
+ * expert, from the expert's first token) and per 128x128 weight block.  MXFP8:
+ * one e8m0 scale 2^X per 32 contraction elements of every operand, X the
+ * smallest integer with amax <= 448 * 2^X.  The FP8 modes need D % 256 == 0 and
+ * F % 256 == 0, and `wprep` (filled by moe_prepare_weights) in moe_fwd/moe_bwd.
  * Intermediates are kept in bf16 (fp32 accumulators, rounded once when stored);
  * SwiGLU, its backward, the routing-weight products and all row sums are fp32.
  *
@@ -95,12 +102,14 @@ typedef struct moe_desc {
  * tensors, "How does the fused kernel work?").  Its layout is private. */
 size_t moe_scratch_bytes(const moe_desc* d);
 
-/* Size in bytes of the prepared-weight buffer (quantised weight copies for the
- * FP8 modes; 0 for the bf16/fp32 modes, where `wprep` may be NULL). */
+/* Size in bytes of the prepared-weight buffer: quantised weight copies for the
+ * FP8 modes (each weight in the orientation of each GEMM that reads it), bf16
+ * copies for MOE_FP32_BF16GEMM, 0 for MOE_BF16 (where `wprep` may be NULL). */
 size_t moe_wprep_bytes(const moe_desc* d);
 
-/* Fill `wprep` from w1/w2 for the FP8 modes (a no-op returning MOE_OK for the
- * other modes).  Must be called again whenever the weights change. */
+/* Fill `wprep` from w1/w2 (bf16 in the FP8 modes, fp32 in MOE_FP32_BF16GEMM; a
+ * no-op returning MOE_OK in MOE_BF16).  Must be called again whenever the
+ * weights change. */
 int moe_prepare_weights(const moe_desc* d, const void* w1, const void* w2,
                         void* wprep, size_t wprep_bytes, void* stream);
 
@@ -128,10 +137,21 @@ int moe_routing_view(const moe_desc* d, const void* scratch, size_t scratch_byte
  *   MOE_VIEW_DYPERM [T*K, D]   dispatched upstream gradient (unweighted)
  *   MOE_VIEW_DH     [T*K, 2F]  gradient wrt linear-1 output
  *   MOE_VIEW_DXPERM [T*K, D]   gradient wrt dispatched tokens
- *   MOE_VIEW_WPERM  [T*K] fp32 routing weight of each routed pair */
+ *   MOE_VIEW_WPERM  [T*K] fp32 routing weight of each routed pair
+ * FP8 modes only (contents of the last GEMM that used them; C = max(D, 2F),
+ * Npad = 128 * floor((T*K + 127*E) / 128)):
+ *   MOE_VIEW_Q_ROWS        [T*K, C] e4m3 codes of an activation quantised along its rows
+ *   MOE_VIEW_Q_ROWS_SCALE  [C/128, T*K] 4-byte scale entries
+ *   MOE_VIEW_Q_TOK_A/B     [C, Npad] e4m3 codes quantised along tokens (expert e's
+ *                          tokens in columns 128*p[e] .. , p = prefix of ceil(count/128))
+ *   MOE_VIEW_Q_TOK_A/B_SCALE [Npad/128, C] 4-byte scale entries
+ * A 4-byte entry is an fp32 scale (blockwise) or four e8m0 bytes, one per 32
+ * consecutive contraction elements of the 128-element step (MXFP8). */
 enum moe_view {
   MOE_VIEW_XPERM = 0, MOE_VIEW_H = 1, MOE_VIEW_A = 2, MOE_VIEW_O = 3,
-  MOE_VIEW_DYPERM = 4, MOE_VIEW_DH = 5, MOE_VIEW_DXPERM = 6, MOE_VIEW_WPERM = 7
+  MOE_VIEW_DYPERM = 4, MOE_VIEW_DH = 5, MOE_VIEW_DXPERM = 6, MOE_VIEW_WPERM = 7,
+  MOE_VIEW_Q_ROWS = 8, MOE_VIEW_Q_ROWS_SCALE = 9, MOE_VIEW_Q_TOK_A = 10,
+  MOE_VIEW_Q_TOK_A_SCALE = 11, MOE_VIEW_Q_TOK_B = 12, MOE_VIEW_Q_TOK_B_SCALE = 13
 };
 int moe_scratch_view(const moe_desc* d, const void* scratch, size_t scratch_bytes,
                      int which, void** ptr, size_t* bytes);

@@ -26,9 +26,10 @@ int check_desc(const moe_desc* d) {
   return MOE_OK;
 }
 
-// Modes whose kernels exist in this build.
+// Modes whose kernels exist in this build, and their shape requirements.
 int check_built(const moe_desc* d) {
-  if (d->mode != MOE_FP32_BF16GEMM && d->mode != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (d->mode == MOE_FP32) return MOE_EUNSUPPORTED;
+  if (fp8_mode(d->mode) && (d->D % 256 != 0 || d->F % 256 != 0)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -42,7 +43,7 @@ int check_scratch(const moe_desc* d, const void* scratch, size_t bytes) {
 size_t wprep_size(const moe_desc& d) {
   if (d.mode == MOE_FP32_BF16GEMM)  // bf16 copies of W1 and W2
     return align256(size_t(d.E) * 2 * d.F * d.D * 2) + align256(size_t(d.E) * d.D * d.F * 2);
-  return 0;
+  return fp8_wprep_bytes(d);  // quantised copies (0 for the bf16 mode)
 }
 
 // ---- profiler state (only touched while enabled) ----
@@ -77,6 +78,7 @@ hipEvent_t prof_event() {
 // Weight pointers the GEMMs read (bf16): the caller's, or the bf16 copies in wprep.
 int gemm_weights(const moe_desc& d, const void* w1, const void* w2, const void* wprep,
                  const uint16_t** g1, const uint16_t** g2) {
+  if (fp8_mode(d.mode) && wprep == nullptr) return MOE_EINVAL;
   if (d.mode == MOE_FP32_BF16GEMM) {
     if (wprep == nullptr) return MOE_EINVAL;
     const char* base = static_cast<const char*>(wprep);
@@ -152,6 +154,9 @@ int moe_prepare_weights(const moe_desc* d, const void* w1, const void* w2, void*
   if (!aligned(w1, 16) || !aligned(w2, 16) || !aligned(wprep, 16)) return MOE_EALIGN;
   if (wprep_bytes < need) return MOE_ESCRATCH;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fp8_mode(d->mode))
+    return fp8_prepare_weights(*d, static_cast<const uint16_t*>(w1),
+                               static_cast<const uint16_t*>(w2), static_cast<char*>(wprep), s);
   const size_t n1 = size_t(d->E) * 2 * d->F * d->D, n2 = size_t(d->E) * d->D * d->F;
   char* base = static_cast<char*>(wprep);
   rc = launch_convert_bf16(static_cast<const float*>(w1), reinterpret_cast<uint16_t*>(base), n1, s);
@@ -203,7 +208,11 @@ int moe_scratch_view(const moe_desc* d, const void* scratch, size_t scratch_byte
     case MOE_VIEW_DH: off = L.dh; n = N * 2 * d->F * ab; break;
     case MOE_VIEW_DXPERM: off = L.dxperm; n = N * d->D * ab; break;
     case MOE_VIEW_WPERM: off = L.wperm; n = N * 4; break;
-    default: return MOE_EINVAL;
+    default:
+      if (!fp8_mode(d->mode) || which < MOE_VIEW_Q_ROWS || which > MOE_VIEW_Q_TOK_B_SCALE)
+        return MOE_EINVAL;
+      return fp8_view(*d, L, const_cast<char*>(static_cast<const char*>(scratch)), which, ptr,
+                      bytes ? bytes : &n);
   }
   *ptr = const_cast<char*>(static_cast<const char*>(scratch)) + off;
   if (bytes) *bytes = n;
@@ -229,7 +238,11 @@ int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const flo
   const bool io_f32 = d->mode == MOE_FP32_BF16GEMM;
   if ((rc = launch_route(*d, L, topk_idx, sc, s))) return rc;
   if ((rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s))) return rc;
-  if ((rc = launch_fwd_gemms(*d, L, g1, g2, sc, s))) return rc;
+  if (fp8_mode(d->mode) && d->mode != MOE_FP8_BWD)
+    rc = fp8_fwd_gemms(*d, L, static_cast<const char*>(wprep), sc, s);
+  else
+    rc = launch_fwd_gemms(*d, L, g1, g2, sc, s);
+  if (rc) return rc;
   return launch_combine(*d, L, topk_w, y, io_f32, sc, s);
 }
 
@@ -252,7 +265,11 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool io_f32 = d->mode == MOE_FP32_BF16GEMM;
   if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s))) return rc;
-  if ((rc = launch_bwd_gemms(*d, L, g1, g2, dw1, dw2, io_f32, sc, s))) return rc;
+  if (fp8_mode(d->mode))
+    rc = fp8_bwd_gemms(*d, L, static_cast<const char*>(wprep), dw1, dw2, sc, s);
+  else
+    rc = launch_bwd_gemms(*d, L, g1, g2, dw1, dw2, io_f32, sc, s);
+  if (rc) return rc;
   return launch_unpermute(*d, L, dx, io_f32, sc, s);
 }
 

@@ -24,12 +24,18 @@ constexpr int kRouteThreads = 256;
 // starts on a 256-byte boundary.  The layout depends only on the descriptor.
 struct Layout {
   size_t err, counts, offsets, tiles[3], chunk_cnt, pos, src, wperm;
-  size_t xperm, h, a, o, dyperm, dh, dxperm, queue, total;
+  size_t xperm, h, a, o, dyperm, dh, dxperm, fp8, queue, total;
   int nchunks;      // routing chunks
   int act_bytes;    // bytes per intermediate element
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// FP8 modes (moe_fp8.hip): extra scratch for quantised operands, prepared
+// weight sizes, weight preparation and the quantised GEMM sequences.
+bool fp8_mode(int mode);
+size_t fp8_scratch_bytes(const moe_desc& d);
+size_t fp8_wprep_bytes(const moe_desc& d);
 
 inline Layout make_layout(const moe_desc& d) {
   Layout L{};
@@ -54,6 +60,7 @@ inline Layout make_layout(const moe_desc& d) {
   L.dyperm = take(N * D * ab);
   L.dh = take(N * 2 * F * ab);
   L.dxperm = take(N * D * ab);
+  L.fp8 = take(fp8_scratch_bytes(d));
   L.queue = take(4096);
   L.total = o;
   return L;
@@ -88,6 +95,14 @@ int launch_convert_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s)
 // Grouped GEMMs (MFMA).  See moe_gemm.hip.
 int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
                      char* scratch, hipStream_t s);
+int fp8_prepare_weights(const moe_desc& d, const uint16_t* w1, const uint16_t* w2, char* wprep,
+                        hipStream_t s);
+int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,
+                  hipStream_t s);
+int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* dw1, void* dw2,
+                  char* scratch, hipStream_t s);
+int fp8_view(const moe_desc& d, const Layout& L, char* scratch, int which, void** ptr,
+             size_t* bytes);
 int launch_bwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
                      void* dw1, void* dw2, bool dw_f32, char* scratch, hipStream_t s);
 

@@ -1,0 +1,823 @@
+// FP8 paths of the MoE layer: blockwise FP8 (fp32 scale per 1x128 activation
+// tile and per 128x128 weight block) and MXFP8 (e8m0 scale per 32 contiguous
+// contraction elements), both on OCP e4m3 elements.  The pages list BF16, MXFP8
+// and blockwise FP8, plus an fp8_bwd mode with a BF16 forward and an FP8
+// backward (Prime Mega MoE news item, "How does the fused kernel work?" and
+// "How do developers use it?").
+//
+// Every FP8 GEMM here is "NT": both operands are stored with the contraction
+// index contiguous, so both are staged with the same direct-to-LDS loads and
+// 128-byte swizzled rows as the bf16 kernels (a 128-element fp8 k-step is 128
+// bytes, like a 64-element bf16 step).  The quantisers produce operands in that
+// orientation: activations whose contraction runs along the row are quantised
+// in place; operands contracted over tokens (the weight-gradient GEMMs) and
+// weights contracted over their first dimension are transposed while being
+// quantised (the quantiser stages a 128 x 128 tile in LDS anyway).
+//
+// Scales are stored as 4-byte entries in [k-step][row] order: an fp32 block
+// scale, or the four e8m0 bytes of the step's four 32-element groups.  For one
+// k-step the entries of a tile's rows are contiguous, so they travel to LDS in
+// the same pipeline as the data (one 1 KB direct-to-LDS load per operand).
+//
+// MXFP8 uses v_mfma_scale_f32_32x32x64_f8f6f4 with the scales applied by the
+// matrix core.  Its operand layout (established with an in-bounds probe): lane
+// l holds row (l & 31); bytes 0-15 are k = 16*(l>>5) + 0..15 and bytes 16-31 are
+// k = 32 + 16*(l>>5) + 0..15 of the 64-wide step; the scale register of lane l
+// covers row (l & 31), k-group (l >> 5), and op_sel picks its byte.
+// Blockwise FP8 runs the same instruction with unit scales over each 128-wide
+// k-step and promotes the partial sum in fp32: acc += partial * s_a * s_b.
+#include <type_traits>
+
+#include "moe_gemm_common.h"
+
+namespace moe {
+namespace {
+
+using namespace gemm;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// Encodings.
+
+// OCP e4m3 code of a finite float: nearest value, ties to even mantissa,
+// magnitudes >= 448 saturate to 448.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t s = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t c;
+  if (!(a < 448.f)) {
+    c = 0x7Eu;
+  } else if (a < 0.015625f) {  // subnormal range: multiples of 2^-9
+    c = uint32_t(__builtin_rintf(a * 512.f));
+  } else {
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);  // round to 3 mantissa bits, ties to even
+    c = (u >> 20) - (120u << 3);       // rebias the exponent 127 -> 7
+  }
+  return s | c;
+}
+
+// Smallest X in [-127, 127] with amax <= 448 * 2^X (0 for amax == 0).
+__device__ __forceinline__ int e8m0_exponent(float amax) {
+  if (amax == 0.f) return 0;
+  int e;
+  const float m = frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1); 448 = 0.875 * 2^9
+  int X = (m <= 0.875f) ? e - 9 : e - 8;
+  return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+enum QMode { Q_BLOCK_ROW = 0, Q_MX = 1, Q_BLOCK_TILE = 2 };
+
+// ---------------------------------------------------------------------------
+// Tile quantiser: one workgroup quantises a 128 (r) x 128 (c) bf16 tile.
+//   TRANS = false: the contraction runs along c; codes out[r][c], scale entry
+//                  [c-step][r].
+//   TRANS = true:  the contraction runs along r; codes out[c][r-slot], scale
+//                  entry [r-step][c].
+// Rows come either from token segments (expert e's permuted rows, the r-steps
+// of the padded token axis listed by the routing step's 128-row tile prefix) or
+// from a uniform batch of matrices (weights: batch = expert).
+struct QArgs {
+  const uint16_t* in;   // bf16 rows of length cols
+  int64_t in_bstride;   // elements between batches
+  int cols;             // input row length (multiple of 128)
+  int rows;             // uniform mode: rows per batch (multiple of 128)
+  uint8_t* out;
+  int64_t out_ld, out_bstride;
+  uint32_t* sc;
+  int64_t sc_ld, sc_bstride;
+  const int32_t* offsets;  // segmented mode: [E+1] expert row offsets
+  const int32_t* tstart;   // segmented mode: [E+1] prefix of ceil(count / 128)
+  int E;
+  int ntr;                 // uniform mode: r-steps per batch
+  int total_rows;          // rows of the input (bounds for untransposed activations)
+};
+
+template <bool TRANS, int MODE, bool SEG>
+__global__ void __launch_bounds__(256) quant_tile_kernel(QArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * 128];
+  __shared__ float red[4];
+  const int ctiles = p.cols / 128;
+  const int rt = blockIdx.x / ctiles, ct = blockIdx.x % ctiles;
+  int b = 0, r0, valid, slot0;  // slot0: first output r-slot (TRANS) of this tile
+  if constexpr (SEG) {
+    if (rt >= p.tstart[p.E]) return;
+    int lo = 0, hi = p.E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.tstart[mid] <= rt) lo = mid; else hi = mid;
+    }
+    r0 = p.offsets[lo] + (rt - p.tstart[lo]) * 128;
+    valid = min(128, p.offsets[lo + 1] - r0);
+    slot0 = rt * 128;
+  } else {
+    b = rt / p.ntr;
+    r0 = (rt % p.ntr) * 128;
+    valid = min(128, p.total_rows - r0);
+    slot0 = r0;
+  }
+  const int c0 = ct * 128;
+  const uint16_t* in = p.in + b * p.in_bstride;
+  const int t = threadIdx.x, lane = t & 63;
+
+  // Each thread owns 64 consecutive values along the contraction axis:
+  // index q (row for !TRANS, column for TRANS) = t / 2, half h = t & 1.
+  const int q = t >> 1, h = t & 1;
+  float v[64];
+  if constexpr (TRANS) {
+    for (int i = t; i < 128 * 16; i += 256) {  // 16 chunks of 8 per row
+      const int r = i >> 4, ch = i & 15;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (r < valid) val = *reinterpret_cast<const uint4*>(in + size_t(r0 + r) * p.cols + c0 + ch * 8);
+      *reinterpret_cast<uint4*>(&tile[r * 128 + ch * 8]) = val;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 64; ++i) v[i] = bf2f(tile[(h * 64 + i) * 128 + q]);
+  } else {
+    const bool ok = q < valid;
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (ok) val = *reinterpret_cast<const uint4*>(in + size_t(r0 + q) * p.cols + c0 + h * 64 + ch * 8);
+      const uint32_t w[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[ch * 8 + 2 * k] = __uint_as_float(w[k] << 16);
+        v[ch * 8 + 2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      }
+    }
+  }
+
+  float am[2] = {0.f, 0.f};  // amax of the two 32-groups
+#pragma unroll
+  for (int i = 0; i < 64; ++i) am[i >> 5] = fmaxf(am[i >> 5], fabsf(v[i]));
+
+  float mul[2];
+  uint32_t entry = 0;  // scale entry written by h == 0
+  if constexpr (MODE == Q_MX) {
+    const int X0 = e8m0_exponent(am[0]), X1 = e8m0_exponent(am[1]);
+    mul[0] = ldexpf(1.f, -X0);
+    mul[1] = ldexpf(1.f, -X1);
+    const uint32_t mine = uint32_t(X0 + 127) | (uint32_t(X1 + 127) << 8);
+    const uint32_t other = __shfl_xor(mine, 1, 64);
+    entry = h == 0 ? (mine | (other << 16)) : 0;
+  } else {
+    float amax = fmaxf(am[0], am[1]);
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    if constexpr (MODE == Q_BLOCK_TILE) {
+#pragma unroll
+      for (int off = 32; off >= 2; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+      if (lane == 0) red[t >> 6] = amax;
+      __syncthreads();
+      amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    }
+    const float s = amax == 0.f ? 1.f : amax / 448.f;
+    mul[0] = mul[1] = s;
+    entry = __float_as_uint(s);
+  }
+
+  uint32_t packed[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = 4 * i + k;
+      const float x = v[idx];
+      const float qv = (MODE == Q_MX) ? x * mul[idx >> 5] : x / mul[idx >> 5];
+      w |= e4m3_code(qv) << (8 * k);
+    }
+    packed[i] = w;
+  }
+  uint8_t* out = p.out + b * p.out_bstride;
+  uint32_t* sc = p.sc + b * p.sc_bstride;
+  if constexpr (TRANS) {
+    uint4* dst = reinterpret_cast<uint4*>(out + size_t(c0 + q) * p.out_ld + slot0 + h * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dst[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+    if (h == 0) sc[size_t(slot0 / 128) * p.sc_ld + c0 + q] = entry;
+  } else {
+    if (q < valid) {
+      uint4* dst = reinterpret_cast<uint4*>(out + size_t(r0 + q) * p.out_ld + c0 + h * 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dst[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+      if (h == 0) sc[size_t(ct) * p.sc_ld + r0 + q] = entry;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 GEMM.
+
+// Scale stager: one 1 KB direct-to-LDS load per k-step (256 four-byte entries
+// of consecutive rows; lane l fetches rows 4l..4l+3).
+struct ScaleStager {
+  i32x4 rsrc;
+  int vb, step;
+  bool active;
+  __device__ __forceinline__ void issue(uint32_t lds, int kt) const {
+    if (active) dma16(rsrc, lds, vb + kt * step);
+  }
+};
+
+// fp8 fragment (32 bytes: two 16-byte chunks of a 128-byte row) for sub-step kk.
+__device__ __forceinline__ i32x8 frag8(const char* tile, int row, int kk, int lane) {
+  const int h = lane >> 5;
+  const int c0 = 4 * kk + h, c1 = 4 * kk + 2 + h;
+  const i32x4 a = *reinterpret_cast<const i32x4*>(tile + row * 128 + ((c0 ^ swz_k(row)) << 4));
+  const i32x4 b = *reinterpret_cast<const i32x4*>(tile + row * 128 + ((c1 ^ swz_k(row)) << 4));
+  const i32x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return r;
+}
+
+template <int SEL>
+__device__ __forceinline__ f32x16 mfma8(i32x8 b, i32x8 a, f32x16 c, int sb, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, SEL, sb, SEL, sa);
+}
+
+template <class TL, bool MX, bool SB_COL, class SA, class SB>
+__device__ __forceinline__ void mainloop8(char* smem, const SA& sa, const SB& sb,
+                                          const ScaleStager& ssa, const ScaleStager& ssb,
+                                          int ktiles, f32x16 (&acc)[TL::WMT][TL::WNT], int wave,
+                                          int lane) {
+  constexpr int BM = TL::BM, BN = TL::BN, WM = TL::WM, WN = TL::WN;
+  constexpr int WMT = TL::WMT, WNT = TL::WNT, STAGES = TL::STAGES;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES + 2048;
+  constexpr int NI = SA::NI + SB::NI;
+  static_assert(STAGES == 2 || STAGES == 3, "two or three stages");
+  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  const uint32_t base = lds_addr(smem);
+  auto issue = [&](int s, int kt) {
+    const uint32_t st = base + s * STAGE;
+    sa.issue(st, wave, kt);
+    sb.issue(st + A_BYTES, wave, kt);
+    ssa.issue(st + A_BYTES + B_BYTES, kt);
+    ssb.issue(st + A_BYTES + B_BYTES + 1024, kt);
+  };
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < ktiles) issue(s, s);
+
+  for (int kt = 0; kt < ktiles; ++kt) {
+    if constexpr (STAGES == 3) {
+      if (kt + 1 < ktiles) {
+        if (wave < 2) wait_vmcnt<NI + 1>(); else wait_vmcnt<NI>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES - 1 < ktiles) issue((kt + STAGES - 1) % STAGES, kt + STAGES - 1);
+    const char* ta = smem + (kt % STAGES) * STAGE;
+    const char* tb = ta + A_BYTES;
+    const uint32_t* sca = reinterpret_cast<const uint32_t*>(tb + B_BYTES);
+    const uint32_t* scb = sca + 256;
+    i32x8 af[2][WMT], bfr[2][WNT];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < WMT; ++i) af[kk][i] = frag8(ta, wm * WM + i * 32 + (lane & 31), kk, lane);
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) bfr[kk][j] = frag8(tb, wn * WN + j * 32 + (lane & 31), kk, lane);
+    }
+    if constexpr (MX) {
+      const int sh = 8 * (lane >> 5);
+      int sa_w[WMT], sb_w[WNT];
+#pragma unroll
+      for (int i = 0; i < WMT; ++i) sa_w[i] = int(sca[wm * WM + i * 32 + (lane & 31)] >> sh);
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) sb_w[j] = int(scb[wn * WN + j * 32 + (lane & 31)] >> sh);
+#pragma unroll
+      for (int i = 0; i < WMT; ++i)
+#pragma unroll
+        for (int j = 0; j < WNT; ++j) {
+          acc[i][j] = mfma8<0>(bfr[0][j], af[0][i], acc[i][j], sb_w[j], sa_w[i]);
+          acc[i][j] = mfma8<2>(bfr[1][j], af[1][i], acc[i][j], sb_w[j], sa_w[i]);
+        }
+    } else {
+      float s_a[WMT];
+#pragma unroll
+      for (int i = 0; i < WMT; ++i) s_a[i] = __uint_as_float(sca[wm * WM + i * 32 + (lane & 31)]);
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) {
+        float s_b[16];
+        if constexpr (SB_COL) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 v4 = *reinterpret_cast<const float4*>(scb + wn * WN + j * 32 + acc_col(g, lane));
+            s_b[4 * g] = v4.x; s_b[4 * g + 1] = v4.y; s_b[4 * g + 2] = v4.z; s_b[4 * g + 3] = v4.w;
+          }
+        } else {
+          const float v = __uint_as_float(scb[wn * WN + j * 32]);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s_b[r] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < WMT; ++i) {
+          f32x16 part = {};
+          part = mfma8<0>(bfr[0][j], af[0][i], part, 127, 127);
+          part = mfma8<0>(bfr[1][j], af[1][i], part, 127, 127);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[r], s_a[i] * s_b[r], acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
+struct F8Args {
+  const int32_t* offsets;  // [E+1] expert row offsets
+  const int32_t* tstart;   // [E+1] m-tile prefix (token-grouped) or 128-token step prefix (wgrad)
+  int E, K, ntn;           // K: contraction of a token-grouped GEMM
+  int M, N, tm, tn;        // wgrad: dW[e] is [M, N]
+  const uint8_t* A;        // token-grouped: [rows, K] codes; wgrad: [M, lda] codes
+  int64_t lda;
+  const uint32_t* SA;      // scale entries [k-step][sa_ld]
+  int64_t sa_ld;
+  uint32_t sa_bytes;
+  const uint8_t* B;        // token-grouped: weights [E][N][K]; wgrad: [N, ldb]
+  int64_t ldb, b_bstride;
+  const uint32_t* SB;
+  int64_t sb_ld, sb_bstride;
+  uint32_t sb_bytes;
+  EpiArgs epi;
+  int F;
+  void* C;                 // wgrad output [E, M, N]
+};
+
+// Token-grouped FP8 GEMM: rows of expert e times B[e]^T ([N, K] codes).
+template <class TL, bool MX, int EPI>
+__global__ void __launch_bounds__(TL::THREADS, 1) f8_grouped_kernel(F8Args p) {
+  constexpr int BM = TL::BM, BN = TL::BN, WN = TL::WN, WAVES = TL::WAVES;
+  static_assert(EPI != EPI_SWIGLU || TL::WNT % 2 == 0, "SwiGLU pairs gate/up sub-tiles");
+  __shared__ __attribute__((aligned(1024))) char smem[TL::STAGES * ((BM + BN) * 128 + 2048)];
+  const int l = xcd_remap(blockIdx.x, gridDim.x);
+  const int mt_g = l / p.ntn, nt = l - mt_g * p.ntn;
+  if (mt_g >= p.tstart[p.E]) return;
+  int lo = 0, hi = p.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.tstart[mid] <= mt_g) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int e0 = p.offsets[e];
+  const int ne = p.offsets[e + 1] - e0;
+  const int m0 = (mt_g - p.tstart[e]) * BM;
+  const int rows_valid = min(BM, ne - m0);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+
+  KStager<BM, WAVES> sa;
+  sa.init(make_rsrc(p.A + size_t(e0) * p.K, uint32_t(ne) * p.K),
+          [&](int r) { return r < rows_valid ? (m0 + r) * p.K : -1; }, wave, lane);
+  auto brow = [&](int n) {
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int w = n / WN, rem = n % WN;
+      const int half = rem / (WN / 2), c = rem % (WN / 2);
+      return half * p.F + nt * (BN / 2) + w * (WN / 2) + c;
+    } else {
+      return nt * BN + n;
+    }
+  };
+  KStager<BN, WAVES> sb;
+  sb.init(make_rsrc(p.B + size_t(e) * p.b_bstride, uint32_t(p.N) * p.K),
+          [&](int n) { return brow(n) * p.K; }, wave, lane);
+  ScaleStager ssa{make_rsrc(p.SA, p.sa_bytes), (e0 + m0 + 4 * lane) * 4, int(p.sa_ld * 4), wave == 0};
+  ScaleStager ssb{make_rsrc(p.SB + size_t(e) * p.sb_bstride, p.sb_bytes),
+                  brow(min(4 * lane, BN - 4)) * 4, int(p.sb_ld * 4), wave == 1};
+
+  f32x16 acc[TL::WMT][TL::WNT];
+  zero(acc);
+  mainloop8<TL, MX, false>(smem, sa, sb, ssa, ssb, p.K / 128, acc, wave, lane);
+  grouped_epilogue<TL, EPI>(p.epi, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane);
+}
+
+// Per-expert FP8 weight-gradient GEMM over the expert's padded token steps.
+template <class TL, bool MX, bool OUT_F32>
+__global__ void __launch_bounds__(TL::THREADS, 1) f8_wgrad_kernel(F8Args p) {
+  constexpr int BM = TL::BM, BN = TL::BN, WAVES = TL::WAVES;
+  __shared__ __attribute__((aligned(1024))) char smem[TL::STAGES * ((BM + BN) * 128 + 2048)];
+  const int l = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = p.tm * p.tn;
+  const int e = l / per, rem = l - e * per;
+  const int mt = rem / p.tn, nt = rem - mt * p.tn;
+  const int s0 = p.tstart[e], ksteps = p.tstart[e + 1] - s0;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+  f32x16 acc[TL::WMT][TL::WNT];
+  zero(acc);
+  if (ksteps > 0) {
+    const size_t kb0 = size_t(s0) * 128;  // first padded token of the expert
+    KStager<BM, WAVES> sa;
+    sa.init(make_rsrc(p.A + size_t(mt) * BM * p.lda + kb0, uint32_t(BM - 1) * p.lda + ksteps * 128),
+            [&](int r) { return r * int(p.lda); }, wave, lane);
+    KStager<BN, WAVES> sb;
+    sb.init(make_rsrc(p.B + size_t(nt) * BN * p.ldb + kb0, uint32_t(BN - 1) * p.ldb + ksteps * 128),
+            [&](int r) { return r * int(p.ldb); }, wave, lane);
+    ScaleStager ssa{make_rsrc(p.SA, p.sa_bytes), int((size_t(s0) * p.sa_ld + mt * BM + 4 * lane) * 4),
+                    int(p.sa_ld * 4), wave == 0};
+    ScaleStager ssb{make_rsrc(p.SB, p.sb_bytes), int((size_t(s0) * p.sb_ld + nt * BN + 4 * lane) * 4),
+                    int(p.sb_ld * 4), wave == 1};
+    mainloop8<TL, MX, true>(smem, sa, sb, ssa, ssb, ksteps, acc, wave, lane);
+  }
+  wgrad_epilogue<TL, OUT_F32>(p.C, p.M, p.N, e, mt, nt, acc, wm, wn, lane);
+}
+
+}  // namespace
+}  // namespace moe
+
+// ---------------------------------------------------------------------------
+// Host side.
+namespace moe {
+namespace {
+
+using namespace gemm;
+
+using TileF8 = Tile<256, 256, 2, 4, 2>;   // MXFP8: scales applied by the matrix core
+using TileF8B = Tile<256, 128, 2, 2, 3>;  // blockwise: fp32 promotion needs more registers
+template <bool MX> using F8Tile = typename std::conditional<MX, TileF8, TileF8B>::type;
+
+inline int max_steps128(const moe_desc& d) {
+  const long long N = (long long)d.T * d.K;
+  return int((N + (long long)d.E * 127) / 128);
+}
+
+int launch_quant(bool trans, int mode, bool seg, const QArgs& a, int blocks, const char* name,
+                 hipStream_t s) {
+  if (blocks <= 0) return MOE_OK;
+  prof_begin(name, s);
+#define MOE_Q(T, M, S) quant_tile_kernel<T, M, S><<<unsigned(blocks), 256, 0, s>>>(a)
+  if (trans) {
+    if (seg) {
+      if (mode == Q_MX) MOE_Q(true, Q_MX, true); else MOE_Q(true, Q_BLOCK_ROW, true);
+    } else {
+      if (mode == Q_MX) MOE_Q(true, Q_MX, false); else MOE_Q(true, Q_BLOCK_TILE, false);
+    }
+  } else {
+    if (mode == Q_MX) MOE_Q(false, Q_MX, false);
+    else if (mode == Q_BLOCK_TILE) MOE_Q(false, Q_BLOCK_TILE, false);
+    else MOE_Q(false, Q_BLOCK_ROW, false);
+  }
+#undef MOE_Q
+  prof_end(s);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// Quantise permuted activations [N, C] along C (rows stay in place).
+int quant_rows(const moe_desc& d, const uint16_t* in, int C, bool mx, uint8_t* out, uint32_t* sc,
+               const char* name, hipStream_t s) {
+  const int N = d.T * d.K;
+  QArgs a{};
+  a.in = in;
+  a.cols = C;
+  a.out = out;
+  a.out_ld = C;
+  a.sc = sc;
+  a.sc_ld = N;
+  a.ntr = (N + 127) / 128;
+  a.total_rows = N;
+  return launch_quant(false, mx ? Q_MX : Q_BLOCK_ROW, false, a, a.ntr * (C / 128), name, s);
+}
+
+// Quantise permuted activations [N, C] along tokens within expert segments,
+// transposed to [C, Npad] (row stride npad) with scale entries [step][C].
+int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, bool mx,
+                 uint8_t* out, uint32_t* sc, const char* name, const char* scratch, hipStream_t s) {
+  QArgs a{};
+  a.in = in;
+  a.cols = C;
+  a.out = out;
+  a.out_ld = int64_t(max_steps128(d)) * 128;
+  a.sc = sc;
+  a.sc_ld = C;
+  a.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
+  a.tstart = reinterpret_cast<const int32_t*>(scratch + L.tiles[1]);
+  a.E = d.E;
+  return launch_quant(true, mx ? Q_MX : Q_BLOCK_ROW, true, a, max_steps128(d) * (C / 128), name, s);
+}
+
+// Quantise a batch of E weight matrices [R, C].  trans = false: contraction along
+// C, codes [E][R][C], entries [E][C/128][R]; trans = true: contraction along R,
+// codes [E][C][R], entries [E][R/128][C].  Blockwise mode uses 128 x 128 blocks.
+int quant_weights(const moe_desc& d, const uint16_t* w, int R, int C, bool trans, bool mx,
+                  uint8_t* out, uint32_t* sc, const char* name, hipStream_t s) {
+  QArgs a{};
+  a.in = w;
+  a.in_bstride = int64_t(R) * C;
+  a.cols = C;
+  a.rows = R;
+  a.total_rows = R;
+  a.ntr = R / 128;
+  a.out = out;
+  a.out_bstride = int64_t(R) * C;
+  if (trans) {
+    a.out_ld = R;
+    a.sc_ld = C;
+    a.sc_bstride = int64_t(R / 128) * C;
+  } else {
+    a.out_ld = C;
+    a.sc_ld = R;
+    a.sc_bstride = int64_t(C / 128) * R;
+  }
+  a.sc = sc;
+  return launch_quant(trans, mx ? Q_MX : Q_BLOCK_TILE, false, a, d.E * (R / 128) * (C / 128), name, s);
+}
+
+template <bool MX, int EPI>
+int run_f8_grouped(const moe_desc& d, const Layout& L, F8Args a, int N, const char* name,
+                   char* scratch, hipStream_t s) {
+  a.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
+  a.tstart = reinterpret_cast<const int32_t*>(scratch + L.tiles[2]);  // 256-row m-tiles
+  a.E = d.E;
+  using TL = F8Tile<MX>;
+  a.ntn = N / TL::BN;
+  a.N = N;
+  const long long Nr = (long long)d.T * d.K;
+  const long long grid = ((Nr + (long long)d.E * 255) / 256) * a.ntn;
+  prof_begin(name, s);
+  f8_grouped_kernel<TL, MX, EPI><<<unsigned(grid), TL::THREADS, 0, s>>>(a);
+  prof_end(s);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+template <bool MX>
+int run_f8_wgrad(const moe_desc& d, const Layout& L, F8Args a, const char* name, char* scratch,
+                 hipStream_t s) {
+  a.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
+  a.tstart = reinterpret_cast<const int32_t*>(scratch + L.tiles[1]);  // 128-token steps
+  a.E = d.E;
+  using TL = F8Tile<MX>;
+  a.tm = a.M / TL::BM;
+  a.tn = a.N / TL::BN;
+  const long long grid = (long long)d.E * a.tm * a.tn;
+  prof_begin(name, s);
+  f8_wgrad_kernel<TL, MX, false><<<unsigned(grid), TL::THREADS, 0, s>>>(a);
+  prof_end(s);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// Regions of the prepared-weight buffer.
+struct WLayout {
+  size_t w1f, w1f_sc, w2f, w2f_sc, w2t, w2t_sc, w1t, w1t_sc, total;
+};
+
+WLayout wlayout(const moe_desc& d) {
+  WLayout W{};
+  const size_t E = d.E, D = d.D, F = d.F;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
+  const bool fwd = d.mode == MOE_MXFP8 || d.mode == MOE_FP8;
+  if (fwd) {
+    W.w1f = take(E * 2 * F * D);
+    W.w1f_sc = take(E * (D / 128) * 2 * F * 4);
+    W.w2f = take(E * D * F);
+    W.w2f_sc = take(E * (F / 128) * D * 4);
+  }
+  W.w2t = take(E * F * D);
+  W.w2t_sc = take(E * (D / 128) * F * 4);
+  W.w1t = take(E * D * 2 * F);
+  W.w1t_sc = take(E * (2 * F / 128) * D * 4);
+  W.total = o;
+  return W;
+}
+
+inline bool fp8_fwd(int mode) { return mode == MOE_MXFP8 || mode == MOE_FP8; }
+
+}  // namespace
+
+bool fp8_mode(int mode) { return mode == MOE_FP8_BWD || mode == MOE_MXFP8 || mode == MOE_FP8; }
+
+size_t fp8_wprep_bytes(const moe_desc& d) { return fp8_mode(d.mode) ? wlayout(d).total : 0; }
+
+size_t fp8_scratch_bytes(const moe_desc& d) {
+  if (!fp8_mode(d.mode)) return 0;
+  const size_t N = size_t(d.T) * d.K, C = d.D > 2 * d.F ? d.D : 2 * d.F;
+  const size_t npad = size_t(max_steps128(d)) * 128;
+  size_t o = 0;
+  o = align256(o + N * C);                 // row-quantised codes
+  o = align256(o + (C / 128) * N * 4);     // their scale entries
+  for (int i = 0; i < 2; ++i) {
+    o = align256(o + C * npad);            // token-quantised codes
+    o = align256(o + (npad / 128) * C * 4);
+  }
+  return o;
+}
+
+int fp8_prepare_weights(const moe_desc& d, const uint16_t* w1, const uint16_t* w2, char* wprep,
+                        hipStream_t s) {
+  const WLayout W = wlayout(d);
+  const bool mx = d.mode == MOE_MXFP8;
+  const int D = d.D, F = d.F;
+  int rc;
+  if (fp8_fwd(d.mode)) {
+    if ((rc = quant_weights(d, w1, 2 * F, D, false, mx, reinterpret_cast<uint8_t*>(wprep + W.w1f),
+                            reinterpret_cast<uint32_t*>(wprep + W.w1f_sc), "quant_w1", s)))
+      return rc;
+    if ((rc = quant_weights(d, w2, D, F, false, mx, reinterpret_cast<uint8_t*>(wprep + W.w2f),
+                            reinterpret_cast<uint32_t*>(wprep + W.w2f_sc), "quant_w2", s)))
+      return rc;
+  }
+  if ((rc = quant_weights(d, w2, D, F, true, mx, reinterpret_cast<uint8_t*>(wprep + W.w2t),
+                          reinterpret_cast<uint32_t*>(wprep + W.w2t_sc), "quant_w2_t", s)))
+    return rc;
+  return quant_weights(d, w1, 2 * F, D, true, mx, reinterpret_cast<uint8_t*>(wprep + W.w1t),
+                       reinterpret_cast<uint32_t*>(wprep + W.w1t_sc), "quant_w1_t", s);
+}
+
+// Scratch regions of the FP8 operands (after the bf16 layout).
+struct F8Scratch {
+  uint8_t *qrow, *qt1, *qt2;
+  uint32_t *qrow_sc, *qt1_sc, *qt2_sc;
+  size_t qrow_sc_bytes, qt_sc_bytes;
+};
+
+static F8Scratch f8scratch(const moe_desc& d, const Layout& L, char* scratch) {
+  const size_t N = size_t(d.T) * d.K, C = d.D > 2 * d.F ? d.D : 2 * d.F;
+  const size_t npad = size_t(max_steps128(d)) * 128;
+  char* b = scratch + L.fp8;
+  F8Scratch f{};
+  size_t o = 0;
+  f.qrow = reinterpret_cast<uint8_t*>(b + o);
+  o = align256(o + N * C);
+  f.qrow_sc = reinterpret_cast<uint32_t*>(b + o);
+  f.qrow_sc_bytes = (C / 128) * N * 4;
+  o = align256(o + f.qrow_sc_bytes);
+  f.qt_sc_bytes = (npad / 128) * C * 4;
+  f.qt1 = reinterpret_cast<uint8_t*>(b + o);
+  o = align256(o + C * npad);
+  f.qt1_sc = reinterpret_cast<uint32_t*>(b + o);
+  o = align256(o + f.qt_sc_bytes);
+  f.qt2 = reinterpret_cast<uint8_t*>(b + o);
+  o = align256(o + C * npad);
+  f.qt2_sc = reinterpret_cast<uint32_t*>(b + o);
+  return f;
+}
+
+int fp8_view(const moe_desc& d, const Layout& L, char* scratch, int which, void** ptr,
+             size_t* bytes) {
+  const F8Scratch f = f8scratch(d, L, scratch);
+  const size_t N = size_t(d.T) * d.K, C = d.D > 2 * d.F ? d.D : 2 * d.F;
+  const size_t npad = size_t(max_steps128(d)) * 128;
+  switch (which) {
+    case MOE_VIEW_Q_ROWS: *ptr = f.qrow; *bytes = N * C; return MOE_OK;
+    case MOE_VIEW_Q_ROWS_SCALE: *ptr = f.qrow_sc; *bytes = f.qrow_sc_bytes; return MOE_OK;
+    case MOE_VIEW_Q_TOK_A: *ptr = f.qt1; *bytes = C * npad; return MOE_OK;
+    case MOE_VIEW_Q_TOK_A_SCALE: *ptr = f.qt1_sc; *bytes = f.qt_sc_bytes; return MOE_OK;
+    case MOE_VIEW_Q_TOK_B: *ptr = f.qt2; *bytes = C * npad; return MOE_OK;
+    case MOE_VIEW_Q_TOK_B_SCALE: *ptr = f.qt2_sc; *bytes = f.qt_sc_bytes; return MOE_OK;
+    default: return MOE_EINVAL;
+  }
+}
+
+int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,
+                  hipStream_t s) {
+  const WLayout W = wlayout(d);
+  const F8Scratch f = f8scratch(d, L, scratch);
+  const bool mx = d.mode == MOE_MXFP8;
+  const int D = d.D, F = d.F, N = d.T * d.K;
+  int rc;
+  // expert linear 1 + SwiGLU
+  if ((rc = quant_rows(d, reinterpret_cast<const uint16_t*>(scratch + L.xperm), D, mx, f.qrow,
+                       f.qrow_sc, "quant_x_rows", s)))
+    return rc;
+  F8Args a{};
+  a.K = D;
+  a.A = f.qrow;
+  a.SA = f.qrow_sc;
+  a.sa_ld = N;
+  a.sa_bytes = uint32_t(f.qrow_sc_bytes);
+  a.B = reinterpret_cast<const uint8_t*>(wprep + W.w1f);
+  a.b_bstride = int64_t(2) * F * D;
+  a.SB = reinterpret_cast<const uint32_t*>(wprep + W.w1f_sc);
+  a.sb_ld = 2 * F;
+  a.sb_bstride = int64_t(D / 128) * 2 * F;
+  a.sb_bytes = uint32_t(size_t(D / 128) * 2 * F * 4);
+  a.F = F;
+  a.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.h), 0,
+                  reinterpret_cast<uint16_t*>(scratch + L.a), nullptr, F};
+  rc = mx ? run_f8_grouped<true, EPI_SWIGLU>(d, L, a, 2 * F, "gemm_w1_swiglu", scratch, s)
+          : run_f8_grouped<false, EPI_SWIGLU>(d, L, a, 2 * F, "gemm_w1_swiglu", scratch, s);
+  if (rc) return rc;
+  // expert linear 2
+  if ((rc = quant_rows(d, reinterpret_cast<const uint16_t*>(scratch + L.a), F, mx, f.qrow,
+                       f.qrow_sc, "quant_a_rows", s)))
+    return rc;
+  F8Args b{};
+  b.K = F;
+  b.A = f.qrow;
+  b.SA = f.qrow_sc;
+  b.sa_ld = N;
+  b.sa_bytes = uint32_t(size_t(F / 128) * N * 4);
+  b.B = reinterpret_cast<const uint8_t*>(wprep + W.w2f);
+  b.b_bstride = int64_t(D) * F;
+  b.SB = reinterpret_cast<const uint32_t*>(wprep + W.w2f_sc);
+  b.sb_ld = D;
+  b.sb_bstride = int64_t(F / 128) * D;
+  b.sb_bytes = uint32_t(size_t(F / 128) * D * 4);
+  b.F = F;
+  b.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.o), D, nullptr, nullptr, F};
+  return mx ? run_f8_grouped<true, EPI_STORE>(d, L, b, D, "gemm_w2", scratch, s)
+            : run_f8_grouped<false, EPI_STORE>(d, L, b, D, "gemm_w2", scratch, s);
+}
+
+int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* dw1, void* dw2,
+                  char* scratch, hipStream_t s) {
+  const WLayout W = wlayout(d);
+  const F8Scratch f = f8scratch(d, L, scratch);
+  const bool mx = d.mode == MOE_MXFP8;
+  const int D = d.D, F = d.F, N = d.T * d.K;
+  const int64_t npad = int64_t(max_steps128(d)) * 128;
+  const auto* dyw = reinterpret_cast<const uint16_t*>(scratch + L.dyperm);
+  const auto* act = reinterpret_cast<const uint16_t*>(scratch + L.a);
+  const auto* dh = reinterpret_cast<const uint16_t*>(scratch + L.dh);
+  const auto* xp = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
+  int rc;
+  // W2 dgrad + SwiGLU-backward
+  if ((rc = quant_rows(d, dyw, D, mx, f.qrow, f.qrow_sc, "quant_dyw_rows", s))) return rc;
+  F8Args a{};
+  a.K = D;
+  a.A = f.qrow;
+  a.SA = f.qrow_sc;
+  a.sa_ld = N;
+  a.sa_bytes = uint32_t(size_t(D / 128) * N * 4);
+  a.B = reinterpret_cast<const uint8_t*>(wprep + W.w2t);
+  a.b_bstride = int64_t(F) * D;
+  a.SB = reinterpret_cast<const uint32_t*>(wprep + W.w2t_sc);
+  a.sb_ld = F;
+  a.sb_bstride = int64_t(D / 128) * F;
+  a.sb_bytes = uint32_t(size_t(D / 128) * F * 4);
+  a.F = F;
+  a.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.dh), 0, nullptr,
+                  reinterpret_cast<const uint16_t*>(scratch + L.h), F};
+  rc = mx ? run_f8_grouped<true, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s)
+          : run_f8_grouped<false, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s);
+  if (rc) return rc;
+  // W2 wgrad over tokens
+  if ((rc = quant_tokens(d, L, dyw, D, mx, f.qt1, f.qt1_sc, "quant_dyw_tokens", scratch, s))) return rc;
+  if ((rc = quant_tokens(d, L, act, F, mx, f.qt2, f.qt2_sc, "quant_a_tokens", scratch, s))) return rc;
+  F8Args w{};
+  w.M = D;
+  w.N = F;
+  w.A = f.qt1;
+  w.lda = npad;
+  w.SA = f.qt1_sc;
+  w.sa_ld = D;
+  w.sa_bytes = uint32_t(f.qt_sc_bytes);
+  w.B = f.qt2;
+  w.ldb = npad;
+  w.SB = f.qt2_sc;
+  w.sb_ld = F;
+  w.sb_bytes = uint32_t(f.qt_sc_bytes);
+  w.C = dw2;
+  rc = mx ? run_f8_wgrad<true>(d, L, w, "gemm_w2_wgrad", scratch, s)
+          : run_f8_wgrad<false>(d, L, w, "gemm_w2_wgrad", scratch, s);
+  if (rc) return rc;
+  // W1 dgrad
+  if ((rc = quant_rows(d, dh, 2 * F, mx, f.qrow, f.qrow_sc, "quant_dh_rows", s))) return rc;
+  F8Args b{};
+  b.K = 2 * F;
+  b.A = f.qrow;
+  b.SA = f.qrow_sc;
+  b.sa_ld = N;
+  b.sa_bytes = uint32_t(size_t(2 * F / 128) * N * 4);
+  b.B = reinterpret_cast<const uint8_t*>(wprep + W.w1t);
+  b.b_bstride = int64_t(D) * 2 * F;
+  b.SB = reinterpret_cast<const uint32_t*>(wprep + W.w1t_sc);
+  b.sb_ld = D;
+  b.sb_bstride = int64_t(2 * F / 128) * D;
+  b.sb_bytes = uint32_t(size_t(2 * F / 128) * D * 4);
+  b.F = F;
+  b.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.dxperm), D, nullptr, nullptr, F};
+  rc = mx ? run_f8_grouped<true, EPI_STORE>(d, L, b, D, "gemm_w1_dgrad", scratch, s)
+          : run_f8_grouped<false, EPI_STORE>(d, L, b, D, "gemm_w1_dgrad", scratch, s);
+  if (rc) return rc;
+  // W1 wgrad over tokens
+  if ((rc = quant_tokens(d, L, dh, 2 * F, mx, f.qt1, f.qt1_sc, "quant_dh_tokens", scratch, s))) return rc;
+  if ((rc = quant_tokens(d, L, xp, D, mx, f.qt2, f.qt2_sc, "quant_x_tokens", scratch, s))) return rc;
+  F8Args v{};
+  v.M = 2 * F;
+  v.N = D;
+  v.A = f.qt1;
+  v.lda = npad;
+  v.SA = f.qt1_sc;
+  v.sa_ld = 2 * F;
+  v.sa_bytes = uint32_t(f.qt_sc_bytes);
+  v.B = f.qt2;
+  v.ldb = npad;
+  v.SB = f.qt2_sc;
+  v.sb_ld = D;
+  v.sb_bytes = uint32_t(f.qt_sc_bytes);
+  v.C = dw1;
+  return mx ? run_f8_wgrad<true>(d, L, v, "gemm_w1_wgrad", scratch, s)
+            : run_f8_wgrad<false>(d, L, v, "gemm_w1_wgrad", scratch, s);
+}
+
+}  // namespace moe

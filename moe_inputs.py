@@ -89,6 +89,16 @@ CONFIGS = {
     "dead_bf16": LayerConfig("dead_bf16", T=300, D=256, F=192, E=12, K=3,
                              routing="dead4", seed=2003),
     "wide_bf16": LayerConfig("wide_bf16", T=1100, D=1024, F=512, E=8, K=2, seed=2004),
+    # FP8 parity shapes (D, F multiples of 256): experts with several 256-row
+    # tiles and 128-token steps, experts with fewer than 128 tokens, dead experts
+    "fp8bwd_small": LayerConfig("fp8bwd_small", T=600, D=512, F=256, E=4, K=2,
+                                mode=MODE_FP8_BWD, seed=3001),
+    "mxfp8_small": LayerConfig("mxfp8_small", T=600, D=512, F=256, E=4, K=2,
+                               mode=MODE_MXFP8, seed=3002),
+    "fp8_small": LayerConfig("fp8_small", T=600, D=512, F=256, E=4, K=2,
+                             mode=MODE_FP8, seed=3003),
+    "mxfp8_zipf_small": LayerConfig("mxfp8_zipf_small", T=512, D=256, F=256, E=16, K=4,
+                                    mode=MODE_MXFP8, routing="zipf", seed=3004),
 }
 
 
