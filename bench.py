@@ -32,6 +32,15 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
 
+FWD_GEMMS = ("gemm_w1_swiglu", "gemm_w2")
+
+
+def gemm_peak(cfg, name: str) -> float:
+    """Dense MFMA peak (TFLOP/s) of the operand type a GEMM runs in for this mode."""
+    fp8 = (cfg.mode in (4, 5)) or (cfg.mode == 3 and name not in FWD_GEMMS)
+    return PEAK_TFLOPS["fp8" if fp8 else "bf16"]
+
+
 def gemm_flops(cfg) -> dict:
     """Algorithmic FLOPs per launch of each GEMM kernel (2 per multiply-add)."""
     ndf = float(cfg.N) * cfg.D * cfg.F
@@ -169,8 +178,10 @@ def main():
 
     flops = cfg.fwd_flops() + cfg.bwd_flops()
     tflops = flops / (ms_step * 1e-3) / 1e12
-    dtype = "bf16" if cfg.io_is_bf16 else "fp32"
-    peak = PEAK_TFLOPS["bf16"]
+    dtype = {0: "fp32", 1: "fp32", 2: "bf16", 3: "bf16+fp8(bwd)", 4: "mxfp8", 5: "fp8"}[cfg.mode]
+    # whole-layer fraction: algorithmic flops over the time the same flops take at each GEMM's peak
+    peak = (cfg.fwd_flops() + cfg.bwd_flops()) / (
+        cfg.fwd_flops() / gemm_peak(cfg, "gemm_w1_swiglu") + cfg.bwd_flops() / gemm_peak(cfg, "gemm_w1_dgrad"))
 
     roof = None
     per_kernel = {}
@@ -182,7 +193,7 @@ def main():
             entry = {"avg_ms": round(avg, 4), "launches": n}
             if name in gf:
                 entry["tflops"] = round(gf[name] / (avg * 1e-3) / 1e12, 1)
-                entry["frac_peak"] = round(gf[name] / (avg * 1e-3) / 1e12 / peak, 3)
+                entry["frac_peak"] = round(gf[name] / (avg * 1e-3) / 1e12 / gemm_peak(cfg, name), 3)
             if name in rb:
                 entry["gbs"] = round(rb[name] / (avg * 1e-3) / 1e9, 1)
                 entry["frac_hbm"] = round(rb[name] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)
@@ -190,8 +201,9 @@ def main():
         dom = max((k for k in kernels if k in gf), key=lambda k: kernels[k][0])
         avg = kernels[dom][0] / kernels[dom][1]
         ach = gf[dom] / (avg * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+        dpeak = gemm_peak(cfg, dom)
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": dpeak,
+                "unit": "TFLOP/s", "frac": round(ach / dpeak, 4),
                 "traffic": measured_traffic(cfg, dom),
                 "flops_per_launch": gf[dom], "avg_ms": round(avg, 4)}
 
@@ -206,6 +218,7 @@ def main():
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "fwd_tflops": round(cfg.fwd_flops() / (fwd_ms * 1e-3) / 1e12, 1),
         "bwd_tflops": round(cfg.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1),
+        "peak_tflops": round(peak, 1),
         "frac_mfma_peak": round(tflops / peak, 4),
         "roofline": roof,
         "kernels": per_kernel,

@@ -374,7 +374,7 @@ __global__ void __launch_bounds__(TL::THREADS, 1) f8_grouped_kernel(F8Args p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / TL::WGN, wn = wave % TL::WGN;
 
-  KStager<BM, WAVES> sa;
+  KStager<BM, WAVES, 128> sa;
   sa.init(make_rsrc(p.A + size_t(e0) * p.K, uint32_t(ne) * p.K),
           [&](int r) { return r < rows_valid ? (m0 + r) * p.K : -1; }, wave, lane);
   auto brow = [&](int n) {
@@ -386,7 +386,7 @@ __global__ void __launch_bounds__(TL::THREADS, 1) f8_grouped_kernel(F8Args p) {
       return nt * BN + n;
     }
   };
-  KStager<BN, WAVES> sb;
+  KStager<BN, WAVES, 128> sb;
   sb.init(make_rsrc(p.B + size_t(e) * p.b_bstride, uint32_t(p.N) * p.K),
           [&](int n) { return brow(n) * p.K; }, wave, lane);
   ScaleStager ssa{make_rsrc(p.SA, p.sa_bytes), (e0 + m0 + 4 * lane) * 4, int(p.sa_ld * 4), wave == 0};
@@ -396,7 +396,8 @@ __global__ void __launch_bounds__(TL::THREADS, 1) f8_grouped_kernel(F8Args p) {
   f32x16 acc[TL::WMT][TL::WNT];
   zero(acc);
   mainloop8<TL, MX, false>(smem, sa, sb, ssa, ssb, p.K / 128, acc, wave, lane);
-  grouped_epilogue<TL, EPI>(p.epi, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane);
+  static_assert(sizeof(smem) >= grouped_epi_lds<TL, EPI>(), "epilogue staging exceeds LDS");
+  grouped_epilogue<TL, EPI>(p.epi, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane, smem);
 }
 
 // Per-expert FP8 weight-gradient GEMM over the expert's padded token steps.
@@ -416,10 +417,10 @@ __global__ void __launch_bounds__(TL::THREADS, 1) f8_wgrad_kernel(F8Args p) {
   zero(acc);
   if (ksteps > 0) {
     const size_t kb0 = size_t(s0) * 128;  // first padded token of the expert
-    KStager<BM, WAVES> sa;
+    KStager<BM, WAVES, 128> sa;
     sa.init(make_rsrc(p.A + size_t(mt) * BM * p.lda + kb0, uint32_t(BM - 1) * p.lda + ksteps * 128),
             [&](int r) { return r * int(p.lda); }, wave, lane);
-    KStager<BN, WAVES> sb;
+    KStager<BN, WAVES, 128> sb;
     sb.init(make_rsrc(p.B + size_t(nt) * BN * p.ldb + kb0, uint32_t(BN - 1) * p.ldb + ksteps * 128),
             [&](int r) { return r * int(p.ldb); }, wave, lane);
     ScaleStager ssa{make_rsrc(p.SA, p.sa_bytes), int((size_t(s0) * p.sa_ld + mt * BM + 4 * lane) * 4),
@@ -428,7 +429,8 @@ __global__ void __launch_bounds__(TL::THREADS, 1) f8_wgrad_kernel(F8Args p) {
                     int(p.sb_ld * 4), wave == 1};
     mainloop8<TL, MX, true>(smem, sa, sb, ssa, ssb, ksteps, acc, wave, lane);
   }
-  wgrad_epilogue<TL, OUT_F32>(p.C, p.M, p.N, e, mt, nt, acc, wm, wn, lane);
+  static_assert(sizeof(smem) >= wgrad_epi_lds<TL, OUT_F32>(), "epilogue staging exceeds LDS");
+  wgrad_epilogue<TL, OUT_F32>(p.C, p.M, p.N, e, mt, nt, acc, wm, wn, lane, smem);
 }
 
 }  // namespace

@@ -14,28 +14,36 @@
 // (dYw_perm holds the dispatched upstream gradient already multiplied by the
 // pair's routing weight.)
 //
-// Work decomposition: a 256-thread workgroup (four wave64s in a 2x2 grid) owns
-// one BM x BN output tile; each wave accumulates (BM/2) x (BN/2) with
-// v_mfma_f32_32x32x16_bf16.  The contraction advances 64 at a time through a
-// ring of STAGES LDS buffers filled by direct-to-LDS buffer loads
-// (buffer_load_dwordx4 ... lds): a wave issues the loads for k-step kt+STAGES-1
-// and goes on to the MFMAs of k-step kt without holding the data in registers,
-// so STAGES-1 k-steps of global latency are in flight.  Loads past the end of
-// an expert's rows (or of its tokens, in the wgrads) fall outside the buffer
-// resource and land as zeros.
+// Work decomposition: a workgroup of WGM x WGN wave64s owns one BM x BN output
+// tile (256 x 256 with a 2 x 4 grid of waves on the large shapes, smaller
+// fallbacks for dimensions that are not multiples of 256); each wave
+// accumulates (BM/WGM) x (BN/WGN) with v_mfma_f32_32x32x16_bf16.  The
+// contraction advances 32 at a time through a ring of STAGES LDS buffers
+// (4 or 5: up to the whole 160 KB) filled by direct-to-LDS buffer loads
+// (buffer_load_dwordx4 ... lds): the loads for k-step kt+STAGES-1 are issued,
+// spread between the MFMAs, while k-step kt is computed, so STAGES-1 k-steps
+// of global latency are in flight without holding any of the data in
+// registers.  One barrier per k-step publishes the next buffer; the first
+// fragments of k-step kt+1 are read across it while the last MFMAs of k-step
+// kt run.  Loads past the end of an expert's rows (or of its tokens, in the
+// wgrads) fall outside the buffer resource and land as zeros.
 //
 // LDS layouts.  An operand whose global rows run along the contraction index
 // ("k-contiguous": activations, and the weights in the forward) is staged as
-// R rows x 64 k, 128 bytes per row; an MFMA fragment (8 consecutive k of one
+// R rows x 32 k, 64 bytes per row; an MFMA fragment (8 consecutive k of one
 // row) is one ds_read_b128.  An operand whose global rows run along the output
 // index ("k-outer": the weights in the dgrads and both operands of the wgrads)
-// is staged as 64 k-rows x R, exactly as it lies in memory, and its fragments
+// is staged as 32 k-rows x R, exactly as it lies in memory, and its fragments
 // are read with ds_read_b64_tr_b16: a 16-lane group pointing at a 4 (k) x 16
 // (m) block gets one column of 4 consecutive k per lane, two reads give the 8
 // consecutive k of an MFMA fragment.  In both layouts the 16-byte chunks of a
 // row are XOR-swizzled so that each read instruction touches every LDS bank
 // once; the swizzle is applied on the load side by choosing which global chunk
 // each lane of the (contiguous) LDS write fetches.
+//
+// Epilogues stage the output tile through the (then idle) LDS ring and write
+// whole rows with 16-byte stores; the SwiGLU backward reads its saved H tile
+// the same way.
 //
 // Token-grouped GEMMs walk a flat list of (expert, m-tile, n-tile) built from
 // the routing step's per-expert m-tile prefix sums; workgroups past the end
@@ -94,7 +102,7 @@ __global__ void __launch_bounds__(TL::THREADS, 1) grouped_gemm_kernel(GroupedArg
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / TL::WGN, wn = wave % TL::WGN;
 
-  KStager<BM, WAVES> sa;
+  KStager<BM, WAVES, kBK * 2> sa;
   sa.init(make_rsrc(p.A + size_t(e0) * p.lda, uint32_t(ne) * p.lda * 2),
           [&](int r) { return r < rows_valid ? (m0 + r) * p.lda * 2 : -1; }, wave, lane);
   const uint16_t* Be = p.B + size_t(e) * p.bstride;
@@ -107,7 +115,7 @@ __global__ void __launch_bounds__(TL::THREADS, 1) grouped_gemm_kernel(GroupedArg
     sb.init(make_rsrc(Be + nt * BN, bbytes - nt * BN * 2), p.ldb * 2, wave, lane);
     mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, true>(smem, sa, sb, ktiles, acc, wave, lane);
   } else {
-    KStager<BN, WAVES> sb;
+    KStager<BN, WAVES, kBK * 2> sb;
     sb.init(make_rsrc(Be, bbytes),
             [&](int n) {
               int row;
@@ -125,7 +133,8 @@ __global__ void __launch_bounds__(TL::THREADS, 1) grouped_gemm_kernel(GroupedArg
   }
 
   EpiArgs ea{p.out, p.ldo, p.out2, p.hsave, p.F};
-  grouped_epilogue<TL, EPI>(ea, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane);
+  static_assert(sizeof(smem) >= grouped_epi_lds<TL, EPI>(), "epilogue staging exceeds LDS");
+  grouped_epilogue<TL, EPI>(ea, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane, smem);
 }
 
 struct WgradArgs {
@@ -167,7 +176,8 @@ __global__ void __launch_bounds__(TL::THREADS, 1) wgrad_gemm_kernel(WgradArgs p)
     mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, true, true>(smem, sa, sb, ktiles, acc, wave, lane);
   }
 
-  wgrad_epilogue<TL, OUT_F32>(p.C, p.M, p.N, e, mt, nt, acc, wm, wn, lane);
+  static_assert(sizeof(smem) >= wgrad_epi_lds<TL, OUT_F32>(), "epilogue staging exceeds LDS");
+  wgrad_epilogue<TL, OUT_F32>(p.C, p.M, p.N, e, mt, nt, acc, wm, wn, lane, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -209,9 +219,11 @@ int run_wgrad(const moe_desc& d, const Layout& L, WgradArgs a, const char* name,
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-// Tile choices (measured on the 30B/235B shapes); narrower fallbacks keep small
-// shapes (D or F not a multiple of 256) working.
-using TileBig = Tile<256, 256, 2, 4, 2>;
+// Tile choices (measured on the 30B shape: the 5-deep ring helps the W1 +
+// SwiGLU GEMM by about 10% and none of the others); narrower fallbacks keep
+// small shapes (D or F not a multiple of 256) working.
+using TileBig = Tile<256, 256, 2, 4, 4>;
+using TileBig5 = Tile<256, 256, 2, 4, 5>;  // whole 160 KB LDS: deeper ring for W1 + SwiGLU
 using TileMid = Tile<128, 128, 2, 2, 4>;
 using TileNarrow = Tile<128, 64, 2, 2, 4>;
 using TileWg128x64 = Tile<128, 64, 2, 2, 4>;
@@ -221,6 +233,8 @@ using TileWg64x64 = Tile<64, 64, 2, 2, 4>;
 template <bool B_T, int EPI>
 int run_grouped_any(const moe_desc& d, const Layout& L, GroupedArgs a, int N, const char* name,
                     char* scratch, hipStream_t s) {
+  if constexpr (EPI == EPI_SWIGLU)
+    if (N % 256 == 0) return run_grouped<TileBig5, B_T, EPI>(d, L, a, N, name, scratch, s);
   if (N % 256 == 0) return run_grouped<TileBig, B_T, EPI>(d, L, a, N, name, scratch, s);
   if (N % 128 == 0) return run_grouped<TileMid, B_T, EPI>(d, L, a, N, name, scratch, s);
   if constexpr (EPI != EPI_SWIGLU) return run_grouped<TileNarrow, B_T, EPI>(d, L, a, N, name, scratch, s);

@@ -4,12 +4,14 @@
 // design notes.
 #pragma once
 
+#include <type_traits>
+
 #include "moe_common.h"
 
 namespace moe {
 namespace gemm {
 
-constexpr int kBK = 64;  // contraction step (bf16 elements)
+constexpr int kBK = 32;  // contraction step of the bf16 GEMMs (elements)
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -55,8 +57,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(AS3(p)));
 }
 
-// Chunk swizzles (chunk = 16 bytes = 8 bf16).
-__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
+// Chunk swizzles (chunk = 16 bytes).  A k-contiguous tile row holds ROWB bytes
+// of one row's k-run; the chunk index is XORed with bits of the row so that the
+// 16 lanes of a fragment read (16 rows, same logical chunk) land on 16 distinct
+// 16-byte bank groups of a 256-byte LDS line.
+template <int ROWB>
+__device__ __forceinline__ int swz_row(int row) {
+  static_assert(ROWB == 64 || ROWB == 128, "k-contiguous rows are 64 or 128 bytes");
+  if constexpr (ROWB == 128) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
+__device__ __forceinline__ int swz_k(int row) { return swz_row<128>(row); }
 template <int R>
 __device__ __forceinline__ int swz_t(int krow) {
   if constexpr (R >= 128) return (krow & 3) << 2;
@@ -68,10 +79,14 @@ __device__ __forceinline__ int swz_t(int krow) {
 // buffer resource, at k-step 0) of the 16-byte chunk that lane fetches for each
 // of the wave's DMA instructions, and how far that offset moves per k-step.
 
-// k-contiguous operand, R rows: row r of the tile is at rowoff(r) bytes.
-template <int R, int WAVES>
+// k-contiguous operand, R rows of ROWB bytes per k-step: row r of the tile is
+// at rowoff(r) bytes (negative: the row does not exist and reads as zeros).
+template <int R, int WAVES, int ROWB>
 struct KStager {
-  static constexpr int NI = R / (8 * WAVES);  // DMA instructions per wave per k-step (1 KB each)
+  static constexpr int LPR = ROWB / 16;               // lanes per row
+  static constexpr int RPI = 64 / LPR;                // rows per DMA instruction
+  static constexpr int NI = R * ROWB / (1024 * WAVES);  // DMA instructions per wave per k-step
+  static_assert(NI >= 1 && NI * 1024 * WAVES == R * ROWB, "tile rows must split evenly over waves");
   i32x4 rsrc;
   int vb[NI];
   template <class RowOff>
@@ -80,27 +95,29 @@ struct KStager {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int q = wave * NI + j;
-      const int row = q * 8 + (lane >> 3);
-      const int logical = (lane & 7) ^ swz_k(row);
+      const int row = q * RPI + lane / LPR;
+      const int logical = (lane % LPR) ^ swz_row<ROWB>(row);
       const int ro = rowoff(row);
       vb[j] = ro < 0 ? int(0x80000000u) : ro + logical * 16;
     }
   }
-  __device__ __forceinline__ void issue(uint32_t lds, int wave, int kt) const {
+  // DMA instructions [j0, j1) of this operand for k-step kt into the stage at lds.
+  __device__ __forceinline__ void issue(uint32_t lds, int wave, int kt, int j0 = 0, int j1 = NI) const {
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-      dma16(rsrc, lds + uint32_t(wave * NI + j) * 1024u, vb[j] + kt * (kBK * 2));
+      if (j >= j0 && j < j1) dma16(rsrc, lds + uint32_t(wave * NI + j) * 1024u, vb[j] + kt * ROWB);
   }
 };
 
-// k-outer operand, R output columns: k-row k of the tile is at k * ld_bytes,
-// column c at c * 2 (relative to the resource base, which includes the tile's
-// first column).
+// k-outer operand, R output columns, kBK k-rows per k-step: k-row k of the
+// tile is at k * ld_bytes, column c at c * 2 (relative to the resource base,
+// which includes the tile's first column).
 template <int R, int WAVES>
 struct TStager {
-  static constexpr int NI = R / (8 * WAVES);
+  static constexpr int NI = R * kBK * 2 / (1024 * WAVES);
   static constexpr int LPR = R / 8;      // lanes per k-row
   static constexpr int RPI = 64 / LPR;   // k-rows per DMA instruction
+  static_assert(NI >= 1 && NI * 1024 * WAVES == R * kBK * 2, "tile k-rows must split evenly over waves");
   i32x4 rsrc;
   int vb[NI];
   int step;  // bytes per k-step
@@ -115,17 +132,18 @@ struct TStager {
       vb[j] = krow * ld_bytes + logical * 16;
     }
   }
-  __device__ __forceinline__ void issue(uint32_t lds, int wave, int kt) const {
+  __device__ __forceinline__ void issue(uint32_t lds, int wave, int kt, int j0 = 0, int j1 = NI) const {
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-      dma16(rsrc, lds + uint32_t(wave * NI + j) * 1024u, vb[j] + kt * step);
+      if (j >= j0 && j < j1) dma16(rsrc, lds + uint32_t(wave * NI + j) * 1024u, vb[j] + kt * step);
   }
 };
 
 // Fragment reads (8 consecutive k of one row/column, k-step sub-block kk).
 __device__ __forceinline__ bf16x8 frag_k(const char* tile, int row, int kk, int lane) {
+  constexpr int ROWB = kBK * 2;
   const int chunk = kk * 2 + (lane >> 5);
-  return *reinterpret_cast<const bf16x8*>(tile + row * 128 + ((chunk ^ swz_k(row)) << 4));
+  return *reinterpret_cast<const bf16x8*>(tile + row * ROWB + ((chunk ^ swz_row<ROWB>(row)) << 4));
 }
 
 template <int R>
@@ -145,78 +163,130 @@ __device__ __forceinline__ bf16x8 frag_t(const char* tile, int col0, int kk, int
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// s_waitcnt vmcnt(n * per) for a runtime n in [0, 3].
+template <int PER>
+__device__ __forceinline__ void wait_vmcnt_n(int n) {
+  if (n >= 3) wait_vmcnt<3 * PER>();
+  else if (n == 2) wait_vmcnt<2 * PER>();
+  else if (n == 1) wait_vmcnt<PER>();
+  else wait_vmcnt<0>();
+}
+
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Scheduling pattern for one sub-step: NMF MFMAs with the NDS LDS reads of the
+// next fragments spread between them (group masks: 0x8 MFMA, 0x100 DS read).
+template <int NMF, int NDS, int M = 0>
+__device__ __forceinline__ void interleave_mfma_ds() {
+  if constexpr (M < NMF) {
+    constexpr int PER = (NDS + NMF - 1) / NMF;
+    constexpr int D0 = M * PER < NDS ? M * PER : NDS;
+    constexpr int D1 = D0 + PER < NDS ? D0 + PER : NDS;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (D1 > D0) __builtin_amdgcn_sched_group_barrier(0x100, D1 - D0, 0);
+    interleave_mfma_ds<NMF, NDS, M + 1>();
+  }
+}
+
 // The pipelined main loop: acc += A_tile * B_tile^T over ktiles k-steps.  The
 // workgroup's WGM x WGN waves each own a (BM/WGM) x (BN/WGN) sub-tile.  The
 // MFMA takes the B fragment as its first operand, so an accumulator register
 // block holds C^T: lane l owns output row (l & 31) of a 32 x 32 block and four
 // consecutive output columns per group of four registers (see acc_col).
+//
+// STAGES k-steps of kBK sit in an LDS ring, filled by
+// direct-to-LDS loads that run STAGES-1 k-steps ahead.  One barrier per k-step,
+// placed before the last 16-deep sub-step: it publishes k-step kt+1 (each wave
+// has waited for its own loads of it) and certifies that every wave has read
+// its fragments of k-step kt-1's slot, which the loads issued from then on
+// overwrite.  The first fragments of k-step kt+1 are read across the barrier
+// while the MFMAs of k-step kt's last sub-step run, and the DMA instructions of
+// a k-step are spread over its sub-steps instead of issued in one burst.  The
+// steady-state body has no branches; the last STAGES-1 k-steps run a copy
+// without loads.
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_T, bool B_T, class SA, class SB>
 __device__ __forceinline__ void mainloop(char* smem, const SA& sa, const SB& sb, int ktiles,
                                          f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int wave,
                                          int lane) {
-  constexpr int WM = BM / WGM, WN = BN / WGN, WMT = WM / 32, WNT = WN / 32;
+  constexpr int WM = BM / WGM, WN = BN / WGN, WMT = WM / 32, WNT = WN / 32, KK = kBK / 16;
   constexpr int A_BYTES = BM * kBK * 2, STAGE = (BM + BN) * kBK * 2;
-  constexpr int NI = SA::NI + SB::NI;  // DMA instructions per wave per stage
+  constexpr int NI = SA::NI + SB::NI;  // DMA instructions per wave per k-step
+  static_assert(STAGES >= 3 && STAGES - 2 <= 3, "ring of 3 to 5 k-steps");
+  static_assert(KK == 2, "two 16-deep sub-steps per k-step");
   const int wm = wave / WGN, wn = wave % WGN;
   const uint32_t base = lds_addr(smem);
 
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < ktiles) {
-      sa.issue(base + s * STAGE, wave, s);
-      sb.issue(base + s * STAGE + A_BYTES, wave, s);
-    }
-
-  for (int kt = 0; kt < ktiles; ++kt) {
-    // wait for this wave's loads of k-step kt (later stages may stay in flight)
-    const int ahead = min(ktiles - 1 - kt, STAGES - 2);
-    if constexpr (STAGES >= 4) {
-      if (ahead >= 2) wait_vmcnt<2 * NI>();
-      else if (ahead == 1) wait_vmcnt<NI>();
-      else wait_vmcnt<0>();
-    } else if constexpr (STAGES == 3) {
-      if (ahead >= 1) wait_vmcnt<NI>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __builtin_amdgcn_s_barrier();
-    const int kn = kt + STAGES - 1;
-    if (kn < ktiles) {
-      const int sn = kn % STAGES;
-      sa.issue(base + sn * STAGE, wave, kn);
-      sb.issue(base + sn * STAGE + A_BYTES, wave, kn);
-    }
+  struct Frags { bf16x8 a[WMT], b[WNT]; };
+  auto load = [&](int kt, int kk, Frags& f) {
     const char* ta = smem + (kt % STAGES) * STAGE;
     const char* tb = ta + A_BYTES;
-    // fragments of sub-step kk+1 are read while the MFMAs of sub-step kk run
-    bf16x8 af[2][WMT], bfr[2][WNT];
-    auto load = [&](int kk, bf16x8 (&a)[WMT], bf16x8 (&b)[WNT]) {
 #pragma unroll
-      for (int i = 0; i < WMT; ++i) {
-        const int r0 = wm * WM + i * 32;
-        if constexpr (A_T) a[i] = frag_t<BM>(ta, r0, kk, lane);
-        else a[i] = frag_k(ta, r0 + (lane & 31), kk, lane);
-      }
-#pragma unroll
-      for (int j = 0; j < WNT; ++j) {
-        const int c0 = wn * WN + j * 32;
-        if constexpr (B_T) b[j] = frag_t<BN>(tb, c0, kk, lane);
-        else b[j] = frag_k(tb, c0 + (lane & 31), kk, lane);
-      }
-    };
-    load(0, af[0], bfr[0]);
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      if (kk + 1 < kBK / 16) load(kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
-#pragma unroll
-      for (int i = 0; i < WMT; ++i)
-#pragma unroll
-        for (int j = 0; j < WNT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk & 1][j], af[kk & 1][i],
-                                                              acc[i][j], 0, 0, 0);
+    for (int i = 0; i < WMT; ++i) {
+      const int r0 = wm * WM + i * 32;
+      if constexpr (A_T) f.a[i] = frag_t<BM>(ta, r0, kk, lane);
+      else f.a[i] = frag_k(ta, r0 + (lane & 31), kk, lane);
     }
-  }
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) {
+      const int c0 = wn * WN + j * 32;
+      if constexpr (B_T) f.b[j] = frag_t<BN>(tb, c0, kk, lane);
+      else f.b[j] = frag_k(tb, c0 + (lane & 31), kk, lane);
+    }
+  };
+  auto mma = [&](const Frags& f, int m0, int m1) {
+#pragma unroll
+    for (int m = 0; m < WMT * WNT; ++m)
+      if (m >= m0 && m < m1) {
+        const int i = m / WNT, j = m % WNT;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+      }
+  };
+  // DMA instructions [j0, j1) (over both operands) of k-step kt
+  auto issue = [&](int kt, int j0, int j1) {
+    const uint32_t st = base + uint32_t(kt % STAGES) * STAGE;
+    sa.issue(st, wave, kt, j0, j1);
+    sb.issue(st + A_BYTES, wave, kt, j0 - SA::NI, j1 - SA::NI);
+  };
+  constexpr int NH = NI / 2;  // instructions issued in the first sub-step
+
+  const int pre = min(STAGES - 1, ktiles);
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < pre) issue(s, 0, NI);
+  wait_vmcnt_n<NI>(pre - 1);
+  __builtin_amdgcn_s_barrier();
+  Frags f0, f1;
+  load(0, 0, f0);
+
+  // LDS read instructions per fragment set (a transposed fragment takes two)
+  constexpr int NDS = WMT * (A_T ? 2 : 1) + WNT * (B_T ? 2 : 1);
+  constexpr int NMF = WMT * WNT;
+  auto step = [&](int kt, auto dma_on) {
+    constexpr bool DMA = decltype(dma_on)::value;
+    const int kn = kt + STAGES - 1;
+    // sub-step 0: fragments of sub-step 1 are read while its MFMAs run
+    load(kt, 1, f1);
+    if constexpr (DMA) issue(kn, 0, NH);
+    mma(f0, 0, NMF);
+    interleave_mfma_ds<NMF, NDS>();
+    __builtin_amdgcn_sched_barrier(0);
+    // sub-step 1
+    if constexpr (DMA) issue(kn, NH, NI);
+    const bool more = DMA || kt + 1 < ktiles;
+    if (more) {
+      wait_vmcnt_n<NI>(DMA ? STAGES - 2 : ktiles - 2 - kt);
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      load(kt + 1, 0, f0);
+    }
+    mma(f1, 0, NMF);
+    if constexpr (DMA) interleave_mfma_ds<NMF, NDS>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int kmain = ktiles - (STAGES - 1);
+  int kt = 0;
+  for (; kt < kmain; ++kt) step(kt, std::true_type{});
+  for (; kt < ktiles; ++kt) step(kt, std::false_type{});
 }
 
 // Column (within a 32x32 block) of accumulator register 4*g (the first of four
@@ -265,68 +335,178 @@ struct EpiArgs {
   int F;
 };
 
+// Epilogues stage the output through LDS, one band of 32-row blocks (one per
+// wave row, WGM * 32 rows) at a time: each wave writes its accumulators into a
+// row-major LDS tile whose 16-byte chunks are XOR-swizzled by row, then the
+// whole workgroup writes complete rows with 16-byte stores, so every store
+// instruction covers whole 128-byte lines.  A band tile has `cols` elements of
+// `ES` bytes per row.
+template <int ES>
+struct BandTile {
+  char* base;
+  int cols;
+  __device__ __forceinline__ int chunks() const { return cols * ES / 16; }
+  __device__ __forceinline__ char* at(int row, int col) const {
+    const int byte = col * ES, ch = byte >> 4, sw = ch ^ (row & (min(chunks(), 32) - 1));
+    return base + row * cols * ES + (sw << 4) + (byte & 15);
+  }
+};
+
+// Cooperative copy of `rows` band rows (of which the first `valid` exist) from
+// LDS to global rows dst(row) (16 bytes per thread per step).
+template <int THREADS, int ES, class Dst>
+__device__ __forceinline__ void band_store(const BandTile<ES>& t, int rows, int valid, Dst dst) {
+  const int per_row = t.chunks();
+  for (int i = threadIdx.x; i < rows * per_row; i += THREADS) {
+    const int r = i / per_row, c = i - r * per_row;
+    if (r < valid)
+      *reinterpret_cast<uint4*>(dst(r) + c * 16) =
+          *reinterpret_cast<const uint4*>(t.base + r * per_row * 16 + ((c ^ (r & (min(per_row, 32) - 1))) << 4));
+  }
+}
+
+// Cooperative copy of global rows src(row) into a band tile (zeros for rows >= valid).
+template <int THREADS, int ES, class Src>
+__device__ __forceinline__ void band_load(const BandTile<ES>& t, int rows, int valid, Src src) {
+  const int per_row = t.chunks();
+  for (int i = threadIdx.x; i < rows * per_row; i += THREADS) {
+    const int r = i / per_row, c = i - r * per_row;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < valid) v = *reinterpret_cast<const uint4*>(src(r) + c * 16);
+    *reinterpret_cast<uint4*>(t.base + r * per_row * 16 + ((c ^ (r & (min(per_row, 32) - 1))) << 4)) = v;
+  }
+}
+
+// LDS bytes the epilogues stage through (the kernels assert that their
+// pipeline buffer is at least this large).
+template <class TL, int EPI>
+constexpr int grouped_epi_lds() {
+  constexpr int RB = TL::WGM * 32;
+  return EPI == EPI_STORE ? RB * TL::BN * 2 : EPI == EPI_SWIGLU ? 3 * RB * TL::BN : 4 * RB * TL::BN;
+}
+template <class TL, bool OUT_F32>
+constexpr int wgrad_epi_lds() { return TL::WGM * 32 * TL::BN * (OUT_F32 ? 4 : 2); }
+
 // Epilogue of a token-grouped GEMM.  Lane owns row (lane & 31) of each 32-row
 // block and, per group g of four registers, four consecutive columns starting
-// at acc_col(g).  grow0 is the tile's first row in the permuted buffers.
+// at acc_col(g).  grow0 is the tile's first row in the permuted buffers; smem is
+// the (now free) pipeline LDS.
 template <class TL, int EPI>
 __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
                                                  f32x16 (&acc)[TL::WMT][TL::WNT], size_t grow0,
-                                                 int rows_valid, int nt, int wm, int wn, int lane) {
+                                                 int rows_valid, int nt, int wm, int wn, int lane,
+                                                 char* smem) {
   constexpr int BN = TL::BN, WM = TL::WM, WN = TL::WN, WMT = TL::WMT, WNT = TL::WNT;
+  constexpr int RB = TL::WGM * 32;  // rows per band
+  const int rr = wm * 32 + (lane & 31);
+  __syncthreads();  // every wave is done reading the pipeline stages
 #pragma unroll
   for (int i = 0; i < WMT; ++i) {
-    const int m = wm * WM + i * 32 + (lane & 31);
-    if (m >= rows_valid) continue;
-    const size_t row = grow0 + m;
+    // band row w*32 + r holds tile row w*WM + i*32 + r (wave row w's i-th 32-row block)
     if constexpr (EPI == EPI_STORE) {
+      BandTile<2> t{smem, BN};
 #pragma unroll
       for (int j = 0; j < WNT; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = nt * BN + wn * WN + j * 32 + acc_col(g, lane);
           const f32x16& a = acc[i][j];
-          *reinterpret_cast<uint2*>(p.out + row * p.ldo + n) =
+          *reinterpret_cast<uint2*>(t.at(rr, wn * WN + j * 32 + acc_col(g, lane))) =
               pack4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
         }
+      __syncthreads();
+      for (int w = 0; w < TL::WGM; ++w) {
+        const int first = w * WM + i * 32, n = min(32, rows_valid - first);
+        if (n <= 0) continue;
+        BandTile<2> sub{smem + w * 32 * BN * 2, BN};
+        band_store<TL::THREADS>(sub, 32, n, [&](int r) {
+          return reinterpret_cast<char*>(p.out + (grow0 + first + r) * p.ldo + nt * BN);
+        });
+      }
     } else if constexpr (EPI == EPI_SWIGLU) {
       const int F = p.F;
+      BandTile<2> tg{smem, BN / 2}, tu{smem + RB * BN, BN / 2}, ta{smem + 2 * RB * BN, BN / 2};
 #pragma unroll
       for (int j = 0; j < WNT / 2; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int f = nt * (BN / 2) + wn * (WN / 2) + j * 32 + acc_col(g, lane);
+          const int c = wn * (WN / 2) + j * 32 + acc_col(g, lane);
           float gv[4], uv[4], av[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            gv[c] = acc[i][j][4 * g + c];
-            uv[c] = acc[i][j + WNT / 2][4 * g + c];
-            av[c] = gv[c] / (1.f + __expf(-gv[c])) * uv[c];
+          for (int q = 0; q < 4; ++q) {
+            gv[q] = acc[i][j][4 * g + q];
+            uv[q] = acc[i][j + WNT / 2][4 * g + q];
+            av[q] = gv[q] / (1.f + __expf(-gv[q])) * uv[q];
           }
-          *reinterpret_cast<uint2*>(p.out + row * 2 * F + f) = pack4(gv[0], gv[1], gv[2], gv[3]);
-          *reinterpret_cast<uint2*>(p.out + row * 2 * F + F + f) = pack4(uv[0], uv[1], uv[2], uv[3]);
-          *reinterpret_cast<uint2*>(p.out2 + row * F + f) = pack4(av[0], av[1], av[2], av[3]);
+          *reinterpret_cast<uint2*>(tg.at(rr, c)) = pack4(gv[0], gv[1], gv[2], gv[3]);
+          *reinterpret_cast<uint2*>(tu.at(rr, c)) = pack4(uv[0], uv[1], uv[2], uv[3]);
+          *reinterpret_cast<uint2*>(ta.at(rr, c)) = pack4(av[0], av[1], av[2], av[3]);
         }
+      __syncthreads();
+      for (int w = 0; w < TL::WGM; ++w) {
+        const int first = w * WM + i * 32, n = min(32, rows_valid - first);
+        if (n <= 0) continue;
+        const int off = w * 32 * BN;  // bytes of 32 rows of BN/2 bf16
+        const int f0 = nt * (BN / 2);
+        band_store<TL::THREADS>(BandTile<2>{smem + off, BN / 2}, 32, n, [&](int r) {
+          return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + f0);
+        });
+        band_store<TL::THREADS>(BandTile<2>{smem + RB * BN + off, BN / 2}, 32, n, [&](int r) {
+          return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + F + f0);
+        });
+        band_store<TL::THREADS>(BandTile<2>{smem + 2 * RB * BN + off, BN / 2}, 32, n, [&](int r) {
+          return reinterpret_cast<char*>(p.out2 + (grow0 + first + r) * F + f0);
+        });
+      }
     } else {  // EPI_DSWIGLU: acc holds dA = (w dy) W2[e] for the tile's F-columns
       const int F = p.F;
+      const int f0 = nt * BN;
+      // stage H (gate and up) of the band's rows, coalesced
+      for (int w = 0; w < TL::WGM; ++w) {
+        const int first = w * WM + i * 32, n = max(0, min(32, rows_valid - first));
+        band_load<TL::THREADS>(BandTile<2>{smem + w * 32 * BN * 2, BN}, 32, n, [&](int r) {
+          return reinterpret_cast<const char*>(p.hsave + (grow0 + first + r) * 2 * F + f0);
+        });
+        band_load<TL::THREADS>(BandTile<2>{smem + RB * BN * 2 + w * 32 * BN * 2, BN}, 32, n,
+                               [&](int r) {
+          return reinterpret_cast<const char*>(p.hsave + (grow0 + first + r) * 2 * F + F + f0);
+        });
+      }
+      __syncthreads();
+      BandTile<2> tg{smem, BN}, tu{smem + RB * BN * 2, BN};
 #pragma unroll
       for (int j = 0; j < WNT; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int f = nt * BN + wn * WN + j * 32 + acc_col(g, lane);
+          const int c = wn * WN + j * 32 + acc_col(g, lane);
+          uint2* pg = reinterpret_cast<uint2*>(tg.at(rr, c));
+          uint2* pu = reinterpret_cast<uint2*>(tu.at(rr, c));
           float gv[4], uv[4], dg[4], du[4];
-          unpack4(*reinterpret_cast<const uint2*>(p.hsave + row * 2 * F + f), gv);
-          unpack4(*reinterpret_cast<const uint2*>(p.hsave + row * 2 * F + F + f), uv);
+          unpack4(*pg, gv);
+          unpack4(*pu, uv);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float dA = acc[i][j][4 * g + c];
-            const float sg = 1.f / (1.f + __expf(-gv[c]));
-            dg[c] = dA * uv[c] * sg * (1.f + gv[c] * (1.f - sg));
-            du[c] = dA * gv[c] * sg;
+          for (int q = 0; q < 4; ++q) {
+            const float dA = acc[i][j][4 * g + q];
+            const float sg = 1.f / (1.f + __expf(-gv[q]));
+            dg[q] = dA * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
+            du[q] = dA * gv[q] * sg;
           }
-          *reinterpret_cast<uint2*>(p.out + row * 2 * F + f) = pack4(dg[0], dg[1], dg[2], dg[3]);
-          *reinterpret_cast<uint2*>(p.out + row * 2 * F + F + f) = pack4(du[0], du[1], du[2], du[3]);
+          *pg = pack4(dg[0], dg[1], dg[2], dg[3]);
+          *pu = pack4(du[0], du[1], du[2], du[3]);
         }
+      __syncthreads();
+      for (int w = 0; w < TL::WGM; ++w) {
+        const int first = w * WM + i * 32, n = min(32, rows_valid - first);
+        if (n <= 0) continue;
+        band_store<TL::THREADS>(BandTile<2>{smem + w * 32 * BN * 2, BN}, 32, n, [&](int r) {
+          return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + f0);
+        });
+        band_store<TL::THREADS>(BandTile<2>{smem + RB * BN * 2 + w * 32 * BN * 2, BN}, 32, n,
+                                [&](int r) {
+          return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + F + f0);
+        });
+      }
     }
+    __syncthreads();  // the band buffers are reused by the next band
   }
 }
 
@@ -334,24 +514,32 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
 template <class TL, bool OUT_F32>
 __device__ __forceinline__ void wgrad_epilogue(void* C, int M, int N, int e, int mt, int nt,
                                                f32x16 (&acc)[TL::WMT][TL::WNT], int wm, int wn,
-                                               int lane) {
+                                               int lane, char* smem) {
+  constexpr int BN = TL::BN, WM = TL::WM, WN = TL::WN, ES = OUT_F32 ? 4 : 2;
+  const int rr = wm * 32 + (lane & 31);
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < TL::WMT; ++i) {
-    const int m = mt * TL::BM + wm * TL::WM + i * 32 + (lane & 31);
+    BandTile<ES> t{smem, BN};
 #pragma unroll
     for (int j = 0; j < TL::WNT; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = nt * TL::BN + wn * TL::WN + j * 32 + acc_col(g, lane);
-        const size_t o = (size_t(e) * M + m) * N + n;
         const f32x16& a = acc[i][j];
+        char* dst = t.at(rr, wn * WN + j * 32 + acc_col(g, lane));
         if constexpr (OUT_F32)
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(C) + o) =
-              make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+          *reinterpret_cast<float4*>(dst) = make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
         else
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(C) + o) =
-              pack4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+          *reinterpret_cast<uint2*>(dst) = pack4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
       }
+    __syncthreads();
+    for (int w = 0; w < TL::WGM; ++w) {
+      const int first = mt * TL::BM + w * WM + i * 32;
+      band_store<TL::THREADS>(BandTile<ES>{smem + w * 32 * BN * ES, BN}, 32, 32, [&](int r) {
+        return reinterpret_cast<char*>(C) + ((size_t(e) * M + first + r) * N + nt * BN) * ES;
+      });
+    }
+    __syncthreads();
   }
 }
 
