@@ -102,6 +102,12 @@ def cpu_baseline(cfg, inp, budget_s: float) -> dict:
                       f"numpy float64, {t:.1f} s"}
 
 
+def queue_capable(cfg) -> bool:
+    """Whether the forward of this workload runs as the persistent overlap kernel
+    (switched off in the library for now: never)."""
+    return False
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +120,8 @@ def main():
                     help="run one device copy of this many MiB first (reference for HBM counters)")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without per-kernel events (no roofline entry)")
+    ap.add_argument("--no-queue", action="store_true",
+                    help="forward as one kernel per step instead of the persistent overlap kernel")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's layer only: the expert-parallel exchange between "
@@ -124,13 +132,14 @@ def main():
 
     import mixture_experts_layer_31_amd as moe
     import moe_inputs as mi
-    from tests.layer_harness import Layer
+    from tests.layer_harness import Layer, desc_of
 
     cfg = mi.CONFIGS[args.config]
     t0 = time.perf_counter()
     inp = mi.make_inputs(cfg, threads=16)
     gen_s = time.perf_counter() - t0
-    L = Layer(cfg, inp, device="cuda:0")
+    flags = moe.MOE_FLAG_NO_QUEUE if args.no_queue else 0
+    L = Layer(cfg, inp, flags=flags, device="cuda:0")
     L.prepare()
     stream = torch.cuda.current_stream()
     if args.calib_copy_mib:
@@ -175,6 +184,26 @@ def main():
     status = L.check()
     if status != moe.MOE_OK:
         raise RuntimeError(moe.strerror(status))
+
+    # the persistent overlap forward against the one-kernel-per-step forward
+    f5 = None
+    if queue_capable(cfg):
+        f5 = {"reps": 10}
+        for key, fl in (("fwd_ms_queue", 0), ("fwd_ms_per_step", moe.MOE_FLAG_NO_QUEUE)):
+            L.desc = desc_of(cfg, fl)
+            L.fwd()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(f5["reps"]):
+                L.fwd()
+            b.record(stream)
+            torch.cuda.synchronize()
+            f5[key] = round(a.elapsed_time(b) / f5["reps"], 4)
+        L.desc = desc_of(cfg, flags)
+        status = L.check()
+        if status != moe.MOE_OK:
+            raise RuntimeError(moe.strerror(status))
 
     flops = cfg.fwd_flops() + cfg.bwd_flops()
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -221,6 +250,7 @@ def main():
         "peak_tflops": round(peak, 1),
         "frac_mfma_peak": round(tflops / peak, 4),
         "roofline": roof,
+        "f5_overlap": f5,
         "kernels": per_kernel,
         "input_gen_s": round(gen_s, 1),
     }

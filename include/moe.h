@@ -83,8 +83,21 @@ enum moe_status {
   MOE_ETIMEOUT = -7      /* (device) a bounded wait in a persistent kernel expired */
 };
 
-/* Flags (moe_desc.flags). */
-#define MOE_FLAG_NO_QUEUE 0x1u  /* forward: separate kernels instead of the persistent overlap kernel */
+/* Flags (moe_desc.flags).
+ *
+ * The library contains a persistent forward that runs dispatch, W1 + SwiGLU
+ * and W2 as one kernel over per-XCD ticket queues, the single-GPU form of the
+ * pages' overlap of token arrival with expert compute (Prime Mega MoE news
+ * item, "How does the fused kernel work?").  It is switched off in this
+ * build (its first GPU run stalled and the cause is not yet known): every
+ * forward runs one kernel per step and both flags below have no effect. */
+#define MOE_FLAG_NO_QUEUE 0x1u  /* forward: one kernel per step even where the persistent kernel applies */
+/* Diagnostics only: every bounded wait of the persistent forward targets a
+ * value that is never reached and gives up after a few polls, so moe_check
+ * reports MOE_ETIMEOUT; the outputs of that call are undefined.  Exists to
+ * test the timeout path without a real stall; no effect where the persistent
+ * kernel does not apply. */
+#define MOE_FLAG_QUEUE_TIMEOUT_TEST 0x2u
 
 /* Layer descriptor, passed by host pointer.  Requirements: T, E, K >= 1;
  * K <= E; E <= 1024; D % 64 == 0 and F % 64 == 0; T * K < 2^31. */

@@ -18,7 +18,7 @@ int check_desc(const moe_desc* d) {
   if (d->T <= 0 || d->D <= 0 || d->F <= 0 || d->E <= 0 || d->K <= 0) return MOE_EINVAL;
   if (d->K > d->E || d->E > 1024) return MOE_EINVAL;
   if (d->mode < MOE_FP32 || d->mode > MOE_FP8) return MOE_EINVAL;
-  if ((d->flags & ~int32_t(MOE_FLAG_NO_QUEUE)) != 0) return MOE_EINVAL;
+  if ((d->flags & ~int32_t(MOE_FLAG_NO_QUEUE | MOE_FLAG_QUEUE_TIMEOUT_TEST)) != 0) return MOE_EINVAL;
   const long long N = (long long)d->T * d->K;
   const long long widest = d->D > 2 * d->F ? d->D : 2 * d->F;
   if (N >= (1LL << 31) || N * widest >= (1LL << 46)) return MOE_EINVAL;
@@ -237,6 +237,10 @@ int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const flo
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool io_f32 = d->mode == MOE_FP32_BF16GEMM;
   if ((rc = launch_route(*d, L, topk_idx, sc, s))) return rc;
+  if (queue_capable(*d)) {
+    if ((rc = launch_fwd_queue(*d, L, x, io_f32, topk_w, g1, g2, sc, s))) return rc;
+    return launch_combine(*d, L, topk_w, y, io_f32, sc, s);
+  }
   if ((rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s))) return rc;
   if (fp8_mode(d->mode) && d->mode != MOE_FP8_BWD)
     rc = fp8_fwd_gemms(*d, L, static_cast<const char*>(wprep), sc, s);

@@ -35,6 +35,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // weight sizes, weight preparation and the quantised GEMM sequences.
 bool fp8_mode(int mode);
 size_t fp8_scratch_bytes(const moe_desc& d);
+size_t queue_scratch_bytes(const moe_desc& d);  // ticket tables and counters of the persistent forward
 size_t fp8_wprep_bytes(const moe_desc& d);
 
 inline Layout make_layout(const moe_desc& d) {
@@ -61,7 +62,7 @@ inline Layout make_layout(const moe_desc& d) {
   L.dh = take(N * 2 * F * ab);
   L.dxperm = take(N * D * ab);
   L.fp8 = take(fp8_scratch_bytes(d));
-  L.queue = take(4096);
+  L.queue = take(queue_scratch_bytes(d));
   L.total = o;
   return L;
 }
@@ -93,6 +94,11 @@ int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool 
 int launch_convert_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
 
 // Grouped GEMMs (MFMA).  See moe_gemm.hip.
+// Persistent forward (dispatch + W1 + SwiGLU + W2 in one launch); see moe_queue.hip.
+bool queue_capable(const moe_desc& d);
+int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_f32,
+                     const float* topk_w, const uint16_t* w1, const uint16_t* w2, char* scratch,
+                     hipStream_t s);
 int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
                      char* scratch, hipStream_t s);
 int fp8_prepare_weights(const moe_desc& d, const uint16_t* w1, const uint16_t* w2, char* wprep,

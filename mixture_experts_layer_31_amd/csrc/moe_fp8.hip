@@ -397,7 +397,7 @@ __global__ void __launch_bounds__(TL::THREADS, 1) f8_grouped_kernel(F8Args p) {
   zero(acc);
   mainloop8<TL, MX, false>(smem, sa, sb, ssa, ssb, p.K / 128, acc, wave, lane);
   static_assert(sizeof(smem) >= grouped_epi_lds<TL, EPI>(), "epilogue staging exceeds LDS");
-  grouped_epilogue<TL, EPI>(p.epi, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane, smem);
+  grouped_epilogue<TL, EPI>(p.epi, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane, smem, threadIdx.x);
 }
 
 // Per-expert FP8 weight-gradient GEMM over the expert's padded token steps.
@@ -430,7 +430,7 @@ __global__ void __launch_bounds__(TL::THREADS, 1) f8_wgrad_kernel(F8Args p) {
     mainloop8<TL, MX, true>(smem, sa, sb, ssa, ssb, ksteps, acc, wave, lane);
   }
   static_assert(sizeof(smem) >= wgrad_epi_lds<TL, OUT_F32>(), "epilogue staging exceeds LDS");
-  wgrad_epilogue<TL, OUT_F32>(p.C, p.M, p.N, e, mt, nt, acc, wm, wn, lane, smem);
+  wgrad_epilogue<TL, OUT_F32>(p.C, p.M, p.N, e, mt, nt, acc, wm, wn, lane, smem, threadIdx.x);
 }
 
 }  // namespace

@@ -52,7 +52,7 @@
 // tokens -> zero gradient, no atomics).  Workgroup ids are remapped so that
 // consecutive tiles of one expert land on the same XCD (hardware dispatch is
 // round-robin over the 8 XCDs) and share its L2.
-#include "moe_gemm_common.h"
+#include "moe_grouped.h"
 
 namespace moe {
 namespace {
@@ -60,81 +60,13 @@ namespace {
 using namespace gemm;
 
 
-struct GroupedArgs {
-  const int32_t* offsets;     // [E+1] first permuted row of each expert
-  const int32_t* tile_start;  // [E+1] prefix sum of ceil(count/BM)
-  int E, K, ntn, F;
-  const uint16_t* A;          // [rows, K] permuted activations (k-contiguous)
-  int lda;
-  const uint16_t* B;          // weights of expert 0; expert e at B + e*bstride
-  int64_t bstride;
-  int ldb;                    // row length of a weight matrix (elements)
-  int brows;                  // rows of a weight matrix
-  uint16_t* out;              // STORE: [rows, ldo]; SWIGLU: H [rows, 2F]; DSWIGLU: dH [rows, 2F]
-  int ldo;
-  uint16_t* out2;             // SWIGLU: A [rows, F]
-  const uint16_t* hsave;      // DSWIGLU: H [rows, 2F]
-};
-
-// B_T = false: B[e] is [N, K] (row n holds the k-run); true: B[e] is [K, N].
+// Token-grouped GEMM: one workgroup per (m-tile, n-tile) of the flat tile list.
 template <class TL, bool B_T, int EPI>
 __global__ void __launch_bounds__(TL::THREADS, 1) grouped_gemm_kernel(GroupedArgs p) {
-  constexpr int BM = TL::BM, BN = TL::BN, WM = TL::WM, WN = TL::WN;
-  constexpr int WMT = TL::WMT, WNT = TL::WNT, WAVES = TL::WAVES;
-  static_assert(EPI != EPI_SWIGLU || (WNT % 2 == 0 && !B_T), "SwiGLU pairs gate/up sub-tiles");
   __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
-
   const int l = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt_g = l / p.ntn, nt = l - mt_g * p.ntn;
-  if (mt_g >= p.tile_start[p.E]) return;
-  int lo = 0, hi = p.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.tile_start[mid] <= mt_g) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int e0 = p.offsets[e];
-  const int ne = p.offsets[e + 1] - e0;
-  const int m0 = (mt_g - p.tile_start[e]) * BM;  // first row of the tile within the expert
-  const int rows_valid = min(BM, ne - m0);
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
-
-  KStager<BM, WAVES, kBK * 2> sa;
-  sa.init(make_rsrc(p.A + size_t(e0) * p.lda, uint32_t(ne) * p.lda * 2),
-          [&](int r) { return r < rows_valid ? (m0 + r) * p.lda * 2 : -1; }, wave, lane);
-  const uint16_t* Be = p.B + size_t(e) * p.bstride;
-  const uint32_t bbytes = uint32_t(p.brows) * p.ldb * 2;
-  f32x16 acc[WMT][WNT];
-  zero(acc);
-  const int ktiles = p.K / kBK;
-  if constexpr (B_T) {
-    TStager<BN, WAVES> sb;
-    sb.init(make_rsrc(Be + nt * BN, bbytes - nt * BN * 2), p.ldb * 2, wave, lane);
-    mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, true>(smem, sa, sb, ktiles, acc, wave, lane);
-  } else {
-    KStager<BN, WAVES, kBK * 2> sb;
-    sb.init(make_rsrc(Be, bbytes),
-            [&](int n) {
-              int row;
-              if constexpr (EPI == EPI_SWIGLU) {
-                const int w = n / WN, rem = n % WN;
-                const int half = rem / (WN / 2), c = rem % (WN / 2);
-                row = half * p.F + nt * (BN / 2) + w * (WN / 2) + c;
-              } else {
-                row = nt * BN + n;
-              }
-              return row * p.ldb * 2;
-            },
-            wave, lane);
-    mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, false>(smem, sa, sb, ktiles, acc, wave, lane);
-  }
-
-  EpiArgs ea{p.out, p.ldo, p.out2, p.hsave, p.F};
-  static_assert(sizeof(smem) >= grouped_epi_lds<TL, EPI>(), "epilogue staging exceeds LDS");
-  grouped_epilogue<TL, EPI>(ea, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane, smem);
+  if (l / p.ntn >= p.tile_start[p.E]) return;
+  grouped_tile<TL, B_T, EPI>(p, decode_tile<TL::BM>(p, l), smem);
 }
 
 struct WgradArgs {
@@ -177,7 +109,7 @@ __global__ void __launch_bounds__(TL::THREADS, 1) wgrad_gemm_kernel(WgradArgs p)
   }
 
   static_assert(sizeof(smem) >= wgrad_epi_lds<TL, OUT_F32>(), "epilogue staging exceeds LDS");
-  wgrad_epilogue<TL, OUT_F32>(p.C, p.M, p.N, e, mt, nt, acc, wm, wn, lane, smem);
+  wgrad_epilogue<TL, OUT_F32>(p.C, p.M, p.N, e, mt, nt, acc, wm, wn, lane, smem, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------

@@ -44,7 +44,7 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds_base), "v"(voff), "s"(rsrc)
-               : "memory");
+               : "memory", "m0");
 }
 
 template <int N>
@@ -173,6 +173,16 @@ __device__ __forceinline__ void wait_vmcnt_n(int n) {
 }
 
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// threadIdx.x through an empty volatile asm: values derived from it are
+// recomputed where they are used instead of being hoisted out of an enclosing
+// loop (a persistent kernel would otherwise keep every per-thread address of
+// every work item's code live across the whole loop).
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
 
 // Scheduling pattern for one sub-step: NMF MFMAs with the NDS LDS reads of the
 // next fragments spread between them (group masks: 0x8 MFMA, 0x100 DS read).
@@ -352,24 +362,35 @@ struct BandTile {
   }
 };
 
+// 16-byte global store that is written through to the device-coherent level
+// (two agent-scope relaxed 8-byte stores), for data another workgroup of the
+// same launch reads after a flag handshake.
+__device__ __forceinline__ void store16_coherent(char* dst, uint4 v) {
+  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
+  __hip_atomic_store(d, uint64_t(v.x) | (uint64_t(v.y) << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d + 1, uint64_t(v.z) | (uint64_t(v.w) << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Cooperative copy of `rows` band rows (of which the first `valid` exist) from
 // LDS to global rows dst(row) (16 bytes per thread per step).
-template <int THREADS, int ES, class Dst>
-__device__ __forceinline__ void band_store(const BandTile<ES>& t, int rows, int valid, Dst dst) {
+template <int THREADS, int ES, bool COH = false, class Dst>
+__device__ __forceinline__ void band_store(const BandTile<ES>& t, int rows, int valid, int tid, Dst dst) {
   const int per_row = t.chunks();
-  for (int i = threadIdx.x; i < rows * per_row; i += THREADS) {
+  for (int i = tid; i < rows * per_row; i += THREADS) {
     const int r = i / per_row, c = i - r * per_row;
-    if (r < valid)
-      *reinterpret_cast<uint4*>(dst(r) + c * 16) =
-          *reinterpret_cast<const uint4*>(t.base + r * per_row * 16 + ((c ^ (r & (min(per_row, 32) - 1))) << 4));
+    if (r < valid) {
+      const uint4 v = *reinterpret_cast<const uint4*>(t.base + r * per_row * 16 + ((c ^ (r & (min(per_row, 32) - 1))) << 4));
+      if constexpr (COH) store16_coherent(dst(r) + c * 16, v);
+      else *reinterpret_cast<uint4*>(dst(r) + c * 16) = v;
+    }
   }
 }
 
 // Cooperative copy of global rows src(row) into a band tile (zeros for rows >= valid).
 template <int THREADS, int ES, class Src>
-__device__ __forceinline__ void band_load(const BandTile<ES>& t, int rows, int valid, Src src) {
+__device__ __forceinline__ void band_load(const BandTile<ES>& t, int rows, int valid, int tid, Src src) {
   const int per_row = t.chunks();
-  for (int i = threadIdx.x; i < rows * per_row; i += THREADS) {
+  for (int i = tid; i < rows * per_row; i += THREADS) {
     const int r = i / per_row, c = i - r * per_row;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (r < valid) v = *reinterpret_cast<const uint4*>(src(r) + c * 16);
@@ -391,11 +412,11 @@ constexpr int wgrad_epi_lds() { return TL::WGM * 32 * TL::BN * (OUT_F32 ? 4 : 2)
 // block and, per group g of four registers, four consecutive columns starting
 // at acc_col(g).  grow0 is the tile's first row in the permuted buffers; smem is
 // the (now free) pipeline LDS.
-template <class TL, int EPI>
+template <class TL, int EPI, bool COH2 = false>
 __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
                                                  f32x16 (&acc)[TL::WMT][TL::WNT], size_t grow0,
                                                  int rows_valid, int nt, int wm, int wn, int lane,
-                                                 char* smem) {
+                                                 char* smem, int tid) {
   constexpr int BN = TL::BN, WM = TL::WM, WN = TL::WN, WMT = TL::WMT, WNT = TL::WNT;
   constexpr int RB = TL::WGM * 32;  // rows per band
   const int rr = wm * 32 + (lane & 31);
@@ -418,7 +439,7 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
         const int first = w * WM + i * 32, n = min(32, rows_valid - first);
         if (n <= 0) continue;
         BandTile<2> sub{smem + w * 32 * BN * 2, BN};
-        band_store<TL::THREADS>(sub, 32, n, [&](int r) {
+        band_store<TL::THREADS>(sub, 32, n, tid, [&](int r) {
           return reinterpret_cast<char*>(p.out + (grow0 + first + r) * p.ldo + nt * BN);
         });
       }
@@ -447,13 +468,13 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
         if (n <= 0) continue;
         const int off = w * 32 * BN;  // bytes of 32 rows of BN/2 bf16
         const int f0 = nt * (BN / 2);
-        band_store<TL::THREADS>(BandTile<2>{smem + off, BN / 2}, 32, n, [&](int r) {
+        band_store<TL::THREADS>(BandTile<2>{smem + off, BN / 2}, 32, n, tid, [&](int r) {
           return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + f0);
         });
-        band_store<TL::THREADS>(BandTile<2>{smem + RB * BN + off, BN / 2}, 32, n, [&](int r) {
+        band_store<TL::THREADS>(BandTile<2>{smem + RB * BN + off, BN / 2}, 32, n, tid, [&](int r) {
           return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + F + f0);
         });
-        band_store<TL::THREADS>(BandTile<2>{smem + 2 * RB * BN + off, BN / 2}, 32, n, [&](int r) {
+        band_store<TL::THREADS, 2, COH2>(BandTile<2>{smem + 2 * RB * BN + off, BN / 2}, 32, n, tid, [&](int r) {
           return reinterpret_cast<char*>(p.out2 + (grow0 + first + r) * F + f0);
         });
       }
@@ -463,10 +484,10 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
       // stage H (gate and up) of the band's rows, coalesced
       for (int w = 0; w < TL::WGM; ++w) {
         const int first = w * WM + i * 32, n = max(0, min(32, rows_valid - first));
-        band_load<TL::THREADS>(BandTile<2>{smem + w * 32 * BN * 2, BN}, 32, n, [&](int r) {
+        band_load<TL::THREADS>(BandTile<2>{smem + w * 32 * BN * 2, BN}, 32, n, tid, [&](int r) {
           return reinterpret_cast<const char*>(p.hsave + (grow0 + first + r) * 2 * F + f0);
         });
-        band_load<TL::THREADS>(BandTile<2>{smem + RB * BN * 2 + w * 32 * BN * 2, BN}, 32, n,
+        band_load<TL::THREADS>(BandTile<2>{smem + RB * BN * 2 + w * 32 * BN * 2, BN}, 32, n, tid,
                                [&](int r) {
           return reinterpret_cast<const char*>(p.hsave + (grow0 + first + r) * 2 * F + F + f0);
         });
@@ -497,10 +518,10 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
       for (int w = 0; w < TL::WGM; ++w) {
         const int first = w * WM + i * 32, n = min(32, rows_valid - first);
         if (n <= 0) continue;
-        band_store<TL::THREADS>(BandTile<2>{smem + w * 32 * BN * 2, BN}, 32, n, [&](int r) {
+        band_store<TL::THREADS>(BandTile<2>{smem + w * 32 * BN * 2, BN}, 32, n, tid, [&](int r) {
           return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + f0);
         });
-        band_store<TL::THREADS>(BandTile<2>{smem + RB * BN * 2 + w * 32 * BN * 2, BN}, 32, n,
+        band_store<TL::THREADS>(BandTile<2>{smem + RB * BN * 2 + w * 32 * BN * 2, BN}, 32, n, tid,
                                 [&](int r) {
           return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + F + f0);
         });
@@ -514,7 +535,7 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
 template <class TL, bool OUT_F32>
 __device__ __forceinline__ void wgrad_epilogue(void* C, int M, int N, int e, int mt, int nt,
                                                f32x16 (&acc)[TL::WMT][TL::WNT], int wm, int wn,
-                                               int lane, char* smem) {
+                                               int lane, char* smem, int tid) {
   constexpr int BN = TL::BN, WM = TL::WM, WN = TL::WN, ES = OUT_F32 ? 4 : 2;
   const int rr = wm * 32 + (lane & 31);
   __syncthreads();
@@ -535,7 +556,7 @@ __device__ __forceinline__ void wgrad_epilogue(void* C, int M, int N, int e, int
     __syncthreads();
     for (int w = 0; w < TL::WGM; ++w) {
       const int first = mt * TL::BM + w * WM + i * 32;
-      band_store<TL::THREADS>(BandTile<ES>{smem + w * 32 * BN * ES, BN}, 32, 32, [&](int r) {
+      band_store<TL::THREADS>(BandTile<ES>{smem + w * 32 * BN * ES, BN}, 32, 32, tid, [&](int r) {
         return reinterpret_cast<char*>(C) + ((size_t(e) * M + first + r) * N + nt * BN) * ES;
       });
     }

@@ -1,0 +1,103 @@
+// Token-grouped GEMM tile: arguments, tile coordinates and the tile body,
+// shared by the one-launch-per-GEMM kernels and the persistent forward.
+#pragma once
+
+#include "moe_gemm_common.h"
+
+namespace moe {
+namespace gemm {
+
+struct GroupedArgs {
+  const int32_t* offsets;     // [E+1] first permuted row of each expert
+  const int32_t* tile_start;  // [E+1] prefix sum of ceil(count/BM)
+  int E, K, ntn, F;
+  const uint16_t* A;          // [rows, K] permuted activations (k-contiguous)
+  int lda;
+  const uint16_t* B;          // weights of expert 0; expert e at B + e*bstride
+  int64_t bstride;
+  int ldb;                    // row length of a weight matrix (elements)
+  int brows;                  // rows of a weight matrix
+  uint16_t* out;              // STORE: [rows, ldo]; SWIGLU: H [rows, 2F]; DSWIGLU: dH [rows, 2F]
+  int ldo;
+  uint16_t* out2;             // SWIGLU: A [rows, F]
+  const uint16_t* hsave;      // DSWIGLU: H [rows, 2F]
+};
+
+// Where flat tile l (= m-tile * ntn + n-tile, m-tiles expert-major) sits.
+struct TileCoord {
+  int e, e0, ne;     // expert, its first permuted row, its row count
+  int mt_g, nt;      // global m-tile index, n-tile index
+  int m0;            // first row of the tile within the expert
+  int rows_valid;    // rows of the tile that exist (1..BM)
+};
+
+template <int BM>
+__device__ __forceinline__ TileCoord decode_tile(const GroupedArgs& p, int l) {
+  TileCoord c;
+  c.mt_g = l / p.ntn;
+  c.nt = l - c.mt_g * p.ntn;
+  int lo = 0, hi = p.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.tile_start[mid] <= c.mt_g) lo = mid; else hi = mid;
+  }
+  c.e = lo;
+  c.e0 = p.offsets[c.e];
+  c.ne = p.offsets[c.e + 1] - c.e0;
+  c.m0 = (c.mt_g - p.tile_start[c.e]) * BM;
+  c.rows_valid = min(BM, c.ne - c.m0);
+  return c;
+}
+
+// One BM x BN output tile.  B_T = false: B[e] is [N, K] (row n holds the
+// k-run); true: B[e] is [K, N].  COH2: the SwiGLU activation output is written
+// with device-coherent stores (read by other workgroups in the same launch).
+template <class TL, bool B_T, int EPI, bool COH2 = false>
+__device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoord& c, char* smem) {
+  constexpr int BM = TL::BM, BN = TL::BN, WN = TL::WN;
+  constexpr int WMT = TL::WMT, WNT = TL::WNT, WAVES = TL::WAVES;
+  static_assert(EPI != EPI_SWIGLU || (WNT % 2 == 0 && !B_T), "SwiGLU pairs gate/up sub-tiles");
+  static_assert(TL::LDS >= grouped_epi_lds<TL, EPI>(), "epilogue staging exceeds LDS");
+  const int e = c.e, e0 = c.e0, ne = c.ne, m0 = c.m0, nt = c.nt, rows_valid = c.rows_valid;
+
+  const int tid = opaque_tid();
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+
+  KStager<BM, WAVES, kBK * 2> sa;
+  sa.init(make_rsrc(p.A + size_t(e0) * p.lda, uint32_t(ne) * p.lda * 2),
+          [&](int r) { return r < rows_valid ? (m0 + r) * p.lda * 2 : -1; }, wave, lane);
+  const uint16_t* Be = p.B + size_t(e) * p.bstride;
+  const uint32_t bbytes = uint32_t(p.brows) * p.ldb * 2;
+  f32x16 acc[WMT][WNT];
+  zero(acc);
+  const int ktiles = p.K / kBK;
+  if constexpr (B_T) {
+    TStager<BN, WAVES> sb;
+    sb.init(make_rsrc(Be + nt * BN, bbytes - nt * BN * 2), p.ldb * 2, wave, lane);
+    mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, true>(smem, sa, sb, ktiles, acc, wave, lane);
+  } else {
+    KStager<BN, WAVES, kBK * 2> sb;
+    sb.init(make_rsrc(Be, bbytes),
+            [&](int n) {
+              int row;
+              if constexpr (EPI == EPI_SWIGLU) {
+                const int w = n / WN, rem = n % WN;
+                const int half = rem / (WN / 2), cc = rem % (WN / 2);
+                row = half * p.F + nt * (BN / 2) + w * (WN / 2) + cc;
+              } else {
+                row = nt * BN + n;
+              }
+              return row * p.ldb * 2;
+            },
+            wave, lane);
+    mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, false>(smem, sa, sb, ktiles, acc, wave, lane);
+  }
+
+  EpiArgs ea{p.out, p.ldo, p.out2, p.hsave, p.F};
+  grouped_epilogue<TL, EPI, COH2>(ea, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane, smem, tid);
+}
+
+}  // namespace gemm
+}  // namespace moe

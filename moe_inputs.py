@@ -89,6 +89,12 @@ CONFIGS = {
     "dead_bf16": LayerConfig("dead_bf16", T=300, D=256, F=192, E=12, K=3,
                              routing="dead4", seed=2003),
     "wide_bf16": LayerConfig("wide_bf16", T=1100, D=1024, F=512, E=8, K=2, seed=2004),
+    # fp32 I/O with bf16 GEMMs, and skewed routing with dead experts, at shapes
+    # the persistent forward takes (D % 256 == 0, F % 128 == 0)
+    "mid_f32io": LayerConfig("mid_f32io", T=700, D=512, F=256, E=8, K=2,
+                             mode=MODE_FP32_BF16GEMM, seed=2005),
+    "zipf_bf16": LayerConfig("zipf_bf16", T=900, D=256, F=128, E=16, K=4, routing="zipf",
+                             seed=2006),
     # FP8 parity shapes (D, F multiples of 256): experts with several 256-row
     # tiles and 128-token steps, experts with fewer than 128 tokens, dead experts
     "fp8bwd_small": LayerConfig("fp8bwd_small", T=600, D=512, F=256, E=4, K=2,

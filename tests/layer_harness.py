@@ -90,6 +90,14 @@ class Layer:
         t = self.scratch[off:off + nbytes].view(dtype)
         return to_host(t).reshape(-1, cols) if cols else to_host(t)
 
+    def view_dev(self, which: int, cols: int, dtype=None) -> torch.Tensor:
+        """Device tensor over an intermediate inside the scratch (no copy)."""
+        rc, addr, nbytes = moe.moe_scratch_view(self.desc, self.scratch, which)
+        moe.check(rc, "scratch_view")
+        off = addr - self.scratch.data_ptr()
+        t = self.scratch[off:off + nbytes].view(dtype or torch.bfloat16)
+        return t.reshape(-1, cols) if cols else t
+
     def outputs(self) -> dict:
         return dict(y=to_host(self.y), dx=to_host(self.dx), dw1=to_host(self.dw1),
                     dw2=to_host(self.dw2), dprob=to_host(self.dprob))

@@ -19,7 +19,8 @@ pytestmark = pytest.mark.gpu
 
 TOL_BF16 = 1e-2
 
-SMALL = ["tiny_bf16gemm", "small_bf16", "dead_bf16", "mid_bf16", "wide_bf16"]
+SMALL = ["tiny_bf16gemm", "small_bf16", "dead_bf16", "mid_bf16", "wide_bf16", "mid_f32io",
+         "zipf_bf16"]
 
 
 @pytest.fixture(scope="module", autouse=True)
