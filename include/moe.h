@@ -19,7 +19,7 @@
  * Backward of a loss L with dL/dy = dy: dx, dW1, dW2 and dtopk_w = <dy_t, o>.
  *
  * Element types by mode:
- *   MOE_FP32            x y dy dx w1 w2 dw1 dw2 fp32; fp32 GEMMs       (not built yet)
+ *   MOE_FP32            x y dy dx w1 w2 dw1 dw2 fp32; fp32 GEMMs (vector ALU)
  *   MOE_FP32_BF16GEMM   fp32 storage, GEMM operands rounded to bf16, fp32 accumulate
  *   MOE_BF16            bf16 storage (raw 16-bit bfloat16), bf16 GEMMs, fp32 accumulate
  *   MOE_FP8_BWD         bf16 storage, bf16 forward, blockwise-FP8 backward GEMMs
@@ -32,8 +32,9 @@
  * one e8m0 scale 2^X per 32 contraction elements of every operand, X the
  * smallest integer with amax <= 448 * 2^X.  The FP8 modes need D % 256 == 0 and
  * F % 256 == 0, and `wprep` (filled by moe_prepare_weights) in moe_fwd/moe_bwd.
- * Intermediates are kept in bf16 (fp32 accumulators, rounded once when stored);
- * SwiGLU, its backward, the routing-weight products and all row sums are fp32.
+ * Intermediates are kept in bf16 (fp32 accumulators, rounded once when stored),
+ * in fp32 in MOE_FP32; SwiGLU, its backward, the routing-weight products and
+ * all row sums are fp32.
  *
  * Ownership and threading:
  *   - Every pointer is a device pointer unless noted.  The caller allocates and

@@ -28,7 +28,6 @@ int check_desc(const moe_desc* d) {
 
 // Modes whose kernels exist in this build, and their shape requirements.
 int check_built(const moe_desc* d) {
-  if (d->mode == MOE_FP32) return MOE_EUNSUPPORTED;
   if (fp8_mode(d->mode) && (d->D % 256 != 0 || d->F % 256 != 0)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
@@ -235,14 +234,17 @@ int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const flo
   const Layout L = make_layout(*d);
   char* sc = static_cast<char*>(scratch);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool io_f32 = d->mode == MOE_FP32_BF16GEMM;
+  const bool io_f32 = d->mode == MOE_FP32 || d->mode == MOE_FP32_BF16GEMM;
   if ((rc = launch_route(*d, L, topk_idx, sc, s))) return rc;
   if (queue_capable(*d)) {
     if ((rc = launch_fwd_queue(*d, L, x, io_f32, topk_w, g1, g2, sc, s))) return rc;
     return launch_combine(*d, L, topk_w, y, io_f32, sc, s);
   }
   if ((rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s))) return rc;
-  if (fp8_mode(d->mode) && d->mode != MOE_FP8_BWD)
+  if (d->mode == MOE_FP32)
+    rc = launch_fwd_gemms_f32(*d, L, static_cast<const float*>(w1), static_cast<const float*>(w2),
+                              sc, s);
+  else if (fp8_mode(d->mode) && d->mode != MOE_FP8_BWD)
     rc = fp8_fwd_gemms(*d, L, static_cast<const char*>(wprep), sc, s);
   else
     rc = launch_fwd_gemms(*d, L, g1, g2, sc, s);
@@ -267,9 +269,12 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
   const Layout L = make_layout(*d);
   char* sc = static_cast<char*>(scratch);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool io_f32 = d->mode == MOE_FP32_BF16GEMM;
+  const bool io_f32 = d->mode == MOE_FP32 || d->mode == MOE_FP32_BF16GEMM;
   if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s))) return rc;
-  if (fp8_mode(d->mode))
+  if (d->mode == MOE_FP32)
+    rc = launch_bwd_gemms_f32(*d, L, static_cast<const float*>(w1), static_cast<const float*>(w2),
+                              static_cast<float*>(dw1), static_cast<float*>(dw2), sc, s);
+  else if (fp8_mode(d->mode))
     rc = fp8_bwd_gemms(*d, L, static_cast<const char*>(wprep), dw1, dw2, sc, s);
   else
     rc = launch_bwd_gemms(*d, L, g1, g2, dw1, dw2, io_f32, sc, s);

@@ -94,6 +94,11 @@ int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool 
 int launch_convert_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
 
 // Grouped GEMMs (MFMA).  See moe_gemm.hip.
+// fp32 GEMMs of mode MOE_FP32 (moe_f32.hip).
+int launch_fwd_gemms_f32(const moe_desc& d, const Layout& L, const float* w1, const float* w2,
+                         char* scratch, hipStream_t s);
+int launch_bwd_gemms_f32(const moe_desc& d, const Layout& L, const float* w1, const float* w2,
+                         float* dw1, float* dw2, char* scratch, hipStream_t s);
 // Persistent forward (dispatch + W1 + SwiGLU + W2 in one launch); see moe_queue.hip.
 bool queue_capable(const moe_desc& d);
 int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_f32,

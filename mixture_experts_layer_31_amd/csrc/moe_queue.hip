@@ -45,8 +45,8 @@ using namespace gemm;
 constexpr int kChunkRows = 256;    // x_perm rows per dispatch item
 constexpr int kLead = 2;           // dispatch items placed ahead of the W1 tiles needing them
 constexpr int kXcds = 8;
-constexpr int kSpinLimit = 1 << 22;    // polls (each with s_sleep) before a wait gives up
-constexpr int kTestSpinLimit = 8;
+constexpr uint64_t kWaitTicks = 50000000;  // 0.5 s of the 100 MHz real-time counter per wait
+constexpr uint64_t kTestWaitTicks = 100;   // 1 us
 enum : int { kItemChunk = 0, kItemW1 = 1, kItemW2 = 2 };
 using TileQ = Tile<256, 256, 2, 4, 5>;
 
@@ -157,12 +157,18 @@ struct QueueArgs {
   const int* table;
   uint32_t* err;
   int nc;                  // dispatch items
-  int spin_limit, unreachable;  // test hook: waits target +unreachable
+  uint64_t wait_ticks;
+  int unreachable;         // test hook: waits target +unreachable
 };
 
-__device__ __forceinline__ void wait_at_least(const int* p, int target, int limit, uint32_t* err) {
-  for (int i = 0; i < limit; ++i) {
+// Polls *p until it reaches target, for at most limit_ticks of the 100 MHz
+// real-time counter; on expiry sets the timeout bit of the error word.
+__device__ __forceinline__ void wait_at_least(const int* p, int target, uint64_t limit_ticks,
+                                              uint32_t* err) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
     if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > limit_ticks) break;
     __builtin_amdgcn_s_sleep(2);
   }
   atomicOr(err, kErrTimeout);
@@ -224,26 +230,26 @@ __global__ void __launch_bounds__(TL::THREADS, 1) fwd_queue_kernel(QueueArgs q) 
       *slot = t < q.ctrl[kXcds + x] ? q.table[q.ctrl[2 * kXcds + x] + t] : -1;
     }
     __syncthreads();
-    const int item = *slot;
+    // broadcast through LDS, then made wave-uniform so that every branch below
+    // (all of which hold workgroup barriers) is a scalar branch
+    const int item = __builtin_amdgcn_readfirstlane(*slot);
     __syncthreads();  // the slot is pipeline LDS: read before the item reuses it
     if (item < 0) break;
     const int kind = item >> 28, idx = item & 0x0fffffff;
     // every table entry is rewritten by the build step; the range checks only
     // keep a corrupted table from turning into out-of-bounds accesses
-    if (kind == kItemChunk) {
-      if (idx >= q.nc) continue;
+    if (kind == kItemChunk && idx < q.nc) {
       dispatch_rows<TL::THREADS>(q, min(idx * kChunkRows, nvalid), min((idx + 1) * kChunkRows, nvalid));
       wait_vmcnt<0>();
       __syncthreads();
       if (threadIdx.x == 0)
         __hip_atomic_store(q.flags + idx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else if (kind == kItemW1) {
-      if (idx >= mtiles * q.w1.ntn) continue;
+    } else if (kind == kItemW1 && idx < mtiles * q.w1.ntn) {
       const TileCoord c = decode_tile<TL::BM>(q.w1, idx);
       if (threadIdx.x == 0) {
         const int r0 = c.e0 + c.m0, r1 = r0 + c.rows_valid - 1;
         for (int ch = r0 / kChunkRows; ch <= r1 / kChunkRows; ++ch)
-          wait_at_least(q.flags + ch, 1 + q.unreachable, q.spin_limit, q.err);
+          wait_at_least(q.flags + ch, 1 + q.unreachable, q.wait_ticks, q.err);
       }
       __syncthreads();
       grouped_tile<TL, false, EPI_SWIGLU, true>(q.w1, c, smem);
@@ -251,11 +257,10 @@ __global__ void __launch_bounds__(TL::THREADS, 1) fwd_queue_kernel(QueueArgs q) 
       __syncthreads();
       if (threadIdx.x == 0)
         __hip_atomic_fetch_add(q.f2done + c.mt_g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      if (kind != kItemW2 || idx >= mtiles * q.w2.ntn) continue;
+    } else if (kind == kItemW2 && idx < mtiles * q.w2.ntn) {
       const TileCoord c = decode_tile<TL::BM>(q.w2, idx);
       if (threadIdx.x == 0)
-        wait_at_least(q.f2done + c.mt_g, q.w1.ntn + q.unreachable, q.spin_limit, q.err);
+        wait_at_least(q.f2done + c.mt_g, q.w1.ntn + q.unreachable, q.wait_ticks, q.err);
       __syncthreads();
       grouped_tile<TL, false, EPI_STORE>(q.w2, c, smem);
     }
@@ -352,7 +357,7 @@ int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_
   q.nc = Q.nc;
   q.err = reinterpret_cast<uint32_t*>(scratch + L.err);
   const bool test = (d.flags & MOE_FLAG_QUEUE_TIMEOUT_TEST) != 0;
-  q.spin_limit = test ? kTestSpinLimit : kSpinLimit;
+  q.wait_ticks = test ? kTestWaitTicks : kWaitTicks;
   q.unreachable = test ? (1 << 28) : 0;
   const int cus = cu_count();
   const int grid = std::max(kXcds, cus / kXcds * kXcds);

@@ -12,6 +12,8 @@
 // and written once (combine): T*D*b + T*K*D*b bytes plus the index traffic.
 // A group of TPR = min(256, D/8) threads owns one token row; a thread moves
 // 16 bytes (8 bf16) per access, so a wavefront touches whole 128-byte lines.
+#include <type_traits>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -39,10 +41,32 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
   return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
 }
 
-template <bool IN_F32>
+// Eight consecutive elements of a row, as fp32, for either storage type
+// (bf16 bit patterns in uint16_t, or fp32); index i8 counts groups of eight.
+__device__ __forceinline__ void load8(const uint16_t* p, size_t i8, float (&f)[8]) {
+  unpack8(reinterpret_cast<const uint4*>(p)[i8], f);
+}
+__device__ __forceinline__ void load8(const float* p, size_t i8, float (&f)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[2 * i8];
+  const float4 b = reinterpret_cast<const float4*>(p)[2 * i8 + 1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+__device__ __forceinline__ void store8(uint16_t* p, size_t i8, const float (&f)[8]) {
+  reinterpret_cast<uint4*>(p)[i8] = pack8(f);
+}
+__device__ __forceinline__ void store8(float* p, size_t i8, const float (&f)[8]) {
+  reinterpret_cast<float4*>(p)[2 * i8] = make_float4(f[0], f[1], f[2], f[3]);
+  reinterpret_cast<float4*>(p)[2 * i8 + 1] = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+// IO: element type of the layer's inputs/outputs; ACT: of the permuted rows in
+// scratch (uint16_t = bf16, or float).  A bf16 -> bf16 or fp32 -> fp32 move is
+// a bitwise copy; fp32 -> bf16 rounds once (RNE).
+template <typename IO, typename ACT>
 __global__ void __launch_bounds__(kRowThreads) dispatch_kernel(
-    const void* __restrict__ rows, int T, int K, int D, const int32_t* __restrict__ pos,
-    const float* __restrict__ topk_w, float* __restrict__ wperm, uint16_t* __restrict__ dst) {
+    const IO* __restrict__ rows, int T, int K, int D, const int32_t* __restrict__ pos,
+    const float* __restrict__ topk_w, float* __restrict__ wperm, ACT* __restrict__ dst) {
   const int chunks = D / 8;
   const int tpr = chunks < kRowThreads ? chunks : kRowThreads;
   const int rpb = kRowThreads / tpr;
@@ -51,18 +75,20 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_kernel(
   if (t >= T || threadIdx.x >= rpb * tpr) return;
   const int32_t* prow = pos + size_t(t) * K;
   for (int c = c0; c < chunks; c += tpr) {
-    uint4 v;
-    if constexpr (IN_F32) {
-      const float4* src = reinterpret_cast<const float4*>(rows) + (size_t(t) * D + c * 8) / 4;
-      const float4 a = src[0], b = src[1];
-      const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      v = pack8(f);
+    const size_t src = (size_t(t) * D) / 8 + c;
+    if constexpr (std::is_same<IO, uint16_t>::value && std::is_same<ACT, uint16_t>::value) {
+      const uint4 v = reinterpret_cast<const uint4*>(rows)[src];
+      for (int k = 0; k < K; ++k) {
+        const int q = prow[k];
+        if (q >= 0) reinterpret_cast<uint4*>(dst)[(size_t(q) * D) / 8 + c] = v;
+      }
     } else {
-      v = reinterpret_cast<const uint4*>(rows)[(size_t(t) * D) / 8 + c];
-    }
-    for (int k = 0; k < K; ++k) {
-      const int q = prow[k];
-      if (q >= 0) reinterpret_cast<uint4*>(dst)[(size_t(q) * D) / 8 + c] = v;
+      float f[8];
+      load8(rows, src, f);
+      for (int k = 0; k < K; ++k) {
+        const int q = prow[k];
+        if (q >= 0) store8(dst, (size_t(q) * D) / 8 + c, f);
+      }
     }
   }
   if (wperm != nullptr) {
@@ -73,10 +99,12 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_kernel(
   }
 }
 
-template <bool OUT_F32, bool WEIGHTED>
+// Per-token gather-reduce over the K pair rows: combine (WEIGHTED: y_t =
+// sum_k w_tk * O[pos]) and the un-permute of dx (plain sum), fp32, k ascending.
+template <typename ACT, typename OUT, bool WEIGHTED>
 __global__ void __launch_bounds__(kRowThreads) gather_reduce_kernel(
-    const uint16_t* __restrict__ rows, const int32_t* __restrict__ pos,
-    const float* __restrict__ topk_w, int T, int K, int D, void* __restrict__ out) {
+    const ACT* __restrict__ rows, const int32_t* __restrict__ pos,
+    const float* __restrict__ topk_w, int T, int K, int D, OUT* __restrict__ out) {
   const int chunks = D / 8;
   const int tpr = chunks < kRowThreads ? chunks : kRowThreads;
   const int rpb = kRowThreads / tpr;
@@ -90,7 +118,7 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_kernel(
       const int q = prow[k];
       if (q < 0) continue;
       float f[8];
-      unpack8(reinterpret_cast<const uint4*>(rows)[(size_t(q) * D) / 8 + c], f);
+      load8(rows, (size_t(q) * D) / 8 + c, f);
       if constexpr (WEIGHTED) {
         const float w = topk_w[size_t(t) * K + k];
 #pragma unroll
@@ -100,26 +128,20 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_kernel(
         for (int i = 0; i < 8; ++i) acc[i] += f[i];
       }
     }
-    if constexpr (OUT_F32) {
-      float4* o = reinterpret_cast<float4*>(out) + (size_t(t) * D + c * 8) / 4;
-      o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-    } else {
-      reinterpret_cast<uint4*>(out)[(size_t(t) * D) / 8 + c] = pack8(acc);
-    }
+    store8(out, (size_t(t) * D) / 8 + c, acc);
   }
 }
 
 // Combine-backward: for each routed pair p of token t (row q = pos[p]),
-//   dYw_perm[q] = w_p * dy_t          (rounded once to bf16)
+//   dYw_perm[q] = w_p * dy_t          (fp32 product, stored as ACT)
 //   dtopk_w[p]  = <dy_t, O[q]>         (fp32, the routing-weight gradient)
 // One wavefront owns one token: its dy row stays in registers while the K
 // expert-output rows are streamed and dotted against it.  CPL = 16-byte chunks
 // per lane (D / 512, at least 1).
-template <bool IN_F32, int CPL>
+template <typename IO, typename ACT, int CPL>
 __global__ void __launch_bounds__(kRowThreads) dispatch_dy_kernel(
-    const void* __restrict__ dy, int T, int K, int D, const int32_t* __restrict__ pos,
-    const float* __restrict__ topk_w, const uint16_t* __restrict__ O, uint16_t* __restrict__ dst,
+    const IO* __restrict__ dy, int T, int K, int D, const int32_t* __restrict__ pos,
+    const float* __restrict__ topk_w, const ACT* __restrict__ O, ACT* __restrict__ dst,
     float* __restrict__ dprob) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
@@ -129,16 +151,7 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_dy_kernel(
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = lane + 64 * j;
-    if (c < chunks) {
-      if constexpr (IN_F32) {
-        const float4* src = reinterpret_cast<const float4*>(dy) + (size_t(t) * D + c * 8) / 4;
-        const float4 a = src[0], b = src[1];
-        v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
-        v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
-      } else {
-        unpack8(reinterpret_cast<const uint4*>(dy)[(size_t(t) * D) / 8 + c], v[j]);
-      }
-    }
+    if (c < chunks) load8(dy, (size_t(t) * D) / 8 + c, v[j]);
   }
   for (int k = 0; k < K; ++k) {
     const int p = t * K + k;
@@ -154,13 +167,13 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_dy_kernel(
       const int c = lane + 64 * j;
       if (c < chunks) {
         float o[8], sc[8];
-        unpack8(reinterpret_cast<const uint4*>(O)[(size_t(q) * D) / 8 + c], o);
+        load8(O, (size_t(q) * D) / 8 + c, o);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           dot = __builtin_fmaf(v[j][i], o[i], dot);
           sc[i] = w * v[j][i];
         }
-        reinterpret_cast<uint4*>(dst)[(size_t(q) * D) / 8 + c] = pack8(sc);
+        store8(dst, (size_t(q) * D) / 8 + c, sc);
       }
     }
 #pragma unroll
@@ -189,18 +202,28 @@ inline int row_blocks(const moe_desc& d) {
 
 }  // namespace
 
+// Element types of a mode: I/O fp32 in the fp32-storage modes, intermediates
+// fp32 only in MOE_FP32.
+template <class F>
+static int with_types(const moe_desc& d, bool io_f32, F f) {
+  if (d.mode == MOE_FP32) return f(float{}, float{});
+  if (io_f32) return f(float{}, uint16_t{});
+  return f(uint16_t{}, uint16_t{});
+}
+
 int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool in_f32,
                     const float* topk_w, char* scratch, size_t dst_off, hipStream_t s) {
   const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
   auto* wperm = topk_w ? reinterpret_cast<float*>(scratch + L.wperm) : nullptr;
-  auto* dst = reinterpret_cast<uint16_t*>(scratch + dst_off);
   prof_begin("dispatch", s);
-  if (in_f32)
-    dispatch_kernel<true><<<row_blocks(d), kRowThreads, 0, s>>>(rows, d.T, d.K, d.D, pos,
-                                                                  topk_w, wperm, dst);
-  else
-    dispatch_kernel<false><<<row_blocks(d), kRowThreads, 0, s>>>(rows, d.T, d.K, d.D, pos,
-                                                                   topk_w, wperm, dst);
+  with_types(d, in_f32, [&](auto io, auto act) {
+    using IO = decltype(io);
+    using ACT = decltype(act);
+    dispatch_kernel<IO, ACT><<<row_blocks(d), kRowThreads, 0, s>>>(
+        static_cast<const IO*>(rows), d.T, d.K, d.D, pos, topk_w, wperm,
+        reinterpret_cast<ACT*>(scratch + dst_off));
+    return 0;
+  });
   prof_end(s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
@@ -208,14 +231,15 @@ int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool i
 int launch_combine(const moe_desc& d, const Layout& L, const float* topk_w, void* y,
                    bool out_f32, const char* scratch, hipStream_t s) {
   const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
-  const auto* o = reinterpret_cast<const uint16_t*>(scratch + L.o);
   prof_begin("combine", s);
-  if (out_f32)
-    gather_reduce_kernel<true, true><<<row_blocks(d), kRowThreads, 0, s>>>(o, pos, topk_w, d.T,
-                                                                            d.K, d.D, y);
-  else
-    gather_reduce_kernel<false, true><<<row_blocks(d), kRowThreads, 0, s>>>(o, pos, topk_w, d.T,
-                                                                             d.K, d.D, y);
+  with_types(d, out_f32, [&](auto io, auto act) {
+    using IO = decltype(io);
+    using ACT = decltype(act);
+    gather_reduce_kernel<ACT, IO, true><<<row_blocks(d), kRowThreads, 0, s>>>(
+        reinterpret_cast<const ACT*>(scratch + L.o), pos, topk_w, d.T, d.K, d.D,
+        static_cast<IO*>(y));
+    return 0;
+  });
   prof_end(s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
@@ -223,25 +247,26 @@ int launch_combine(const moe_desc& d, const Layout& L, const float* topk_w, void
 int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
                      const char* scratch, hipStream_t s) {
   const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
-  const auto* rows = reinterpret_cast<const uint16_t*>(scratch + L.dxperm);
   prof_begin("unpermute", s);
-  if (out_f32)
-    gather_reduce_kernel<true, false><<<row_blocks(d), kRowThreads, 0, s>>>(rows, pos, nullptr,
-                                                                             d.T, d.K, d.D, dx);
-  else
-    gather_reduce_kernel<false, false><<<row_blocks(d), kRowThreads, 0, s>>>(rows, pos, nullptr,
-                                                                              d.T, d.K, d.D, dx);
+  with_types(d, out_f32, [&](auto io, auto act) {
+    using IO = decltype(io);
+    using ACT = decltype(act);
+    gather_reduce_kernel<ACT, IO, false><<<row_blocks(d), kRowThreads, 0, s>>>(
+        reinterpret_cast<const ACT*>(scratch + L.dxperm), pos, nullptr, d.T, d.K, d.D,
+        static_cast<IO*>(dx));
+    return 0;
+  });
   prof_end(s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-template <bool IN_F32>
-static int dispatch_dy_cpl(const moe_desc& d, const void* dy, const int32_t* pos,
-                           const float* topk_w, const uint16_t* o, uint16_t* dst, float* dprob,
+template <typename IO, typename ACT>
+static int dispatch_dy_cpl(const moe_desc& d, const IO* dy, const int32_t* pos,
+                           const float* topk_w, const ACT* o, ACT* dst, float* dprob,
                            hipStream_t s) {
   const unsigned blocks = unsigned((d.T + kRowThreads / 64 - 1) / (kRowThreads / 64));
   const int cpl = (d.D / 8 + 63) / 64;
-#define MOE_DY(C) dispatch_dy_kernel<IN_F32, C><<<blocks, kRowThreads, 0, s>>>(dy, d.T, d.K, d.D, pos, topk_w, o, dst, dprob)
+#define MOE_DY(C) dispatch_dy_kernel<IO, ACT, C><<<blocks, kRowThreads, 0, s>>>(dy, d.T, d.K, d.D, pos, topk_w, o, dst, dprob)
   if (cpl <= 1) MOE_DY(1);
   else if (cpl <= 2) MOE_DY(2);
   else if (cpl <= 4) MOE_DY(4);
@@ -255,11 +280,14 @@ static int dispatch_dy_cpl(const moe_desc& d, const void* dy, const int32_t* pos
 int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool in_f32,
                        const float* topk_w, float* dtopk_w, char* scratch, hipStream_t s) {
   const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
-  const auto* o = reinterpret_cast<const uint16_t*>(scratch + L.o);
-  auto* dst = reinterpret_cast<uint16_t*>(scratch + L.dyperm);
   prof_begin("dispatch_dy", s);
-  const int rc = in_f32 ? dispatch_dy_cpl<true>(d, dy, pos, topk_w, o, dst, dtopk_w, s)
-                        : dispatch_dy_cpl<false>(d, dy, pos, topk_w, o, dst, dtopk_w, s);
+  const int rc = with_types(d, in_f32, [&](auto io, auto act) {
+    using IO = decltype(io);
+    using ACT = decltype(act);
+    return dispatch_dy_cpl<IO, ACT>(d, static_cast<const IO*>(dy), pos, topk_w,
+                                    reinterpret_cast<const ACT*>(scratch + L.o),
+                                    reinterpret_cast<ACT*>(scratch + L.dyperm), dtopk_w, s);
+  });
   prof_end(s);
   if (rc) return rc;
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;

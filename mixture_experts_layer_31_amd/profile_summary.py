@@ -1,0 +1,179 @@
+"""Summarises rocprofv3 output of `bench.py` into the committed profile files.
+
+Inputs (CSV output of three rocprofv3 runs of the same bench command, which
+must include `--calib-copy-mib M`):
+  * `--kernel-trace --stats`  -> <trace>_kernel_trace.csv
+  * `--pmc FETCH_SIZE`        -> <fetch>_counter_collection.csv
+  * `--pmc WRITE_SIZE`        -> <write>_counter_collection.csv
+Outputs: profiles/layer_<config>_bf16.md (per-kernel durations and calibrated
+HBM bytes, with the commands) and profiles/traffic_<config>_bf16.json (the
+bytes per launch that bench.py reports as roofline traffic, keyed to a hash of
+the GEMM sources so a stale file is ignored).
+
+Kernels are named after the layer step they run: the GEMMs by their template
+arguments (operand layout and epilogue), the two weight-gradient GEMMs by grid
+size (the W1 one has twice the output tiles of the W2 one).  The calibration
+scales each counter so that the device copy of M MiB reads and writes M MiB.
+
+    python -m mixture_experts_layer_31_amd.profile_summary --config 30b \\
+        --trace gpurun_out/prof/trace --fetch gpurun_out/prof/fetch \\
+        --write gpurun_out/prof/write --calib-mib 512 --commands "..."
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+GEMM_SOURCES = [
+    "mixture_experts_layer_31_amd/csrc/moe_gemm.hip",
+    "mixture_experts_layer_31_amd/csrc/moe_gemm_common.h",
+    "mixture_experts_layer_31_amd/csrc/moe_grouped.h",
+    "mixture_experts_layer_31_amd/csrc/moe_common.h",
+]
+_GROUPED = {("false", "1"): "gemm_w1_swiglu", ("false", "0"): "gemm_w2",
+            ("true", "2"): "gemm_w2_dgrad_dswiglu", ("true", "0"): "gemm_w1_dgrad"}
+_PLAIN = [("clear_err_kernel", "clear_err"), ("route_count_kernel", "route_count"),
+          ("route_scan_kernel", "route_scan"), ("route_scatter_kernel", "route_scatter"),
+          ("dispatch_dy_kernel", "dispatch_dy"), ("dispatch_kernel", "dispatch"),
+          ("convert_bf16_kernel", "convert_bf16"), ("__amd_rocclr_copyBuffer", "copyBuffer")]
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def step_name(kernel: str) -> str | None:
+    m = re.search(r"grouped_gemm_kernel<.*Tile<[^>]*>, (true|false), (\d)>", kernel)
+    if m:
+        return _GROUPED.get((m.group(1), m.group(2)))
+    if "wgrad_gemm_kernel" in kernel:
+        return "wgrad"
+    m = re.search(r"gather_reduce_kernel<(true|false), (true|false)>", kernel)
+    if m:
+        return "combine" if m.group(2) == "true" else "unpermute"
+    for key, name in _PLAIN:
+        if key in kernel:
+            return name
+    return None
+
+
+def _grid(row) -> int:
+    for k in ("Grid_Size", "Grid_Size_X"):
+        if k in row and row[k] != "":
+            return int(float(row[k]))
+    return 0
+
+
+def _wgrad_split(rows):
+    """Names the two wgrad GEMMs: larger grid -> W1, smaller -> W2."""
+    grids = sorted({_grid(r) for r in rows if step_name(r["Kernel_Name"]) == "wgrad"})
+    names = {}
+    if len(grids) == 2:
+        names = {grids[0]: "gemm_w2_wgrad", grids[1]: "gemm_w1_wgrad"}
+    return names
+
+
+def name_rows(rows):
+    split = _wgrad_split(rows)
+    out = []
+    for r in rows:
+        n = step_name(r["Kernel_Name"])
+        if n == "wgrad":
+            n = split.get(_grid(r), "gemm_wgrad")
+        if n:
+            out.append((n, r))
+    return out
+
+
+def trace_table(prefix: str):
+    rows = list(csv.DictReader(open(prefix + "_kernel_trace.csv")))
+    dur = collections.defaultdict(list)
+    for n, r in name_rows(rows):
+        dur[n].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return dur
+
+
+def counter_table(prefix: str, counter: str):
+    rows = [r for r in csv.DictReader(open(prefix + "_counter_collection.csv"))
+            if r["Counter_Name"] == counter]
+    per = collections.defaultdict(list)
+    for n, r in name_rows(rows):
+        per[n].append(float(r["Counter_Value"]))  # KiB per dispatch
+    return per
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--config", required=True)
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--calib-mib", type=int, required=True)
+    ap.add_argument("--commands", required=True, help="the rocprofv3 commands, ';'-separated")
+    ap.add_argument("--workload", default="")
+    args = ap.parse_args()
+
+    dur = trace_table(args.trace)
+    fetch = counter_table(args.fetch, "FETCH_SIZE")
+    write = counter_table(args.write, "WRITE_SIZE")
+    mib_kib = args.calib_mib * 1024.0
+    rf = mib_kib / max(fetch["copyBuffer"]) if fetch.get("copyBuffer") else None
+    wf = mib_kib / max(write["copyBuffer"]) if write.get("copyBuffer") else None
+    if rf is None or wf is None:
+        raise SystemExit("no calibration copy in the counter runs (bench.py --calib-copy-mib)")
+
+    total = sum(sum(v) for k, v in dur.items() if k != "copyBuffer")
+    h = sources_hash()
+    kernels = {}
+    for n in sorted(fetch):
+        if n == "copyBuffer" or n not in write:
+            continue
+        f = sum(fetch[n]) / len(fetch[n]) * 1024 * rf
+        w = sum(write[n]) / len(write[n]) * 1024 * wf
+        kernels[n] = {"fetch_bytes": int(f), "write_bytes": int(w)}
+    rec = {"workload": args.workload or args.config, "source_sha256_16": h,
+           "sources": GEMM_SOURCES, "read_factor": round(rf, 4), "write_factor": round(wf, 4),
+           "kernels": kernels}
+    base = os.path.join(ROOT, "profiles")
+    with open(os.path.join(base, f"traffic_{args.config}_bf16.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+
+    lines = [f"# {args.config} layer, bf16: per-kernel time and HBM traffic", "",
+             f"Workload: {args.workload or args.config}.  GEMM source hash (sha256 of "
+             f"{', '.join(os.path.basename(p) for p in GEMM_SOURCES)}, first 16 hex digits): "
+             f"`{h}`.", "", "Commands (from the repository root on the GPU box):", ""]
+    lines += [f"    {c.strip()}" for c in args.commands.split(";") if c.strip()]
+    lines += ["", "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+              "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for n, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        if n == "copyBuffer":
+            continue
+        lines.append(f"| {n} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} | "
+                     f"{100 * sum(v) / total:.1f} |")
+    lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+              f"Calibration: the runs copy {args.calib_mib} MiB device-to-device first; FETCH_SIZE "
+              f"reads {max(fetch['copyBuffer']):.0f} KiB and WRITE_SIZE {max(write['copyBuffer']):.0f} "
+              f"KiB for it, so reads are scaled by {rf:.3f} and writes by {wf:.3f}.", "",
+              "| kernel | FETCH_SIZE KiB/launch | WRITE_SIZE KiB/launch | scaled read GB | scaled write GB |",
+              "|---|---|---|---|---|"]
+    for n, k in kernels.items():
+        fk = sum(fetch[n]) / len(fetch[n])
+        wk = sum(write[n]) / len(write[n])
+        lines.append(f"| {n} | {fk:.0f} | {wk:.0f} | {k['fetch_bytes'] / 1e9:.3f} | "
+                     f"{k['write_bytes'] / 1e9:.3f} |")
+    with open(os.path.join(base, f"layer_{args.config}_bf16.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -83,6 +83,13 @@ CONFIGS = {
                                mode=MODE_FP8_BWD, seed=1003),
     "30b_mxfp8": LayerConfig("30b_mxfp8", T=16384, D=2048, F=768, E=128, K=8,
                              mode=MODE_MXFP8, routing="zipf", seed=1004),
+    # one expert-parallel rank's share (EP = 8): 16 local experts receiving the
+    # 131072 routed rows of the 30B/235B layers, one row per received pair
+    # (top-1 over the local experts), so n_e is about 8192 and N, D, F and the
+    # flop count are those of the whole-layer workloads
+    "30b_ep_share": LayerConfig("30b_ep_share", T=131072, D=2048, F=768, E=16, K=1, seed=1005),
+    "235b_ep_share": LayerConfig("235b_ep_share", T=131072, D=4096, F=1536, E=16, K=1,
+                                 seed=1006),
     # parity shapes
     "small_bf16": LayerConfig("small_bf16", T=200, D=192, F=128, E=16, K=4, seed=2001),
     "mid_bf16": LayerConfig("mid_bf16", T=700, D=512, F=256, E=8, K=2, seed=2002),

@@ -81,7 +81,7 @@ def test_fwd_validation():
     assert _fwd(d, nbytes=moe.moe_scratch_bytes(d) - 1) == moe.MOE_ESCRATCH
     assert _fwd(moe.make_desc(64, 100, 64, 8, 2)) == moe.MOE_EUNSUPPORTED
     assert _fwd(moe.make_desc(64, 128, 96, 8, 2)) == moe.MOE_EUNSUPPORTED
-    for mode in (moe.MOE_FP32, moe.MOE_FP8_BWD, moe.MOE_MXFP8, moe.MOE_FP8):
+    for mode in (moe.MOE_FP8_BWD, moe.MOE_MXFP8, moe.MOE_FP8):  # FP8 modes need D, F % 256
         assert _fwd(moe.make_desc(64, 128, 64, 8, 2, mode)) == moe.MOE_EUNSUPPORTED
     assert _fwd(moe.make_desc(64, 128, 64, 8, 2, 9)) == moe.MOE_EINVAL
     assert _fwd(moe.make_desc(64, 128, 64, 8, 0)) == moe.MOE_EINVAL
