@@ -35,7 +35,6 @@ GEMM_SOURCES = [
     "mixture_experts_layer_31_amd/csrc/moe_gemm.hip",
     "mixture_experts_layer_31_amd/csrc/moe_gemm_common.h",
     "mixture_experts_layer_31_amd/csrc/moe_grouped.h",
-    "mixture_experts_layer_31_amd/csrc/moe_common.h",
 ]
 _GROUPED = {("false", "1"): "gemm_w1_swiglu", ("false", "0"): "gemm_w2",
             ("true", "2"): "gemm_w2_dgrad_dswiglu", ("true", "0"): "gemm_w1_dgrad"}
@@ -121,6 +120,8 @@ def main():
     ap.add_argument("--calib-mib", type=int, required=True)
     ap.add_argument("--commands", required=True, help="the rocprofv3 commands, ';'-separated")
     ap.add_argument("--workload", default="")
+    ap.add_argument("--skip", type=int, default=0,
+                    help="warm-up launches per kernel left out of the 'timed avg' column")
     args = ap.parse_args()
 
     dur = trace_table(args.trace)
@@ -154,12 +155,17 @@ def main():
              f"`{h}`.", "", "Commands (from the repository root on the GPU box):", ""]
     lines += [f"    {c.strip()}" for c in args.commands.split(";") if c.strip()]
     lines += ["", "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
-              "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+              f"'timed avg' leaves out the first {args.skip} launches of each kernel (the bench's "
+              "warm-up steps), matching the steps bench.py times.", "",
+              "| kernel | calls | avg us | timed avg us | min us | max us | % of GPU time |",
+              "|---|---|---|---|---|---|---|"]
     for n, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
         if n == "copyBuffer":
             continue
-        lines.append(f"| {n} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} | "
-                     f"{100 * sum(v) / total:.1f} |")
+        per_step = len(v) // (len(dur["dispatch"]) if dur.get("dispatch") else len(v)) or 1
+        timed = v[args.skip * per_step:] or v
+        lines.append(f"| {n} | {len(v)} | {sum(v) / len(v):.1f} | {sum(timed) / len(timed):.1f} | "
+                     f"{min(v):.1f} | {max(v):.1f} | {100 * sum(v) / total:.1f} |")
     lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
               f"Calibration: the runs copy {args.calib_mib} MiB device-to-device first; FETCH_SIZE "
               f"reads {max(fetch['copyBuffer']):.0f} KiB and WRITE_SIZE {max(write['copyBuffer']):.0f} "
