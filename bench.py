@@ -103,9 +103,8 @@ def cpu_baseline(cfg, inp, budget_s: float) -> dict:
 
 
 def queue_capable(cfg) -> bool:
-    """Whether the forward of this workload runs as the persistent overlap kernel
-    (switched off in the library for now: never)."""
-    return False
+    """Whether the forward of this workload runs as the overlapped one-launch kernel."""
+    return cfg.mode in (1, 2, 3) and cfg.D % 256 == 0 and (2 * cfg.F) % 256 == 0
 
 
 def main():
@@ -120,8 +119,8 @@ def main():
                     help="run one device copy of this many MiB first (reference for HBM counters)")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without per-kernel events (no roofline entry)")
-    ap.add_argument("--no-queue", action="store_true",
-                    help="forward as one kernel per step instead of the persistent overlap kernel")
+    ap.add_argument("--overlap", action="store_true",
+                    help="time the overlapped one-launch forward instead of one kernel per step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's layer only: the expert-parallel exchange between "
@@ -138,7 +137,7 @@ def main():
     t0 = time.perf_counter()
     inp = mi.make_inputs(cfg, threads=16)
     gen_s = time.perf_counter() - t0
-    flags = moe.MOE_FLAG_NO_QUEUE if args.no_queue else 0
+    flags = moe.MOE_FLAG_OVERLAP if args.overlap else 0
     L = Layer(cfg, inp, flags=flags, device="cuda:0")
     L.prepare()
     stream = torch.cuda.current_stream()
@@ -185,11 +184,11 @@ def main():
     if status != moe.MOE_OK:
         raise RuntimeError(moe.strerror(status))
 
-    # the persistent overlap forward against the one-kernel-per-step forward
+    # the overlapped one-launch forward against the one-kernel-per-step forward
     f5 = None
     if queue_capable(cfg):
         f5 = {"reps": 10}
-        for key, fl in (("fwd_ms_queue", 0), ("fwd_ms_per_step", moe.MOE_FLAG_NO_QUEUE)):
+        for key, fl in (("fwd_ms_overlapped", moe.MOE_FLAG_OVERLAP), ("fwd_ms_per_step", 0)):
             L.desc = desc_of(cfg, fl)
             L.fwd()
             torch.cuda.synchronize()

@@ -84,20 +84,21 @@ enum moe_status {
   MOE_ETIMEOUT = -7      /* (device) a bounded wait in a persistent kernel expired */
 };
 
-/* Flags (moe_desc.flags).
- *
- * The library contains a persistent forward that runs dispatch, W1 + SwiGLU
- * and W2 as one kernel over per-XCD ticket queues, the single-GPU form of the
- * pages' overlap of token arrival with expert compute (Prime Mega MoE news
- * item, "How does the fused kernel work?").  It is switched off in this
- * build (its first GPU run stalled and the cause is not yet known): every
- * forward runs one kernel per step and both flags below have no effect. */
-#define MOE_FLAG_NO_QUEUE 0x1u  /* forward: one kernel per step even where the persistent kernel applies */
-/* Diagnostics only: every bounded wait of the persistent forward targets a
- * value that is never reached and gives up after a few polls, so moe_check
- * reports MOE_ETIMEOUT; the outputs of that call are undefined.  Exists to
- * test the timeout path without a real stall; no effect where the persistent
- * kernel does not apply. */
+/* Flags (moe_desc.flags). */
+/* Forward as one overlapped launch: dispatch, W1 + SwiGLU and W2 ordered by
+ * per-XCD ticket queues, the single-GPU form of the pages' overlap of token
+ * arrival with expert compute (Prime Mega MoE news item, "How does the fused
+ * kernel work?"): a W1 tile starts as soon as the dispatch items holding its
+ * rows are written, a W2 tile as soon as the W1 tiles of its rows are done.
+ * Applies to the bf16-GEMM modes (MOE_FP32_BF16GEMM, MOE_BF16, MOE_FP8_BWD)
+ * with D % 256 == 0 and F % 128 == 0; elsewhere it has no effect.  Results are
+ * bit-identical to the default one-kernel-per-step forward, which is faster on
+ * MI355X at the Qwen3 shapes and therefore the default. */
+#define MOE_FLAG_OVERLAP 0x1u
+/* Diagnostics only, with MOE_FLAG_OVERLAP: every bounded wait of the
+ * overlapped forward targets a value that is never reached and gives up after
+ * 1 us, so moe_check reports MOE_ETIMEOUT; the outputs of that call are
+ * undefined.  Exists to test the timeout path without a real stall. */
 #define MOE_FLAG_QUEUE_TIMEOUT_TEST 0x2u
 
 /* Layer descriptor, passed by host pointer.  Requirements: T, E, K >= 1;

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 MOE_FP32, MOE_FP32_BF16GEMM, MOE_BF16, MOE_FP8_BWD, MOE_MXFP8, MOE_FP8 = range(6)
 MOE_OK, MOE_EINVAL, MOE_ESCRATCH, MOE_EALIGN, MOE_EUNSUPPORTED, MOE_EHIP, MOE_EINDEX, \
     MOE_ETIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7
-MOE_FLAG_NO_QUEUE = 0x1
+MOE_FLAG_OVERLAP = 0x1
 MOE_FLAG_QUEUE_TIMEOUT_TEST = 0x2
 (MOE_VIEW_XPERM, MOE_VIEW_H, MOE_VIEW_A, MOE_VIEW_O, MOE_VIEW_DYPERM, MOE_VIEW_DH,
  MOE_VIEW_DXPERM, MOE_VIEW_WPERM, MOE_VIEW_Q_ROWS, MOE_VIEW_Q_ROWS_SCALE, MOE_VIEW_Q_TOK_A,

@@ -1,37 +1,45 @@
-// Persistent forward: dispatch, W1 + SwiGLU and W2 in one launch, driven by
+// Overlapped forward: dispatch, W1 + SwiGLU and W2 in one launch, ordered by
 // per-XCD ticket queues.
 //
-// The pages overlap the arrival of tokens with expert compute: a persistent
-// kernel computes on a group of tokens as soon as that group has arrived,
-// keeping intermediates in GPU scratch buffers (Prime Mega MoE news item, "How
-// does the fused kernel work?").  On one GPU the "arrival" is the local
-// permute, so the same schedule here overlaps the (HBM-bound) dispatch with the
-// (matrix-core-bound) expert GEMMs and lets the W2 tiles of early experts fill
-// the tail of the W1 GEMM.
+// The pages overlap the arrival of tokens with expert compute: the kernel
+// computes on a group of tokens as soon as that group has arrived, keeping
+// intermediates in GPU scratch buffers (Prime Mega MoE news item, "How does the
+// fused kernel work?").  On one GPU the "arrival" is the local permute, so the
+// same schedule here overlaps the (HBM-bound) dispatch with the (matrix-core-
+// bound) expert GEMMs, and lets the W2 tiles of early experts fill the tail of
+// the W1 GEMM.
 //
-// Work items, per XCD (workgroup b runs on XCD b % 8 under round-robin dispatch):
-//   * dispatch item c: x_perm rows [256c, 256c + 256) gathered from x (and the
-//     matching routing weights), then flag[c] = 1;
-//   * W1 tile g: waits until the dispatch items holding its rows are flagged,
+// Partition: the expert-major list of 256-row m-tiles is cut into 8 contiguous
+// ranges, one per XCD (workgroup b takes its tickets from queue b % 8, and
+// round-robin dispatch places it on XCD b % 8, so an expert's tiles share one
+// L2).  XCD x owns the x_perm rows [R_x, R_x+1) of its m-tiles and the items
+//   * dispatch item: 256 of those rows gathered from x (with their routing
+//     weights), then flag[item] = 1;
+//   * W1 tile: waits until the dispatch items holding its rows are flagged,
 //     computes H and A = silu(gate) * up, then f2done[m-tile] += 1;
-//   * W2 tile h: waits until f2done[m-tile] equals the number of W1 tiles of
-//     that m-tile, then computes O.
-// XCD x owns the x-th eighth of each item list (W1 and W2 tiles in flat
-// expert-major order, so the tiles sharing an expert's weights share one L2).
-// Its ticket order merges its dispatch items into its W1 tiles so that each W1
-// tile comes kLead items after the last dispatch item it needs, then lists its
-// W2 tiles.  Items are taken in ticket order and an item only waits on items
-// with smaller tickets (dispatch items never wait), so the schedule cannot
-// deadlock whether or not every workgroup is resident; every wait is bounded
-// and reports MOE_ETIMEOUT through the error word when the bound is hit.
+//   * W2 tile: waits until f2done[m-tile] equals the number of W1 tiles of that
+//     m-tile, then computes O.
+// Its ticket order merges the dispatch items into the W1 tiles so that each W1
+// tile comes kLead items after the last dispatch item it needs, then lists the
+// W2 tiles.  Every workgroup takes one ticket, runs that one item and exits.
+// An item waits only on items of its own queue with smaller tickets, which
+// were taken by workgroups already running (dispatch items never wait), so the
+// schedule cannot deadlock whether or not all workgroups are resident.  Each
+// wait is bounded in time and reports MOE_ETIMEOUT through the error word.
+//
+// Selected with MOE_FLAG_OVERLAP.  On MI355X at the Qwen3 shapes it is slower
+// than one kernel per step (30B forward 2.4 ms against 1.9 ms): each workgroup
+// pays a ticket round trip before its tile starts, the rows crossing
+// workgroups are written through, and the L2 hit rate drops (67% against 76%
+// for the separate GEMMs), which outweighs the overlap it buys.
 //
 // Coherence: the XCDs' L2 caches are not coherent with each other.  Rows that
-// cross workgroups inside the launch (x_perm, A) are written with device-coherent
-// stores (written through to the coherence point), each producer waits for its
-// stores to complete before the flag is raised, and a consumer touches no line of
-// those rows before their flag is up (rows are whole 128-byte lines and a tile
-// reads only its own rows), so no XCD can hold a stale copy and consumers need
-// no cache invalidation.
+// cross workgroups inside the launch (x_perm, A) are written with device-
+// coherent stores (written through to the coherence point), each producer waits
+// for its stores to complete before its flag is raised, and a consumer touches
+// no line of those rows before their flag is up (rows are whole 128-byte lines
+// and a tile reads only its own rows), so no XCD holds a stale copy and
+// consumers need no cache invalidation.
 #include <algorithm>
 
 #include "moe_grouped.h"
@@ -42,17 +50,25 @@ namespace {
 
 using namespace gemm;
 
-constexpr int kChunkRows = 256;    // x_perm rows per dispatch item
-constexpr int kLead = 2;           // dispatch items placed ahead of the W1 tiles needing them
+// A dispatch item copies its rows on one CU, so it takes much longer than its
+// share of a whole-GPU copy; items are therefore small and placed far ahead of
+// the tiles that need them (measured at the 30B shape: 256-row items two ahead
+// took the forward from 1.9 to 3.8 ms, 64-row items 160 ahead to 2.4 ms).
+constexpr int kChunkRows = 64;  // x_perm rows per dispatch item
+constexpr int kLead = 160;      // dispatch items placed ahead of the W1 tiles needing them
 constexpr int kXcds = 8;
-constexpr uint64_t kWaitTicks = 50000000;  // 0.5 s of the 100 MHz real-time counter per wait
-constexpr uint64_t kTestWaitTicks = 100;   // 1 us
+constexpr uint64_t kWaitTicks = 2000000;  // 20 ms of the 100 MHz real-time counter per wait
+constexpr uint64_t kTestWaitTicks = 100;  // 1 us
 enum : int { kItemChunk = 0, kItemW1 = 1, kItemW2 = 2 };
 using TileQ = Tile<256, 256, 2, 4, 5>;
 
+// ctrl words: tickets [8], totals [8], table bases [8], row bounds R [9],
+// dispatch-item bases CB [9]
+enum : int { kTickets = 0, kTotals = 8, kBases = 16, kRows = 24, kChunkBase = 33, kCtrlWords = 42 };
+
 struct QLayout {
   size_t ctrl, flags, f2done, table, total;  // byte offsets inside the queue region
-  int nc, mt, ntn2, ntn3;
+  int nc, mt, ntn2, ntn3;                    // capacities: dispatch items, m-tiles; n-tiles
 };
 
 inline int max_mtiles256(const moe_desc& d) {
@@ -63,13 +79,13 @@ inline int max_mtiles256(const moe_desc& d) {
 inline QLayout qlayout(const moe_desc& d) {
   QLayout q{};
   const long long N = (long long)d.T * d.K;
-  q.nc = int((N + kChunkRows - 1) / kChunkRows);
+  q.nc = int((N + kChunkRows - 1) / kChunkRows) + kXcds;
   q.mt = max_mtiles256(d);
   q.ntn2 = (2 * d.F) / 256;
   q.ntn3 = d.D / 256;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
-  q.ctrl = take(3 * kXcds * 4);
+  q.ctrl = take(kCtrlWords * 4);
   q.flags = take(size_t(q.nc) * 4);
   q.f2done = take(size_t(q.mt) * 4);
   q.table = take((size_t(q.nc) + size_t(q.mt) * (q.ntn2 + q.ntn3)) * 4);
@@ -80,8 +96,8 @@ inline QLayout qlayout(const moe_desc& d) {
 struct BuildArgs {
   const int32_t* offsets;
   const int32_t* tile256;  // [E+1] prefix sum of ceil(count / 256)
-  int E, nc, ntn2, ntn3;
-  int* ctrl;               // [3][8]: tickets, totals, bases
+  int E, ntn2, ntn3;
+  int* ctrl;
   int* flags;
   int* f2done;
   int* table;
@@ -89,57 +105,83 @@ struct BuildArgs {
 
 __device__ __forceinline__ int part(int n, int x) { return int((long long)n * x / kXcds); }
 
+// Expert of global 256-row m-tile mt (largest e with tile256[e] <= mt).
+__device__ __forceinline__ int expert_of(const int32_t* tile256, int E, int mt) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile256[mid] <= mt) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 // Builds the per-XCD ticket tables and clears the counters for one forward.
 __global__ void __launch_bounds__(256) queue_build_kernel(BuildArgs a) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const int MT = a.tile256[a.E];
-  const int G2 = MT * a.ntn2, G3 = MT * a.ntn3, NC = a.nc;
-  auto base = [&](int x) { return part(NC, x) + part(G2, x) + part(G3, x); };
-  // last dispatch item holding a row of W1 tile g
-  auto need = [&](int g) {
-    const int mt = g / a.ntn2;
-    int lo = 0, hi = a.E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.tile256[mid] <= mt) lo = mid; else hi = mid;
-    }
-    const int e0 = a.offsets[lo], ne = a.offsets[lo + 1] - e0;
-    const int m0 = (mt - a.tile256[lo]) * 256;
-    return (e0 + m0 + min(256, ne - m0) - 1) / kChunkRows;
+  const int E = a.E, MT = a.tile256[E], nvalid = a.offsets[E];
+  // first x_perm row of m-tile mt (nvalid past the last one)
+  auto first_row = [&](int mt) {
+    if (mt >= MT) return nvalid;
+    const int e = expert_of(a.tile256, E, mt);
+    return a.offsets[e] + (mt - a.tile256[e]) * 256;
   };
-  // dispatch items of XCD x placed before its W1 tile g
+  int R[kXcds + 1], CB[kXcds + 1], BASE[kXcds + 1];
+  CB[0] = 0;
+  BASE[0] = 0;
+  for (int x = 0; x <= kXcds; ++x) R[x] = first_row(part(MT, x));
+  for (int x = 0; x < kXcds; ++x) {
+    const int nc = (R[x + 1] - R[x] + kChunkRows - 1) / kChunkRows;
+    const int nm = part(MT, x + 1) - part(MT, x);
+    CB[x + 1] = CB[x] + nc;
+    BASE[x + 1] = BASE[x] + nc + nm * (a.ntn2 + a.ntn3);
+  }
+  const int G2 = MT * a.ntn2, G3 = MT * a.ntn3, NC = CB[kXcds];
+  // XCD owning global m-tile mt
+  auto xcd_of_mtile = [&](int mt) {
+    int x = 0;
+    while (x + 1 < kXcds && part(MT, x + 1) <= mt) ++x;
+    return x;
+  };
+  // local dispatch items of XCD x placed before its W1 tile g
   auto before = [&](int g, int x) {
-    const int n = part(NC, x + 1) - part(NC, x);
-    return min(max(need(g) + 1 + kLead - part(NC, x), 0), n);
+    const int mt = g / a.ntn2;
+    const int e = expert_of(a.tile256, E, mt);
+    const int e0 = a.offsets[e], ne = a.offsets[e + 1] - e0, m0 = (mt - a.tile256[e]) * 256;
+    const int last = e0 + m0 + min(256, ne - m0) - 1;
+    return min((last - R[x]) / kChunkRows + 1 + kLead, CB[x + 1] - CB[x]);
   };
   if (i < G2) {
-    int x = 0;
-    while (x + 1 < kXcds && part(G2, x + 1) <= i) ++x;
-    a.table[base(x) + (i - part(G2, x)) + before(i, x)] = (kItemW1 << 28) | i;
+    const int x = xcd_of_mtile(i / a.ntn2);
+    a.table[BASE[x] + (i - part(MT, x) * a.ntn2) + before(i, x)] = (kItemW1 << 28) | i;
   }
   if (i < NC) {
     int x = 0;
-    while (x + 1 < kXcds && part(NC, x + 1) <= i) ++x;
-    const int cl = i - part(NC, x);
-    int lo = part(G2, x), hi = part(G2, x + 1);  // first W1 tile placed after this item
+    while (x + 1 < kXcds && CB[x + 1] <= i) ++x;
+    const int cl = i - CB[x];
+    int lo = part(MT, x) * a.ntn2, hi = part(MT, x + 1) * a.ntn2;  // first W1 tile after it
+    const int g0 = lo;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (before(mid, x) <= cl) lo = mid + 1; else hi = mid;
     }
-    a.table[base(x) + cl + (lo - part(G2, x))] = (kItemChunk << 28) | i;
+    a.table[BASE[x] + cl + (lo - g0)] = (kItemChunk << 28) | i;
     a.flags[i] = 0;
   }
   if (i < G3) {
-    int x = 0;
-    while (x + 1 < kXcds && part(G3, x + 1) <= i) ++x;
-    const int first = base(x) + (part(NC, x + 1) - part(NC, x)) + (part(G2, x + 1) - part(G2, x));
-    a.table[first + (i - part(G3, x))] = (kItemW2 << 28) | i;
+    const int x = xcd_of_mtile(i / a.ntn3);
+    const int nm = part(MT, x + 1) - part(MT, x);
+    a.table[BASE[x] + (CB[x + 1] - CB[x]) + nm * a.ntn2 + (i - part(MT, x) * a.ntn3)] =
+        (kItemW2 << 28) | i;
   }
   if (i < MT) a.f2done[i] = 0;
   if (i < kXcds) {
-    a.ctrl[i] = 0;
-    a.ctrl[kXcds + i] = base(i + 1) - base(i);
-    a.ctrl[2 * kXcds + i] = base(i);
+    a.ctrl[kTickets + i] = 0;
+    a.ctrl[kTotals + i] = BASE[i + 1] - BASE[i];
+    a.ctrl[kBases + i] = BASE[i];
+  }
+  if (i <= kXcds) {
+    a.ctrl[kRows + i] = R[i];
+    a.ctrl[kChunkBase + i] = CB[i];
   }
 }
 
@@ -156,7 +198,6 @@ struct QueueArgs {
   int* f2done;
   const int* table;
   uint32_t* err;
-  int nc;                  // dispatch items
   uint64_t wait_ticks;
   int unreachable;         // test hook: waits target +unreachable
 };
@@ -216,78 +257,65 @@ __device__ __forceinline__ void dispatch_rows(const QueueArgs& q, int r0, int r1
   }
 }
 
+// One work item per workgroup, in per-XCD ticket order.
 template <class TL>
 __global__ void __launch_bounds__(TL::THREADS, 1) fwd_queue_kernel(QueueArgs q) {
   __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
   typedef volatile __attribute__((address_space(3))) int lds_int;
   lds_int* slot = static_cast<lds_int*>(AS3(smem));
   const int x = blockIdx.x % kXcds;
-  const int nvalid = q.w1.offsets[q.w1.E];
+  if (threadIdx.x == 0) {
+    const int t = __hip_atomic_fetch_add(q.ctrl + kTickets + x, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    *slot = t < q.ctrl[kTotals + x] ? q.table[q.ctrl[kBases + x] + t] : -1;
+  }
+  __syncthreads();
+  // broadcast through LDS, then made wave-uniform so that the branches below
+  // (which hold workgroup barriers) are scalar branches
+  const int item = __builtin_amdgcn_readfirstlane(*slot);
+  __syncthreads();  // the slot is pipeline LDS: read before the item reuses it
+  if (item < 0) return;
+  const int kind = item >> 28, idx = item & 0x0fffffff;
   const int mtiles = q.w1.tile_start[q.w1.E];
-  for (;;) {
+  const int r_lo = q.ctrl[kRows + x], r_hi = q.ctrl[kRows + x + 1], cb = q.ctrl[kChunkBase + x];
+  // every table entry is rewritten by the build step; the range checks only
+  // keep a corrupted table from turning into out-of-bounds accesses
+  if (kind == kItemChunk && idx >= cb && idx < q.ctrl[kChunkBase + x + 1]) {
+    const int r0 = r_lo + (idx - cb) * kChunkRows;
+    dispatch_rows<TL::THREADS>(q, r0, min(r0 + kChunkRows, r_hi));
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_store(q.flags + idx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (kind == kItemW1 && idx < mtiles * q.w1.ntn) {
+    const TileCoord c = decode_tile<TL::BM>(q.w1, idx);
     if (threadIdx.x == 0) {
-      const int t = __hip_atomic_fetch_add(q.ctrl + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *slot = t < q.ctrl[kXcds + x] ? q.table[q.ctrl[2 * kXcds + x] + t] : -1;
+      const int first = c.e0 + c.m0, last = first + c.rows_valid - 1;
+      for (int ch = (first - r_lo) / kChunkRows; ch <= (last - r_lo) / kChunkRows; ++ch)
+        wait_at_least(q.flags + cb + ch, 1 + q.unreachable, q.wait_ticks, q.err);
     }
     __syncthreads();
-    // broadcast through LDS, then made wave-uniform so that every branch below
-    // (all of which hold workgroup barriers) is a scalar branch
-    const int item = __builtin_amdgcn_readfirstlane(*slot);
-    __syncthreads();  // the slot is pipeline LDS: read before the item reuses it
-    if (item < 0) break;
-    const int kind = item >> 28, idx = item & 0x0fffffff;
-    // every table entry is rewritten by the build step; the range checks only
-    // keep a corrupted table from turning into out-of-bounds accesses
-    if (kind == kItemChunk && idx < q.nc) {
-      dispatch_rows<TL::THREADS>(q, min(idx * kChunkRows, nvalid), min((idx + 1) * kChunkRows, nvalid));
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (threadIdx.x == 0)
-        __hip_atomic_store(q.flags + idx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else if (kind == kItemW1 && idx < mtiles * q.w1.ntn) {
-      const TileCoord c = decode_tile<TL::BM>(q.w1, idx);
-      if (threadIdx.x == 0) {
-        const int r0 = c.e0 + c.m0, r1 = r0 + c.rows_valid - 1;
-        for (int ch = r0 / kChunkRows; ch <= r1 / kChunkRows; ++ch)
-          wait_at_least(q.flags + ch, 1 + q.unreachable, q.wait_ticks, q.err);
-      }
-      __syncthreads();
-      grouped_tile<TL, false, EPI_SWIGLU, true>(q.w1, c, smem);
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(q.f2done + c.mt_g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else if (kind == kItemW2 && idx < mtiles * q.w2.ntn) {
-      const TileCoord c = decode_tile<TL::BM>(q.w2, idx);
-      if (threadIdx.x == 0)
-        wait_at_least(q.f2done + c.mt_g, q.w1.ntn + q.unreachable, q.wait_ticks, q.err);
-      __syncthreads();
-      grouped_tile<TL, false, EPI_STORE>(q.w2, c, smem);
-    }
+    grouped_tile<TL, false, EPI_SWIGLU, true>(q.w1, c, smem);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(q.f2done + c.mt_g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (kind == kItemW2 && idx < mtiles * q.w2.ntn) {
+    const TileCoord c = decode_tile<TL::BM>(q.w2, idx);
+    if (threadIdx.x == 0)
+      wait_at_least(q.f2done + c.mt_g, q.w1.ntn + q.unreachable, q.wait_ticks, q.err);
+    __syncthreads();
+    grouped_tile<TL, false, EPI_STORE>(q.w2, c, smem);
   }
-}
-
-int cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  return n;
 }
 
 }  // namespace
 
 size_t queue_scratch_bytes(const moe_desc& d) { return qlayout(d).total; }
 
-// Switched off: the first GPU run of this kernel (the small bf16 parity case)
-// stopped making progress and was killed, and the cause has not been
-// identified.  Until it is, every forward takes the one-kernel-per-step path;
-// the kernel is still compiled so that it keeps building.
-constexpr bool kQueueEnabled = false;
-
 bool queue_capable(const moe_desc& d) {
   const bool bf16_fwd = d.mode == MOE_FP32_BF16GEMM || d.mode == MOE_BF16 || d.mode == MOE_FP8_BWD;
-  return kQueueEnabled && bf16_fwd && (2 * d.F) % 256 == 0 && d.D % 256 == 0 &&
-         !(d.flags & MOE_FLAG_NO_QUEUE);
+  return bf16_fwd && (2 * d.F) % 256 == 0 && d.D % 256 == 0 && (d.flags & MOE_FLAG_OVERLAP);
 }
 
 int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_f32,
@@ -299,7 +327,6 @@ int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_
   b.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
   b.tile256 = reinterpret_cast<const int32_t*>(scratch + L.tiles[2]);
   b.E = d.E;
-  b.nc = Q.nc;
   b.ntn2 = Q.ntn2;
   b.ntn3 = Q.ntn3;
   b.ctrl = reinterpret_cast<int*>(qbase + Q.ctrl);
@@ -307,7 +334,8 @@ int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_
   b.f2done = reinterpret_cast<int*>(qbase + Q.f2done);
   b.table = reinterpret_cast<int*>(qbase + Q.table);
   const long long items = std::max<long long>(
-      {(long long)Q.nc, (long long)Q.mt * std::max(Q.ntn2, Q.ntn3), (long long)Q.mt, kXcds});
+      {(long long)Q.nc, (long long)Q.mt * std::max(Q.ntn2, Q.ntn3), (long long)Q.mt,
+       (long long)kXcds + 1});
   prof_begin("queue_build", s);
   queue_build_kernel<<<unsigned((items + 255) / 256), 256, 0, s>>>(b);
   prof_end(s);
@@ -354,13 +382,15 @@ int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_
   q.flags = b.flags;
   q.f2done = b.f2done;
   q.table = b.table;
-  q.nc = Q.nc;
   q.err = reinterpret_cast<uint32_t*>(scratch + L.err);
   const bool test = (d.flags & MOE_FLAG_QUEUE_TIMEOUT_TEST) != 0;
   q.wait_ticks = test ? kTestWaitTicks : kWaitTicks;
   q.unreachable = test ? (1 << 28) : 0;
-  const int cus = cu_count();
-  const int grid = std::max(kXcds, cus / kXcds * kXcds);
+  // per XCD at most ceil(mt/8) m-tiles, with their W1 and W2 tiles and the
+  // dispatch items of their rows (at most 256 / kChunkRows per m-tile), plus one
+  const long long per_xcd = (long long)(Q.mt + kXcds - 1) / kXcds *
+                                ((256 + kChunkRows - 1) / kChunkRows + Q.ntn2 + Q.ntn3) + 1;
+  const long long grid = per_xcd * kXcds;
   prof_begin("fwd_queue", s);
   fwd_queue_kernel<TileQ><<<unsigned(grid), TileQ::THREADS, 0, s>>>(q);
   prof_end(s);

@@ -1,5 +1,5 @@
-"""The persistent forward (dispatch + W1 + SwiGLU + W2 over ticket queues)
-against the one-kernel-per-step forward, through the C ABI.
+"""The overlapped forward (dispatch + W1 + SwiGLU + W2 in one launch over ticket
+queues) against the one-kernel-per-step forward, through the C ABI.
 
 Both paths run the same tile code in the same accumulation order, so every
 forward output and intermediate must agree bit for bit; the per-step path is
@@ -17,11 +17,7 @@ import mixture_experts_layer_31_amd as moe
 import moe_inputs as mi
 from tests.layer_harness import Layer
 
-pytestmark = [
-    pytest.mark.gpu,
-    pytest.mark.skip(reason="persistent forward switched off: its first GPU run (mid_bf16) "
-                            "stalled and the cause is not yet identified"),
-]
+pytestmark = pytest.mark.gpu
 
 QUEUE_CASES = ["mid_bf16", "wide_bf16", "mid_f32io", "zipf_bf16", "fp8bwd_small"]
 
@@ -69,8 +65,8 @@ def test_queue_forward_is_bitwise_the_per_step_forward(name):
     inp = mi.make_inputs(cfg)
     print(f"[case] {name} T={cfg.T} D={cfg.D} F={cfg.F} E={cfg.E} K={cfg.K} mode={cfg.mode}",
           flush=True)
-    Lq, rcq = _fwd(cfg, inp, 0)
-    Ls, rcs = _fwd(cfg, inp, moe.MOE_FLAG_NO_QUEUE)
+    Lq, rcq = _fwd(cfg, inp, moe.MOE_FLAG_OVERLAP)
+    Ls, rcs = _fwd(cfg, inp, 0)
     assert rcq == moe.MOE_OK and rcs == moe.MOE_OK
     nv = int(np.bincount(inp["topk_idx"].ravel(), minlength=cfg.E).sum())
     _assert_same(_views(Lq), _views(Ls), nv)
@@ -89,8 +85,8 @@ def test_queue_forward_with_out_of_range_indices():
     idx[5, 0] = cfg.E + 3
     idx[611, 1] = -1
     inp = dict(inp, topk_idx=idx)
-    Lq, rcq = _fwd(cfg, inp, 0)
-    Ls, rcs = _fwd(cfg, inp, moe.MOE_FLAG_NO_QUEUE)
+    Lq, rcq = _fwd(cfg, inp, moe.MOE_FLAG_OVERLAP)
+    Ls, rcs = _fwd(cfg, inp, 0)
     assert rcq == moe.MOE_EINDEX and rcs == moe.MOE_EINDEX
     nv = int(((idx >= 0) & (idx < cfg.E)).sum())
     _assert_same(_views(Lq), _views(Ls), nv)
@@ -99,10 +95,10 @@ def test_queue_forward_with_out_of_range_indices():
 def test_queue_timeout_is_reported_then_cleared():
     cfg = mi.CONFIGS["mid_bf16"]
     inp = mi.make_inputs(cfg)
-    L, rc = _fwd(cfg, inp, moe.MOE_FLAG_QUEUE_TIMEOUT_TEST)
+    L, rc = _fwd(cfg, inp, moe.MOE_FLAG_OVERLAP | moe.MOE_FLAG_QUEUE_TIMEOUT_TEST)
     assert rc == moe.MOE_ETIMEOUT
     assert L.check() == moe.MOE_OK  # cleared by the read
-    L2, rc2 = _fwd(cfg, inp, 0)
+    L2, rc2 = _fwd(cfg, inp, moe.MOE_FLAG_OVERLAP)
     assert rc2 == moe.MOE_OK
 
 
@@ -111,10 +107,10 @@ def test_queue_forward_full_size_30b_bitwise():
     cfg = mi.CONFIGS["30b"]
     inp = mi.make_inputs(cfg)
     print("[case] 30b queue vs per-step forward", flush=True)
-    Lq, rcq = _fwd(cfg, inp, 0)
+    Lq, rcq = _fwd(cfg, inp, moe.MOE_FLAG_OVERLAP)
     vq = _views(Lq)
     del Lq
     torch.cuda.empty_cache()
-    Ls, rcs = _fwd(cfg, inp, moe.MOE_FLAG_NO_QUEUE)
+    Ls, rcs = _fwd(cfg, inp, 0)
     assert rcq == moe.MOE_OK and rcs == moe.MOE_OK
     _assert_same(vq, _views(Ls), cfg.N)
