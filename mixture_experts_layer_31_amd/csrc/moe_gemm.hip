@@ -105,7 +105,8 @@ __global__ void __launch_bounds__(TL::THREADS, 1) wgrad_gemm_kernel(WgradArgs p)
             p.M * 2, wave, lane);
     sb.init(make_rsrc(p.B + size_t(off) * p.N + nt * BN, uint32_t(ne) * p.N * 2 - nt * BN * 2),
             p.N * 2, wave, lane);
-    mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, true, true>(smem, sa, sb, ktiles, acc, wave, lane);
+    mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, true, true, TL::WMT>(smem, sa, sb, ktiles, acc,
+                                                                         wave, lane);
   }
 
   static_assert(sizeof(smem) >= wgrad_epi_lds<TL, OUT_F32>(), "epilogue staging exceeds LDS");

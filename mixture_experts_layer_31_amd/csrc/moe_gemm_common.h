@@ -214,11 +214,28 @@ __device__ __forceinline__ void interleave_mfma_ds() {
 // a k-step are spread over its sub-steps instead of issued in one burst.  The
 // steady-state body has no branches; the last STAGES-1 k-steps run a copy
 // without loads.
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_T, bool B_T, class SA, class SB>
+// Calls f(std::integral_constant<int, A>) for the largest A <= TOP with A <= act
+// (act is wave-uniform, so this is a chain of scalar branches).
+template <int TOP, class F>
+__device__ __forceinline__ void with_active(int act, F&& f) {
+  if constexpr (TOP == 0) {
+    f(std::integral_constant<int, 0>{});
+  } else {
+    if (act >= TOP) f(std::integral_constant<int, TOP>{});
+    else with_active<TOP - 1>(act, f);
+  }
+}
+
+// ACT: how many of this wave's 32-row blocks of A hold rows (the rest of a
+// ragged last tile are past the expert's end): only those are read and
+// multiplied.  Every variant issues the same loads and barriers.
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_T, bool B_T, int ACT, class SA,
+          class SB>
 __device__ __forceinline__ void mainloop(char* smem, const SA& sa, const SB& sb, int ktiles,
                                          f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int wave,
                                          int lane) {
   constexpr int WM = BM / WGM, WN = BN / WGN, WMT = WM / 32, WNT = WN / 32, KK = kBK / 16;
+  static_assert(ACT >= 0 && ACT <= WMT, "active blocks within the wave tile");
   constexpr int A_BYTES = BM * kBK * 2, STAGE = (BM + BN) * kBK * 2;
   constexpr int NI = SA::NI + SB::NI;  // DMA instructions per wave per k-step
   static_assert(STAGES >= 3 && STAGES - 2 <= 3, "ring of 3 to 5 k-steps");
@@ -228,10 +245,11 @@ __device__ __forceinline__ void mainloop(char* smem, const SA& sa, const SB& sb,
 
   struct Frags { bf16x8 a[WMT], b[WNT]; };
   auto load = [&](int kt, int kk, Frags& f) {
+    if constexpr (ACT == 0) return;
     const char* ta = smem + (kt % STAGES) * STAGE;
     const char* tb = ta + A_BYTES;
 #pragma unroll
-    for (int i = 0; i < WMT; ++i) {
+    for (int i = 0; i < ACT; ++i) {
       const int r0 = wm * WM + i * 32;
       if constexpr (A_T) f.a[i] = frag_t<BM>(ta, r0, kk, lane);
       else f.a[i] = frag_k(ta, r0 + (lane & 31), kk, lane);
@@ -245,7 +263,7 @@ __device__ __forceinline__ void mainloop(char* smem, const SA& sa, const SB& sb,
   };
   auto mma = [&](const Frags& f, int m0, int m1) {
 #pragma unroll
-    for (int m = 0; m < WMT * WNT; ++m)
+    for (int m = 0; m < ACT * WNT; ++m)
       if (m >= m0 && m < m1) {
         const int i = m / WNT, j = m % WNT;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
@@ -269,8 +287,8 @@ __device__ __forceinline__ void mainloop(char* smem, const SA& sa, const SB& sb,
   load(0, 0, f0);
 
   // LDS read instructions per fragment set (a transposed fragment takes two)
-  constexpr int NDS = WMT * (A_T ? 2 : 1) + WNT * (B_T ? 2 : 1);
-  constexpr int NMF = WMT * WNT;
+  constexpr int NDS = ACT == 0 ? 0 : ACT * (A_T ? 2 : 1) + WNT * (B_T ? 2 : 1);
+  constexpr int NMF = ACT * WNT;
   auto step = [&](int kt, auto dma_on) {
     constexpr bool DMA = decltype(dma_on)::value;
     const int kn = kt + STAGES - 1;

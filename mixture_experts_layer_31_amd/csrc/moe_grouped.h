@@ -73,10 +73,15 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoo
   f32x16 acc[WMT][WNT];
   zero(acc);
   const int ktiles = p.K / kBK;
+  // 32-row blocks of this wave's share of the tile that hold rows
+  const int act = min(WMT, max(0, (rows_valid - wm * TL::WM + 31) / 32));
   if constexpr (B_T) {
     TStager<BN, WAVES> sb;
     sb.init(make_rsrc(Be + nt * BN, bbytes - nt * BN * 2), p.ldb * 2, wave, lane);
-    mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, true>(smem, sa, sb, ktiles, acc, wave, lane);
+    with_active<WMT>(act, [&](auto a) {
+      mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, true, decltype(a)::value>(
+          smem, sa, sb, ktiles, acc, wave, lane);
+    });
   } else {
     KStager<BN, WAVES, kBK * 2> sb;
     sb.init(make_rsrc(Be, bbytes),
@@ -92,7 +97,10 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoo
               return row * p.ldb * 2;
             },
             wave, lane);
-    mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, false>(smem, sa, sb, ktiles, acc, wave, lane);
+    with_active<WMT>(act, [&](auto a) {
+      mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, false, decltype(a)::value>(
+          smem, sa, sb, ktiles, acc, wave, lane);
+    });
   }
 
   EpiArgs ea{p.out, p.ldo, p.out2, p.hsave, p.F};

@@ -102,6 +102,10 @@ CONFIGS = {
                              mode=MODE_FP32_BF16GEMM, seed=2005),
     "zipf_bf16": LayerConfig("zipf_bf16", T=900, D=256, F=128, E=16, K=4, routing="zipf",
                              seed=2006),
+    # degenerate shapes: one token; one expert; every expert chosen (K = E)
+    "one_token": LayerConfig("one_token", T=1, D=128, F=64, E=4, K=2, seed=2101),
+    "one_expert": LayerConfig("one_expert", T=100, D=128, F=64, E=1, K=1, seed=2102),
+    "all_experts": LayerConfig("all_experts", T=50, D=128, F=128, E=8, K=8, seed=2103),
     # FP8 parity shapes (D, F multiples of 256): experts with several 256-row
     # tiles and 128-token steps, experts with fewer than 128 tokens, dead experts
     "fp8bwd_small": LayerConfig("fp8bwd_small", T=600, D=512, F=256, E=4, K=2,

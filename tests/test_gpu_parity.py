@@ -196,3 +196,39 @@ def test_full_size_235b_sampled():
 def test_full_size_30b_ep_share_sampled():
     # one expert-parallel rank's share: 16 experts with about 8192 rows each
     _full_size("30b_ep_share", ntok=24, nexp=1)
+
+
+def _check_layer(cfg, inp, tol=TOL_BF16):
+    L = _run(cfg, inp)
+    _routing_bitexact(L, inp["topk_idx"])
+    f = orc.forward(inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"], inp["w2"])
+    b = orc.backward(inp["dy"], inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"], inp["w2"], f)
+    out = L.outputs()
+    errs = {k: rel_err(out[k], ref) for k, ref in
+            (("y", f["y"]), ("dx", b["dx"]), ("dw1", b["dw1"]), ("dw2", b["dw2"]),
+             ("dprob", b["dprob"]))}
+    print(cfg.name, errs, flush=True)
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
+    return L, out, b
+
+
+@pytest.mark.parametrize("name", ["one_token", "one_expert", "all_experts"])
+def test_degenerate_shapes(name):
+    cfg = mi.CONFIGS[name]
+    print(f"[case] {name} T={cfg.T} D={cfg.D} F={cfg.F} E={cfg.E} K={cfg.K}", flush=True)
+    _check_layer(cfg, mi.make_inputs(cfg))
+
+
+def test_all_pairs_on_two_experts():
+    # maximal skew: every token picks experts 0 and 1 (in either slot order);
+    # the other six get no rows and must get exactly zero weight gradients
+    cfg = mi.CONFIGS["mid_bf16"]
+    inp = mi.make_inputs(cfg)
+    idx = np.zeros_like(inp["topk_idx"])
+    idx[:, 1] = 1
+    idx[::3] = idx[::3, ::-1]
+    print("[case] mid_bf16 with all pairs on experts 0 and 1", flush=True)
+    L, out, b = _check_layer(cfg, dict(inp, topk_idx=idx))
+    for e in range(2, cfg.E):
+        assert np.all(out["dw1"][e] == 0) and np.all(out["dw2"][e] == 0)
