@@ -21,7 +21,8 @@ routing variant are this project's readings (the pages do not state them):
   logits before the softmax.
 
 Every tensor gets its own numpy PCG64 child stream spawned from one
-SeedSequence, in a fixed order, so a tensor does not change when another is
+SeedSequence, in a fixed order (logits, permutation, x, W1, W2, dY, then the
+router's upstream gradient dtopk_w), so a tensor does not change when another is
 resized.  Expert weights take one child per expert so they can be drawn in
 parallel threads.
 """
@@ -151,10 +152,11 @@ def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
     return a
 
 
-def _route(rng_logits: np.random.Generator, rng_perm: np.random.Generator,
-           cfg: LayerConfig):
-    """Draw logits and turn them into a top-k routing decision (input generation)."""
-    T, E, K = cfg.T, cfg.E, cfg.K
+def _router_logits(rng_logits: np.random.Generator, rng_perm: np.random.Generator,
+                   cfg: LayerConfig) -> np.ndarray:
+    """Router logits [T, E] float32: N(0, 1) draws plus the routing variant's
+    per-expert bias (-inf for dead experts)."""
+    T, E = cfg.T, cfg.E
     logits = rng_logits.standard_normal((T, E), dtype=np.float32)
     bias = np.zeros(E, np.float32)
     if cfg.routing == "zipf":
@@ -172,7 +174,16 @@ def _route(rng_logits: np.random.Generator, rng_perm: np.random.Generator,
         bias[perm[E - ndead:]] = -np.inf
     elif cfg.routing != "uniform":
         raise ValueError(cfg.routing)
-    z = logits + bias[None, :]
+    return logits + bias[None, :]
+
+
+def _route(rng_logits: np.random.Generator, rng_perm: np.random.Generator,
+           cfg: LayerConfig):
+    """Draw logits and turn them into a top-k routing decision (input generation:
+    the layer consumes a routing decision; the router step itself is checked
+    against its own oracle, never against this draw)."""
+    K = cfg.K
+    z = _router_logits(rng_logits, rng_perm, cfg)
     z = z - z.max(axis=1, keepdims=True)
     p = np.exp(z, dtype=np.float32)
     p /= p.sum(axis=1, keepdims=True)
@@ -190,6 +201,19 @@ def make_routing(cfg: LayerConfig):
     c_logits, c_perm = ss.spawn(6)[:2]
     return _route(np.random.Generator(np.random.PCG64(c_logits)),
                   np.random.Generator(np.random.PCG64(c_perm)), cfg)
+
+
+def make_router_inputs(cfg: LayerConfig) -> dict:
+    """Inputs of the router step of a workload: the float32 logits [T, E] the
+    workload's routing decision is drawn from, and an upstream gradient
+    dtopk_w [T, K] ~ N(0, 1) float32 (its own child stream)."""
+    ss = np.random.SeedSequence(cfg.seed)
+    kids = ss.spawn(7)
+    c_logits, c_perm, c_dw = kids[0], kids[1], kids[6]
+    z = _router_logits(np.random.Generator(np.random.PCG64(c_logits)),
+                       np.random.Generator(np.random.PCG64(c_perm)), cfg)
+    dw = np.random.Generator(np.random.PCG64(c_dw)).standard_normal((cfg.T, cfg.K), dtype=np.float32)
+    return {"logits": np.ascontiguousarray(z, np.float32), "dtopk_w": dw}
 
 
 def make_inputs(cfg: LayerConfig, threads: int = 8, with_dy: bool = True) -> dict:
