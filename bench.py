@@ -204,6 +204,36 @@ def main():
         if status != moe.MOE_OK:
             raise RuntimeError(moe.strerror(status))
 
+    # the router ahead of the layer (softmax -> top-k -> renormalise, and its
+    # backward to the logits), timed on its own: not part of the layer step
+    router = None
+    if cfg.E <= 512 and cfg.K <= 64:
+        r = mi.make_router_inputs(cfg)
+        rd = moe.make_desc(cfg.T, 0, 0, cfg.E, cfg.K)
+        z = torch.from_numpy(r["logits"]).to("cuda:0")
+        rdw = torch.from_numpy(r["dtopk_w"]).to("cuda:0")
+        ridx = torch.empty((cfg.T, cfg.K), dtype=torch.int32, device="cuda:0")
+        rw = torch.empty((cfg.T, cfg.K), dtype=torch.float32, device="cuda:0")
+        rdz = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda:0")
+        router = {"reps": 50,
+                  "bytes_fwd": cfg.T * cfg.E * 4 + cfg.T * cfg.K * 8,
+                  "bytes_bwd": cfg.T * cfg.K * 12 + cfg.T * cfg.E * 4}
+        calls = {"fwd": lambda: moe.moe_router_fwd(rd, z, ridx, rw),
+                 "bwd": lambda: moe.moe_router_bwd(rd, ridx, rw, rdw, rdz)}
+        for key, call in calls.items():
+            if call() != moe.MOE_OK:
+                raise RuntimeError(f"router {key} failed")
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(router["reps"]):
+                call()
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / router["reps"] * 1e3
+            router[f"{key}_us"] = round(us, 2)
+            router[f"{key}_gbs"] = round(router[f"bytes_{key}"] / (us * 1e-6) / 1e9, 1)
+
     flops = cfg.fwd_flops() + cfg.bwd_flops()
     tflops = flops / (ms_step * 1e-3) / 1e12
     dtype = {0: "fp32", 1: "fp32", 2: "bf16", 3: "bf16+fp8(bwd)", 4: "mxfp8", 5: "fp8"}[cfg.mode]
@@ -250,6 +280,7 @@ def main():
         "frac_mfma_peak": round(tflops / peak, 4),
         "roofline": roof,
         "f5_overlap": f5,
+        "router": router,
         "kernels": per_kernel,
         "input_gen_s": round(gen_s, 1),
     }

@@ -195,6 +195,32 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w,
             void* dx, void* dw1, void* dw2, float* dtopk_w,
             void* scratch, size_t scratch_bytes, void* stream);
 
+/* Router ahead of the layer (the step that makes the top-k routing decision the
+ * layer consumes: Prime Mega MoE news item, "TL;DR", 128 experts with top-8
+ * routing, and "Why is MoE training communication-bound?", each token goes to a
+ * small subset of experts).  Per token t, with logits z = logits[t, 0..E-1]:
+ *   p = softmax(z); the K experts of largest p in descending order, ties to the
+ *   lower expert index (the selection is exactly that of the logits);
+ *   topk_w[t,k] = p[topk_idx[t,k]] / sum_k' p[topk_idx[t,k']] (fp32).
+ * Reads only T, E, K of `d`: requires T >= 1, 1 <= K <= E (else MOE_EINVAL),
+ * E <= 512 and K <= 64 (else MOE_EUNSUPPORTED).  logits: device float32
+ * [T, E] row-major, not NaN; topk_idx: device int32 [T, K] and topk_w: device
+ * float32 [T, K], written (the layout moe_fwd reads).  A token whose logits are
+ * all -inf gets NaN weights, as the definition does.  All pointers 4-byte
+ * aligned (MOE_EALIGN).  Asynchronous on `stream`; allocates nothing. */
+int moe_router_fwd(const moe_desc* d, const float* logits, int32_t* topk_idx, float* topk_w,
+                   void* stream);
+
+/* Router backward: dlogits = dL/dlogits for the upstream gradient
+ * dtopk_w = dL/dtopk_w [T, K] (for instance moe_bwd's), by the chain rule
+ * through the renormalisation and the softmax, which reduces to
+ * dlogits[t, j] = w_j (dw_j - sum_k w_k dw_k) for a selected expert j and 0 for
+ * every other expert.  topk_idx and topk_w are moe_router_fwd's outputs
+ * (distinct ids per token; ids outside [0, E) are skipped).  dlogits: device
+ * float32 [T, E], every entry written.  Same requirements as moe_router_fwd. */
+int moe_router_bwd(const moe_desc* d, const int32_t* topk_idx, const float* topk_w,
+                   const float* dtopk_w, float* dlogits, void* stream);
+
 /* Synchronizes `stream`, returns the latched device error (MOE_OK, MOE_EINDEX
  * or MOE_ETIMEOUT) of `scratch` and clears it. */
 int moe_check(const moe_desc* d, void* scratch, size_t scratch_bytes, void* stream);

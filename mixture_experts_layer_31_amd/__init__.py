@@ -26,8 +26,8 @@ MOE_FLAG_QUEUE_TIMEOUT_TEST = 0x2
 # Exported symbols, in the order include/moe.h declares them.
 EXPORTS = (
     "moe_scratch_bytes", "moe_wprep_bytes", "moe_prepare_weights", "moe_route",
-    "moe_routing_view", "moe_scratch_view", "moe_fwd", "moe_bwd", "moe_check",
-    "moe_strerror", "moe_abi_version", "moe_profile_enable", "moe_profile_collect",
+    "moe_routing_view", "moe_scratch_view", "moe_fwd", "moe_bwd", "moe_router_fwd",
+    "moe_router_bwd", "moe_check", "moe_strerror", "moe_abi_version", "moe_profile_enable", "moe_profile_collect",
     "moe_profile_get", "moe_profile_reset",
 )
 
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
             "moe_scratch_view": (_i32, [_dp, _vp, _sz, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_sz)]),
             "moe_fwd": (_i32, [_dp] + [_vp] * 8 + [_sz, _vp]),
             "moe_bwd": (_i32, [_dp] + [_vp] * 10 + [_sz, _vp]),
+            "moe_router_fwd": (_i32, [_dp, _vp, _vp, _vp, _vp]),
+            "moe_router_bwd": (_i32, [_dp, _vp, _vp, _vp, _vp, _vp]),
             "moe_check": (_i32, [_dp, _vp, _sz, _vp]),
             "moe_strerror": (ctypes.c_char_p, [_i32]),
             "moe_abi_version": (_i32, []),
@@ -129,6 +131,16 @@ def moe_prepare_weights(desc, w1, w2, wprep, stream=None) -> int:
 def moe_route(desc, topk_idx, scratch, stream=None) -> int:
     return lib().moe_route(ctypes.byref(desc), _p(topk_idx), _p(scratch), _nbytes(scratch),
                            _stream(stream))
+
+
+def moe_router_fwd(desc, logits, topk_idx, topk_w, stream=None) -> int:
+    return lib().moe_router_fwd(ctypes.byref(desc), _p(logits), _p(topk_idx), _p(topk_w),
+                                _stream(stream))
+
+
+def moe_router_bwd(desc, topk_idx, topk_w, dtopk_w, dlogits, stream=None) -> int:
+    return lib().moe_router_bwd(ctypes.byref(desc), _p(topk_idx), _p(topk_w), _p(dtopk_w),
+                                _p(dlogits), _stream(stream))
 
 
 def moe_routing_view(desc, scratch) -> tuple:

@@ -282,6 +282,36 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
   return launch_unpermute(*d, L, dx, io_f32, sc, s);
 }
 
+// The router reads only T, E and K of the descriptor.
+static int check_router_desc(const moe_desc* d) {
+  if (d == nullptr) return MOE_EINVAL;
+  if (d->T <= 0 || d->E <= 0 || d->K <= 0 || d->K > d->E) return MOE_EINVAL;
+  if (d->E > 512 || d->K > 64) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int moe_router_fwd(const moe_desc* d, const float* logits, int32_t* topk_idx, float* topk_w,
+                   void* stream) {
+  const int rc = check_router_desc(d);
+  if (rc) return rc;
+  if (logits == nullptr || topk_idx == nullptr || topk_w == nullptr) return MOE_EINVAL;
+  if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_EALIGN;
+  return launch_router_fwd(d->T, d->E, d->K, logits, topk_idx, topk_w,
+                           static_cast<hipStream_t>(stream));
+}
+
+int moe_router_bwd(const moe_desc* d, const int32_t* topk_idx, const float* topk_w,
+                   const float* dtopk_w, float* dlogits, void* stream) {
+  const int rc = check_router_desc(d);
+  if (rc) return rc;
+  if (topk_idx == nullptr || topk_w == nullptr || dtopk_w == nullptr || dlogits == nullptr)
+    return MOE_EINVAL;
+  if (!aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(dtopk_w, 4) || !aligned(dlogits, 4))
+    return MOE_EALIGN;
+  return launch_router_bwd(d->T, d->E, d->K, topk_idx, topk_w, dtopk_w, dlogits,
+                           static_cast<hipStream_t>(stream));
+}
+
 int moe_check(const moe_desc* d, void* scratch, size_t scratch_bytes, void* stream) {
   int rc = check_desc(d);
   if (rc) return rc;

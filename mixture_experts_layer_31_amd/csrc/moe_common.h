@@ -92,6 +92,12 @@ int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
 int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool in_f32,
                        const float* topk_w, float* dtopk_w, char* scratch, hipStream_t s);
 int launch_convert_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
+// Router ahead of the layer (moe_router.hip): softmax -> top-K -> renormalise,
+// and its backward to the logits.  Requires 1 <= K <= min(E, 64), E <= 512.
+int launch_router_fwd(int T, int E, int K, const float* logits, int32_t* topk_idx, float* topk_w,
+                      hipStream_t s);
+int launch_router_bwd(int T, int E, int K, const int32_t* topk_idx, const float* topk_w,
+                      const float* dtopk_w, float* dlogits, hipStream_t s);
 
 // Grouped GEMMs (MFMA).  See moe_gemm.hip.
 // fp32 GEMMs of mode MOE_FP32 (moe_f32.hip).

@@ -116,6 +116,23 @@ def test_route_and_prepare_validation():
     assert L.moe_prepare_weights(ctypes.byref(d1), FAKE + 4, FAKE, FAKE, need, None) == moe.MOE_EALIGN
 
 
+def test_router_validation():
+    L = moe.lib()
+    ok = moe.make_desc(64, 0, 0, 128, 8)  # the router reads only T, E and K
+    for bad, code in ((moe.make_desc(0, 0, 0, 128, 8), moe.MOE_EINVAL),
+                      (moe.make_desc(64, 0, 0, 8, 9), moe.MOE_EINVAL),
+                      (moe.make_desc(64, 0, 0, 8, 0), moe.MOE_EINVAL),
+                      (moe.make_desc(64, 0, 0, 1024, 8), moe.MOE_EUNSUPPORTED),
+                      (moe.make_desc(64, 0, 0, 128, 65), moe.MOE_EUNSUPPORTED)):
+        assert L.moe_router_fwd(ctypes.byref(bad), FAKE, FAKE, FAKE, None) == code
+        assert L.moe_router_bwd(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == code
+    assert L.moe_router_fwd(None, FAKE, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert L.moe_router_fwd(ctypes.byref(ok), None, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert L.moe_router_fwd(ctypes.byref(ok), FAKE + 2, FAKE, FAKE, None) == moe.MOE_EALIGN
+    assert L.moe_router_bwd(ctypes.byref(ok), FAKE, FAKE, None, FAKE, None) == moe.MOE_EINVAL
+    assert L.moe_router_bwd(ctypes.byref(ok), FAKE, FAKE, FAKE, FAKE + 1, None) == moe.MOE_EALIGN
+
+
 def test_views_are_disjoint_regions_of_scratch():
     d = moe.make_desc(300, 256, 192, 12, 3)
     n = moe.moe_scratch_bytes(d)
