@@ -121,6 +121,8 @@ def main():
                     help="time without per-kernel events (no roofline entry)")
     ap.add_argument("--overlap", action="store_true",
                     help="time the overlapped one-launch forward instead of one kernel per step")
+    ap.add_argument("--recompute", action="store_true",
+                    help="activation recompute: the forward keeps no H, the backward rebuilds it")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's layer only: the expert-parallel exchange between "
@@ -137,7 +139,7 @@ def main():
     t0 = time.perf_counter()
     inp = mi.make_inputs(cfg, threads=16)
     gen_s = time.perf_counter() - t0
-    flags = moe.MOE_FLAG_OVERLAP if args.overlap else 0
+    flags = (moe.MOE_FLAG_OVERLAP if args.overlap else 0) | (moe.MOE_FLAG_RECOMPUTE if args.recompute else 0)
     L = Layer(cfg, inp, flags=flags, device="cuda:0")
     L.prepare()
     stream = torch.cuda.current_stream()
@@ -189,7 +191,7 @@ def main():
     if queue_capable(cfg):
         f5 = {"reps": 10}
         for key, fl in (("fwd_ms_overlapped", moe.MOE_FLAG_OVERLAP), ("fwd_ms_per_step", 0)):
-            L.desc = desc_of(cfg, fl)
+            L.desc = desc_of(cfg, fl | (flags & moe.MOE_FLAG_RECOMPUTE))
             L.fwd()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -272,7 +274,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: Qwen3 MoE layer T={cfg.T} D={cfg.D} F={cfg.F} "
                                f"E={cfg.E} top-{cfg.K}, {cfg.routing} routing",
-                   "T": cfg.T, "D": cfg.D, "F": cfg.F, "E": cfg.E, "K": cfg.K, "mode": cfg.mode},
+                   "T": cfg.T, "D": cfg.D, "F": cfg.F, "E": cfg.E, "K": cfg.K, "mode": cfg.mode,
+                   "recompute": bool(args.recompute)},
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "fwd_tflops": round(cfg.fwd_flops() / (fwd_ms * 1e-3) / 1e12, 1),
         "bwd_tflops": round(cfg.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1),

@@ -100,6 +100,16 @@ enum moe_status {
  * 1 us, so moe_check reports MOE_ETIMEOUT; the outputs of that call are
  * undefined.  Exists to test the timeout path without a real stall. */
 #define MOE_FLAG_QUEUE_TIMEOUT_TEST 0x2u
+/* Activation recompute, the layer-level form of the full activation
+ * checkpointing the pages' training runs use (Prime Mega MoE news item, "How
+ * fast is Prime Mega MoE?"): the forward keeps the linear-1 output H [T*K, 2F]
+ * out of the saved state (the W1 epilogue stores only the SwiGLU output A), and
+ * moe_bwd first recomputes H with the same W1 GEMM, bit-identical to the
+ * forward's, into the buffer the SwiGLU backward then overwrites in place with
+ * dH.  moe_scratch_bytes is smaller by the H region (T*K*2F elements); every
+ * output is bit-identical to the default; the backward does 4*T*K*D*F more
+ * flops.  MOE_VIEW_H is not available (MOE_EINVAL).  All modes. */
+#define MOE_FLAG_RECOMPUTE 0x4u
 
 /* Layer descriptor, passed by host pointer.  Requirements: T, E, K >= 1;
  * K <= E; E <= 1024; D % 64 == 0 and F % 64 == 0; T * K < 2^31. */

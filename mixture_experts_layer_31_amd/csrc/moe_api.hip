@@ -18,7 +18,8 @@ int check_desc(const moe_desc* d) {
   if (d->T <= 0 || d->D <= 0 || d->F <= 0 || d->E <= 0 || d->K <= 0) return MOE_EINVAL;
   if (d->K > d->E || d->E > 1024) return MOE_EINVAL;
   if (d->mode < MOE_FP32 || d->mode > MOE_FP8) return MOE_EINVAL;
-  if ((d->flags & ~int32_t(MOE_FLAG_OVERLAP | MOE_FLAG_QUEUE_TIMEOUT_TEST)) != 0) return MOE_EINVAL;
+  if ((d->flags & ~int32_t(MOE_FLAG_OVERLAP | MOE_FLAG_QUEUE_TIMEOUT_TEST | MOE_FLAG_RECOMPUTE)) != 0)
+    return MOE_EINVAL;
   const long long N = (long long)d->T * d->K;
   const long long widest = d->D > 2 * d->F ? d->D : 2 * d->F;
   if (N >= (1LL << 31) || N * widest >= (1LL << 46)) return MOE_EINVAL;
@@ -200,7 +201,11 @@ int moe_scratch_view(const moe_desc* d, const void* scratch, size_t scratch_byte
   size_t off, n;
   switch (which) {
     case MOE_VIEW_XPERM: off = L.xperm; n = N * d->D * ab; break;
-    case MOE_VIEW_H: off = L.h; n = N * 2 * d->F * ab; break;
+    case MOE_VIEW_H:
+      if (L.recompute) return MOE_EINVAL;  // the forward keeps no H
+      off = L.h;
+      n = N * 2 * d->F * ab;
+      break;
     case MOE_VIEW_A: off = L.a; n = N * d->F * ab; break;
     case MOE_VIEW_O: off = L.o; n = N * d->D * ab; break;
     case MOE_VIEW_DYPERM: off = L.dyperm; n = N * d->D * ab; break;
@@ -271,6 +276,15 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool io_f32 = d->mode == MOE_FP32 || d->mode == MOE_FP32_BF16GEMM;
   if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s))) return rc;
+  if (L.recompute) {  // H again, by the forward's own W1 GEMM
+    if (d->mode == MOE_FP32)
+      rc = launch_recompute_h_f32(*d, L, static_cast<const float*>(w1), sc, s);
+    else if (fp8_mode(d->mode) && d->mode != MOE_FP8_BWD)
+      rc = fp8_recompute_h(*d, L, static_cast<const char*>(wprep), sc, s);
+    else
+      rc = launch_recompute_h(*d, L, g1, sc, s);
+    if (rc) return rc;
+  }
   if (d->mode == MOE_FP32)
     rc = launch_bwd_gemms_f32(*d, L, static_cast<const float*>(w1), static_cast<const float*>(w2),
                               static_cast<float*>(dw1), static_cast<float*>(dw2), sc, s);

@@ -25,6 +25,7 @@ constexpr int kRouteThreads = 256;
 struct Layout {
   size_t err, counts, offsets, tiles[3], chunk_cnt, pos, src, wperm;
   size_t xperm, h, a, o, dyperm, dh, dxperm, fp8, queue, total;
+  bool recompute;   // MOE_FLAG_RECOMPUTE: no H region; H is rebuilt in the dH region
   int nchunks;      // routing chunks
   int act_bytes;    // bytes per intermediate element
 };
@@ -55,12 +56,14 @@ inline Layout make_layout(const moe_desc& d) {
   L.wperm = take(N * 4);
   const size_t ab = L.act_bytes;
   L.xperm = take(N * D * ab);
-  L.h = take(N * 2 * F * ab);
+  L.recompute = (d.flags & MOE_FLAG_RECOMPUTE) != 0;
+  L.h = L.recompute ? 0 : take(N * 2 * F * ab);
   L.a = take(N * F * ab);
   L.o = take(N * D * ab);
   L.dyperm = take(N * D * ab);
   L.dh = take(N * 2 * F * ab);
   L.dxperm = take(N * D * ab);
+  if (L.recompute) L.h = L.dh;  // written by the backward's recompute, then overwritten by dH
   L.fp8 = take(fp8_scratch_bytes(d));
   L.queue = take(queue_scratch_bytes(d));
   L.total = o;
@@ -112,6 +115,14 @@ int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_
                      hipStream_t s);
 int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
                      char* scratch, hipStream_t s);
+// MOE_FLAG_RECOMPUTE: the forward's W1 GEMM again, storing only H (into L.h,
+// the dH region), with the same kernels and operands as the forward.
+int launch_recompute_h(const moe_desc& d, const Layout& L, const uint16_t* w1, char* scratch,
+                       hipStream_t s);
+int launch_recompute_h_f32(const moe_desc& d, const Layout& L, const float* w1, char* scratch,
+                           hipStream_t s);
+int fp8_recompute_h(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,
+                    hipStream_t s);
 int fp8_prepare_weights(const moe_desc& d, const uint16_t* w1, const uint16_t* w2, char* wprep,
                         hipStream_t s);
 int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,

@@ -30,10 +30,11 @@ struct F32Grouped {
   const float* B;             // weights of expert 0; expert e at B + e * bstride
   int64_t bstride;
   int ldb;
-  float* out;                 // STORE: [rows, ldo]; SWIGLU: H [rows, 2F]; DSWIGLU: dH [rows, 2F]
+  float* out;                 // STORE: [rows, ldo]; SWIGLU: H [rows, 2F] or null; DSWIGLU: dH [rows, 2F]
   int ldo;
-  float* out2;                // SWIGLU: A [rows, F]
-  const float* hsave;         // DSWIGLU: H [rows, 2F]
+  float* out2;                // SWIGLU: A [rows, F] or null
+  const float* hsave;         // DSWIGLU: H [rows, 2F] (may equal out: each thread reads its
+                              // g and u before it stores their gradients)
 };
 
 __device__ __forceinline__ float sigmoidf(float z) { return 1.f / (1.f + expf(-z)); }
@@ -111,9 +112,11 @@ __global__ void __launch_bounds__(kThr) f32_grouped_kernel(F32Grouped p) {
       for (int j = 0; j < 2; ++j) {
         const int f = nt * 32 + 2 * tx + j;
         const float g = acc[i][j], u = acc[i][2 + j];
-        p.out[row * 2 * p.F + f] = g;
-        p.out[row * 2 * p.F + p.F + f] = u;
-        p.out2[row * p.F + f] = g * sigmoidf(g) * u;
+        if (p.out != nullptr) {
+          p.out[row * 2 * p.F + f] = g;
+          p.out[row * 2 * p.F + p.F + f] = u;
+        }
+        if (p.out2 != nullptr) p.out2[row * p.F + f] = g * sigmoidf(g) * u;
       }
     } else {  // DSWIGLU: acc is dA for features nt*64 + 4tx + j
 #pragma unroll
@@ -221,7 +224,7 @@ int launch_fwd_gemms_f32(const moe_desc& d, const Layout& L, const float* w1, co
     a.B = w1;
     a.bstride = int64_t(2) * F * D;
     a.ldb = D;
-    a.out = reinterpret_cast<float*>(scratch + L.h);
+    a.out = L.recompute ? nullptr : reinterpret_cast<float*>(scratch + L.h);
     a.out2 = reinterpret_cast<float*>(scratch + L.a);
     if ((rc = run_f32<false, F32_SWIGLU>(d, L, a, F / 32, "gemm_w1_swiglu", scratch, s))) return rc;
   }
@@ -239,6 +242,21 @@ int launch_fwd_gemms_f32(const moe_desc& d, const Layout& L, const float* w1, co
     if ((rc = run_f32<false, F32_STORE>(d, L, a, D / kT, "gemm_w2", scratch, s))) return rc;
   }
   return MOE_OK;
+}
+
+int launch_recompute_h_f32(const moe_desc& d, const Layout& L, const float* w1, char* scratch,
+                           hipStream_t s) {
+  F32Grouped a{};
+  a.K = d.D;
+  a.F = d.F;
+  a.A = reinterpret_cast<const float*>(scratch + L.xperm);
+  a.lda = d.D;
+  a.B = w1;
+  a.bstride = int64_t(2) * d.F * d.D;
+  a.ldb = d.D;
+  a.out = reinterpret_cast<float*>(scratch + L.h);
+  a.out2 = nullptr;
+  return run_f32<false, F32_SWIGLU>(d, L, a, d.F / 32, "gemm_w1_recompute", scratch, s);
 }
 
 int launch_bwd_gemms_f32(const moe_desc& d, const Layout& L, const float* w1, const float* w2,

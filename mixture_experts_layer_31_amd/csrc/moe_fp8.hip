@@ -679,14 +679,15 @@ int fp8_view(const moe_desc& d, const Layout& L, char* scratch, int which, void*
   }
 }
 
-int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,
-                  hipStream_t s) {
+// Expert linear 1 + SwiGLU on the quantised x rows: stores H into `h` and A
+// into `act` (either may be null, as in the bf16 path).
+static int fp8_w1_swiglu(const moe_desc& d, const Layout& L, const char* wprep, uint16_t* h,
+                         uint16_t* act, const char* name, char* scratch, hipStream_t s) {
   const WLayout W = wlayout(d);
   const F8Scratch f = f8scratch(d, L, scratch);
   const bool mx = d.mode == MOE_MXFP8;
   const int D = d.D, F = d.F, N = d.T * d.K;
   int rc;
-  // expert linear 1 + SwiGLU
   if ((rc = quant_rows(d, reinterpret_cast<const uint16_t*>(scratch + L.xperm), D, mx, f.qrow,
                        f.qrow_sc, "quant_x_rows", s)))
     return rc;
@@ -703,10 +704,26 @@ int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* s
   a.sb_bstride = int64_t(D / 128) * 2 * F;
   a.sb_bytes = uint32_t(size_t(D / 128) * 2 * F * 4);
   a.F = F;
-  a.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.h), 0,
-                  reinterpret_cast<uint16_t*>(scratch + L.a), nullptr, F};
-  rc = mx ? run_f8_grouped<true, EPI_SWIGLU>(d, L, a, 2 * F, "gemm_w1_swiglu", scratch, s)
-          : run_f8_grouped<false, EPI_SWIGLU>(d, L, a, 2 * F, "gemm_w1_swiglu", scratch, s);
+  a.epi = EpiArgs{h, 0, act, nullptr, F};
+  return mx ? run_f8_grouped<true, EPI_SWIGLU>(d, L, a, 2 * F, name, scratch, s)
+            : run_f8_grouped<false, EPI_SWIGLU>(d, L, a, 2 * F, name, scratch, s);
+}
+
+int fp8_recompute_h(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,
+                    hipStream_t s) {
+  return fp8_w1_swiglu(d, L, wprep, reinterpret_cast<uint16_t*>(scratch + L.h), nullptr,
+                       "gemm_w1_recompute", scratch, s);
+}
+
+int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,
+                  hipStream_t s) {
+  const WLayout W = wlayout(d);
+  const F8Scratch f = f8scratch(d, L, scratch);
+  const bool mx = d.mode == MOE_MXFP8;
+  const int D = d.D, F = d.F, N = d.T * d.K;
+  int rc = fp8_w1_swiglu(d, L, wprep,
+                         L.recompute ? nullptr : reinterpret_cast<uint16_t*>(scratch + L.h),
+                         reinterpret_cast<uint16_t*>(scratch + L.a), "gemm_w1_swiglu", scratch, s);
   if (rc) return rc;
   // expert linear 2
   if ((rc = quant_rows(d, reinterpret_cast<const uint16_t*>(scratch + L.a), F, mx, f.qrow,

@@ -184,27 +184,39 @@ int run_wgrad_any(const moe_desc& d, const Layout& L, WgradArgs a, const char* n
   return run_wgrad<TileWg64x64, OUT_F32>(d, L, a, name, scratch, s);
 }
 
+// Expert linear 1 with the SwiGLU epilogue; W1[e] is [2F, D].  Stores H into
+// `h` and A into `act` (either may be null: the recompute forward skips H, the
+// backward's recompute skips A).
+int run_w1_swiglu(const moe_desc& d, const Layout& L, const uint16_t* w1, uint16_t* h,
+                  uint16_t* act, const char* name, char* scratch, hipStream_t s) {
+  GroupedArgs a{};
+  a.K = d.D;
+  a.F = d.F;
+  a.A = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
+  a.lda = d.D;
+  a.B = w1;
+  a.bstride = int64_t(2) * d.F * d.D;
+  a.ldb = d.D;
+  a.brows = 2 * d.F;
+  a.out = h;
+  a.out2 = act;
+  return run_grouped_any<false, EPI_SWIGLU>(d, L, a, 2 * d.F, name, scratch, s);
+}
+
 }  // namespace
+
+int launch_recompute_h(const moe_desc& d, const Layout& L, const uint16_t* w1, char* scratch,
+                       hipStream_t s) {
+  return run_w1_swiglu(d, L, w1, reinterpret_cast<uint16_t*>(scratch + L.h), nullptr,
+                       "gemm_w1_recompute", scratch, s);
+}
 
 int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
                      char* scratch, hipStream_t s) {
   const int D = d.D, F = d.F;
-  int rc;
-  {  // expert linear 1 with SwiGLU epilogue: H, A.  W1[e] is [2F, D].
-    GroupedArgs a{};
-    a.K = D;
-    a.F = F;
-    a.A = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
-    a.lda = D;
-    a.B = w1;
-    a.bstride = int64_t(2) * F * D;
-    a.ldb = D;
-    a.brows = 2 * F;
-    a.out = reinterpret_cast<uint16_t*>(scratch + L.h);
-    a.out2 = reinterpret_cast<uint16_t*>(scratch + L.a);
-    rc = run_grouped_any<false, EPI_SWIGLU>(d, L, a, 2 * F, "gemm_w1_swiglu", scratch, s);
-    if (rc) return rc;
-  }
+  int rc = run_w1_swiglu(d, L, w1, L.recompute ? nullptr : reinterpret_cast<uint16_t*>(scratch + L.h),
+                         reinterpret_cast<uint16_t*>(scratch + L.a), "gemm_w1_swiglu", scratch, s);
+  if (rc) return rc;
   {  // expert linear 2: O.  W2[e] is [D, F].
     GroupedArgs a{};
     a.K = F;

@@ -356,10 +356,11 @@ struct Tile {
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };
 
 struct EpiArgs {
-  uint16_t* out;          // STORE: [rows, ldo]; SWIGLU: H [rows, 2F]; DSWIGLU: dH [rows, 2F]
+  uint16_t* out;          // STORE: [rows, ldo]; SWIGLU: H [rows, 2F] or null; DSWIGLU: dH [rows, 2F]
   int ldo;
-  uint16_t* out2;         // SWIGLU: A [rows, F]
-  const uint16_t* hsave;  // DSWIGLU: H [rows, 2F]
+  uint16_t* out2;         // SWIGLU: A [rows, F] or null
+  const uint16_t* hsave;  // DSWIGLU: H [rows, 2F]; may equal out (each tile reads its H band
+                          // into LDS before it stores the same band's dH)
   int F;
 };
 
@@ -486,15 +487,19 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
         if (n <= 0) continue;
         const int off = w * 32 * BN;  // bytes of 32 rows of BN/2 bf16
         const int f0 = nt * (BN / 2);
-        band_store<TL::THREADS>(BandTile<2>{smem + off, BN / 2}, 32, n, tid, [&](int r) {
-          return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + f0);
-        });
-        band_store<TL::THREADS>(BandTile<2>{smem + RB * BN + off, BN / 2}, 32, n, tid, [&](int r) {
-          return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + F + f0);
-        });
-        band_store<TL::THREADS, 2, COH2>(BandTile<2>{smem + 2 * RB * BN + off, BN / 2}, 32, n, tid, [&](int r) {
-          return reinterpret_cast<char*>(p.out2 + (grow0 + first + r) * F + f0);
-        });
+        if (p.out != nullptr) {  // H (not kept under activation recompute)
+          band_store<TL::THREADS>(BandTile<2>{smem + off, BN / 2}, 32, n, tid, [&](int r) {
+            return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + f0);
+          });
+          band_store<TL::THREADS>(BandTile<2>{smem + RB * BN + off, BN / 2}, 32, n, tid, [&](int r) {
+            return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + F + f0);
+          });
+        }
+        if (p.out2 != nullptr)  // A (not needed when H is recomputed in the backward)
+          band_store<TL::THREADS, 2, COH2>(BandTile<2>{smem + 2 * RB * BN + off, BN / 2}, 32, n, tid,
+                                           [&](int r) {
+            return reinterpret_cast<char*>(p.out2 + (grow0 + first + r) * F + f0);
+          });
       }
     } else {  // EPI_DSWIGLU: acc holds dA = (w dy) W2[e] for the tile's F-columns
       const int F = p.F;

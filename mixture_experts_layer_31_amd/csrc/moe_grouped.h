@@ -17,10 +17,10 @@ struct GroupedArgs {
   int64_t bstride;
   int ldb;                    // row length of a weight matrix (elements)
   int brows;                  // rows of a weight matrix
-  uint16_t* out;              // STORE: [rows, ldo]; SWIGLU: H [rows, 2F]; DSWIGLU: dH [rows, 2F]
+  uint16_t* out;              // STORE: [rows, ldo]; SWIGLU: H [rows, 2F] or null; DSWIGLU: dH [rows, 2F]
   int ldo;
-  uint16_t* out2;             // SWIGLU: A [rows, F]
-  const uint16_t* hsave;      // DSWIGLU: H [rows, 2F]
+  uint16_t* out2;             // SWIGLU: A [rows, F] or null
+  const uint16_t* hsave;      // DSWIGLU: H [rows, 2F] (may equal out: read before written, per tile)
 };
 
 // Where flat tile l (= m-tile * ntn + n-tile, m-tiles expert-major) sits.

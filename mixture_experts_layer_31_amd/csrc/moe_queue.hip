@@ -354,7 +354,7 @@ int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_
   q.w1.bstride = int64_t(2) * d.F * d.D;
   q.w1.ldb = d.D;
   q.w1.brows = 2 * d.F;
-  q.w1.out = reinterpret_cast<uint16_t*>(scratch + L.h);
+  q.w1.out = L.recompute ? nullptr : reinterpret_cast<uint16_t*>(scratch + L.h);
   q.w1.out2 = reinterpret_cast<uint16_t*>(scratch + L.a);
   q.w2.offsets = b.offsets;
   q.w2.tile_start = b.tile256;

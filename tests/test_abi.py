@@ -116,6 +116,25 @@ def test_route_and_prepare_validation():
     assert L.moe_prepare_weights(ctypes.byref(d1), FAKE + 4, FAKE, FAKE, need, None) == moe.MOE_EALIGN
 
 
+def test_recompute_drops_the_h_region():
+    for T, D, F, E, K, mode in ((16384, 2048, 768, 128, 8, moe.MOE_BF16), (64, 128, 64, 8, 2, moe.MOE_FP32),
+                                (700, 256, 256, 8, 2, moe.MOE_MXFP8)):
+        d0 = moe.make_desc(T, D, F, E, K, mode)
+        d1 = moe.make_desc(T, D, F, E, K, mode, moe.MOE_FLAG_RECOMPUTE)
+        ab = 4 if mode == moe.MOE_FP32 else 2
+        h = (T * K * 2 * F * ab + 255) // 256 * 256
+        assert moe.moe_scratch_bytes(d0) - moe.moe_scratch_bytes(d1) == h
+        n1 = moe.moe_scratch_bytes(d1)
+        ptr, nbytes = ctypes.c_void_p(), ctypes.c_size_t()
+        L = moe.lib()
+        assert L.moe_scratch_view(ctypes.byref(d1), FAKE, n1, moe.MOE_VIEW_H, ctypes.byref(ptr),
+                                  ctypes.byref(nbytes)) == moe.MOE_EINVAL
+        # dH, which the recomputed H shares, is still there
+        assert L.moe_scratch_view(ctypes.byref(d1), FAKE, n1, moe.MOE_VIEW_DH, ctypes.byref(ptr),
+                                  ctypes.byref(nbytes)) == moe.MOE_OK
+        assert nbytes.value == T * K * 2 * F * ab
+
+
 def test_router_validation():
     L = moe.lib()
     ok = moe.make_desc(64, 0, 0, 128, 8)  # the router reads only T, E and K
