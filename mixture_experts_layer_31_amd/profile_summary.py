@@ -5,6 +5,8 @@ must include `--calib-copy-mib M`):
   * `--kernel-trace --stats`  -> <trace>_kernel_trace.csv
   * `--pmc FETCH_SIZE`        -> <fetch>_counter_collection.csv
   * `--pmc WRITE_SIZE`        -> <write>_counter_collection.csv
+With --stats-only, only the trace run is read and profiles/kernels_<config>.md
+lists every kernel's launches and durations (the FP8 workloads).
 Outputs: profiles/layer_<config>_bf16.md (per-kernel durations and calibrated
 HBM bytes, with the commands) and profiles/traffic_<config>_bf16.json (the
 bytes per launch that bench.py reports as roofline traffic, keyed to a hash of
@@ -57,9 +59,9 @@ def step_name(kernel: str) -> str | None:
         return _GROUPED.get((m.group(1), m.group(2)))
     if "wgrad_gemm_kernel" in kernel:
         return "wgrad"
-    m = re.search(r"gather_reduce_kernel<(true|false), (true|false)>", kernel)
+    m = re.search(r"gather_reduce_kernel<[^>]*\b(true|false)>", kernel)  # last argument: weighted
     if m:
-        return "combine" if m.group(2) == "true" else "unpermute"
+        return "combine" if m.group(1) == "true" else "unpermute"
     for key, name in _PLAIN:
         if key in kernel:
             return name
@@ -111,18 +113,47 @@ def counter_table(prefix: str, counter: str):
     return per
 
 
+def stats_summary(args):
+    """profiles/kernels_<config>.md from a --kernel-trace --stats run alone: every
+    kernel of the run by total time (for workloads without a traffic summary)."""
+    rows = list(csv.DictReader(open(args.trace + "_kernel_stats.csv")))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = [f"# {args.config} layer: per-kernel time", "",
+             f"Workload: {args.workload or args.config}.", "",
+             "Commands (from the repository root on the GPU box):", ""]
+    lines += [f"    {c.strip()}" for c in args.commands.split(";") if c.strip()]
+    lines += ["", "## Kernel statistics (rocprofv3 --kernel-trace --stats)", "",
+              "Every launch of the run, warm-up included (the bench also times the overlapped "
+              "forward and the router after its steps).", "",
+              "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = re.sub(r"\(anonymous namespace\)::", "", r["Name"]).split("(")[0]
+        name = name.replace("void ", "").replace("moe::", "").replace("gemm::", "")
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{100 * float(r['TotalDurationNs']) / tot:.1f} |")
+    with open(os.path.join(ROOT, "profiles", f"kernels_{args.config}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", required=True)
     ap.add_argument("--trace", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--calib-mib", type=int, required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--calib-mib", type=int)
+    ap.add_argument("--stats-only", action="store_true",
+                    help="only the kernel statistics of the trace run (profiles/kernels_<config>.md)")
     ap.add_argument("--commands", required=True, help="the rocprofv3 commands, ';'-separated")
     ap.add_argument("--workload", default="")
     ap.add_argument("--skip", type=int, default=0,
                     help="warm-up launches per kernel left out of the 'timed avg' column")
     args = ap.parse_args()
+    if args.stats_only:
+        return stats_summary(args)
+    if not (args.fetch and args.write and args.calib_mib):
+        raise SystemExit("--fetch, --write and --calib-mib are required without --stats-only")
 
     dur = trace_table(args.trace)
     fetch = counter_table(args.fetch, "FETCH_SIZE")
