@@ -215,6 +215,156 @@ __global__ void __launch_bounds__(256) quant_tile_kernel(QArgs p) {
   }
 }
 
+// Row quantiser for activations whose contraction runs along the row: one
+// workgroup per 128 (rows) x 128 (columns) tile; sixteen lanes share a row
+// (eight consecutive values each), so every load and store instruction covers
+// four whole 256-byte (in) / 128-byte (out) row segments, and the group amax is
+// a reduction over 4 (MX, 32 columns) or 16 (blockwise, 128 columns) lanes.
+template <bool MX>
+__global__ void __launch_bounds__(256) quant_rows_kernel(QArgs p) {
+  const int ctiles = p.cols / 128;
+  const int rt = blockIdx.x / ctiles, ct = blockIdx.x % ctiles;
+  const int r0 = rt * 128, valid = min(128, p.total_rows - r0);
+  const int c0 = ct * 128;
+  const int lane = threadIdx.x & 63, l16 = lane & 15;
+  const int rw = (threadIdx.x >> 6) * 4 + (lane >> 4);  // row within a 16-row slab
+  uint4 raw[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int r = it * 16 + rw;
+    raw[it] = r < valid ? *reinterpret_cast<const uint4*>(p.in + size_t(r0 + r) * p.cols + c0 + 8 * l16)
+                        : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int r = it * 16 + rw;
+    float v[8];
+    const uint32_t w[4] = {raw[it].x, raw[it].y, raw[it].z, raw[it].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(w[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(v[k]));
+    uint32_t entry;
+    uint2 codes;
+    if constexpr (MX) {
+      am = fmaxf(am, __shfl_xor(am, 1, 64));
+      am = fmaxf(am, __shfl_xor(am, 2, 64));
+      const int X = e8m0_exponent(am);
+      const float m = ldexpf(1.f, -X);
+      codes.x = pack_e4m3x4(v[0] * m, v[1] * m, v[2] * m, v[3] * m);
+      codes.y = pack_e4m3x4(v[4] * m, v[5] * m, v[6] * m, v[7] * m);
+      entry = uint32_t(X + 127) << (8 * (l16 >> 2));  // byte g of the entry: group g's exponent
+      entry |= __shfl_xor(entry, 4, 64);
+      entry |= __shfl_xor(entry, 8, 64);
+    } else {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+      const float sc = am == 0.f ? 1.f : am / 448.f;
+      const float rc = 1.f / sc;
+      float y[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[k] = block_quotient(v[k], sc, rc);
+      codes.x = pack_e4m3x4(y[0], y[1], y[2], y[3]);
+      codes.y = pack_e4m3x4(y[4], y[5], y[6], y[7]);
+      entry = __float_as_uint(sc);
+    }
+    if (r < valid) {
+      *reinterpret_cast<uint2*>(p.out + size_t(r0 + r) * p.out_ld + c0 + 8 * l16) = codes;
+      if (l16 == 0) p.sc[size_t(ct) * p.sc_ld + r0 + r] = entry;
+    }
+  }
+}
+
+// Token quantiser for activations contracted over tokens (the weight-gradient
+// operands): one workgroup per 128-token step of an expert segment x 128
+// columns.  The tile is loaded with whole 256-byte row segments per sixteen
+// lanes into LDS, its 32-byte column blocks XOR-swizzled by row; then each
+// thread takes one column and 64 consecutive tokens, four tokens per
+// ds_read_b64_tr_b16 (a sixteen-lane group reads a 4-token x 16-column block
+// and lane i receives column i).  The other 64 tokens of the column are in
+// lane ^ 16, so the 128-token amax is one shuffle away.
+template <bool MX>
+__global__ void __launch_bounds__(256) quant_tokens_kernel(QArgs p) {
+  __shared__ __attribute__((aligned(16))) char tile[128 * 256];
+  const int ctiles = p.cols / 128;
+  const int rt = blockIdx.x / ctiles, ct = blockIdx.x % ctiles;
+  if (rt >= p.tstart[p.E]) return;
+  int lo = 0, hi = p.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.tstart[mid] <= rt) lo = mid; else hi = mid;
+  }
+  const int r0 = p.offsets[lo] + (rt - p.tstart[lo]) * 128;
+  const int valid = min(128, p.offsets[lo + 1] - r0);
+  const int slot0 = rt * 128, c0 = ct * 128;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15;
+  auto at = [&](int r, int cb) { return r * 256 + ((cb ^ (r & 7)) << 5); };  // 32-byte block cb of row r
+  {
+    uint4 raw[8];
+    const int rw = w * 4 + (lane >> 4);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 16 + rw;
+      raw[it] = r < valid ? *reinterpret_cast<const uint4*>(p.in + size_t(r0 + r) * p.cols + c0 + 8 * l16)
+                          : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 16 + rw;
+      *reinterpret_cast<uint4*>(tile + at(r, l16 >> 1) + (l16 & 1) * 16) = raw[it];
+    }
+  }
+  __syncthreads();
+  const int g = lane >> 4, h = g & 1, cb = 2 * w + (g >> 1);
+  const int q = 16 * cb + l16;  // this thread's column; tokens 64h .. 64h + 63
+  float v[64];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = 64 * h + 4 * j + (l16 >> 2);
+    const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)AS3(tile + at(r, cb) + (l16 & 3) * 8));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[4 * j + k] = __uint_as_float(uint32_t(uint16_t(x[k])) << 16);
+  }
+  float am[2] = {0.f, 0.f};  // amax of the two 32-token groups
+#pragma unroll
+  for (int i = 0; i < 64; ++i) am[i >> 5] = fmaxf(am[i >> 5], fabsf(v[i]));
+  uint32_t packed[16], entry;
+  if constexpr (MX) {
+    const int X0 = e8m0_exponent(am[0]), X1 = e8m0_exponent(am[1]);
+    const float mul[2] = {ldexpf(1.f, -X0), ldexpf(1.f, -X1)};
+    const uint32_t mine = uint32_t(X0 + 127) | (uint32_t(X1 + 127) << 8);
+    entry = mine | (__shfl_xor(mine, 16, 64) << 16);  // meaningful in the h == 0 lane
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float m = mul[i >> 3];
+      packed[i] = pack_e4m3x4(v[4 * i] * m, v[4 * i + 1] * m, v[4 * i + 2] * m, v[4 * i + 3] * m);
+    }
+  } else {
+    float amax = fmaxf(am[0], am[1]);
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    const float sc = amax == 0.f ? 1.f : amax / 448.f;
+    const float rc = 1.f / sc;
+    entry = __float_as_uint(sc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float y[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) y[k] = block_quotient(v[4 * i + k], sc, rc);
+      packed[i] = pack_e4m3x4(y[0], y[1], y[2], y[3]);
+    }
+  }
+  uint4* dst = reinterpret_cast<uint4*>(p.out + size_t(c0 + q) * p.out_ld + slot0 + h * 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dst[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+  if (h == 0) p.sc[size_t(slot0 / 128) * p.sc_ld + c0 + q] = entry;
+}
+
 // ---------------------------------------------------------------------------
 // FP8 GEMM.
 
@@ -633,7 +783,13 @@ int quant_rows(const moe_desc& d, const uint16_t* in, int C, bool mx, uint8_t* o
   a.sc_ld = N;
   a.ntr = (N + 127) / 128;
   a.total_rows = N;
-  return launch_quant(false, mx ? Q_MX : Q_BLOCK_ROW, false, a, a.ntr * (C / 128), name, s);
+  const int blocks = a.ntr * (C / 128);
+  if (blocks <= 0) return MOE_OK;
+  prof_begin(name, s);
+  if (mx) quant_rows_kernel<true><<<unsigned(blocks), 256, 0, s>>>(a);
+  else quant_rows_kernel<false><<<unsigned(blocks), 256, 0, s>>>(a);
+  prof_end(s);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 // Quantise permuted activations [N, C] along tokens within expert segments,
@@ -650,7 +806,13 @@ int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, 
   a.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
   a.tstart = reinterpret_cast<const int32_t*>(scratch + L.tiles[1]);
   a.E = d.E;
-  return launch_quant(true, mx ? Q_MX : Q_BLOCK_ROW, true, a, max_steps128(d) * (C / 128), name, s);
+  const int blocks = max_steps128(d) * (C / 128);
+  if (blocks <= 0) return MOE_OK;
+  prof_begin(name, s);
+  if (mx) quant_tokens_kernel<true><<<unsigned(blocks), 256, 0, s>>>(a);
+  else quant_tokens_kernel<false><<<unsigned(blocks), 256, 0, s>>>(a);
+  prof_end(s);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 // Quantise a batch of E weight matrices [R, C].  trans = false: contraction along
