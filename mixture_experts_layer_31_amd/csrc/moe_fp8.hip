@@ -616,6 +616,7 @@ __device__ __forceinline__ void ring8(char* smem, const SA& sa, const SB& sb,
 
 struct F8Args {
   const int32_t* offsets;  // [E+1] expert row offsets
+  const int32_t* eorder;   // [E+1] experts longest first, then the skew flag (wgrad)
   const int32_t* tstart;   // [E+1] m-tile prefix (token-grouped) or 128-token step prefix (wgrad)
   int E, K, ntn;           // K: contraction of a token-grouped GEMM
   int M, N, tm, tn;        // wgrad: dW[e] is [M, N]
@@ -691,10 +692,8 @@ __global__ void __launch_bounds__(TL::THREADS, 1) f8_wgrad_kernel(F8Args p) {
   constexpr int BM = TL::BM, BN = TL::BN, WAVES = TL::WAVES;
   constexpr int ROWB = 128;
   __shared__ __attribute__((aligned(1024))) char smem[TL::STAGES * ((BM + BN) * ROWB + 2048)];
-  const int l = xcd_remap(blockIdx.x, gridDim.x);
-  const int per = p.tm * p.tn;
-  const int e = l / per, rem = l - e * per;
-  const int mt = rem / p.tn, nt = rem - mt * p.tn;
+  const ExpertTile et = expert_tile(p.eorder, p.E, p.tm * p.tn);
+  const int e = et.e, mt = et.rem / p.tn, nt = et.rem - mt * p.tn;
   const int s0 = p.tstart[e], ksteps = p.tstart[e + 1] - s0;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -864,6 +863,7 @@ int run_f8_wgrad(const moe_desc& d, const Layout& L, F8Args a, const char* name,
                  hipStream_t s) {
   a.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
   a.tstart = reinterpret_cast<const int32_t*>(scratch + L.tiles[1]);  // 128-token steps
+  a.eorder = reinterpret_cast<const int32_t*>(scratch + L.eorder);
   a.E = d.E;
   using TL = F8WgTile<MX>;
   a.tm = a.M / TL::BM;

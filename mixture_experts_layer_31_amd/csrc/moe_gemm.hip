@@ -71,6 +71,7 @@ __global__ void __launch_bounds__(TL::THREADS, 1) grouped_gemm_kernel(GroupedArg
 
 struct WgradArgs {
   const int32_t* offsets;  // [E+1]
+  const int32_t* eorder;   // [E+1] experts longest first, then the skew flag
   int E, M, N, tm, tn;
   const uint16_t* A;       // [rows, M]: element (m, k) of expert e at A[(off_e + k)*M + m]
   const uint16_t* B;       // [rows, N]: element (n, k) at B[(off_e + k)*N + n]
@@ -83,10 +84,8 @@ __global__ void __launch_bounds__(TL::THREADS, 1) wgrad_gemm_kernel(WgradArgs p)
   constexpr int WMT = TL::WMT, WNT = TL::WNT, WAVES = TL::WAVES;
   __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
 
-  const int l = xcd_remap(blockIdx.x, gridDim.x);
-  const int per = p.tm * p.tn;
-  const int e = l / per, rem = l - e * per;
-  const int mt = rem / p.tn, nt = rem - mt * p.tn;
+  const ExpertTile et = expert_tile(p.eorder, p.E, p.tm * p.tn);
+  const int e = et.e, mt = et.rem / p.tn, nt = et.rem - mt * p.tn;
   const int off = p.offsets[e];
   const int ne = p.offsets[e + 1] - off;
 
@@ -142,6 +141,7 @@ template <class TL, bool OUT_F32>
 int run_wgrad(const moe_desc& d, const Layout& L, WgradArgs a, const char* name, char* scratch,
               hipStream_t s) {
   a.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
+  a.eorder = reinterpret_cast<const int32_t*>(scratch + L.eorder);
   a.E = d.E;
   a.tm = a.M / TL::BM;
   a.tn = a.N / TL::BN;

@@ -23,6 +23,19 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
   return xcd * q + (xcd < r ? xcd : r) + local;
 }
 
+// Tile l of a per-expert (weight-gradient) GEMM with `per` tiles per expert:
+// experts are taken longest first (eorder, written by the routing step); when
+// the routing is skewed (eorder[E] set) workgroups keep the hardware's
+// round-robin over the XCDs so the longest tiles start first on every XCD,
+// otherwise consecutive tiles of an expert share an XCD and its L2.
+struct ExpertTile { int e, rem; };
+__device__ __forceinline__ ExpertTile expert_tile(const int32_t* eorder, int E, int per) {
+  const int b = blockIdx.x, G = gridDim.x;
+  const int l = eorder[E] ? b : xcd_remap(b, G);
+  const int rank = l / per;
+  return {eorder[rank], l - rank * per};
+}
+
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 

@@ -43,12 +43,18 @@ __global__ void __launch_bounds__(kRouteThreads) route_count_kernel(
     chunk_cnt[size_t(blockIdx.x) * E + e] = hist[e];
 }
 
-// One block of 1024 threads; thread e owns expert e.
+// One block of 1024 threads; thread e owns expert e.  Besides the offsets and
+// tile prefixes it writes eorder: the experts by descending token count (ties
+// to the lower index), the longest-first order in which the weight-gradient
+// GEMMs take their experts, and in eorder[E] a skew flag (the largest count
+// above twice the mean) that makes them spread each expert's tiles over all
+// XCDs instead of grouping them on one.
 __global__ void __launch_bounds__(1024) route_scan_kernel(
     int E, int nchunks, int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tiles64,
-    int32_t* __restrict__ tiles128, int32_t* __restrict__ tiles256) {
+    int32_t* __restrict__ tiles128, int32_t* __restrict__ tiles256, int32_t* __restrict__ eorder) {
   __shared__ int sc[4][1024];
+  __shared__ int cnt[1024];
   const int e = threadIdx.x;
   int total = 0;
   if (e < E) {
@@ -66,7 +72,13 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(
   v[2] = e < E ? (total + 127) / 128 : 0;
   v[3] = e < E ? (total + 255) / 256 : 0;
   for (int q = 0; q < 4; ++q) sc[q][e] = v[q];
+  cnt[e] = v[0];
   __syncthreads();
+  if (e < E) {
+    int rank = 0;
+    for (int f = 0; f < E; ++f) rank += (cnt[f] > total || (cnt[f] == total && f < e)) ? 1 : 0;
+    eorder[rank] = e;
+  }
   for (int step = 1; step < 1024; step <<= 1) {
     int add[4];
     for (int q = 0; q < 4; ++q) add[q] = e >= step ? sc[q][e - step] : 0;
@@ -81,6 +93,9 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(
     tiles128[e] = sc[2][e] - v[2];
     tiles256[e] = sc[3][e] - v[3];
     if (e == E - 1) {
+      int mx = 0;
+      for (int f = 0; f < E; ++f) mx = max(mx, cnt[f]);
+      eorder[E] = (long long)mx * E > 2LL * sc[0][e] ? 1 : 0;
       offsets[E] = sc[0][e];
       tiles64[E] = sc[1][e];
       tiles128[E] = sc[2][e];
@@ -169,7 +184,8 @@ int launch_route(const moe_desc& d, const Layout& L, const int32_t* idx, char* s
       reinterpret_cast<int32_t*>(scratch + L.offsets),
       reinterpret_cast<int32_t*>(scratch + L.tiles[0]),
       reinterpret_cast<int32_t*>(scratch + L.tiles[1]),
-      reinterpret_cast<int32_t*>(scratch + L.tiles[2]));
+      reinterpret_cast<int32_t*>(scratch + L.tiles[2]),
+      reinterpret_cast<int32_t*>(scratch + L.eorder));
   prof_end(s);
   prof_begin("route_scatter", s);
   route_scatter_kernel<<<L.nchunks, kRouteThreads, 0, s>>>(
