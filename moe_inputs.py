@@ -84,6 +84,9 @@ CONFIGS = {
                                mode=MODE_FP8_BWD, seed=1003),
     "30b_mxfp8": LayerConfig("30b_mxfp8", T=16384, D=2048, F=768, E=128, K=8,
                              mode=MODE_MXFP8, routing="zipf", seed=1004),
+    # blockwise FP8 in both passes (the pages' "fp8" precision) at the 30B shape
+    "30b_fp8": LayerConfig("30b_fp8", T=16384, D=2048, F=768, E=128, K=8, mode=MODE_FP8,
+                           seed=1007),
     # one expert-parallel rank's share (EP = 8): 16 local experts receiving the
     # 131072 routed rows of the 30B/235B layers, one row per received pair
     # (top-1 over the local experts), so n_e is about 8192 and N, D, F and the

@@ -239,3 +239,8 @@ def test_full_size_235b_fp8bwd_sampled():
 @pytest.mark.timeout(600)
 def test_full_size_30b_mxfp8_sampled():
     _full_size_fp8("30b_mxfp8", ntok=24, nexp=2)
+
+
+@pytest.mark.timeout(600)
+def test_full_size_30b_fp8_sampled():
+    _full_size_fp8("30b_fp8", ntok=24, nexp=2)
