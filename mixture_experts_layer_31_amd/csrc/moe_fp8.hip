@@ -735,11 +735,15 @@ using namespace gemm;
 //  * blockwise token-grouped GEMMs: 256 x 256, eight waves, the four-stage
 //    64-element ring (about 30% faster than four waves of 128 x 64);
 //  * blockwise weight-gradient GEMMs, whose scales vary along both output
-//    axes (a scale product per output element and 128-token block): 256 x
-//    128, four waves, the promoting 128-element loop.
+//    axes (a scale product per output element and 128-token block): the
+//    promoting 128-element loop on 256 x 128 tiles of eight 64 x 64 waves,
+//    three stages.  The accumulators, partials, fragments and each column's
+//    scales fit in about 190 registers, so two waves share a SIMD and one's
+//    promotion overlaps the other's MFMAs (about 30% faster than four waves
+//    of 128 x 64, one per SIMD).
 using TileF8 = Tile<256, 256, 2, 4, 2>;
 using TileF8R = Tile<256, 256, 2, 4, 4>;
-using TileF8B = Tile<256, 128, 2, 2, 3>;
+using TileF8B = Tile<256, 128, 4, 2, 3>;
 template <bool MX> using F8GrTile = typename std::conditional<MX, TileF8, TileF8R>::type;
 template <bool MX> using F8WgTile = typename std::conditional<MX, TileF8, TileF8B>::type;
 
