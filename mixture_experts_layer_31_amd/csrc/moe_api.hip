@@ -275,8 +275,8 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
   char* sc = static_cast<char*>(scratch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool io_f32 = d->mode == MOE_FP32 || d->mode == MOE_FP32_BF16GEMM;
-  if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s))) return rc;
-  if (L.recompute) {  // H again, by the forward's own W1 GEMM
+  if (L.recompute) {  // H again, by the forward's own W1 GEMM (before the combine-backward,
+                      // whose fused FP8 row codes the FP8 recompute's x codes would overwrite)
     if (d->mode == MOE_FP32)
       rc = launch_recompute_h_f32(*d, L, static_cast<const float*>(w1), sc, s);
     else if (fp8_mode(d->mode) && d->mode != MOE_FP8_BWD)
@@ -285,11 +285,21 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
       rc = launch_recompute_h(*d, L, g1, sc, s);
     if (rc) return rc;
   }
+  if (fp8_mode(d->mode)) {  // the combine-backward also quantises dYw's rows for the W2 dgrad
+    uint8_t* qc;
+    uint32_t* qs;
+    fp8_row_codes(*d, L, sc, &qc, &qs);
+    if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s,
+                                 d->mode == MOE_MXFP8 ? 1 : 2, qc, qs)))
+      return rc;
+  } else if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s))) {
+    return rc;
+  }
   if (d->mode == MOE_FP32)
     rc = launch_bwd_gemms_f32(*d, L, static_cast<const float*>(w1), static_cast<const float*>(w2),
                               static_cast<float*>(dw1), static_cast<float*>(dw2), sc, s);
   else if (fp8_mode(d->mode))
-    rc = fp8_bwd_gemms(*d, L, static_cast<const char*>(wprep), dw1, dw2, sc, s);
+    rc = fp8_bwd_gemms(*d, L, static_cast<const char*>(wprep), dw1, dw2, sc, s, true);
   else
     rc = launch_bwd_gemms(*d, L, g1, g2, dw1, dw2, io_f32, sc, s);
   if (rc) return rc;

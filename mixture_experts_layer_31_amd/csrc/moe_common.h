@@ -92,9 +92,12 @@ int launch_combine(const moe_desc& d, const Layout& L, const float* topk_w, void
                    bool out_f32, const char* scratch, hipStream_t s);
 int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
                      const char* scratch, hipStream_t s);
-// Combine-backward: dYw_perm rows (w * dy, bf16) and dtopk_w = <dy, o>.
+// Combine-backward: dYw_perm rows (w * dy, bf16) and dtopk_w = <dy, o>.  With
+// qmode 1 (MX) or 2 (blockwise) it also writes the rows' e4m3 quantisation
+// along D (codes [N, D], scale entries [D/128][N]); bf16 rows only.
 int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool in_f32,
-                       const float* topk_w, float* dtopk_w, char* scratch, hipStream_t s);
+                       const float* topk_w, float* dtopk_w, char* scratch, hipStream_t s,
+                       int qmode = 0, uint8_t* qcodes = nullptr, uint32_t* qsc = nullptr);
 int launch_convert_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
 // Router ahead of the layer (moe_router.hip): softmax -> top-K -> renormalise,
 // and its backward to the logits.  Requires 1 <= K <= min(E, 64), E <= 512.
@@ -128,8 +131,12 @@ int fp8_prepare_weights(const moe_desc& d, const uint16_t* w1, const uint16_t* w
                         hipStream_t s);
 int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,
                   hipStream_t s);
+// The FP8 backward; dyw_quantised: the combine-backward already wrote dYw's row
+// quantisation into the row-code buffer (fp8_row_codes).
 int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* dw1, void* dw2,
-                  char* scratch, hipStream_t s);
+                  char* scratch, hipStream_t s, bool dyw_quantised = false);
+void fp8_row_codes(const moe_desc& d, const Layout& L, char* scratch, uint8_t** codes,
+                   uint32_t** scales);
 int fp8_view(const moe_desc& d, const Layout& L, char* scratch, int which, void** ptr,
              size_t* bytes);
 int launch_bwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,

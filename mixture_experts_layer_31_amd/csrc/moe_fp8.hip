@@ -28,6 +28,7 @@
 // k-step and promotes the partial sum in fp32: acc += partial * s_a * s_b.
 #include <type_traits>
 
+#include "moe_fp8_codec.h"
 #include "moe_gemm_common.h"
 
 namespace moe {
@@ -39,40 +40,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
 // Encodings.
-
-// Smallest X in [-127, 127] with amax <= 448 * 2^X (0 for amax == 0).
-__device__ __forceinline__ int e8m0_exponent(float amax) {
-  if (amax == 0.f) return 0;
-  int e;
-  const float m = frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1); 448 = 0.875 * 2^9
-  int X = (m <= 0.875f) ? e - 9 : e - 8;
-  return X < -127 ? -127 : (X > 127 ? 127 : X);
-}
-
-// Four OCP e4m3 codes (byte k = code of value k) by the hardware conversion:
-// nearest value, ties to even mantissa, magnitudes >= 448 saturate to 448
-// (checked against a software encoder of that rule with an in-bounds probe
-// over every code, every rounding midpoint and its neighbours, and 4e5 random
-// values).
-__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return uint32_t(w);
-}
-
-// x / sc rounded to fp32 (IEEE division), the value whose e4m3 code a
-// blockwise tile stores.  The product x * rc (rc = 1/sc) lies within about
-// 1.5 fp32 ulps of that quotient, so both have the same e4m3 code unless an
-// e4m3 rounding midpoint lies within a few ulps of the product (its low 20
-// mantissa bits near 0x80000 in the normal e4m3 range) or the product is in the
-// subnormal e4m3 range (below 2^-6); only then is the division done.
-__device__ __forceinline__ float block_quotient(float x, float sc, float rc) {
-  const float y = x * rc;
-  const float a = fabsf(y);
-  const int d = int(__float_as_uint(a) & 0xFFFFFu) - 0x80000;
-  const bool exact = (a < 0.015625f && a != 0.f) || (d >= -4 && d <= 4);
-  return exact ? x / sc : y;
-}
 
 enum QMode { Q_BLOCK_ROW = 0, Q_MX = 1, Q_BLOCK_TILE = 2 };
 
@@ -189,11 +156,11 @@ __global__ void __launch_bounds__(256) quant_tile_kernel(QArgs p) {
     entry = __float_as_uint(sc);
     const float rc = 1.f / sc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float y[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) y[k] = block_quotient(v[4 * i + k], sc, rc);
-      packed[i] = pack_e4m3x4(y[0], y[1], y[2], y[3]);
+    for (int i = 0; i < 8; ++i) {
+      float y[8];
+      block_quotients(v + 8 * i, sc, rc, y);
+      packed[2 * i] = pack_e4m3x4(y[0], y[1], y[2], y[3]);
+      packed[2 * i + 1] = pack_e4m3x4(y[4], y[5], y[6], y[7]);
     }
   }
   uint8_t* out = p.out + b * p.out_bstride;
@@ -251,23 +218,19 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QArgs p) {
     uint32_t entry;
     uint2 codes;
     if constexpr (MX) {
-      am = fmaxf(am, __shfl_xor(am, 1, 64));
-      am = fmaxf(am, __shfl_xor(am, 2, 64));
+      am = max4(am);
       const int X = e8m0_exponent(am);
       const float m = ldexpf(1.f, -X);
       codes.x = pack_e4m3x4(v[0] * m, v[1] * m, v[2] * m, v[3] * m);
       codes.y = pack_e4m3x4(v[4] * m, v[5] * m, v[6] * m, v[7] * m);
-      entry = uint32_t(X + 127) << (8 * (l16 >> 2));  // byte g of the entry: group g's exponent
-      entry |= __shfl_xor(entry, 4, 64);
-      entry |= __shfl_xor(entry, 8, 64);
+      // byte g of the entry: group g's exponent
+      entry = or16_of_quads(uint32_t(X + 127) << (8 * (l16 >> 2)));
     } else {
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+      am = max16(am);
       const float sc = am == 0.f ? 1.f : am / 448.f;
       const float rc = 1.f / sc;
       float y[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) y[k] = block_quotient(v[k], sc, rc);
+      block_quotients(v, sc, rc, y);
       codes.x = pack_e4m3x4(y[0], y[1], y[2], y[3]);
       codes.y = pack_e4m3x4(y[4], y[5], y[6], y[7]);
       entry = __float_as_uint(sc);
@@ -351,11 +314,11 @@ __global__ void __launch_bounds__(256) quant_tokens_kernel(QArgs p) {
     const float rc = 1.f / sc;
     entry = __float_as_uint(sc);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float y[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) y[k] = block_quotient(v[4 * i + k], sc, rc);
-      packed[i] = pack_e4m3x4(y[0], y[1], y[2], y[3]);
+    for (int i = 0; i < 8; ++i) {
+      float y[8];
+      block_quotients(v + 8 * i, sc, rc, y);
+      packed[2 * i] = pack_e4m3x4(y[0], y[1], y[2], y[3]);
+      packed[2 * i + 1] = pack_e4m3x4(y[4], y[5], y[6], y[7]);
     }
   }
   uint4* dst = reinterpret_cast<uint4*>(p.out + size_t(c0 + q) * p.out_ld + slot0 + h * 64);
@@ -1060,8 +1023,15 @@ int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* s
             : run_f8_grouped<false, EPI_STORE>(d, L, b, D, "gemm_w2", scratch, s);
 }
 
+void fp8_row_codes(const moe_desc& d, const Layout& L, char* scratch, uint8_t** codes,
+                   uint32_t** scales) {
+  const F8Scratch f = f8scratch(d, L, scratch);
+  *codes = f.qrow;
+  *scales = f.qrow_sc;
+}
+
 int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* dw1, void* dw2,
-                  char* scratch, hipStream_t s) {
+                  char* scratch, hipStream_t s, bool dyw_quantised) {
   const WLayout W = wlayout(d);
   const F8Scratch f = f8scratch(d, L, scratch);
   const bool mx = d.mode == MOE_MXFP8;
@@ -1073,7 +1043,8 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   const auto* xp = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
   int rc;
   // W2 dgrad + SwiGLU-backward
-  if ((rc = quant_rows(d, dyw, D, mx, f.qrow, f.qrow_sc, "quant_dyw_rows", s))) return rc;
+  if (!dyw_quantised && (rc = quant_rows(d, dyw, D, mx, f.qrow, f.qrow_sc, "quant_dyw_rows", s)))
+    return rc;
   F8Args a{};
   a.K = D;
   a.A = f.qrow;

@@ -15,6 +15,7 @@
 #include <type_traits>
 
 #include "moe_common.h"
+#include "moe_fp8_codec.h"
 
 namespace moe {
 
@@ -138,11 +139,20 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_kernel(
 // One wavefront owns one token: its dy row stays in registers while the K
 // expert-output rows are streamed and dotted against it.  CPL = 16-byte chunks
 // per lane (D / 512, at least 1).
-template <typename IO, typename ACT, int CPL>
+// QM (FP8 backward modes, bf16 rows): the kernel also writes the e4m3 row
+// quantisation of each dYw row along D (the W2 dgrad's A operand), from the
+// same bf16-rounded values it stores: QM_BLOCK, an fp32 scale per 128 columns
+// (a group is 16 consecutive lanes' chunks); QM_MX, an e8m0 scale per 32 (4
+// lanes).  Codes are [N, D] bytes, scale entries [D/128][N], as the standalone
+// row quantiser writes them.  D / 8 must be a multiple of 16 so a group never
+// straddles active and idle lanes.
+enum { QM_NONE = 0, QM_MX = 1, QM_BLOCK = 2 };
+
+template <typename IO, typename ACT, int CPL, int QM>
 __global__ void __launch_bounds__(kRowThreads) dispatch_dy_kernel(
     const IO* __restrict__ dy, int T, int K, int D, const int32_t* __restrict__ pos,
     const float* __restrict__ topk_w, const ACT* __restrict__ O, ACT* __restrict__ dst,
-    float* __restrict__ dprob) {
+    float* __restrict__ dprob, uint8_t* __restrict__ qcodes, uint32_t* __restrict__ qsc, int N) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -165,8 +175,9 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_dy_kernel(
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = lane + 64 * j;
+      float sc[8];
       if (c < chunks) {
-        float o[8], sc[8];
+        float o[8];
         load8(O, (size_t(q) * D) / 8 + c, o);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -174,6 +185,38 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_dy_kernel(
           sc[i] = w * v[j][i];
         }
         store8(dst, (size_t(q) * D) / 8 + c, sc);
+      }
+      if constexpr (QM != QM_NONE) {
+        // quantise the stored (bf16-rounded) values; idle lanes join the reductions with 0
+        float am = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          sc[i] = c < chunks ? float((__bf16)sc[i]) : 0.f;  // the value store8 wrote
+          am = fmaxf(am, fabsf(sc[i]));
+        }
+        uint32_t entry;
+        uint2 codes;
+        if constexpr (QM == QM_MX) {
+          am = max4(am);
+          const int X = e8m0_exponent(am);
+          const float m = ldexpf(1.f, -X);
+          codes.x = pack_e4m3x4(sc[0] * m, sc[1] * m, sc[2] * m, sc[3] * m);
+          codes.y = pack_e4m3x4(sc[4] * m, sc[5] * m, sc[6] * m, sc[7] * m);
+          entry = or16_of_quads(uint32_t(X + 127) << (8 * ((lane & 15) >> 2)));
+        } else {
+          am = max16(am);
+          const float s = am == 0.f ? 1.f : am / 448.f;
+          const float r = 1.f / s;
+          float y[8];
+          block_quotients(sc, s, r, y);
+          codes.x = pack_e4m3x4(y[0], y[1], y[2], y[3]);
+          codes.y = pack_e4m3x4(y[4], y[5], y[6], y[7]);
+          entry = __float_as_uint(s);
+        }
+        if (c < chunks) {
+          *reinterpret_cast<uint2*>(qcodes + size_t(q) * D + 8 * c) = codes;
+          if ((lane & 15) == 0) qsc[size_t(c >> 4) * N + q] = entry;
+        }
       }
     }
 #pragma unroll
@@ -260,13 +303,13 @@ int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-template <typename IO, typename ACT>
+template <typename IO, typename ACT, int QM>
 static int dispatch_dy_cpl(const moe_desc& d, const IO* dy, const int32_t* pos,
                            const float* topk_w, const ACT* o, ACT* dst, float* dprob,
-                           hipStream_t s) {
+                           uint8_t* qcodes, uint32_t* qsc, hipStream_t s) {
   const unsigned blocks = unsigned((d.T + kRowThreads / 64 - 1) / (kRowThreads / 64));
   const int cpl = (d.D / 8 + 63) / 64;
-#define MOE_DY(C) dispatch_dy_kernel<IO, ACT, C><<<blocks, kRowThreads, 0, s>>>(dy, d.T, d.K, d.D, pos, topk_w, o, dst, dprob)
+#define MOE_DY(C) dispatch_dy_kernel<IO, ACT, C, QM><<<blocks, kRowThreads, 0, s>>>(dy, d.T, d.K, d.D, pos, topk_w, o, dst, dprob, qcodes, qsc, d.T * d.K)
   if (cpl <= 1) MOE_DY(1);
   else if (cpl <= 2) MOE_DY(2);
   else if (cpl <= 4) MOE_DY(4);
@@ -278,15 +321,24 @@ static int dispatch_dy_cpl(const moe_desc& d, const IO* dy, const int32_t* pos,
 }
 
 int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool in_f32,
-                       const float* topk_w, float* dtopk_w, char* scratch, hipStream_t s) {
+                       const float* topk_w, float* dtopk_w, char* scratch, hipStream_t s,
+                       int qmode, uint8_t* qcodes, uint32_t* qsc) {
   const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
   prof_begin("dispatch_dy", s);
   const int rc = with_types(d, in_f32, [&](auto io, auto act) {
     using IO = decltype(io);
     using ACT = decltype(act);
-    return dispatch_dy_cpl<IO, ACT>(d, static_cast<const IO*>(dy), pos, topk_w,
-                                    reinterpret_cast<const ACT*>(scratch + L.o),
-                                    reinterpret_cast<ACT*>(scratch + L.dyperm), dtopk_w, s);
+    const IO* src = static_cast<const IO*>(dy);
+    const ACT* o = reinterpret_cast<const ACT*>(scratch + L.o);
+    ACT* dst = reinterpret_cast<ACT*>(scratch + L.dyperm);
+    if constexpr (std::is_same<ACT, uint16_t>::value) {
+      if (qmode == 1)
+        return dispatch_dy_cpl<IO, ACT, QM_MX>(d, src, pos, topk_w, o, dst, dtopk_w, qcodes, qsc, s);
+      if (qmode == 2)
+        return dispatch_dy_cpl<IO, ACT, QM_BLOCK>(d, src, pos, topk_w, o, dst, dtopk_w, qcodes, qsc, s);
+    }
+    if (qmode != 0) return int(MOE_EUNSUPPORTED);
+    return dispatch_dy_cpl<IO, ACT, QM_NONE>(d, src, pos, topk_w, o, dst, dtopk_w, nullptr, nullptr, s);
   });
   prof_end(s);
   if (rc) return rc;

@@ -125,6 +125,21 @@ def test_fp8_quantisers_and_gemms(name):
     L.bwd()
     torch.cuda.synchronize()
     assert L.check() == moe.MOE_OK
+    # the W2 dgrad consumed dYw's row codes written by the combine-backward: its SwiGLU-backward
+    # output must equal the oracle's row quantisation of the dYw rows times the quantised W2
+    dYw = L.view(moe.MOE_VIEW_DYPERM, D)[:len(src)]
+    qc, qs = f8.quant_rows(dYw, 32 if mx else 128, mx)
+    dYdq = f8.dequant_rows(qc, qs, 32 if mx else 128, mx)
+    H = L.view(moe.MOE_VIEW_H, 2 * F)[:len(src)].astype(np.float64)
+    dA = np.zeros((len(src), F))
+    for e in range(cfg.E):
+        rows = slice(offsets[e], offsets[e + 1])
+        dA[rows] = dYdq[rows] @ _w_deq(inp["w2"][e], True, mx)
+    g, u = H[:, :F], H[:, F:]
+    sg = 1.0 / (1.0 + np.exp(-g))
+    dH_ref = np.concatenate([dA * u * sg * (1 + g * (1 - sg)), dA * g * sg], axis=1)
+    dH_gpu = L.view(moe.MOE_VIEW_DH, 2 * F)[:len(src)]
+    assert rel_err(dH_gpu, dH_ref) <= 1e-2, ("dH from fused dYw codes", rel_err(dH_gpu, dH_ref))
     # the backward's last quantised operands: dH rows (W1 dgrad), dH and x_perm along tokens (W1 wgrad)
     dH = L.view(moe.MOE_VIEW_DH, 2 * F)[:len(src)]
     xp = L.view(moe.MOE_VIEW_XPERM, D)[:len(src)]
