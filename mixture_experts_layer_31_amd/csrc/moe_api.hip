@@ -245,12 +245,22 @@ int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const flo
     if ((rc = launch_fwd_queue(*d, L, x, io_f32, topk_w, g1, g2, sc, s))) return rc;
     return launch_combine(*d, L, topk_w, y, io_f32, sc, s);
   }
-  if ((rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s))) return rc;
+  const bool fwd_q = fp8_mode(d->mode) && d->mode != MOE_FP8_BWD;
+  if (fwd_q) {  // the dispatch also quantises x's rows for the W1 GEMM
+    uint8_t* qc;
+    uint32_t* qs;
+    fp8_row_codes(*d, L, sc, &qc, &qs);
+    if ((rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s,
+                              d->mode == MOE_MXFP8 ? 1 : 2, qc, qs)))
+      return rc;
+  } else if ((rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s))) {
+    return rc;
+  }
   if (d->mode == MOE_FP32)
     rc = launch_fwd_gemms_f32(*d, L, static_cast<const float*>(w1), static_cast<const float*>(w2),
                               sc, s);
   else if (fp8_mode(d->mode) && d->mode != MOE_FP8_BWD)
-    rc = fp8_fwd_gemms(*d, L, static_cast<const char*>(wprep), sc, s);
+    rc = fp8_fwd_gemms(*d, L, static_cast<const char*>(wprep), sc, s, true);
   else
     rc = launch_fwd_gemms(*d, L, g1, g2, sc, s);
   if (rc) return rc;

@@ -87,7 +87,8 @@ int launch_clear_err(char* scratch, const Layout& L, hipStream_t s);
 // Row gathers/scatters: dispatch (x -> expert-contiguous rows), combine and the
 // un-permute reduction.  `in_f32`/`out_f32` select fp32 instead of bf16 I/O.
 int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool in_f32,
-                    const float* topk_w, char* scratch, size_t dst_off, hipStream_t s);
+                    const float* topk_w, char* scratch, size_t dst_off, hipStream_t s,
+                    int qmode = 0, uint8_t* qcodes = nullptr, uint32_t* qsc = nullptr);
 int launch_combine(const moe_desc& d, const Layout& L, const float* topk_w, void* y,
                    bool out_f32, const char* scratch, hipStream_t s);
 int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
@@ -129,8 +130,9 @@ int fp8_recompute_h(const moe_desc& d, const Layout& L, const char* wprep, char*
                     hipStream_t s);
 int fp8_prepare_weights(const moe_desc& d, const uint16_t* w1, const uint16_t* w2, char* wprep,
                         hipStream_t s);
+// x_quantised: the dispatch already wrote x_perm's row quantisation (fp8_row_codes).
 int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,
-                  hipStream_t s);
+                  hipStream_t s, bool x_quantised = false);
 // The FP8 backward; dyw_quantised: the combine-backward already wrote dYw's row
 // quantisation into the row-code buffer (fp8_row_codes).
 int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* dw1, void* dw2,

@@ -958,13 +958,15 @@ int fp8_view(const moe_desc& d, const Layout& L, char* scratch, int which, void*
 // Expert linear 1 + SwiGLU on the quantised x rows: stores H into `h` and A
 // into `act` (either may be null, as in the bf16 path).
 static int fp8_w1_swiglu(const moe_desc& d, const Layout& L, const char* wprep, uint16_t* h,
-                         uint16_t* act, const char* name, char* scratch, hipStream_t s) {
+                         uint16_t* act, const char* name, char* scratch, hipStream_t s,
+                         bool x_quantised = false) {
   const WLayout W = wlayout(d);
   const F8Scratch f = f8scratch(d, L, scratch);
   const bool mx = d.mode == MOE_MXFP8;
   const int D = d.D, F = d.F, N = d.T * d.K;
   int rc;
-  if ((rc = quant_rows(d, reinterpret_cast<const uint16_t*>(scratch + L.xperm), D, mx, f.qrow,
+  if (!x_quantised &&
+      (rc = quant_rows(d, reinterpret_cast<const uint16_t*>(scratch + L.xperm), D, mx, f.qrow,
                        f.qrow_sc, "quant_x_rows", s)))
     return rc;
   F8Args a{};
@@ -992,14 +994,15 @@ int fp8_recompute_h(const moe_desc& d, const Layout& L, const char* wprep, char*
 }
 
 int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,
-                  hipStream_t s) {
+                  hipStream_t s, bool x_quantised) {
   const WLayout W = wlayout(d);
   const F8Scratch f = f8scratch(d, L, scratch);
   const bool mx = d.mode == MOE_MXFP8;
   const int D = d.D, F = d.F, N = d.T * d.K;
   int rc = fp8_w1_swiglu(d, L, wprep,
                          L.recompute ? nullptr : reinterpret_cast<uint16_t*>(scratch + L.h),
-                         reinterpret_cast<uint16_t*>(scratch + L.a), "gemm_w1_swiglu", scratch, s);
+                         reinterpret_cast<uint16_t*>(scratch + L.a), "gemm_w1_swiglu", scratch, s,
+                         x_quantised);
   if (rc) return rc;
   // expert linear 2
   if ((rc = quant_rows(d, reinterpret_cast<const uint16_t*>(scratch + L.a), F, mx, f.qrow,

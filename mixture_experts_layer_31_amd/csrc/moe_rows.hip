@@ -61,13 +61,50 @@ __device__ __forceinline__ void store8(float* p, size_t i8, const float (&f)[8])
   reinterpret_cast<float4*>(p)[2 * i8 + 1] = make_float4(f[4], f[5], f[6], f[7]);
 }
 
+// Row quantisation fused into a row mover (FP8 modes, bf16 rows): none, MXFP8
+// (e8m0 scale per 32 columns) or blockwise (fp32 scale per 128 columns).
+enum { QM_NONE = 0, QM_MX = 1, QM_BLOCK = 2 };
+
+// e4m3 codes (and the group's scale entry, valid in every lane) of eight
+// consecutive values whose 32-column (MX: 4 lanes) or 128-column (blockwise:
+// 16 lanes) group is held by aligned consecutive lanes, all of which call this.
+template <int QM>
+__device__ __forceinline__ uint2 quantise8(const float (&v)[8], int lane, uint32_t& entry) {
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+  uint2 codes;
+  if constexpr (QM == QM_MX) {
+    am = max4(am);
+    const int X = e8m0_exponent(am);
+    const float m = ldexpf(1.f, -X);
+    codes.x = pack_e4m3x4(v[0] * m, v[1] * m, v[2] * m, v[3] * m);
+    codes.y = pack_e4m3x4(v[4] * m, v[5] * m, v[6] * m, v[7] * m);
+    entry = or16_of_quads(uint32_t(X + 127) << (8 * ((lane & 15) >> 2)));
+  } else {
+    am = max16(am);
+    const float s = am == 0.f ? 1.f : am / 448.f;
+    float y[8];
+    block_quotients(v, s, 1.f / s, y);
+    codes.x = pack_e4m3x4(y[0], y[1], y[2], y[3]);
+    codes.y = pack_e4m3x4(y[4], y[5], y[6], y[7]);
+    entry = __float_as_uint(s);
+  }
+  return codes;
+}
+
 // IO: element type of the layer's inputs/outputs; ACT: of the permuted rows in
 // scratch (uint16_t = bf16, or float).  A bf16 -> bf16 or fp32 -> fp32 move is
-// a bitwise copy; fp32 -> bf16 rounds once (RNE).
-template <typename IO, typename ACT>
+// a bitwise copy; fp32 -> bf16 rounds once (RNE).  With QM (FP8 forward modes,
+// bf16 rows) the token's row is also quantised along D once and its codes
+// written with every copy: codes [N, D], scale entries [D/128][N], as the
+// standalone row quantiser writes them (a token's chunks sit on consecutive
+// threads, so the groups are aligned lanes when D / 8 is a multiple of 16).
+template <typename IO, typename ACT, int QM>
 __global__ void __launch_bounds__(kRowThreads) dispatch_kernel(
     const IO* __restrict__ rows, int T, int K, int D, const int32_t* __restrict__ pos,
-    const float* __restrict__ topk_w, float* __restrict__ wperm, ACT* __restrict__ dst) {
+    const float* __restrict__ topk_w, float* __restrict__ wperm, ACT* __restrict__ dst,
+    uint8_t* __restrict__ qcodes, uint32_t* __restrict__ qsc, int N) {
   const int chunks = D / 8;
   const int tpr = chunks < kRowThreads ? chunks : kRowThreads;
   const int rpb = kRowThreads / tpr;
@@ -79,9 +116,24 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_kernel(
     const size_t src = (size_t(t) * D) / 8 + c;
     if constexpr (std::is_same<IO, uint16_t>::value && std::is_same<ACT, uint16_t>::value) {
       const uint4 v = reinterpret_cast<const uint4*>(rows)[src];
-      for (int k = 0; k < K; ++k) {
-        const int q = prow[k];
-        if (q >= 0) reinterpret_cast<uint4*>(dst)[(size_t(q) * D) / 8 + c] = v;
+      if constexpr (QM != QM_NONE) {
+        float f[8];
+        unpack8(v, f);
+        uint32_t entry;
+        const uint2 codes = quantise8<QM>(f, threadIdx.x & 63, entry);
+        for (int k = 0; k < K; ++k) {
+          const int q = prow[k];
+          if (q >= 0) {
+            reinterpret_cast<uint4*>(dst)[(size_t(q) * D) / 8 + c] = v;
+            *reinterpret_cast<uint2*>(qcodes + size_t(q) * D + 8 * c) = codes;
+            if ((c & 15) == 0) qsc[size_t(c >> 4) * N + q] = entry;
+          }
+        }
+      } else {
+        for (int k = 0; k < K; ++k) {
+          const int q = prow[k];
+          if (q >= 0) reinterpret_cast<uint4*>(dst)[(size_t(q) * D) / 8 + c] = v;
+        }
       }
     } else {
       float f[8];
@@ -146,7 +198,6 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_kernel(
 // lanes).  Codes are [N, D] bytes, scale entries [D/128][N], as the standalone
 // row quantiser writes them.  D / 8 must be a multiple of 16 so a group never
 // straddles active and idle lanes.
-enum { QM_NONE = 0, QM_MX = 1, QM_BLOCK = 2 };
 
 template <typename IO, typename ACT, int CPL, int QM>
 __global__ void __launch_bounds__(kRowThreads) dispatch_dy_kernel(
@@ -188,31 +239,10 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_dy_kernel(
       }
       if constexpr (QM != QM_NONE) {
         // quantise the stored (bf16-rounded) values; idle lanes join the reductions with 0
-        float am = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          sc[i] = c < chunks ? float((__bf16)sc[i]) : 0.f;  // the value store8 wrote
-          am = fmaxf(am, fabsf(sc[i]));
-        }
+        for (int i = 0; i < 8; ++i) sc[i] = c < chunks ? float((__bf16)sc[i]) : 0.f;
         uint32_t entry;
-        uint2 codes;
-        if constexpr (QM == QM_MX) {
-          am = max4(am);
-          const int X = e8m0_exponent(am);
-          const float m = ldexpf(1.f, -X);
-          codes.x = pack_e4m3x4(sc[0] * m, sc[1] * m, sc[2] * m, sc[3] * m);
-          codes.y = pack_e4m3x4(sc[4] * m, sc[5] * m, sc[6] * m, sc[7] * m);
-          entry = or16_of_quads(uint32_t(X + 127) << (8 * ((lane & 15) >> 2)));
-        } else {
-          am = max16(am);
-          const float s = am == 0.f ? 1.f : am / 448.f;
-          const float r = 1.f / s;
-          float y[8];
-          block_quotients(sc, s, r, y);
-          codes.x = pack_e4m3x4(y[0], y[1], y[2], y[3]);
-          codes.y = pack_e4m3x4(y[4], y[5], y[6], y[7]);
-          entry = __float_as_uint(s);
-        }
+        const uint2 codes = quantise8<QM>(sc, lane, entry);
         if (c < chunks) {
           *reinterpret_cast<uint2*>(qcodes + size_t(q) * D + 8 * c) = codes;
           if ((lane & 15) == 0) qsc[size_t(c >> 4) * N + q] = entry;
@@ -255,19 +285,36 @@ static int with_types(const moe_desc& d, bool io_f32, F f) {
 }
 
 int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool in_f32,
-                    const float* topk_w, char* scratch, size_t dst_off, hipStream_t s) {
+                    const float* topk_w, char* scratch, size_t dst_off, hipStream_t s,
+                    int qmode, uint8_t* qcodes, uint32_t* qsc) {
   const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
   auto* wperm = topk_w ? reinterpret_cast<float*>(scratch + L.wperm) : nullptr;
   prof_begin("dispatch", s);
-  with_types(d, in_f32, [&](auto io, auto act) {
+  const int rc = with_types(d, in_f32, [&](auto io, auto act) {
     using IO = decltype(io);
     using ACT = decltype(act);
-    dispatch_kernel<IO, ACT><<<row_blocks(d), kRowThreads, 0, s>>>(
-        static_cast<const IO*>(rows), d.T, d.K, d.D, pos, topk_w, wperm,
-        reinterpret_cast<ACT*>(scratch + dst_off));
+    const IO* src = static_cast<const IO*>(rows);
+    ACT* dst = reinterpret_cast<ACT*>(scratch + dst_off);
+    const int N = d.T * d.K;
+    if constexpr (std::is_same<IO, uint16_t>::value && std::is_same<ACT, uint16_t>::value) {
+      if (qmode == 1) {
+        dispatch_kernel<IO, ACT, QM_MX><<<row_blocks(d), kRowThreads, 0, s>>>(
+            src, d.T, d.K, d.D, pos, topk_w, wperm, dst, qcodes, qsc, N);
+        return 0;
+      }
+      if (qmode == 2) {
+        dispatch_kernel<IO, ACT, QM_BLOCK><<<row_blocks(d), kRowThreads, 0, s>>>(
+            src, d.T, d.K, d.D, pos, topk_w, wperm, dst, qcodes, qsc, N);
+        return 0;
+      }
+    }
+    if (qmode != 0) return int(MOE_EUNSUPPORTED);
+    dispatch_kernel<IO, ACT, QM_NONE><<<row_blocks(d), kRowThreads, 0, s>>>(
+        src, d.T, d.K, d.D, pos, topk_w, wperm, dst, nullptr, nullptr, N);
     return 0;
   });
   prof_end(s);
+  if (rc) return rc;
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

@@ -113,6 +113,16 @@ def test_fp8_quantisers_and_gemms(name):
     src = r["src"]
     e_of = np.repeat(np.arange(cfg.E), np.diff(offsets))
     D, F = cfg.D, cfg.F
+    if fwd_q:  # x_perm's rows were quantised by the dispatch: H = quantised x times quantised W1
+        xp = L.view(moe.MOE_VIEW_XPERM, D)[:len(src)]
+        qc, qs = f8.quant_rows(xp, 32 if mx else 128, mx)
+        xdq = f8.dequant_rows(qc, qs, 32 if mx else 128, mx)
+        Hg = L.view(moe.MOE_VIEW_H, 2 * F)[:len(src)]
+        Href = np.zeros_like(Hg, dtype=np.float64)
+        for e in range(cfg.E):
+            rows = slice(offsets[e], offsets[e + 1])
+            Href[rows] = xdq[rows] @ _w_deq(inp["w1"][e], False, mx).T
+        assert rel_err(Hg, Href) <= 1e-2, ("H from fused x codes", rel_err(Hg, Href))
     if fwd_q:  # the forward's last quantised operand: A rows for the W2 GEMM
         A = L.view(moe.MOE_VIEW_A, F)[:len(src)]
         Adq = _check_rows(L, A, mx)
