@@ -41,56 +41,43 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // ---------------------------------------------------------------------------
 // Encodings.
 
-enum QMode { Q_BLOCK_ROW = 0, Q_MX = 1, Q_BLOCK_TILE = 2 };
+enum QMode { Q_MX = 1, Q_BLOCK_TILE = 2 };  // weight quantiser modes
 
 // ---------------------------------------------------------------------------
-// Tile quantiser: one workgroup quantises a 128 (r) x 128 (c) bf16 tile.
+// Weight quantiser (moe_prepare_weights): one workgroup quantises a 128 (r) x
+// 128 (c) tile of one expert's bf16 weight matrix [R, C].
 //   TRANS = false: the contraction runs along c; codes out[r][c], scale entry
 //                  [c-step][r].
-//   TRANS = true:  the contraction runs along r; codes out[c][r-slot], scale
-//                  entry [r-step][c].
-// Rows come either from token segments (expert e's permuted rows, the r-steps
-// of the padded token axis listed by the routing step's 128-row tile prefix) or
-// from a uniform batch of matrices (weights: batch = expert).
+//   TRANS = true:  the contraction runs along r; codes out[c][r], scale entry
+//                  [r-step][c].
+// Blockwise tiles share one fp32 scale (the 128 x 128 block's amax / 448);
+// MXFP8 groups are 32 consecutive contraction elements.  Activations have
+// their own kernels below (quant_rows_kernel, quant_tokens_kernel).
 struct QArgs {
   const uint16_t* in;   // bf16 rows of length cols
-  int64_t in_bstride;   // elements between batches
+  int64_t in_bstride;   // elements between batches (weights: between experts)
   int cols;             // input row length (multiple of 128)
-  int rows;             // uniform mode: rows per batch (multiple of 128)
+  int rows;             // weights: rows per expert (multiple of 128)
   uint8_t* out;
   int64_t out_ld, out_bstride;
   uint32_t* sc;
   int64_t sc_ld, sc_bstride;
-  const int32_t* offsets;  // segmented mode: [E+1] expert row offsets
-  const int32_t* tstart;   // segmented mode: [E+1] prefix of ceil(count / 128)
+  const int32_t* offsets;  // token quantiser: [E+1] expert row offsets
+  const int32_t* tstart;   // token quantiser: [E+1] prefix of ceil(count / 128)
   int E;
-  int ntr;                 // uniform mode: r-steps per batch
-  int total_rows;          // rows of the input (bounds for untransposed activations)
+  int ntr;                 // weights: r-steps per expert
+  int total_rows;          // row quantiser: rows of the input
 };
 
-template <bool TRANS, int MODE, bool SEG>
+template <bool TRANS, int MODE>
 __global__ void __launch_bounds__(256) quant_tile_kernel(QArgs p) {
+  static_assert(MODE == Q_MX || MODE == Q_BLOCK_TILE, "weights: MXFP8 groups or 128x128 blocks");
   __shared__ __attribute__((aligned(16))) uint16_t tile[128 * 128];
   __shared__ float red[4];
   const int ctiles = p.cols / 128;
   const int rt = blockIdx.x / ctiles, ct = blockIdx.x % ctiles;
-  int b = 0, r0, valid, slot0;  // slot0: first output r-slot (TRANS) of this tile
-  if constexpr (SEG) {
-    if (rt >= p.tstart[p.E]) return;
-    int lo = 0, hi = p.E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.tstart[mid] <= rt) lo = mid; else hi = mid;
-    }
-    r0 = p.offsets[lo] + (rt - p.tstart[lo]) * 128;
-    valid = min(128, p.offsets[lo + 1] - r0);
-    slot0 = rt * 128;
-  } else {
-    b = rt / p.ntr;
-    r0 = (rt % p.ntr) * 128;
-    valid = min(128, p.total_rows - r0);
-    slot0 = r0;
-  }
+  const int b = rt / p.ntr;  // expert
+  const int r0 = (rt % p.ntr) * 128, valid = min(128, p.total_rows - r0), slot0 = r0;
   const int c0 = ct * 128;
   const uint16_t* in = p.in + b * p.in_bstride;
   const int t = threadIdx.x, lane = t & 63;
@@ -143,15 +130,13 @@ __global__ void __launch_bounds__(256) quant_tile_kernel(QArgs p) {
       packed[i] = pack_e4m3x4(v[4 * i] * m, v[4 * i + 1] * m, v[4 * i + 2] * m, v[4 * i + 3] * m);
     }
   } else {
+    // the whole 128 x 128 block's amax
     float amax = fmaxf(am[0], am[1]);
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    if constexpr (MODE == Q_BLOCK_TILE) {
 #pragma unroll
-      for (int off = 32; off >= 2; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-      if (lane == 0) red[t >> 6] = amax;
-      __syncthreads();
-      amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    }
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    if (lane == 0) red[t >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float sc = amax == 0.f ? 1.f : amax / 448.f;
     entry = __float_as_uint(sc);
     const float rc = 1.f / sc;
@@ -715,23 +700,17 @@ inline int max_steps128(const moe_desc& d) {
   return int((N + (long long)d.E * 127) / 128);
 }
 
-int launch_quant(bool trans, int mode, bool seg, const QArgs& a, int blocks, const char* name,
-                 hipStream_t s) {
+int launch_quant_weights(bool trans, bool mx, const QArgs& a, int blocks, const char* name,
+                         hipStream_t s) {
   if (blocks <= 0) return MOE_OK;
   prof_begin(name, s);
-#define MOE_Q(T, M, S) quant_tile_kernel<T, M, S><<<unsigned(blocks), 256, 0, s>>>(a)
   if (trans) {
-    if (seg) {
-      if (mode == Q_MX) MOE_Q(true, Q_MX, true); else MOE_Q(true, Q_BLOCK_ROW, true);
-    } else {
-      if (mode == Q_MX) MOE_Q(true, Q_MX, false); else MOE_Q(true, Q_BLOCK_TILE, false);
-    }
+    if (mx) quant_tile_kernel<true, Q_MX><<<unsigned(blocks), 256, 0, s>>>(a);
+    else quant_tile_kernel<true, Q_BLOCK_TILE><<<unsigned(blocks), 256, 0, s>>>(a);
   } else {
-    if (mode == Q_MX) MOE_Q(false, Q_MX, false);
-    else if (mode == Q_BLOCK_TILE) MOE_Q(false, Q_BLOCK_TILE, false);
-    else MOE_Q(false, Q_BLOCK_ROW, false);
+    if (mx) quant_tile_kernel<false, Q_MX><<<unsigned(blocks), 256, 0, s>>>(a);
+    else quant_tile_kernel<false, Q_BLOCK_TILE><<<unsigned(blocks), 256, 0, s>>>(a);
   }
-#undef MOE_Q
   prof_end(s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
@@ -805,7 +784,7 @@ int quant_weights(const moe_desc& d, const uint16_t* w, int R, int C, bool trans
     a.sc_bstride = int64_t(C / 128) * R;
   }
   a.sc = sc;
-  return launch_quant(trans, mx ? Q_MX : Q_BLOCK_TILE, false, a, d.E * (R / 128) * (C / 128), name, s);
+  return launch_quant_weights(trans, mx, a, d.E * (R / 128) * (C / 128), name, s);
 }
 
 template <bool MX, int EPI>
