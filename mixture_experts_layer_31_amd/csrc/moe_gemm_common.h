@@ -431,14 +431,99 @@ __device__ __forceinline__ void band_load(const BandTile<ES>& t, int rows, int v
 }
 
 // LDS bytes the epilogues stage through (the kernels assert that their
-// pipeline buffer is at least this large).
+// pipeline buffer is at least this large): one band of output for a store,
+// gate + up + A for SwiGLU, two bands of H (gate + up) for the SwiGLU backward.
 template <class TL, int EPI>
 constexpr int grouped_epi_lds() {
   constexpr int RB = TL::WGM * 32;
-  return EPI == EPI_STORE ? RB * TL::BN * 2 : EPI == EPI_SWIGLU ? 3 * RB * TL::BN : 4 * RB * TL::BN;
+  return EPI == EPI_STORE ? RB * TL::BN * 2 : EPI == EPI_SWIGLU ? 3 * RB * TL::BN : 8 * RB * TL::BN;
 }
 template <class TL, bool OUT_F32>
 constexpr int wgrad_epi_lds() { return TL::WGM * 32 * TL::BN * (OUT_F32 ? 4 : 2); }
+
+// SwiGLU-backward epilogue: acc holds dA = (w dy) W2[e] for the tile's
+// F-columns; dH = [dg; du] from the saved H (gate, up).  The tile goes out one
+// band of WGM x 32 rows at a time through two LDS band buffers: band i+1's H
+// arrives by direct-to-LDS loads (into the XOR-swizzled band layout) while
+// band i is computed in place and stored, so the H loads overlap the previous
+// band's work instead of preceding it.
+template <class TL>
+__device__ __forceinline__ void dswiglu_epilogue(const EpiArgs& p,
+                                                 f32x16 (&acc)[TL::WMT][TL::WNT], size_t grow0,
+                                                 int rows_valid, int nt, int wm, int wn, int lane,
+                                                 char* smem) {
+  constexpr int BN = TL::BN, WM = TL::WM, WN = TL::WN, WMT = TL::WMT, WNT = TL::WNT;
+  constexpr int RB = TL::WGM * 32;       // rows per band
+  constexpr int TILE = RB * BN * 2;      // one band's gate (or up) columns, bytes
+  constexpr int BUF = 2 * TILE;          // gate + up
+  constexpr int NQ = BUF / 1024;         // 1 KB direct-to-LDS loads per band
+  constexpr int CH = BN * 2 / 16;        // 16-byte chunks per band row
+  // (callers assert that their LDS holds grouped_epi_lds<TL, EPI_DSWIGLU>() = 2 * BUF bytes)
+  static_assert(NQ % TL::WAVES == 0 && CH <= 32, "band loads split over the waves");
+  const int F = p.F, f0 = nt * BN;
+  const int wave = wm * TL::WGN + wn;
+  const int rr = wm * 32 + (lane & 31);
+  const i32x4 hr = make_rsrc(p.hsave + grow0 * 2 * F, uint32_t(rows_valid) * 2 * F * 2);
+  const uint32_t base = lds_addr(smem);
+  // band i's H into buffer b: load q fills bytes [1024 q, 1024 q + 1024) of the buffer
+  auto issue = [&](int i, int b) {
+#pragma unroll
+    for (int k = 0; k < NQ / TL::WAVES; ++k) {
+      const int q = wave + k * TL::WAVES;
+      const int half = q / (TILE / 1024);                       // 0 gate, 1 up
+      const int o = (q % (TILE / 1024)) * 1024 + lane * 16;     // byte in the band tile
+      const int brow = o / (BN * 2), pch = (o % (BN * 2)) / 16;
+      const int lch = pch ^ (brow & (CH - 1));                  // BandTile swizzle
+      const int trow = (brow / 32) * WM + i * 32 + (brow % 32);  // tile row
+      const int voff = trow < rows_valid ? (trow * 2 * F + half * F + f0 + lch * 8) * 2
+                                         : int(0x80000000u);   // past the expert: zeros
+      dma16(hr, base + uint32_t(b * BUF + q * 1024), voff);
+    }
+  };
+  issue(0, 0);
+#pragma unroll
+  for (int i = 0; i < WMT; ++i) {
+    const int b = i & 1;
+    wait_vmcnt<0>();   // band i's H (and the previous band's stores)
+    __syncthreads();   // ... for every wave; buffer b ^ 1 is free again
+    if (i + 1 < WMT) issue(i + 1, b ^ 1);
+    char* buf = smem + b * BUF;
+    BandTile<2> tg{buf, BN}, tu{buf + TILE, BN};
+#pragma unroll
+    for (int j = 0; j < WNT; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = wn * WN + j * 32 + acc_col(g, lane);
+        uint2* pg = reinterpret_cast<uint2*>(tg.at(rr, c));
+        uint2* pu = reinterpret_cast<uint2*>(tu.at(rr, c));
+        float gv[4], uv[4], dg[4], du[4];
+        unpack4(*pg, gv);
+        unpack4(*pu, uv);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float dA = acc[i][j][4 * g + q];
+          const float sg = 1.f / (1.f + __expf(-gv[q]));
+          dg[q] = dA * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
+          du[q] = dA * gv[q] * sg;
+        }
+        *pg = pack4(dg[0], dg[1], dg[2], dg[3]);
+        *pu = pack4(du[0], du[1], du[2], du[3]);
+      }
+    __syncthreads();
+    const int tid = wave * 64 + lane;
+    for (int w = 0; w < TL::WGM; ++w) {
+      const int first = w * WM + i * 32, n = min(32, rows_valid - first);
+      if (n <= 0) continue;
+      band_store<TL::THREADS>(BandTile<2>{buf + w * 32 * BN * 2, BN}, 32, n, tid, [&](int r) {
+        return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + f0);
+      });
+      band_store<TL::THREADS>(BandTile<2>{buf + TILE + w * 32 * BN * 2, BN}, 32, n, tid,
+                              [&](int r) {
+        return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + F + f0);
+      });
+    }
+  }
+}
 
 // Epilogue of a token-grouped GEMM.  Lane owns row (lane & 31) of each 32-row
 // block and, per group g of four registers, four consecutive columns starting
@@ -453,6 +538,10 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
   constexpr int RB = TL::WGM * 32;  // rows per band
   const int rr = wm * 32 + (lane & 31);
   __syncthreads();  // every wave is done reading the pipeline stages
+  if constexpr (EPI == EPI_DSWIGLU) {
+    dswiglu_epilogue<TL>(p, acc, grow0, rows_valid, nt, wm, wn, lane, smem);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < WMT; ++i) {
     // band row w*32 + r holds tile row w*WM + i*32 + r (wave row w's i-th 32-row block)
@@ -513,54 +602,6 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
                                            [&](int r) {
             return reinterpret_cast<char*>(p.out2 + (grow0 + first + r) * F + f0);
           });
-      }
-    } else {  // EPI_DSWIGLU: acc holds dA = (w dy) W2[e] for the tile's F-columns
-      const int F = p.F;
-      const int f0 = nt * BN;
-      // stage H (gate and up) of the band's rows, coalesced
-      for (int w = 0; w < TL::WGM; ++w) {
-        const int first = w * WM + i * 32, n = max(0, min(32, rows_valid - first));
-        band_load<TL::THREADS>(BandTile<2>{smem + w * 32 * BN * 2, BN}, 32, n, tid, [&](int r) {
-          return reinterpret_cast<const char*>(p.hsave + (grow0 + first + r) * 2 * F + f0);
-        });
-        band_load<TL::THREADS>(BandTile<2>{smem + RB * BN * 2 + w * 32 * BN * 2, BN}, 32, n, tid,
-                               [&](int r) {
-          return reinterpret_cast<const char*>(p.hsave + (grow0 + first + r) * 2 * F + F + f0);
-        });
-      }
-      __syncthreads();
-      BandTile<2> tg{smem, BN}, tu{smem + RB * BN * 2, BN};
-#pragma unroll
-      for (int j = 0; j < WNT; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c = wn * WN + j * 32 + acc_col(g, lane);
-          uint2* pg = reinterpret_cast<uint2*>(tg.at(rr, c));
-          uint2* pu = reinterpret_cast<uint2*>(tu.at(rr, c));
-          float gv[4], uv[4], dg[4], du[4];
-          unpack4(*pg, gv);
-          unpack4(*pu, uv);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float dA = acc[i][j][4 * g + q];
-            const float sg = 1.f / (1.f + __expf(-gv[q]));
-            dg[q] = dA * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
-            du[q] = dA * gv[q] * sg;
-          }
-          *pg = pack4(dg[0], dg[1], dg[2], dg[3]);
-          *pu = pack4(du[0], du[1], du[2], du[3]);
-        }
-      __syncthreads();
-      for (int w = 0; w < TL::WGM; ++w) {
-        const int first = w * WM + i * 32, n = min(32, rows_valid - first);
-        if (n <= 0) continue;
-        band_store<TL::THREADS>(BandTile<2>{smem + w * 32 * BN * 2, BN}, 32, n, tid, [&](int r) {
-          return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + f0);
-        });
-        band_store<TL::THREADS>(BandTile<2>{smem + RB * BN * 2 + w * 32 * BN * 2, BN}, 32, n, tid,
-                                [&](int r) {
-          return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + F + f0);
-        });
       }
     }
     __syncthreads();  // the band buffers are reused by the next band
