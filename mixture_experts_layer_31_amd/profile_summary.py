@@ -136,6 +136,47 @@ def stats_summary(args):
         fh.write("\n".join(lines) + "\n")
 
 
+def clock_summary(args):
+    """profiles/clock_<config>.md from a --kernel-trace --pmc GRBM_GUI_ACTIVE GRBM_COUNT
+    SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES run: per kernel, the shader clock over its
+    dispatches (GRBM cycles, summed over the 8 XCD instances, divided by 8 and by the
+    duration) and the MFMA-busy fraction (busy cycles over active cycles x 1024 SIMDs)."""
+    rows = list(csv.DictReader(open(args.trace + "_counter_collection.csv")))
+    by, meta = collections.defaultdict(dict), {}
+    for r in rows:
+        d = int(r["Dispatch_Id"])
+        by[d][r["Counter_Name"]] = float(r["Counter_Value"])
+        meta[d] = r
+    agg = collections.defaultdict(list)
+    for n, r in name_rows(list(meta.values())):
+        if n == "copyBuffer":
+            continue
+        c = by[int(r["Dispatch_Id"])]
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        agg[n].append((dur, c.get("GRBM_COUNT", 0.0), c.get("GRBM_GUI_ACTIVE", 0.0),
+                       c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)))
+    lines = [f"# {args.config} layer: shader clock and MFMA busy per kernel", "",
+             f"Workload: {args.workload or args.config}.", "",
+             "Commands (from the repository root on the GPU box):", ""]
+    lines += [f"    {c.strip()}" for c in args.commands.split(";") if c.strip()]
+    lines += ["", "GRBM counters are summed over the 8 XCD instances, so the clock is "
+              "GRBM_COUNT / 8 / duration; MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES / "
+              "(GRBM_GUI_ACTIVE / 8 x 1024 SIMDs).  Kernels shorter than 50 us are "
+              "dominated by counter set-up and are left out.", "",
+              "| kernel | dispatches | avg us | clock GHz | MFMA busy % |", "|---|---|---|---|---|"]
+    for n, v in sorted(agg.items(), key=lambda kv: -sum(x[0] for x in kv[1])):
+        dur = sum(x[0] for x in v) / len(v)
+        if dur < 50e3:
+            continue
+        cnt = sum(x[1] for x in v) / len(v)
+        act = sum(x[2] for x in v) / len(v)
+        mf = sum(x[3] for x in v) / len(v)
+        lines.append(f"| {n} | {len(v)} | {dur / 1e3:.1f} | {cnt / 8 / dur:.2f} | "
+                     f"{100 * mf / (act / 8 * 1024) if act else 0:.1f} |")
+    with open(os.path.join(ROOT, "profiles", f"clock_{args.config}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", required=True)
@@ -145,6 +186,8 @@ def main():
     ap.add_argument("--calib-mib", type=int)
     ap.add_argument("--stats-only", action="store_true",
                     help="only the kernel statistics of the trace run (profiles/kernels_<config>.md)")
+    ap.add_argument("--clock", action="store_true",
+                    help="clock and MFMA-busy table of a GRBM/SQ counter run (profiles/clock_<config>.md)")
     ap.add_argument("--commands", required=True, help="the rocprofv3 commands, ';'-separated")
     ap.add_argument("--workload", default="")
     ap.add_argument("--skip", type=int, default=0,
@@ -152,6 +195,8 @@ def main():
     args = ap.parse_args()
     if args.stats_only:
         return stats_summary(args)
+    if args.clock:
+        return clock_summary(args)
     if not (args.fetch and args.write and args.calib_mib):
         raise SystemExit("--fetch, --write and --calib-mib are required without --stats-only")
 
