@@ -298,7 +298,7 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
   if (fp8_mode(d->mode)) {  // the combine-backward also quantises dYw's rows for the W2 dgrad
     uint8_t* qc;
     uint32_t* qs;
-    fp8_row_codes(*d, L, sc, &qc, &qs);
+    fp8_dyw_codes(*d, L, sc, &qc, &qs);
     if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s,
                                  d->mode == MOE_MXFP8 ? 1 : 2, qc, qs)))
       return rc;

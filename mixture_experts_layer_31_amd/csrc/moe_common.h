@@ -134,10 +134,13 @@ int fp8_prepare_weights(const moe_desc& d, const uint16_t* w1, const uint16_t* w
 int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,
                   hipStream_t s, bool x_quantised = false);
 // The FP8 backward; dyw_quantised: the combine-backward already wrote dYw's row
-// quantisation into the row-code buffer (fp8_row_codes).
+// quantisation (fp8_dyw_codes).
 int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* dw1, void* dw2,
                   char* scratch, hipStream_t s, bool dyw_quantised = false);
+// Where the dispatch writes x_perm's row codes, and the combine-backward dYw's.
 void fp8_row_codes(const moe_desc& d, const Layout& L, char* scratch, uint8_t** codes,
+                   uint32_t** scales);
+void fp8_dyw_codes(const moe_desc& d, const Layout& L, char* scratch, uint8_t** codes,
                    uint32_t** scales);
 int fp8_view(const moe_desc& d, const Layout& L, char* scratch, int which, void** ptr,
              size_t* bytes);

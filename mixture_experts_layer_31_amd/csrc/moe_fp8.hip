@@ -693,6 +693,8 @@ using TileF8 = Tile<256, 256, 2, 4, 2>;
 using TileF8R = Tile<256, 256, 2, 4, 4>;
 using TileF8B = Tile<256, 128, 4, 2, 3>;
 template <bool MX> using F8GrTile = typename std::conditional<MX, TileF8, TileF8R>::type;
+static_assert(TileF8::BN % 128 == 0 && TileF8R::BN % 128 == 0,
+              "the SwiGLU-backward epilogue quantises whole 128-column groups of dH");
 template <bool MX> using F8WgTile = typename std::conditional<MX, TileF8, TileF8B>::type;
 
 inline int max_steps128(const moe_desc& d) {
@@ -1012,6 +1014,17 @@ void fp8_row_codes(const moe_desc& d, const Layout& L, char* scratch, uint8_t** 
   *scales = f.qrow_sc;
 }
 
+// dYw's row codes live in the first token-code buffer: the W2 dgrad reads them
+// before the W2 weight gradient quantises dYw over tokens into that buffer, and
+// the row-code buffer meanwhile receives dH's row codes from the W2 dgrad's
+// epilogue.
+void fp8_dyw_codes(const moe_desc& d, const Layout& L, char* scratch, uint8_t** codes,
+                   uint32_t** scales) {
+  const F8Scratch f = f8scratch(d, L, scratch);
+  *codes = f.qt1;
+  *scales = f.qt1_sc;
+}
+
 int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* dw1, void* dw2,
                   char* scratch, hipStream_t s, bool dyw_quantised) {
   const WLayout W = wlayout(d);
@@ -1024,13 +1037,13 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   const auto* dh = reinterpret_cast<const uint16_t*>(scratch + L.dh);
   const auto* xp = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
   int rc;
-  // W2 dgrad + SwiGLU-backward
-  if (!dyw_quantised && (rc = quant_rows(d, dyw, D, mx, f.qrow, f.qrow_sc, "quant_dyw_rows", s)))
+  // W2 dgrad + SwiGLU-backward; its epilogue also writes dH's row codes for the W1 dgrad
+  if (!dyw_quantised && (rc = quant_rows(d, dyw, D, mx, f.qt1, f.qt1_sc, "quant_dyw_rows", s)))
     return rc;
   F8Args a{};
   a.K = D;
-  a.A = f.qrow;
-  a.SA = f.qrow_sc;
+  a.A = f.qt1;
+  a.SA = f.qt1_sc;
   a.sa_ld = N;
   a.sa_bytes = uint32_t(size_t(D / 128) * N * 4);
   a.B = reinterpret_cast<const uint8_t*>(wprep + W.w2t);
@@ -1041,7 +1054,8 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   a.sb_bytes = uint32_t(size_t(D / 128) * F * 4);
   a.F = F;
   a.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.dh), 0, nullptr,
-                  reinterpret_cast<const uint16_t*>(scratch + L.h), F};
+                  reinterpret_cast<const uint16_t*>(scratch + L.h), F, f.qrow, f.qrow_sc, N,
+                  mx ? QM_MX : QM_BLOCK};
   rc = mx ? run_f8_grouped<true, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s)
           : run_f8_grouped<false, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s);
   if (rc) return rc;
@@ -1065,8 +1079,7 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   rc = mx ? run_f8_wgrad<true>(d, L, w, "gemm_w2_wgrad", scratch, s)
           : run_f8_wgrad<false>(d, L, w, "gemm_w2_wgrad", scratch, s);
   if (rc) return rc;
-  // W1 dgrad
-  if ((rc = quant_rows(d, dh, 2 * F, mx, f.qrow, f.qrow_sc, "quant_dh_rows", s))) return rc;
+  // W1 dgrad on dH's row codes
   F8Args b{};
   b.K = 2 * F;
   b.A = f.qrow;

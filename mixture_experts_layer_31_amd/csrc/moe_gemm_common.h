@@ -7,6 +7,7 @@
 #include <type_traits>
 
 #include "moe_common.h"
+#include "moe_fp8_codec.h"
 
 namespace moe {
 namespace gemm {
@@ -375,6 +376,11 @@ struct EpiArgs {
   const uint16_t* hsave;  // DSWIGLU: H [rows, 2F]; may equal out (each tile reads its H band
                           // into LDS before it stores the same band's dH)
   int F;
+  // DSWIGLU in the FP8 backward: also the e4m3 row quantisation of dH along 2F
+  // (qmode QM_MX or QM_BLOCK): codes [rows, 2F] bytes, scale entries [2F/128][qn]
+  uint8_t* qcodes;
+  uint32_t* qsc;
+  int qn, qmode;
 };
 
 // Epilogues stage the output through LDS, one band of 32-row blocks (one per
@@ -480,6 +486,34 @@ __device__ __forceinline__ void dswiglu_epilogue(const EpiArgs& p,
       dma16(hr, base + uint32_t(b * BUF + q * 1024), voff);
     }
   };
+  // dH rows of one 32-row slice of a band tile (column `col0` of the dH row onwards),
+  // and in the FP8 backward their e4m3 row codes: a row's chunks are consecutive
+  // threads, so a 128-column group is 16 aligned lanes (an MX group 4)
+  const int tid = wave * 64 + lane;
+  auto store_slice = [&](const BandTile<2>& t, int n, size_t row0, int col0) {
+    constexpr int PR = CH;  // chunks per row
+    for (int k = tid; k < 32 * PR; k += TL::THREADS) {
+      const int r = k / PR, c = k - r * PR;
+      const uint4 v = *reinterpret_cast<const uint4*>(t.base + r * PR * 16 + ((c ^ (r & (CH - 1))) << 4));
+      const size_t row = row0 + r;
+      const int col = col0 + 8 * c;
+      if (r < n) *reinterpret_cast<uint4*>(p.out + row * 2 * F + col) = v;
+      // (tiles narrower than 128 columns never quantise: the FP8 tiles are 256 wide)
+      if (CH % 16 == 0 && p.qmode != QM_NONE) {
+        const float f[8] = {__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                            __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u),
+                            __uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u),
+                            __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u)};
+        uint32_t entry;
+        const uint2 codes = p.qmode == QM_MX ? quantise8<QM_MX>(f, lane, entry)
+                                             : quantise8<QM_BLOCK>(f, lane, entry);
+        if (r < n) {
+          *reinterpret_cast<uint2*>(p.qcodes + row * 2 * F + col) = codes;
+          if ((c & 15) == 0) p.qsc[size_t(col >> 7) * p.qn + row] = entry;
+        }
+      }
+    }
+  };
   issue(0, 0);
 #pragma unroll
   for (int i = 0; i < WMT; ++i) {
@@ -510,17 +544,11 @@ __device__ __forceinline__ void dswiglu_epilogue(const EpiArgs& p,
         *pu = pack4(du[0], du[1], du[2], du[3]);
       }
     __syncthreads();
-    const int tid = wave * 64 + lane;
     for (int w = 0; w < TL::WGM; ++w) {
       const int first = w * WM + i * 32, n = min(32, rows_valid - first);
       if (n <= 0) continue;
-      band_store<TL::THREADS>(BandTile<2>{buf + w * 32 * BN * 2, BN}, 32, n, tid, [&](int r) {
-        return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + f0);
-      });
-      band_store<TL::THREADS>(BandTile<2>{buf + TILE + w * 32 * BN * 2, BN}, 32, n, tid,
-                              [&](int r) {
-        return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + F + f0);
-      });
+      store_slice(BandTile<2>{buf + w * 32 * BN * 2, BN}, n, grow0 + first, f0);
+      store_slice(BandTile<2>{buf + TILE + w * 32 * BN * 2, BN}, n, grow0 + first, F + f0);
     }
   }
 }

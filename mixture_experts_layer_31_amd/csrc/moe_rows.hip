@@ -61,38 +61,6 @@ __device__ __forceinline__ void store8(float* p, size_t i8, const float (&f)[8])
   reinterpret_cast<float4*>(p)[2 * i8 + 1] = make_float4(f[4], f[5], f[6], f[7]);
 }
 
-// Row quantisation fused into a row mover (FP8 modes, bf16 rows): none, MXFP8
-// (e8m0 scale per 32 columns) or blockwise (fp32 scale per 128 columns).
-enum { QM_NONE = 0, QM_MX = 1, QM_BLOCK = 2 };
-
-// e4m3 codes (and the group's scale entry, valid in every lane) of eight
-// consecutive values whose 32-column (MX: 4 lanes) or 128-column (blockwise:
-// 16 lanes) group is held by aligned consecutive lanes, all of which call this.
-template <int QM>
-__device__ __forceinline__ uint2 quantise8(const float (&v)[8], int lane, uint32_t& entry) {
-  float am = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
-  uint2 codes;
-  if constexpr (QM == QM_MX) {
-    am = max4(am);
-    const int X = e8m0_exponent(am);
-    const float m = ldexpf(1.f, -X);
-    codes.x = pack_e4m3x4(v[0] * m, v[1] * m, v[2] * m, v[3] * m);
-    codes.y = pack_e4m3x4(v[4] * m, v[5] * m, v[6] * m, v[7] * m);
-    entry = or16_of_quads(uint32_t(X + 127) << (8 * ((lane & 15) >> 2)));
-  } else {
-    am = max16(am);
-    const float s = am == 0.f ? 1.f : am / 448.f;
-    float y[8];
-    block_quotients(v, s, 1.f / s, y);
-    codes.x = pack_e4m3x4(y[0], y[1], y[2], y[3]);
-    codes.y = pack_e4m3x4(y[4], y[5], y[6], y[7]);
-    entry = __float_as_uint(s);
-  }
-  return codes;
-}
-
 // IO: element type of the layer's inputs/outputs; ACT: of the permuted rows in
 // scratch (uint16_t = bf16, or float).  A bf16 -> bf16 or fp32 -> fp32 move is
 // a bitwise copy; fp32 -> bf16 rounds once (RNE).  With QM (FP8 forward modes,
