@@ -122,7 +122,11 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_kernel(
 
 // Per-token gather-reduce over the K pair rows: combine (WEIGHTED: y_t =
 // sum_k w_tk * O[pos]) and the un-permute of dx (plain sum), fp32, k ascending.
-template <typename ACT, typename OUT, bool WEIGHTED>
+// Pairs are taken KB at a time with no branch between the loads, so each
+// thread keeps KB 16-byte loads in flight: a pair with no row (pos < 0) loads
+// row 0 and its sum is dropped by a select (the accumulator is left exactly as
+// it was).  The last K % KB pairs go one at a time.
+template <typename ACT, typename OUT, bool WEIGHTED, int KB>
 __global__ void __launch_bounds__(kRowThreads) gather_reduce_kernel(
     const ACT* __restrict__ rows, const int32_t* __restrict__ pos,
     const float* __restrict__ topk_w, int T, int K, int D, OUT* __restrict__ out) {
@@ -133,21 +137,35 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_kernel(
   const int c0 = threadIdx.x % tpr;
   if (t >= T || threadIdx.x >= rpb * tpr) return;
   const int32_t* prow = pos + size_t(t) * K;
+  const float* wrow = WEIGHTED ? topk_w + size_t(t) * K : nullptr;
+  const int kfull = K - K % KB;
   for (int c = c0; c < chunks; c += tpr) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < K; ++k) {
-      const int q = prow[k];
-      if (q < 0) continue;
-      float f[8];
-      load8(rows, (size_t(q) * D) / 8 + c, f);
-      if constexpr (WEIGHTED) {
-        const float w = topk_w[size_t(t) * K + k];
+    auto add = [&](bool live, float w, const float (&f)[8]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(w, f[i], acc[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += f[i];
+      for (int i = 0; i < 8; ++i) {
+        const float s = WEIGHTED ? __builtin_fmaf(w, f[i], acc[i]) : acc[i] + f[i];
+        acc[i] = live ? s : acc[i];
       }
+    };
+    for (int k0 = 0; k0 < kfull; k0 += KB) {
+      int q[KB];
+      float w[KB], f[KB][8];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        q[j] = prow[k0 + j];
+        w[j] = WEIGHTED ? wrow[k0 + j] : 1.f;
+      }
+#pragma unroll
+      for (int j = 0; j < KB; ++j) load8(rows, (size_t(q[j] < 0 ? 0 : q[j]) * D) / 8 + c, f[j]);
+#pragma unroll
+      for (int j = 0; j < KB; ++j) add(q[j] >= 0, w[j], f[j]);
+    }
+    for (int k = kfull; k < K; ++k) {
+      const int q = prow[k];
+      float f[8];
+      load8(rows, (size_t(q < 0 ? 0 : q) * D) / 8 + c, f);
+      add(q >= 0, WEIGHTED ? wrow[k] : 1.f, f);
     }
     store8(out, (size_t(t) * D) / 8 + c, acc);
   }
@@ -241,6 +259,18 @@ inline int row_blocks(const moe_desc& d) {
   return (d.T + rpb - 1) / rpb;
 }
 
+// Pairs per batch for a top-K: at most 8, and no more than K.
+template <typename ACT, typename OUT, bool WEIGHTED>
+static void launch_gather_reduce(const moe_desc& d, const ACT* rows, const int32_t* pos,
+                                 const float* topk_w, OUT* out, hipStream_t s) {
+#define MOE_GR(KB) gather_reduce_kernel<ACT, OUT, WEIGHTED, KB><<<row_blocks(d), kRowThreads, 0, s>>>(rows, pos, topk_w, d.T, d.K, d.D, out)
+  if (d.K >= 8) MOE_GR(8);
+  else if (d.K >= 4) MOE_GR(4);
+  else if (d.K >= 2) MOE_GR(2);
+  else MOE_GR(1);
+#undef MOE_GR
+}
+
 }  // namespace
 
 // Element types of a mode: I/O fp32 in the fp32-storage modes, intermediates
@@ -293,9 +323,8 @@ int launch_combine(const moe_desc& d, const Layout& L, const float* topk_w, void
   with_types(d, out_f32, [&](auto io, auto act) {
     using IO = decltype(io);
     using ACT = decltype(act);
-    gather_reduce_kernel<ACT, IO, true><<<row_blocks(d), kRowThreads, 0, s>>>(
-        reinterpret_cast<const ACT*>(scratch + L.o), pos, topk_w, d.T, d.K, d.D,
-        static_cast<IO*>(y));
+    launch_gather_reduce<ACT, IO, true>(d, reinterpret_cast<const ACT*>(scratch + L.o), pos,
+                                        topk_w, static_cast<IO*>(y), s);
     return 0;
   });
   prof_end(s);
@@ -309,9 +338,8 @@ int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
   with_types(d, out_f32, [&](auto io, auto act) {
     using IO = decltype(io);
     using ACT = decltype(act);
-    gather_reduce_kernel<ACT, IO, false><<<row_blocks(d), kRowThreads, 0, s>>>(
-        reinterpret_cast<const ACT*>(scratch + L.dxperm), pos, nullptr, d.T, d.K, d.D,
-        static_cast<IO*>(dx));
+    launch_gather_reduce<ACT, IO, false>(d, reinterpret_cast<const ACT*>(scratch + L.dxperm),
+                                         pos, nullptr, static_cast<IO*>(dx), s);
     return 0;
   });
   prof_end(s);

@@ -36,6 +36,7 @@ ROOT = os.path.dirname(HERE)
 GEMM_SOURCES = [
     "mixture_experts_layer_31_amd/csrc/moe_gemm.hip",
     "mixture_experts_layer_31_amd/csrc/moe_gemm_common.h",
+    "mixture_experts_layer_31_amd/csrc/moe_fp8_codec.h",
     "mixture_experts_layer_31_amd/csrc/moe_grouped.h",
 ]
 _GROUPED = {("false", "1"): "gemm_w1_swiglu", ("false", "0"): "gemm_w2",
