@@ -160,6 +160,21 @@ def test_fp8_quantisers_and_gemms(name):
         rows = slice(offsets[e], offsets[e + 1])
         ref[rows] = dHdq[rows] @ _w_deq(inp["w1"][e], True, mx)
     assert rel_err(dXp, ref) <= 1e-2, ("dX_perm", rel_err(dXp, ref))
+    # the W2 weight gradient: dYw (built from dy by the token quantiser) and A along tokens
+    A = L.view(moe.MOE_VIEW_A, F)[:len(src)]
+    rc1, rs1, poff = f8.quant_tokens(dYw, offsets, 32 if mx else 128, mx)
+    rc2, rs2, _ = f8.quant_tokens(A, offsets, 32 if mx else 128, mx)
+    deq = ((lambda c, s_: f8.dequant_rows(c, s_, 32, True)) if mx else
+           (lambda c, s_: f8.e4m3_decode(c) * np.repeat(s_.T, 128, axis=1)))
+    dYt, At = deq(rc1, rs1), deq(rc2, rs2)
+    dw2 = to_host(L.dw2)
+    for e in range(cfg.E):
+        cols = slice(poff[e], poff[e + 1])
+        if offsets[e + 1] == offsets[e]:
+            assert np.all(dw2[e] == 0)
+        else:
+            ref = dYt[:, cols] @ At[:, cols].T
+            assert rel_err(dw2[e], ref) <= 1e-2, ("dW2", e, rel_err(dw2[e], ref))
     dHt, poff = _check_tokens(L, moe.MOE_VIEW_Q_TOK_A, moe.MOE_VIEW_Q_TOK_A_SCALE, dH, offsets, mx)
     xt, _ = _check_tokens(L, moe.MOE_VIEW_Q_TOK_B, moe.MOE_VIEW_Q_TOK_B_SCALE, xp, offsets, mx)
     dw1 = to_host(L.dw1)
