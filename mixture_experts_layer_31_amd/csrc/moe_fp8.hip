@@ -937,7 +937,10 @@ int fp8_view(const moe_desc& d, const Layout& L, char* scratch, int which, void*
 }
 
 // Expert linear 1 + SwiGLU on the quantised x rows: stores H into `h` and A
-// into `act` (either may be null, as in the bf16 path).
+// into `act` (either may be null, as in the bf16 path).  MXFP8: the epilogue
+// also writes A's row codes for the W2 GEMM, into the first token-code buffer
+// (free until the backward); the blockwise quotients cost the epilogue more
+// than a separate pass over A, so blockwise A is quantised by quant_rows.
 static int fp8_w1_swiglu(const moe_desc& d, const Layout& L, const char* wprep, uint16_t* h,
                          uint16_t* act, const char* name, char* scratch, hipStream_t s,
                          bool x_quantised = false) {
@@ -963,7 +966,7 @@ static int fp8_w1_swiglu(const moe_desc& d, const Layout& L, const char* wprep, 
   a.sb_bstride = int64_t(D / 128) * 2 * F;
   a.sb_bytes = uint32_t(size_t(D / 128) * 2 * F * 4);
   a.F = F;
-  a.epi = EpiArgs{h, 0, act, nullptr, F};
+  a.epi = EpiArgs{h, 0, act, nullptr, F, f.qt1, f.qt1_sc, N, mx ? QM_MX : QM_NONE};
   return mx ? run_f8_grouped<true, EPI_SWIGLU>(d, L, a, 2 * F, name, scratch, s)
             : run_f8_grouped<false, EPI_SWIGLU>(d, L, a, 2 * F, name, scratch, s);
 }
@@ -985,14 +988,14 @@ int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* s
                          reinterpret_cast<uint16_t*>(scratch + L.a), "gemm_w1_swiglu", scratch, s,
                          x_quantised);
   if (rc) return rc;
-  // expert linear 2
-  if ((rc = quant_rows(d, reinterpret_cast<const uint16_t*>(scratch + L.a), F, mx, f.qrow,
-                       f.qrow_sc, "quant_a_rows", s)))
+  // expert linear 2, on A's row codes (MXFP8: from the W1 epilogue)
+  if (!mx && (rc = quant_rows(d, reinterpret_cast<const uint16_t*>(scratch + L.a), F, false,
+                              f.qt1, f.qt1_sc, "quant_a_rows", s)))
     return rc;
   F8Args b{};
   b.K = F;
-  b.A = f.qrow;
-  b.SA = f.qrow_sc;
+  b.A = f.qt1;
+  b.SA = f.qt1_sc;
   b.sa_ld = N;
   b.sa_bytes = uint32_t(size_t(F / 128) * N * 4);
   b.B = reinterpret_cast<const uint8_t*>(wprep + W.w2f);

@@ -51,11 +51,12 @@ def _mx_bytes(entries):
     return b.transpose(1, 0, 2).reshape(entries.shape[1], -1)
 
 
-def _check_rows(L, src, mx):
-    """Row-quantised operand in scratch == oracle quant of `src` [N, C]."""
+def _check_rows(L, src, mx, views=(moe.MOE_VIEW_Q_ROWS, moe.MOE_VIEW_Q_ROWS_SCALE)):
+    """Row-quantised operand in scratch (codes [N, C], entries [C/128, N] at the
+    start of the two views) == oracle quant of `src` [N, C]."""
     N, C = src.shape
-    codes = _u8(L, moe.MOE_VIEW_Q_ROWS)[:N * C].reshape(N, C)
-    ent = _entries(L, moe.MOE_VIEW_Q_ROWS_SCALE)[:(C // 128) * N].reshape(C // 128, N)
+    codes = _u8(L, views[0])[:N * C].reshape(N, C)
+    ent = _entries(L, views[1])[:(C // 128) * N].reshape(C // 128, N)
     rc, rs = f8.quant_rows(src, 32 if mx else 128, mx)
     np.testing.assert_array_equal(codes, rc)
     if mx:
@@ -123,9 +124,10 @@ def test_fp8_quantisers_and_gemms(name):
             rows = slice(offsets[e], offsets[e + 1])
             Href[rows] = xdq[rows] @ _w_deq(inp["w1"][e], False, mx).T
         assert rel_err(Hg, Href) <= 1e-2, ("H from fused x codes", rel_err(Hg, Href))
-    if fwd_q:  # the forward's last quantised operand: A rows for the W2 GEMM
+    if fwd_q:  # A's row codes for the W2 GEMM, written by the W1 GEMM's SwiGLU epilogue into
+        # the first token-code buffer (unused until the backward)
         A = L.view(moe.MOE_VIEW_A, F)[:len(src)]
-        Adq = _check_rows(L, A, mx)
+        Adq = _check_rows(L, A, mx, (moe.MOE_VIEW_Q_TOK_A, moe.MOE_VIEW_Q_TOK_A_SCALE))
         O = L.view(moe.MOE_VIEW_O, D)[:len(src)]
         ref = np.zeros_like(O, dtype=np.float64)
         for e in range(cfg.E):
@@ -236,6 +238,13 @@ def _full_size_fp8(name, ntok, nexp):
     L = Layer(cfg, inp)
     L.prepare()
     L.fwd()
+    if cfg.mode in (mi.MODE_MXFP8, mi.MODE_FP8):  # A's row codes from the W1 epilogue, sampled
+        torch.cuda.synchronize()
+        N, F = cfg.N, cfg.F
+        rows = np.sort(np.random.default_rng(2).choice(N, size=64, replace=False))
+        codes = _u8(L, moe.MOE_VIEW_Q_TOK_A)[:N * F].reshape(N, F)[rows]
+        rc, _ = f8.quant_rows(L.view(moe.MOE_VIEW_A, F)[rows], 32 if mx else 128, mx)
+        np.testing.assert_array_equal(codes, rc)
     L.bwd()
     torch.cuda.synchronize()
     assert L.check() == moe.MOE_OK
