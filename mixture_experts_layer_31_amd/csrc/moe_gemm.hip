@@ -157,6 +157,7 @@ int run_wgrad(const moe_desc& d, const Layout& L, WgradArgs a, const char* name,
 // small shapes (D or F not a multiple of 256) working.
 using TileBig = Tile<256, 256, 2, 4, 4>;
 using TileBig5 = Tile<256, 256, 2, 4, 5>;  // whole 160 KB LDS: deeper ring for W1 + SwiGLU
+using TileWide = Tile<256, 256, 2, 4, 2, true>;
 using TileMid = Tile<128, 128, 2, 2, 4>;
 using TileNarrow = Tile<128, 64, 2, 2, 4>;
 using TileWg128x64 = Tile<128, 64, 2, 2, 4>;
@@ -166,6 +167,8 @@ using TileWg64x64 = Tile<64, 64, 2, 2, 4>;
 template <bool B_T, int EPI>
 int run_grouped_any(const moe_desc& d, const Layout& L, GroupedArgs a, int N, const char* name,
                     char* scratch, hipStream_t s) {
+  if constexpr (!B_T)
+    if (N % 256 == 0 && a.K % 64 == 0) return run_grouped<TileWide, B_T, EPI>(d, L, a, N, name, scratch, s);
   if constexpr (EPI == EPI_SWIGLU)
     if (N % 256 == 0) return run_grouped<TileBig5, B_T, EPI>(d, L, a, N, name, scratch, s);
   if (N % 256 == 0) return run_grouped<TileBig, B_T, EPI>(d, L, a, N, name, scratch, s);

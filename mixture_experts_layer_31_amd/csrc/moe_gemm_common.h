@@ -331,6 +331,67 @@ __device__ __forceinline__ void mainloop(char* smem, const SA& sa, const SB& sb,
   for (; kt < ktiles; ++kt) step(kt, std::false_type{});
 }
 
+// Fragment of a 128-byte (64-k) row for 16-deep sub-step kk (0..3).
+__device__ __forceinline__ bf16x8 frag_w(const char* tile, int row, int kk, int lane) {
+  const int chunk = kk * 2 + (lane >> 5);
+  return *reinterpret_cast<const bf16x8*>(tile + row * 128 + ((chunk ^ swz_row<128>(row)) << 4));
+}
+
+// Wide-row main loop: bf16 operands in 128-byte rows (64 k per step), two
+// stages.  Each step waits for its own loads and meets every wave at the
+// barrier (after which the other stage is free); its four 16-deep sub-steps
+// then each run their MFMAs while the next sub-step's fragments are read and a
+// quarter of the next step's loads is issued into the free stage.  A and B are
+// both k-contiguous.
+template <int BM, int BN, int WGM, int WGN, int ACT, class SA, class SB>
+__device__ __forceinline__ void mainloop_w(char* smem, const SA& sa, const SB& sb, int ktiles,
+                                           f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int wave,
+                                           int lane) {
+  constexpr int WM = BM / WGM, WN = BN / WGN, WMT = WM / 32, WNT = WN / 32;
+  constexpr int A_BYTES = BM * 128, STAGE = (BM + BN) * 128;
+  constexpr int NI = SA::NI + SB::NI, NQ = (NI + 3) / 4;  // DMA instructions per sub-step
+  static_assert(ACT >= 0 && ACT <= WMT, "active blocks within the wave tile");
+  const int wm = wave / WGN, wn = wave % WGN;
+  const uint32_t base = lds_addr(smem);
+  // DMA instructions [j0, j1) (over both operands) of k-step kt into stage s
+  auto issue = [&](int s, int kt, int j0, int j1) {
+    sa.issue(base + uint32_t(s * STAGE), wave, kt, j0, j1);
+    sb.issue(base + uint32_t(s * STAGE + A_BYTES), wave, kt, j0 - SA::NI, j1 - SA::NI);
+  };
+  struct Frags { bf16x8 a[WMT], b[WNT]; };
+  auto load = [&](const char* ta, int kk, Frags& f) {
+#pragma unroll
+    for (int i = 0; i < ACT; ++i) f.a[i] = frag_w(ta, wm * WM + i * 32 + (lane & 31), kk, lane);
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) f.b[j] = frag_w(ta + A_BYTES, wn * WN + j * 32 + (lane & 31), kk, lane);
+  };
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < ACT; ++i)
+#pragma unroll
+      for (int j = 0; j < WNT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  };
+  constexpr int NMF = ACT * WNT, NDS = ACT == 0 ? 0 : ACT + WNT;
+  if (ktiles > 0) issue(0, 0, 0, NI);
+  for (int kt = 0; kt < ktiles; ++kt) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    const bool next = kt + 1 < ktiles;
+    const char* ta = smem + (kt & 1) * STAGE;
+    Frags f[2];
+    load(ta, 0, f[0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (next) issue((kt + 1) & 1, kt + 1, kk * NQ, (kk + 1) * NQ);
+      if (kk < 3) load(ta, kk + 1, f[(kk + 1) & 1]);
+      mma(f[kk & 1]);
+      if (kk < 3) interleave_mfma_ds<NMF, NDS>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // Column (within a 32x32 block) of accumulator register 4*g (the first of four
 // consecutive columns); the row is lane & 31.
 __device__ __forceinline__ int acc_col(int g, int lane) { return 8 * g + 4 * (lane >> 5); }
@@ -358,13 +419,17 @@ __device__ __forceinline__ void unpack4(uint2 v, float (&f)[4]) {
 }
 
 // Tile shape of a GEMM kernel: BM x BN outputs per workgroup of WGM x WGN waves.
-template <int BM_, int BN_, int WGM_, int WGN_, int STAGES_>
+// WIDE: the two-stage main loop on 128-byte rows (mainloop_w) instead of the
+// STAGES-deep ring on 64-byte rows.
+template <int BM_, int BN_, int WGM_, int WGN_, int STAGES_, bool WIDE_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, STAGES = STAGES_;
+  static constexpr bool WIDE = WIDE_;
   static constexpr int WAVES = WGM * WGN, THREADS = 64 * WAVES;
   static constexpr int WM = BM / WGM, WN = BN / WGN, WMT = WM / 32, WNT = WN / 32;
-  static constexpr int LDS = STAGES * (BM + BN) * kBK * 2;
+  static constexpr int LDS = WIDE ? 2 * (BM + BN) * 128 : STAGES * (BM + BN) * kBK * 2;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32x32");
+  static_assert(!WIDE || STAGES == 2, "the wide-row loop has two stages");
 };
 
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2 };

@@ -65,14 +65,16 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoo
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / TL::WGN, wn = wave % TL::WGN;
 
-  KStager<BM, WAVES, kBK * 2> sa;
+  constexpr int ROWB = TL::WIDE ? 128 : kBK * 2;  // bytes of a k-step's row
+  static_assert(!TL::WIDE || !B_T, "the wide-row loop takes k-contiguous operands");
+  KStager<BM, WAVES, ROWB> sa;
   sa.init(make_rsrc(p.A + size_t(e0) * p.lda, uint32_t(ne) * p.lda * 2),
           [&](int r) { return r < rows_valid ? (m0 + r) * p.lda * 2 : -1; }, wave, lane);
   const uint16_t* Be = p.B + size_t(e) * p.bstride;
   const uint32_t bbytes = uint32_t(p.brows) * p.ldb * 2;
   f32x16 acc[WMT][WNT];
   zero(acc);
-  const int ktiles = p.K / kBK;
+  const int ktiles = p.K / (ROWB / 2);
   // 32-row blocks of this wave's share of the tile that hold rows
   const int act = min(WMT, max(0, (rows_valid - wm * TL::WM + 31) / 32));
   if constexpr (B_T) {
@@ -83,7 +85,7 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoo
           smem, sa, sb, ktiles, acc, wave, lane);
     });
   } else {
-    KStager<BN, WAVES, kBK * 2> sb;
+    KStager<BN, WAVES, ROWB> sb;
     sb.init(make_rsrc(Be, bbytes),
             [&](int n) {
               int row;
@@ -98,8 +100,12 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoo
             },
             wave, lane);
     with_active<WMT>(act, [&](auto a) {
-      mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, false, decltype(a)::value>(
-          smem, sa, sb, ktiles, acc, wave, lane);
+      if constexpr (TL::WIDE)
+        mainloop_w<BM, BN, TL::WGM, TL::WGN, decltype(a)::value>(smem, sa, sb, ktiles, acc, wave,
+                                                                 lane);
+      else
+        mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, false, decltype(a)::value>(
+            smem, sa, sb, ktiles, acc, wave, lane);
     });
   }
 
