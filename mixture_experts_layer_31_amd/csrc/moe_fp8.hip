@@ -584,15 +584,16 @@ struct F8Args {
 };
 
 // Token-grouped FP8 GEMM: rows of expert e times B[e]^T ([N, K] codes).
+template <class TL, bool MX>
+constexpr int f8_grouped_lds() {
+  return TL::STAGES * ((TL::BM + TL::BN) * (MX ? 128 : 64) + 2048);
+}
 template <class TL, bool MX, int EPI>
-__global__ void __launch_bounds__(TL::THREADS, 1) f8_grouped_kernel(F8Args p) {
+__device__ __forceinline__ void f8_grouped_tile(const F8Args& p, int l, char* smem) {
   constexpr int BM = TL::BM, BN = TL::BN, WN = TL::WN, WAVES = TL::WAVES;
   static_assert(EPI != EPI_SWIGLU || TL::WNT % 2 == 0, "SwiGLU pairs gate/up sub-tiles");
   constexpr int ROWB = MX ? 128 : 64;  // MX: 128-element loop; blockwise: the 64-element ring
-  __shared__ __attribute__((aligned(1024))) char smem[TL::STAGES * ((BM + BN) * ROWB + 2048)];
-  const int l = xcd_remap(blockIdx.x, gridDim.x);
   const int mt_g = l / p.ntn, nt = l - mt_g * p.ntn;
-  if (mt_g >= p.tstart[p.E]) return;
   int lo = 0, hi = p.E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -630,17 +631,30 @@ __global__ void __launch_bounds__(TL::THREADS, 1) f8_grouped_kernel(F8Args p) {
   zero(acc);
   if constexpr (MX) mainloop8<TL, true, false>(smem, sa, sb, ssa, ssb, p.K / 128, acc, wave, lane);
   else ring8<TL>(smem, sa, sb, ssa, ssb, p.K / 64, acc, wave, lane);
-  static_assert(sizeof(smem) >= grouped_epi_lds<TL, EPI>(), "epilogue staging exceeds LDS");
+  static_assert(f8_grouped_lds<TL, MX>() >= grouped_epi_lds<TL, EPI>(), "epilogue staging exceeds LDS");
   grouped_epilogue<TL, EPI>(p.epi, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane, smem, threadIdx.x);
 }
 
+// The tiles from a grid of resident workgroups, in rounds of gridDim.x (an XCD
+// takes a contiguous run of the list per round), as the bf16 grouped GEMM.
+template <class TL, bool MX, int EPI>
+__global__ void __launch_bounds__(TL::THREADS, 1) f8_grouped_kernel(F8Args p) {
+  __shared__ __attribute__((aligned(1024))) char smem[f8_grouped_lds<TL, MX>()];
+  const int total = p.tstart[p.E] * p.ntn;
+  for (int l = xcd_remap(blockIdx.x, gridDim.x); l < total; l += gridDim.x) {
+    f8_grouped_tile<TL, MX, EPI>(p, l, smem);
+    __syncthreads();  // the next tile's loads overwrite the epilogue's staging
+  }
+}
+
 // Per-expert FP8 weight-gradient GEMM over the expert's padded token steps.
+template <class TL>
+constexpr int f8_wgrad_lds() { return TL::STAGES * ((TL::BM + TL::BN) * 128 + 2048); }
 template <class TL, bool MX, bool OUT_F32>
-__global__ void __launch_bounds__(TL::THREADS, 1) f8_wgrad_kernel(F8Args p) {
+__device__ __forceinline__ void f8_wgrad_tile(const F8Args& p, int l, char* smem) {
   constexpr int BM = TL::BM, BN = TL::BN, WAVES = TL::WAVES;
   constexpr int ROWB = 128;
-  __shared__ __attribute__((aligned(1024))) char smem[TL::STAGES * ((BM + BN) * ROWB + 2048)];
-  const ExpertTile et = expert_tile(p.eorder, p.E, p.tm * p.tn);
+  const ExpertTile et = expert_tile(p.eorder, l, p.tm * p.tn);
   const int e = et.e, mt = et.rem / p.tn, nt = et.rem - mt * p.tn;
   const int s0 = p.tstart[e], ksteps = p.tstart[e + 1] - s0;
   const int lane = threadIdx.x & 63;
@@ -662,8 +676,15 @@ __global__ void __launch_bounds__(TL::THREADS, 1) f8_wgrad_kernel(F8Args p) {
                     int(p.sb_ld * 4), wave == 1};
     mainloop8<TL, MX, true>(smem, sa, sb, ssa, ssb, ksteps, acc, wave, lane);
   }
-  static_assert(sizeof(smem) >= wgrad_epi_lds<TL, OUT_F32>(), "epilogue staging exceeds LDS");
+  static_assert(f8_wgrad_lds<TL>() >= wgrad_epi_lds<TL, OUT_F32>(), "epilogue staging exceeds LDS");
   wgrad_epilogue<TL, OUT_F32>(p.C, p.M, p.N, e, mt, nt, acc, wm, wn, lane, smem, threadIdx.x);
+}
+
+// Experts longest first, one workgroup per tile, as the bf16 weight-gradient GEMM.
+template <class TL, bool MX, bool OUT_F32>
+__global__ void __launch_bounds__(TL::THREADS, 1) f8_wgrad_kernel(F8Args p) {
+  __shared__ __attribute__((aligned(1024))) char smem[f8_wgrad_lds<TL>()];
+  f8_wgrad_tile<TL, MX, OUT_F32>(p, expert_tile_start(p.eorder, p.E), smem);
 }
 
 }  // namespace
@@ -800,8 +821,10 @@ int run_f8_grouped(const moe_desc& d, const Layout& L, F8Args a, int N, const ch
   a.N = N;
   const long long Nr = (long long)d.T * d.K;
   const long long grid = ((Nr + (long long)d.E * 255) / 256) * a.ntn;
+  int resident;
+  if (int rc = resident_grid<f8_grouped_kernel<TL, MX, EPI>>(TL::THREADS, &resident)) return rc;
   prof_begin(name, s);
-  f8_grouped_kernel<TL, MX, EPI><<<unsigned(grid), TL::THREADS, 0, s>>>(a);
+  f8_grouped_kernel<TL, MX, EPI><<<unsigned(grid < resident ? grid : resident), TL::THREADS, 0, s>>>(a);
   prof_end(s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }

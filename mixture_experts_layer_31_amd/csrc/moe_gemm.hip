@@ -60,13 +60,21 @@ namespace {
 using namespace gemm;
 
 
-// Token-grouped GEMM: one workgroup per (m-tile, n-tile) of the flat tile list.
+// Token-grouped GEMM over the flat (m-tile, n-tile) list, from a grid of
+// resident workgroups that take the tiles in rounds of gridDim.x: in each
+// round an XCD takes a contiguous run of the list, so the tiles that share an
+// A or B slice start together and meet in that XCD's L2 (one workgroup per
+// tile, dispatched as CUs free up, lets them drift apart by several k-steps
+// and misses there about twice as often).
 template <class TL, bool B_T, int EPI>
 __global__ void __launch_bounds__(TL::THREADS, 1) grouped_gemm_kernel(GroupedArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
-  const int l = xcd_remap(blockIdx.x, gridDim.x);
-  if (l / p.ntn >= p.tile_start[p.E]) return;
-  grouped_tile<TL, B_T, EPI>(p, decode_tile<TL::BM>(p, l), smem);
+  const int total = p.tile_start[p.E] * p.ntn;
+  const int G = gridDim.x, w = xcd_remap(blockIdx.x, G);
+  for (int l = w; l < total; l += G) {
+    grouped_tile<TL, B_T, EPI>(p, decode_tile<TL::BM>(p, l), smem);
+    __syncthreads();  // the next tile's loads overwrite the epilogue's staging
+  }
 }
 
 struct WgradArgs {
@@ -79,12 +87,11 @@ struct WgradArgs {
 };
 
 template <class TL, bool OUT_F32>
-__global__ void __launch_bounds__(TL::THREADS, 1) wgrad_gemm_kernel(WgradArgs p) {
+__device__ __forceinline__ void wgrad_tile(const WgradArgs& p, int l, char* smem) {
   constexpr int BM = TL::BM, BN = TL::BN, WM = TL::WM, WN = TL::WN;
   constexpr int WMT = TL::WMT, WNT = TL::WNT, WAVES = TL::WAVES;
-  __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
 
-  const ExpertTile et = expert_tile(p.eorder, p.E, p.tm * p.tn);
+  const ExpertTile et = expert_tile(p.eorder, l, p.tm * p.tn);
   const int e = et.e, mt = et.rem / p.tn, nt = et.rem - mt * p.tn;
   const int off = p.offsets[e];
   const int ne = p.offsets[e + 1] - off;
@@ -108,8 +115,19 @@ __global__ void __launch_bounds__(TL::THREADS, 1) wgrad_gemm_kernel(WgradArgs p)
                                                                          wave, lane);
   }
 
-  static_assert(sizeof(smem) >= wgrad_epi_lds<TL, OUT_F32>(), "epilogue staging exceeds LDS");
+  static_assert(TL::LDS >= wgrad_epi_lds<TL, OUT_F32>(), "epilogue staging exceeds LDS");
   wgrad_epilogue<TL, OUT_F32>(p.C, p.M, p.N, e, mt, nt, acc, wm, wn, lane, smem, threadIdx.x);
+}
+
+// Per-expert weight-gradient tiles (experts longest first), one workgroup per
+// tile: their lengths follow the experts' token counts, and the hardware's
+// dispatch of the next tile to whichever CU frees up balances them (resident
+// workgroups in fixed rounds, as the grouped GEMM uses, lose 20-30% here under
+// skewed routing and gain nothing under uniform routing).
+template <class TL, bool OUT_F32>
+__global__ void __launch_bounds__(TL::THREADS, 1) wgrad_gemm_kernel(WgradArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
+  wgrad_tile<TL, OUT_F32>(p, expert_tile_start(p.eorder, p.E), smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -131,8 +149,10 @@ int run_grouped(const moe_desc& d, const Layout& L, GroupedArgs a, int N, const 
   a.ntn = N / TL::BN;
   const long long grid = (long long)max_mtiles(d, TL::BM) * a.ntn;
   if (grid <= 0) return MOE_OK;
+  int resident;
+  if (int rc = resident_grid<grouped_gemm_kernel<TL, B_T, EPI>>(TL::THREADS, &resident)) return rc;
   prof_begin(name, s);
-  grouped_gemm_kernel<TL, B_T, EPI><<<unsigned(grid), TL::THREADS, 0, s>>>(a);
+  grouped_gemm_kernel<TL, B_T, EPI><<<unsigned(grid < resident ? grid : resident), TL::THREADS, 0, s>>>(a);
   prof_end(s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }

@@ -24,15 +24,37 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
   return xcd * q + (xcd < r ? xcd : r) + local;
 }
 
-// Tile l of a per-expert (weight-gradient) GEMM with `per` tiles per expert:
-// experts are taken longest first (eorder, written by the routing step); when
-// the routing is skewed (eorder[E] set) workgroups keep the hardware's
+// Workgroups of KERNEL that fit on the current device at once (CUs times the
+// occupancy per CU), queried once per kernel and device.
+template <auto KERNEL>
+int resident_grid(int threads, int* out) {
+  static int cached[64] = {};
+  int dev;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_EHIP;
+  if (cached[dev] == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, KERNEL, threads, 0) != hipSuccess ||
+        cus <= 0 || per <= 0)
+      return MOE_EHIP;
+    cached[dev] = cus * per;
+  }
+  *out = cached[dev];
+  return MOE_OK;
+}
+
+// Tiles of a per-expert (weight-gradient) GEMM with `per` tiles per expert,
+// one workgroup per tile: experts are taken longest first (eorder, written by
+// the routing step).  Workgroup b takes tile expert_tile_start: when the
+// routing is skewed (eorder[E] set) b itself, keeping the hardware's
 // round-robin over the XCDs so the longest tiles start first on every XCD,
-// otherwise consecutive tiles of an expert share an XCD and its L2.
+// otherwise its XCD's contiguous run, so consecutive tiles of an expert share
+// that XCD's L2.
+__device__ __forceinline__ int expert_tile_start(const int32_t* eorder, int E) {
+  return eorder[E] ? int(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
+}
 struct ExpertTile { int e, rem; };
-__device__ __forceinline__ ExpertTile expert_tile(const int32_t* eorder, int E, int per) {
-  const int b = blockIdx.x, G = gridDim.x;
-  const int l = eorder[E] ? b : xcd_remap(b, G);
+__device__ __forceinline__ ExpertTile expert_tile(const int32_t* eorder, int l, int per) {
   const int rank = l / per;
   return {eorder[rank], l - rank * per};
 }
