@@ -567,6 +567,7 @@ struct F8Args {
   const int32_t* eorder;   // [E+1] experts longest first, then the skew flag (wgrad)
   const int32_t* tstart;   // [E+1] m-tile prefix (token-grouped) or 128-token step prefix (wgrad)
   int E, K, ntn;           // K: contraction of a token-grouped GEMM
+  int nmajor;              // token-grouped: n-tiles outer within an expert (1) or m-tiles (0)
   int M, N, tm, tn;        // wgrad: dW[e] is [M, N]
   const uint8_t* A;        // token-grouped: [rows, K] codes; wgrad: [M, lda] codes
   int64_t lda;
@@ -593,11 +594,23 @@ __device__ __forceinline__ void f8_grouped_tile(const F8Args& p, int l, char* sm
   constexpr int BM = TL::BM, BN = TL::BN, WN = TL::WN, WAVES = TL::WAVES;
   static_assert(EPI != EPI_SWIGLU || TL::WNT % 2 == 0, "SwiGLU pairs gate/up sub-tiles");
   constexpr int ROWB = MX ? 128 : 64;  // MX: 128-element loop; blockwise: the 64-element ring
-  const int mt_g = l / p.ntn, nt = l - mt_g * p.ntn;
-  int lo = 0, hi = p.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.tstart[mid] <= mt_g) lo = mid; else hi = mid;
+  int mt_g, nt, lo = 0, hi = p.E;
+  if (p.nmajor) {  // expert e owns flat tiles [tstart[e] * ntn, tstart[e + 1] * ntn)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.tstart[mid] * p.ntn <= l) lo = mid; else hi = mid;
+    }
+    const int t0 = p.tstart[lo], mte = p.tstart[lo + 1] - t0;
+    const int local = l - t0 * p.ntn;
+    nt = local / mte;
+    mt_g = t0 + (local - nt * mte);
+  } else {
+    mt_g = l / p.ntn;
+    nt = l - mt_g * p.ntn;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.tstart[mid] <= mt_g) lo = mid; else hi = mid;
+    }
   }
   const int e = lo;
   const int e0 = p.offsets[e];
@@ -819,6 +832,7 @@ int run_f8_grouped(const moe_desc& d, const Layout& L, F8Args a, int N, const ch
   using TL = F8GrTile<MX>;
   a.ntn = N / TL::BN;
   a.N = N;
+  a.nmajor = EPI == EPI_STORE;  // tile order within an expert, as the bf16 grouped GEMM
   const long long Nr = (long long)d.T * d.K;
   const long long grid = ((Nr + (long long)d.E * 255) / 256) * a.ntn;
   int resident;

@@ -147,6 +147,10 @@ int run_grouped(const moe_desc& d, const Layout& L, GroupedArgs a, int N, const 
   a.tile_start = reinterpret_cast<const int32_t*>(scratch + L.tiles[tile_index(TL::BM)]);
   a.E = d.E;
   a.ntn = N / TL::BN;
+  // n-tiles outer within an expert for the plain stores (W2, W1 dgrad: a round's
+  // tiles then span all of an expert's m-tiles and fewer n-tiles, 3-6% faster);
+  // m-tiles outer for the SwiGLU epilogues (as fast or faster)
+  a.nmajor = EPI == EPI_STORE;
   const long long grid = (long long)max_mtiles(d, TL::BM) * a.ntn;
   if (grid <= 0) return MOE_OK;
   int resident;

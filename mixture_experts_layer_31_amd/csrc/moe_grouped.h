@@ -21,9 +21,11 @@ struct GroupedArgs {
   int ldo;
   uint16_t* out2;             // SWIGLU: A [rows, F] or null
   const uint16_t* hsave;      // DSWIGLU: H [rows, 2F] (may equal out: read before written, per tile)
+  int nmajor;                 // tile order within an expert: n-tiles outer (1) or m-tiles outer (0)
 };
 
-// Where flat tile l (= m-tile * ntn + n-tile, m-tiles expert-major) sits.
+// Where flat tile l sits: experts in order, and within an expert either
+// m-tile * ntn + n-tile (nmajor 0) or n-tile * (its m-tiles) + m-tile (nmajor 1).
 struct TileCoord {
   int e, e0, ne;     // expert, its first permuted row, its row count
   int mt_g, nt;      // global m-tile index, n-tile index
@@ -34,12 +36,23 @@ struct TileCoord {
 template <int BM>
 __device__ __forceinline__ TileCoord decode_tile(const GroupedArgs& p, int l) {
   TileCoord c;
-  c.mt_g = l / p.ntn;
-  c.nt = l - c.mt_g * p.ntn;
   int lo = 0, hi = p.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.tile_start[mid] <= c.mt_g) lo = mid; else hi = mid;
+  if (p.nmajor) {  // expert e owns flat tiles [tile_start[e] * ntn, tile_start[e + 1] * ntn)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.tile_start[mid] * p.ntn <= l) lo = mid; else hi = mid;
+    }
+    const int t0 = p.tile_start[lo], mte = p.tile_start[lo + 1] - t0;
+    const int local = l - t0 * p.ntn;
+    c.nt = local / mte;
+    c.mt_g = t0 + (local - c.nt * mte);
+  } else {
+    c.mt_g = l / p.ntn;
+    c.nt = l - c.mt_g * p.ntn;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.tile_start[mid] <= c.mt_g) lo = mid; else hi = mid;
+    }
   }
   c.e = lo;
   c.e0 = p.offsets[c.e];

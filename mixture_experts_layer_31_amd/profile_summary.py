@@ -60,7 +60,7 @@ def step_name(kernel: str) -> str | None:
         return _GROUPED.get((m.group(1), m.group(2)))
     if "wgrad_gemm_kernel" in kernel:
         return "wgrad"
-    m = re.search(r"gather_reduce_kernel<[^>]*\b(true|false)>", kernel)  # last argument: weighted
+    m = re.search(r"gather_reduce_kernel<[^>]*\b(true|false), \d+>", kernel)  # weighted, batch
     if m:
         return "combine" if m.group(1) == "true" else "unpermute"
     for key, name in _PLAIN:
