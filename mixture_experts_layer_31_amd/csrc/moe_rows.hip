@@ -53,6 +53,42 @@ __device__ __forceinline__ void load8(const float* p, size_t i8, float (&f)[8]) 
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
+// Streaming forms for rows touched exactly once per pass: a nontemporal access
+// keeps the row out of the caches' working set.  Measured on gfx950 at the 30B
+// shape: streaming loads take the top-8 gather-reduce from 5.0 to 6.2 TB/s; the
+// dispatch keeps plain stores (streaming ones measured slower there: 5.6 -> 5.2
+// TB/s, the next kernel reading the rows back).
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(static_cast<const nt_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store16_nt(void* p, const uint4& a) {
+  const nt_u32x4 v = {a.x, a.y, a.z, a.w};
+  __builtin_nontemporal_store(v, static_cast<nt_u32x4*>(p));
+}
+__device__ __forceinline__ void load8_nt(const uint16_t* p, size_t i8, float (&f)[8]) {
+  unpack8(load16_nt(reinterpret_cast<const uint4*>(p) + i8), f);
+}
+__device__ __forceinline__ void load8_nt(const float* p, size_t i8, float (&f)[8]) {
+  const uint4 a = load16_nt(reinterpret_cast<const float4*>(p) + 2 * i8);
+  const uint4 b = load16_nt(reinterpret_cast<const float4*>(p) + 2 * i8 + 1);
+  f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y);
+  f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+  f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y);
+  f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
+}
+__device__ __forceinline__ void store8_nt(uint16_t* p, size_t i8, const float (&f)[8]) {
+  store16_nt(reinterpret_cast<uint4*>(p) + i8, pack8(f));
+}
+__device__ __forceinline__ void store8_nt(float* p, size_t i8, const float (&f)[8]) {
+  store16_nt(reinterpret_cast<float4*>(p) + 2 * i8,
+             make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                        __float_as_uint(f[3])));
+  store16_nt(reinterpret_cast<float4*>(p) + 2 * i8 + 1,
+             make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]),
+                        __float_as_uint(f[7])));
+}
 __device__ __forceinline__ void store8(uint16_t* p, size_t i8, const float (&f)[8]) {
   reinterpret_cast<uint4*>(p)[i8] = pack8(f);
 }
@@ -157,17 +193,17 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_kernel(
         w[j] = WEIGHTED ? wrow[k0 + j] : 1.f;
       }
 #pragma unroll
-      for (int j = 0; j < KB; ++j) load8(rows, (size_t(q[j] < 0 ? 0 : q[j]) * D) / 8 + c, f[j]);
+      for (int j = 0; j < KB; ++j) load8_nt(rows, (size_t(q[j] < 0 ? 0 : q[j]) * D) / 8 + c, f[j]);
 #pragma unroll
       for (int j = 0; j < KB; ++j) add(q[j] >= 0, w[j], f[j]);
     }
     for (int k = kfull; k < K; ++k) {
       const int q = prow[k];
       float f[8];
-      load8(rows, (size_t(q < 0 ? 0 : q) * D) / 8 + c, f);
+      load8_nt(rows, (size_t(q < 0 ? 0 : q) * D) / 8 + c, f);
       add(q >= 0, WEIGHTED ? wrow[k] : 1.f, f);
     }
-    store8(out, (size_t(t) * D) / 8 + c, acc);
+    store8_nt(out, (size_t(t) * D) / 8 + c, acc);
   }
 }
 
@@ -215,7 +251,7 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_dy_kernel(
       float sc[8];
       if (c < chunks) {
         float o[8];
-        load8(O, (size_t(q) * D) / 8 + c, o);
+        load8_nt(O, (size_t(q) * D) / 8 + c, o);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           dot = __builtin_fmaf(v[j][i], o[i], dot);
