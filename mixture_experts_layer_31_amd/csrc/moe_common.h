@@ -23,7 +23,7 @@ constexpr int kRouteThreads = 256;
 // Byte offsets of the regions of the caller's scratch buffer.  Every region
 // starts on a 256-byte boundary.  The layout depends only on the descriptor.
 struct Layout {
-  size_t err, counts, offsets, tiles[3], eorder, chunk_cnt, pos, src, wperm;
+  size_t err, counts, offsets, tiles[3], eorder, chunk_cnt, chunk_bad, pos, src, wperm;
   size_t xperm, h, a, o, dyperm, dh, dxperm, fp8, queue, total;
   bool recompute;   // MOE_FLAG_RECOMPUTE: no H region; H is rebuilt in the dH region
   int nchunks;      // routing chunks
@@ -52,6 +52,7 @@ inline Layout make_layout(const moe_desc& d) {
   for (int i = 0; i < 3; ++i) L.tiles[i] = take((E + 1) * 4);
   L.eorder = take((E + 1) * 4);  // experts by descending count, then the skew flag
   L.chunk_cnt = take(size_t(L.nchunks) * E * 4);
+  L.chunk_bad = take(size_t(L.nchunks) * 4);  // per-chunk flag: an index outside [0, E)
   L.pos = take(N * 4);
   L.src = take(N * 4);
   L.wperm = take(N * 4);

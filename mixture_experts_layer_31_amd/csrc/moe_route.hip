@@ -4,11 +4,14 @@
 // MoE news item, "Why is MoE training communication-bound?").  Here that sort
 // is a counting sort of the flat pair index p = t*K + k, in three launches:
 //   1. count:   each block takes a chunk of 2048 pairs and counts them per
-//               expert with LDS atomics (counting only; ranks come later).
+//               expert with LDS atomics (counting only; ranks come later), and
+//               flags the chunk if it holds an index outside [0, E).
 //   2. scan:    one block turns the per-chunk counts into per-chunk bases (an
 //               exclusive scan over chunks for every expert), per-expert totals,
 //               the expert offsets (exclusive scan over experts) and the
-//               per-expert m-tile prefix sums used by the grouped GEMMs.
+//               per-expert m-tile prefix sums used by the grouped GEMMs.  It
+//               also starts the device error word afresh from the chunk flags
+//               (the caller's scratch may hold anything).
 //   3. scatter: each block re-reads its chunk in order; inside a wavefront the
 //               lanes holding the same expert are found with one ballot per
 //               expert-id bit, the in-wave rank is the popcount of that match
@@ -21,7 +24,7 @@ namespace moe {
 
 __global__ void __launch_bounds__(kRouteThreads) route_count_kernel(
     const int32_t* __restrict__ idx, int N, int E, int32_t* __restrict__ chunk_cnt,
-    uint32_t* __restrict__ err) {
+    int32_t* __restrict__ chunk_bad) {
   __shared__ int hist[1024];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
@@ -37,10 +40,10 @@ __global__ void __launch_bounds__(kRouteThreads) route_count_kernel(
         bad = true;
     }
   }
-  if (bad) atomicOr(err, kErrIndex);
-  __syncthreads();
+  const int any_bad = __syncthreads_or(bad);
   for (int e = threadIdx.x; e < E; e += blockDim.x)
     chunk_cnt[size_t(blockIdx.x) * E + e] = hist[e];
+  if (threadIdx.x == 0) chunk_bad[blockIdx.x] = any_bad ? 1 : 0;
 }
 
 // One block of 1024 threads; thread e owns expert e.  Besides the offsets and
@@ -50,18 +53,30 @@ __global__ void __launch_bounds__(kRouteThreads) route_count_kernel(
 // above twice the mean) that makes them spread each expert's tiles over all
 // XCDs instead of grouping them on one.
 __global__ void __launch_bounds__(1024) route_scan_kernel(
-    int E, int nchunks, int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ tiles64,
-    int32_t* __restrict__ tiles128, int32_t* __restrict__ tiles256, int32_t* __restrict__ eorder) {
+    int E, int nchunks, int32_t* __restrict__ chunk_cnt, const int32_t* __restrict__ chunk_bad,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tiles64,
+    int32_t* __restrict__ tiles128, int32_t* __restrict__ tiles256, int32_t* __restrict__ eorder,
+    uint32_t* __restrict__ err) {
   __shared__ int sc[4][1024];
   __shared__ int cnt[1024];
   const int e = threadIdx.x;
+  int bad = 0;
+  for (int b = e; b < nchunks; b += blockDim.x) bad |= chunk_bad[b];
+  bad = __syncthreads_or(bad);
+  if (e == 0) err[0] = bad ? kErrIndex : 0u;
   int total = 0;
   if (e < E) {
-    for (int b = 0; b < nchunks; ++b) {
-      const int c = chunk_cnt[size_t(b) * E + e];
-      chunk_cnt[size_t(b) * E + e] = total;  // becomes the chunk's base within expert e
-      total += c;
+    // the chunk counts of expert e, 16 independent loads at a time
+    constexpr int kB = 16;
+    for (int b0 = 0; b0 < nchunks; b0 += kB) {
+      int c[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) c[j] = b0 + j < nchunks ? chunk_cnt[size_t(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        if (b0 + j < nchunks) chunk_cnt[size_t(b0 + j) * E + e] = total;  // the chunk's base within e
+        total += c[j];
+      }
     }
     counts[e] = total;
   }
@@ -171,21 +186,18 @@ int launch_route(const moe_desc& d, const Layout& L, const int32_t* idx, char* s
   while ((1 << nbits) < E) ++nbits;
   auto* err = reinterpret_cast<uint32_t*>(scratch + L.err);
   auto* chunk = reinterpret_cast<int32_t*>(scratch + L.chunk_cnt);
-  // the caller's scratch may hold anything: start the error word from zero
-  prof_begin("clear_err", s);
-  clear_err_kernel<<<1, 64, 0, s>>>(err);
-  prof_end(s);
+  auto* bad = reinterpret_cast<int32_t*>(scratch + L.chunk_bad);
   prof_begin("route_count", s);
-  route_count_kernel<<<L.nchunks, kRouteThreads, 0, s>>>(idx, N, E, chunk, err);
+  route_count_kernel<<<L.nchunks, kRouteThreads, 0, s>>>(idx, N, E, chunk, bad);
   prof_end(s);
   prof_begin("route_scan", s);
   route_scan_kernel<<<1, 1024, 0, s>>>(
-      E, L.nchunks, chunk, reinterpret_cast<int32_t*>(scratch + L.counts),
+      E, L.nchunks, chunk, bad, reinterpret_cast<int32_t*>(scratch + L.counts),
       reinterpret_cast<int32_t*>(scratch + L.offsets),
       reinterpret_cast<int32_t*>(scratch + L.tiles[0]),
       reinterpret_cast<int32_t*>(scratch + L.tiles[1]),
       reinterpret_cast<int32_t*>(scratch + L.tiles[2]),
-      reinterpret_cast<int32_t*>(scratch + L.eorder));
+      reinterpret_cast<int32_t*>(scratch + L.eorder), err);
   prof_end(s);
   prof_begin("route_scatter", s);
   route_scatter_kernel<<<L.nchunks, kRouteThreads, 0, s>>>(
