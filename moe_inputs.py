@@ -106,6 +106,11 @@ CONFIGS = {
                              mode=MODE_FP32_BF16GEMM, seed=2005),
     "zipf_bf16": LayerConfig("zipf_bf16", T=900, D=256, F=128, E=16, K=4, routing="zipf",
                              seed=2006),
+    # token rows of 512 and 1024 16-byte chunks (the row movers give each thread
+    # several chunks of a row), top-8, bf16 I/O and fp32 I/O
+    "rows4k_bf16": LayerConfig("rows4k_bf16", T=96, D=4096, F=128, E=12, K=8, seed=2007),
+    "rows8k_f32io": LayerConfig("rows8k_f32io", T=40, D=8192, F=128, E=8, K=8,
+                                mode=MODE_FP32_BF16GEMM, seed=2008),
     # degenerate shapes: one token; one expert; every expert chosen (K = E)
     "one_token": LayerConfig("one_token", T=1, D=128, F=64, E=4, K=2, seed=2101),
     "one_expert": LayerConfig("one_expert", T=100, D=128, F=64, E=1, K=1, seed=2102),

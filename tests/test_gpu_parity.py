@@ -23,7 +23,7 @@ TOL_BF16 = 1e-2
 TOL_F32 = 1e-4
 
 SMALL = ["tiny", "tiny_bf16gemm", "small_bf16", "dead_bf16", "mid_bf16", "wide_bf16", "mid_f32io",
-         "zipf_bf16"]
+         "zipf_bf16", "rows4k_bf16", "rows8k_f32io"]
 
 
 @pytest.fixture(scope="module", autouse=True)
