@@ -111,8 +111,11 @@ enum moe_status {
  * flops.  MOE_VIEW_H is not available (MOE_EINVAL).  All modes. */
 #define MOE_FLAG_RECOMPUTE 0x4u
 
-/* Layer descriptor, passed by host pointer.  Requirements: T, E, K >= 1;
- * K <= E; E <= 1024; D % 64 == 0 and F % 64 == 0; T * K < 2^31. */
+/* Layer descriptor, passed by host pointer.  Requirements: T >= 0; E, K >= 1;
+ * K <= E; E <= 1024; D % 64 == 0 and F % 64 == 0; T * K < 2^31.  T = 0 is a
+ * layer with no tokens: moe_route and moe_fwd leave zero counts and offsets,
+ * moe_bwd writes zero dw1 and dw2 (every expert has no tokens), and the [T, ...]
+ * buffers (x, y, dy, dx, topk_idx, topk_w, dtopk_w) may be null. */
 typedef struct moe_desc {
   int32_t T, D, F, E, K;
   int32_t mode;  /* enum moe_mode */
@@ -212,12 +215,13 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w,
  *   p = softmax(z); the K experts of largest p in descending order, ties to the
  *   lower expert index (the selection is exactly that of the logits);
  *   topk_w[t,k] = p[topk_idx[t,k]] / sum_k' p[topk_idx[t,k']] (fp32).
- * Reads only T, E, K of `d`: requires T >= 1, 1 <= K <= E (else MOE_EINVAL),
+ * Reads only T, E, K of `d`: requires T >= 0, 1 <= K <= E (else MOE_EINVAL),
  * E <= 512 and K <= 64 (else MOE_EUNSUPPORTED).  logits: device float32
  * [T, E] row-major, not NaN; topk_idx: device int32 [T, K] and topk_w: device
  * float32 [T, K], written (the layout moe_fwd reads).  A token whose logits are
  * all -inf gets NaN weights, as the definition does.  All pointers 4-byte
- * aligned (MOE_EALIGN).  Asynchronous on `stream`; allocates nothing. */
+ * aligned (MOE_EALIGN).  With T = 0 it returns MOE_OK and touches nothing
+ * (pointers may be null).  Asynchronous on `stream`; allocates nothing. */
 int moe_router_fwd(const moe_desc* d, const float* logits, int32_t* topk_idx, float* topk_w,
                    void* stream);
 

@@ -15,7 +15,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // Descriptor checks shared by every entry point.
 int check_desc(const moe_desc* d) {
   if (d == nullptr) return MOE_EINVAL;
-  if (d->T <= 0 || d->D <= 0 || d->F <= 0 || d->E <= 0 || d->K <= 0) return MOE_EINVAL;
+  if (d->T < 0 || d->D <= 0 || d->F <= 0 || d->E <= 0 || d->K <= 0) return MOE_EINVAL;
   if (d->K > d->E || d->E > 1024) return MOE_EINVAL;
   if (d->mode < MOE_FP32 || d->mode > MOE_FP8) return MOE_EINVAL;
   if ((d->flags & ~int32_t(MOE_FLAG_OVERLAP | MOE_FLAG_QUEUE_TIMEOUT_TEST | MOE_FLAG_RECOMPUTE)) != 0)
@@ -169,7 +169,7 @@ int moe_route(const moe_desc* d, const int32_t* topk_idx, void* scratch, size_t 
               void* stream) {
   int rc = check_desc(d);
   if (rc) return rc;
-  if (topk_idx == nullptr) return MOE_EINVAL;
+  if (topk_idx == nullptr && d->T > 0) return MOE_EINVAL;
   if (!aligned(topk_idx, 4)) return MOE_EALIGN;
   if ((rc = check_scratch(d, scratch, scratch_bytes))) return rc;
   const Layout L = make_layout(*d);
@@ -229,7 +229,8 @@ int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const flo
   int rc = check_desc(d);
   if (rc) return rc;
   if ((rc = check_built(d))) return rc;
-  if (!x || !topk_idx || !topk_w || !w1 || !w2 || !y) return MOE_EINVAL;
+  // with no tokens the [T, ...] buffers are empty and may be null
+  if (!w1 || !w2 || (d->T > 0 && (!x || !topk_idx || !topk_w || !y))) return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w1, 16) || !aligned(w2, 16) ||
       !aligned(topk_idx, 4) || !aligned(topk_w, 4) || (wprep && !aligned(wprep, 16)))
     return MOE_EALIGN;
@@ -241,6 +242,7 @@ int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const flo
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool io_f32 = d->mode == MOE_FP32 || d->mode == MOE_FP32_BF16GEMM;
   if ((rc = launch_route(*d, L, topk_idx, sc, s))) return rc;
+  if (d->T == 0) return MOE_OK;  // routing metadata of no pairs; y is empty
   if (queue_capable(*d)) {
     if ((rc = launch_fwd_queue(*d, L, x, io_f32, topk_w, g1, g2, sc, s))) return rc;
     return launch_combine(*d, L, topk_w, y, io_f32, sc, s);
@@ -273,7 +275,8 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
   int rc = check_desc(d);
   if (rc) return rc;
   if ((rc = check_built(d))) return rc;
-  if (!dy || !topk_w || !w1 || !w2 || !dx || !dw1 || !dw2 || !dtopk_w) return MOE_EINVAL;
+  if (!w1 || !w2 || !dw1 || !dw2 || (d->T > 0 && (!dy || !topk_w || !dx || !dtopk_w)))
+    return MOE_EINVAL;
   if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(w1, 16) || !aligned(w2, 16) ||
       !aligned(dw1, 16) || !aligned(dw2, 16) || !aligned(topk_w, 4) || !aligned(dtopk_w, 4) ||
       (wprep && !aligned(wprep, 16)))
@@ -285,6 +288,11 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
   char* sc = static_cast<char*>(scratch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool io_f32 = d->mode == MOE_FP32 || d->mode == MOE_FP32_BF16GEMM;
+  if (d->T == 0) {  // no tokens: every expert's weight gradient is zero; dx, dtopk_w are empty
+    const size_t es = io_f32 ? 4 : 2, n1 = size_t(d->E) * 2 * d->F * d->D * es;
+    if ((rc = launch_zero(dw1, n1, s))) return rc;
+    return launch_zero(dw2, n1 / 2, s);
+  }
   if (L.recompute) {  // H again, by the forward's own W1 GEMM (before the combine-backward,
                       // whose fused FP8 row codes the FP8 recompute's x codes would overwrite)
     if (d->mode == MOE_FP32)
@@ -319,7 +327,7 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
 // The router reads only T, E and K of the descriptor.
 static int check_router_desc(const moe_desc* d) {
   if (d == nullptr) return MOE_EINVAL;
-  if (d->T <= 0 || d->E <= 0 || d->K <= 0 || d->K > d->E) return MOE_EINVAL;
+  if (d->T < 0 || d->E <= 0 || d->K <= 0 || d->K > d->E) return MOE_EINVAL;
   if (d->E > 512 || d->K > 64) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
@@ -328,6 +336,7 @@ int moe_router_fwd(const moe_desc* d, const float* logits, int32_t* topk_idx, fl
                    void* stream) {
   const int rc = check_router_desc(d);
   if (rc) return rc;
+  if (d->T == 0) return MOE_OK;  // no tokens: nothing to route
   if (logits == nullptr || topk_idx == nullptr || topk_w == nullptr) return MOE_EINVAL;
   if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_EALIGN;
   return launch_router_fwd(d->T, d->E, d->K, logits, topk_idx, topk_w,
@@ -338,6 +347,7 @@ int moe_router_bwd(const moe_desc* d, const int32_t* topk_idx, const float* topk
                    const float* dtopk_w, float* dlogits, void* stream) {
   const int rc = check_router_desc(d);
   if (rc) return rc;
+  if (d->T == 0) return MOE_OK;
   if (topk_idx == nullptr || topk_w == nullptr || dtopk_w == nullptr || dlogits == nullptr)
     return MOE_EINVAL;
   if (!aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(dtopk_w, 4) || !aligned(dlogits, 4))

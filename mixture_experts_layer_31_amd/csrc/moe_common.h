@@ -100,6 +100,7 @@ int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
 int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool in_f32,
                        const float* topk_w, float* dtopk_w, char* scratch, hipStream_t s,
                        int qmode = 0, uint8_t* qcodes = nullptr, uint32_t* qsc = nullptr);
+int launch_zero(void* p, size_t bytes, hipStream_t s);  // bytes % 16 == 0
 int launch_convert_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
 // Router ahead of the layer (moe_router.hip): softmax -> top-K -> renormalise,
 // and its backward to the logits.  Requires 1 <= K <= min(E, 64), E <= 512.

@@ -187,9 +187,12 @@ int launch_route(const moe_desc& d, const Layout& L, const int32_t* idx, char* s
   auto* err = reinterpret_cast<uint32_t*>(scratch + L.err);
   auto* chunk = reinterpret_cast<int32_t*>(scratch + L.chunk_cnt);
   auto* bad = reinterpret_cast<int32_t*>(scratch + L.chunk_bad);
-  prof_begin("route_count", s);
-  route_count_kernel<<<L.nchunks, kRouteThreads, 0, s>>>(idx, N, E, chunk, bad);
-  prof_end(s);
+  // with no pairs (T = 0) only the scan runs: zero counts and offsets, a clear error word
+  if (L.nchunks > 0) {
+    prof_begin("route_count", s);
+    route_count_kernel<<<L.nchunks, kRouteThreads, 0, s>>>(idx, N, E, chunk, bad);
+    prof_end(s);
+  }
   prof_begin("route_scan", s);
   route_scan_kernel<<<1, 1024, 0, s>>>(
       E, L.nchunks, chunk, bad, reinterpret_cast<int32_t*>(scratch + L.counts),
@@ -199,11 +202,13 @@ int launch_route(const moe_desc& d, const Layout& L, const int32_t* idx, char* s
       reinterpret_cast<int32_t*>(scratch + L.tiles[2]),
       reinterpret_cast<int32_t*>(scratch + L.eorder), err);
   prof_end(s);
-  prof_begin("route_scatter", s);
-  route_scatter_kernel<<<L.nchunks, kRouteThreads, 0, s>>>(
-      idx, N, E, nbits, chunk, reinterpret_cast<const int32_t*>(scratch + L.offsets),
-      reinterpret_cast<int32_t*>(scratch + L.pos), reinterpret_cast<int32_t*>(scratch + L.src));
-  prof_end(s);
+  if (L.nchunks > 0) {
+    prof_begin("route_scatter", s);
+    route_scatter_kernel<<<L.nchunks, kRouteThreads, 0, s>>>(
+        idx, N, E, nbits, chunk, reinterpret_cast<const int32_t*>(scratch + L.offsets),
+        reinterpret_cast<int32_t*>(scratch + L.pos), reinterpret_cast<int32_t*>(scratch + L.src));
+    prof_end(s);
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

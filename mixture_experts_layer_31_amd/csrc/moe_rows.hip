@@ -500,6 +500,24 @@ int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool 
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
+__global__ void zero16_kernel(uint4* __restrict__ out, size_t n16) {
+  for (size_t i = blockIdx.x * size_t(blockDim.x) + threadIdx.x; i < n16;
+       i += size_t(gridDim.x) * blockDim.x)
+    out[i] = make_uint4(0, 0, 0, 0);
+}
+
+int launch_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes % 16 != 0) return MOE_EINVAL;
+  const size_t n16 = bytes / 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks == 0) return MOE_OK;
+  prof_begin("zero", s);
+  zero16_kernel<<<unsigned(blocks), 256, 0, s>>>(static_cast<uint4*>(p), n16);
+  prof_end(s);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
 int launch_convert_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s) {
   const size_t n8 = n / 8;
   size_t blocks = (n8 + 255) / 256;

@@ -46,7 +46,9 @@ def test_scratch_bytes():
     assert moe.moe_wprep_bytes(d) == 0
     d1 = moe.make_desc(64, 128, 64, 8, 2, moe.MOE_FP32_BF16GEMM)
     assert moe.moe_wprep_bytes(d1) >= 8 * 3 * 128 * 64 * 2
-    for bad in (moe.make_desc(0, 128, 64, 8, 2), moe.make_desc(64, 128, 64, 8, 9),
+    # no tokens is a valid layer (zero weight gradients); a negative count is not
+    assert moe.moe_scratch_bytes(moe.make_desc(0, 128, 64, 8, 2)) > 0
+    for bad in (moe.make_desc(-1, 128, 64, 8, 2), moe.make_desc(64, 128, 64, 8, 9),
                 moe.make_desc(64, 128, 64, 2000, 2), moe.make_desc(64, 128, 64, 8, 2, 7),
                 moe.make_desc(64, 128, 64, 8, 2, 2, 0x10)):
         assert moe.moe_scratch_bytes(bad) == 0
@@ -89,6 +91,15 @@ def test_fwd_validation():
     assert _fwd(moe.make_desc(64, 128, 64, 8, 2, moe.MOE_FP32_BF16GEMM)) == moe.MOE_EINVAL
     assert moe.lib().moe_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40,
                              None) == moe.MOE_EINVAL
+
+
+def test_empty_layer_validation():
+    # T = 0: the token buffers may be null, the weights and weight gradients may not
+    d = moe.make_desc(0, 128, 64, 8, 2)
+    assert _fwd(d, w1=None, x=None, idx=None, w=None, y=None) == moe.MOE_EINVAL
+    assert _bwd(d, dw1=None, dy=None, w=None, dx=None, dw=None) == moe.MOE_EINVAL
+    assert _bwd(d, dw2=None) == moe.MOE_EINVAL
+    assert _fwd(d, scratch=None) == moe.MOE_EINVAL
 
 
 def test_bwd_validation():
@@ -138,7 +149,10 @@ def test_recompute_drops_the_h_region():
 def test_router_validation():
     L = moe.lib()
     ok = moe.make_desc(64, 0, 0, 128, 8)  # the router reads only T, E and K
-    for bad, code in ((moe.make_desc(0, 0, 0, 128, 8), moe.MOE_EINVAL),
+    empty = moe.make_desc(0, 0, 0, 128, 8)  # no tokens: nothing to do, nothing touched
+    assert L.moe_router_fwd(ctypes.byref(empty), None, None, None, None) == moe.MOE_OK
+    assert L.moe_router_bwd(ctypes.byref(empty), None, None, None, None, None) == moe.MOE_OK
+    for bad, code in ((moe.make_desc(-1, 0, 0, 128, 8), moe.MOE_EINVAL),
                       (moe.make_desc(64, 0, 0, 8, 9), moe.MOE_EINVAL),
                       (moe.make_desc(64, 0, 0, 8, 0), moe.MOE_EINVAL),
                       (moe.make_desc(64, 0, 0, 1024, 8), moe.MOE_EUNSUPPORTED),

@@ -232,3 +232,37 @@ def test_all_pairs_on_two_experts():
     L, out, b = _check_layer(cfg, dict(inp, topk_idx=idx))
     for e in range(2, cfg.E):
         assert np.all(out["dw1"][e] == 0) and np.all(out["dw2"][e] == 0)
+
+
+@pytest.mark.parametrize("mode", [moe.MOE_FP32, moe.MOE_FP32_BF16GEMM, moe.MOE_BF16,
+                                  moe.MOE_FP8_BWD, moe.MOE_MXFP8, moe.MOE_FP8])
+def test_empty_layer(mode):
+    """No tokens (T = 0): null token buffers are accepted, the routing metadata
+    is all zeros even in a scratch full of garbage, and the backward writes zero
+    weight gradients (every expert has no tokens, as the oracle's empty sums)."""
+    T, D, F, E, K = 0, 256, 256, 4, 2
+    d = moe.make_desc(T, D, F, E, K, mode)
+    dt = torch.float32 if mode in (moe.MOE_FP32, moe.MOE_FP32_BF16GEMM) else torch.bfloat16
+    g = torch.Generator().manual_seed(2200 + mode)
+    w1 = (torch.randn(E, 2 * F, D, generator=g) * 0.02).to(dt).cuda()
+    w2 = (torch.randn(E, D, F, generator=g) * 0.02).to(dt).cuda()
+    nwp = moe.moe_wprep_bytes(d)
+    wprep = torch.empty(nwp, dtype=torch.uint8, device="cuda") if nwp else None
+    if wprep is not None:
+        moe.check(moe.moe_prepare_weights(d, w1, w2, wprep), "moe_prepare_weights")
+    scratch = torch.full((moe.moe_scratch_bytes(d),), 0xAB, dtype=torch.uint8, device="cuda")
+    dw1 = torch.full_like(w1, float("nan"))
+    dw2 = torch.full_like(w2, float("nan"))
+    moe.check(moe.moe_fwd(d, None, None, None, w1, w2, wprep, None, scratch), "moe_fwd")
+    moe.check(moe.moe_bwd(d, None, None, w1, w2, wprep, None, dw1, dw2, None, scratch), "moe_bwd")
+    assert moe.moe_check(d, scratch) == moe.MOE_OK
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(dw1)) == 0 and int(torch.count_nonzero(dw2)) == 0
+    rc, counts, offsets, _, _ = moe.moe_routing_view(d, scratch)
+    moe.check(rc, "moe_routing_view")
+    base = scratch.data_ptr()
+    got_c = scratch[counts - base:counts - base + 4 * E].view(torch.int32).cpu().numpy()
+    got_o = scratch[offsets - base:offsets - base + 4 * (E + 1)].view(torch.int32).cpu().numpy()
+    ref = orc.route(np.zeros((0, K), np.int32), E)
+    np.testing.assert_array_equal(got_c, ref["counts"])
+    np.testing.assert_array_equal(got_o, ref["offsets"])

@@ -177,6 +177,21 @@ def test_zero_token_expert_has_zero_wgrad():
     assert r["counts"].sum() == idx.size and r["offsets"][-1] == idx.size
 
 
+def test_no_tokens_gives_zero_weight_gradients():
+    # T = 0: every expert receives no tokens, so each weight gradient is an empty
+    # sum (zero), the routing has zero counts and the token outputs are empty
+    _, w1, w2, _, _, _ = _rand_layer(9, T=3, D=6, F=4, E=5, K=2)
+    x, dy = np.zeros((0, 6)), np.zeros((0, 6))
+    idx, w = np.zeros((0, 2), np.int32), np.zeros((0, 2))
+    f = orc.forward(x, idx, w, w1, w2)
+    b = orc.backward(dy, x, idx, w, w1, w2, f)
+    assert f["y"].shape == (0, 6) and b["dx"].shape == (0, 6) and b["dprob"].shape == (0, 2)
+    assert b["dw1"].shape == w1.shape and not np.any(b["dw1"])
+    assert b["dw2"].shape == w2.shape and not np.any(b["dw2"])
+    r = orc.route(idx, 5)
+    assert not np.any(r["counts"]) and not np.any(r["offsets"]) and r["pos"].size == 0
+
+
 def test_linear_in_routing_weights():
     x, w1, w2, dy, idx, w = _rand_layer(9, T=6, D=5, F=3, E=4, K=2)
     y1 = orc.forward(x, idx, w, w1, w2)["y"]
