@@ -272,9 +272,13 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_kernel(
 // Combine-backward: for each routed pair p of token t (row q = pos[p]),
 //   dYw_perm[q] = w_p * dy_t          (fp32 product, stored as ACT)
 //   dtopk_w[p]  = <dy_t, O[q]>         (fp32, the routing-weight gradient)
-// One wavefront owns one token: its dy row stays in registers while the K
-// expert-output rows are streamed and dotted against it.  CPL = 16-byte chunks
-// per lane (D / 512, at least 1).
+// WPT wavefronts own one token, each a contiguous quarter, half or all of the
+// row (64 * CPL chunks of 16 bytes: CPL per lane); their dy slices stay in
+// registers while the K expert-output rows are streamed and dotted against
+// them.  With WPT > 1 the waves' partial dot products meet in LDS and are
+// added in wave order (fixed, so the result is the same on every run); rows of
+// 512 or 1024 chunks (D = 4096 or 8192) take two or four waves, which halves
+// or quarters each wave's registers and puts more rows in flight.
 // QM (FP8 backward modes, bf16 rows): the kernel also writes the e4m3 row
 // quantisation of each dYw row along D (the W2 dgrad's A operand), from the
 // same bf16-rounded values it stores: QM_BLOCK, an fp32 scale per 128 columns
@@ -282,60 +286,84 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_kernel(
 // lanes).  Codes are [N, D] bytes, scale entries [D/128][N], as the standalone
 // row quantiser writes them.  D / 8 must be a multiple of 16 so a group never
 // straddles active and idle lanes.
+constexpr int kSplitMaxK = 64;  // K up to this many slots may split a row over waves
 
-template <typename IO, typename ACT, int CPL, int QM>
+template <typename IO, typename ACT, int CPL, int QM, int WPT>
 __global__ void __launch_bounds__(kRowThreads) dispatch_dy_kernel(
     const IO* __restrict__ dy, int T, int K, int D, const int32_t* __restrict__ pos,
     const float* __restrict__ topk_w, const ACT* __restrict__ O, ACT* __restrict__ dst,
     float* __restrict__ dprob, uint8_t* __restrict__ qcodes, uint32_t* __restrict__ qsc, int N) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * (kRowThreads / 64) + (threadIdx.x >> 6);
-  if (t >= T) return;
+  constexpr int WAVES = kRowThreads / 64;
+  __shared__ float sdot[WPT > 1 ? WAVES : 1][WPT > 1 ? kSplitMaxK : 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * (WAVES / WPT) + wave / WPT;
+  const int c0 = (wave % WPT) * 64 * CPL + lane;  // this lane's first chunk of the row
+  const bool live = t < T;
+  if (WPT == 1 && !live) return;
   const int chunks = D / 8;
-  float v[CPL][8];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = lane + 64 * j;
-    if (c < chunks) load8(dy, (size_t(t) * D) / 8 + c, v[j]);
-  }
-  for (int k = 0; k < K; ++k) {
-    const int p = t * K + k;
-    const int q = pos[p];
-    if (q < 0) {
-      if (lane == 0) dprob[p] = 0.f;
-      continue;
-    }
-    const float w = topk_w[p];
-    float dot = 0.f;
+  if (live) {
+    float v[CPL][8];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      float sc[8];
-      if (c < chunks) {
-        float o[8];
-        load8_nt(O, (size_t(q) * D) / 8 + c, o);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          dot = __builtin_fmaf(v[j][i], o[i], dot);
-          sc[i] = w * v[j][i];
+      const int c = c0 + 64 * j;
+      if (c < chunks) load8(dy, (size_t(t) * D) / 8 + c, v[j]);
+    }
+    for (int k = 0; k < K; ++k) {
+      const int p = t * K + k;
+      const int q = pos[p];
+      if (q < 0) {
+        if (lane == 0) {
+          if constexpr (WPT > 1) sdot[wave][k] = 0.f;
+          else dprob[p] = 0.f;
         }
-        store8(dst, (size_t(q) * D) / 8 + c, sc);
+        continue;
       }
-      if constexpr (QM != QM_NONE) {
-        // quantise the stored (bf16-rounded) values; idle lanes join the reductions with 0
+      const float w = topk_w[p];
+      float dot = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sc[i] = c < chunks ? float((__bf16)sc[i]) : 0.f;
-        uint32_t entry;
-        const uint2 codes = quantise8<QM>(sc, lane, entry);
+      for (int j = 0; j < CPL; ++j) {
+        const int c = c0 + 64 * j;
+        float sc[8];
         if (c < chunks) {
-          *reinterpret_cast<uint2*>(qcodes + size_t(q) * D + 8 * c) = codes;
-          if ((lane & 15) == 0) qsc[size_t(c >> 4) * N + q] = entry;
+          float o[8];
+          load8_nt(O, (size_t(q) * D) / 8 + c, o);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            dot = __builtin_fmaf(v[j][i], o[i], dot);
+            sc[i] = w * v[j][i];
+          }
+          store8(dst, (size_t(q) * D) / 8 + c, sc);
         }
+        if constexpr (QM != QM_NONE) {
+          // quantise the stored (bf16-rounded) values; idle lanes join the reductions with 0
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sc[i] = c < chunks ? float((__bf16)sc[i]) : 0.f;
+          uint32_t entry;
+          const uint2 codes = quantise8<QM>(sc, lane, entry);
+          if (c < chunks) {
+            *reinterpret_cast<uint2*>(qcodes + size_t(q) * D + 8 * c) = codes;
+            if ((lane & 15) == 0) qsc[size_t(c >> 4) * N + q] = entry;
+          }
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+      if (lane == 0) {
+        if constexpr (WPT > 1) sdot[wave][k] = dot;
+        else dprob[p] = dot;
       }
     }
+  }
+  if constexpr (WPT > 1) {
+    __syncthreads();
+    if (live && wave % WPT == 0) {
+      for (int k = lane; k < K; k += 64) {
+        float sum = sdot[wave][k];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
-    if (lane == 0) dprob[p] = dot;
+        for (int i = 1; i < WPT; ++i) sum += sdot[wave + i][k];
+        dprob[size_t(t) * K + k] = sum;
+      }
+    }
   }
 }
 
@@ -462,14 +490,15 @@ template <typename IO, typename ACT, int QM>
 static int dispatch_dy_cpl(const moe_desc& d, const IO* dy, const int32_t* pos,
                            const float* topk_w, const ACT* o, ACT* dst, float* dprob,
                            uint8_t* qcodes, uint32_t* qsc, hipStream_t s) {
-  const unsigned blocks = unsigned((d.T + kRowThreads / 64 - 1) / (kRowThreads / 64));
-  const int cpl = (d.D / 8 + 63) / 64;
-#define MOE_DY(C) dispatch_dy_kernel<IO, ACT, C, QM><<<blocks, kRowThreads, 0, s>>>(dy, d.T, d.K, d.D, pos, topk_w, o, dst, dprob, qcodes, qsc, d.T * d.K)
-  if (cpl <= 1) MOE_DY(1);
-  else if (cpl <= 2) MOE_DY(2);
-  else if (cpl <= 4) MOE_DY(4);
-  else if (cpl <= 8) MOE_DY(8);
-  else if (cpl <= 16) MOE_DY(16);
+  const int cpl = (d.D / 8 + 63) / 64;  // 16-byte chunks per lane with one wave per token
+  const int waves = kRowThreads / 64;
+  auto blocks = [&](int wpt) { return unsigned((d.T + waves / wpt - 1) / (waves / wpt)); };
+#define MOE_DY(C, W) dispatch_dy_kernel<IO, ACT, C, QM, W><<<blocks(W), kRowThreads, 0, s>>>(dy, d.T, d.K, d.D, pos, topk_w, o, dst, dprob, qcodes, qsc, d.T * d.K)
+  if (cpl <= 1) MOE_DY(1, 1);
+  else if (cpl <= 2) MOE_DY(2, 1);
+  else if (cpl <= 4) MOE_DY(4, 1);
+  else if (cpl <= 8) { if (d.K <= kSplitMaxK) MOE_DY(4, 2); else MOE_DY(8, 1); }
+  else if (cpl <= 16) { if (d.K <= kSplitMaxK) MOE_DY(4, 4); else MOE_DY(16, 1); }
   else return MOE_EUNSUPPORTED;
 #undef MOE_DY
   return MOE_OK;
