@@ -13,6 +13,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// 16-byte streaming (nontemporal) load and store, for data touched once per
+// pass: the access keeps it out of the caches' working set.
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(static_cast<const nt_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store16_nt(void* p, const uint4& a) {
+  const nt_u32x4 v = {a.x, a.y, a.z, a.w};
+  __builtin_nontemporal_store(v, static_cast<nt_u32x4*>(p));
+}
+
 // Bits of the device error word kept in scratch.
 enum : uint32_t { kErrIndex = 1u, kErrTimeout = 2u };
 

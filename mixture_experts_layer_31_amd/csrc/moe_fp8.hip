@@ -230,11 +230,15 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QArgs p) {
 // Token quantiser for activations contracted over tokens (the weight-gradient
 // operands): one workgroup per 128-token step of an expert segment x 128
 // columns.  The tile is loaded with whole 256-byte row segments per sixteen
-// lanes into LDS, its 32-byte column blocks XOR-swizzled by row; then each
-// thread takes one column and 64 consecutive tokens, four tokens per
-// ds_read_b64_tr_b16 (a sixteen-lane group reads a 4-token x 16-column block
-// and lane i receives column i).  The other 64 tokens of the column are in
-// lane ^ 16, so the 128-token amax is one shuffle away.
+// lanes into LDS (streaming loads: each input row is read once), its 32-byte
+// column blocks XOR-swizzled by row; then each thread takes one column and 64
+// consecutive tokens, four tokens per ds_read_b64_tr_b16 (a sixteen-lane group
+// reads a 4-token x 16-column block and lane i receives column i).  The other
+// 64 tokens of the column are in lane ^ 16, so the 128-token amax is one
+// shuffle away.  The codes go back through the same LDS tile as 128 rows of
+// 128 bytes (one per column, 16-byte chunks XOR-swizzled by row), so each
+// wave's store covers eight whole 128-byte output rows instead of 16-byte
+// pieces of 32 rows.
 template <bool MX>
 __global__ void __launch_bounds__(256) quant_tokens_kernel(QArgs p) {
   __shared__ __attribute__((aligned(16))) char tile[128 * 256];
@@ -257,7 +261,7 @@ __global__ void __launch_bounds__(256) quant_tokens_kernel(QArgs p) {
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int r = it * 16 + rw;
-      raw[it] = r < valid ? *reinterpret_cast<const uint4*>(p.in + size_t(r0 + r) * p.cols + c0 + 8 * l16)
+      raw[it] = r < valid ? load16_nt(p.in + size_t(r0 + r) * p.cols + c0 + 8 * l16)
                           : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
@@ -306,11 +310,21 @@ __global__ void __launch_bounds__(256) quant_tokens_kernel(QArgs p) {
       packed[2 * i + 1] = pack_e4m3x4(y[4], y[5], y[6], y[7]);
     }
   }
-  uint4* dst = reinterpret_cast<uint4*>(p.out + size_t(c0 + q) * p.out_ld + slot0 + h * 64);
+  if (h == 0) p.sc[size_t(slot0 / 128) * p.sc_ld + c0 + q] = entry;
+  // codes of column q, tokens 64h .. 64h + 63: chunks 4h .. 4h + 3 of LDS row q
+  auto oat = [&](int row, int ch) { return row * 128 + ((ch ^ (row & 7)) << 4); };
+  __syncthreads();  // every wave is done reading the input tile
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    dst[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
-  if (h == 0) p.sc[size_t(slot0 / 128) * p.sc_ld + c0 + q] = entry;
+    *reinterpret_cast<uint4*>(tile + oat(q, 4 * h + i)) =
+        make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {  // 128 rows x 8 chunks, eight lanes per row
+    const int id = threadIdx.x + 256 * u, row = id >> 3, ch = id & 7;
+    *reinterpret_cast<uint4*>(p.out + size_t(c0 + row) * p.out_ld + slot0 + 16 * ch) =
+        *reinterpret_cast<const uint4*>(tile + oat(row, ch));
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -53,20 +53,11 @@ __device__ __forceinline__ void load8(const float* p, size_t i8, float (&f)[8]) 
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
-// Streaming forms for rows touched exactly once per pass: a nontemporal access
-// keeps the row out of the caches' working set.  Measured on gfx950 at the 30B
-// shape: streaming loads take the top-8 gather-reduce from 5.0 to 6.2 TB/s; the
-// dispatch keeps plain stores (streaming ones measured slower there: 5.6 -> 5.2
-// TB/s, the next kernel reading the rows back).
-typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load16_nt(const void* p) {
-  const nt_u32x4 v = __builtin_nontemporal_load(static_cast<const nt_u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ void store16_nt(void* p, const uint4& a) {
-  const nt_u32x4 v = {a.x, a.y, a.z, a.w};
-  __builtin_nontemporal_store(v, static_cast<nt_u32x4*>(p));
-}
+// Streaming forms (load16_nt, store16_nt in moe_common.h) for rows touched
+// exactly once per pass.  Measured on gfx950 at the 30B shape: streaming loads
+// take the top-8 gather-reduce from 5.0 to 6.2 TB/s; the dispatch keeps plain
+// stores (streaming ones measured slower there: 5.6 -> 5.2 TB/s, the next
+// kernel reading the rows back).
 __device__ __forceinline__ void load8_nt(const uint16_t* p, size_t i8, float (&f)[8]) {
   unpack8(load16_nt(reinterpret_cast<const uint4*>(p) + i8), f);
 }
