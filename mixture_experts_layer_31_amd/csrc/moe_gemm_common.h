@@ -359,19 +359,28 @@ __device__ __forceinline__ bf16x8 frag_w(const char* tile, int row, int kk, int 
   return *reinterpret_cast<const bf16x8*>(tile + row * 128 + ((chunk ^ swz_row<128>(row)) << 4));
 }
 
+// Sub-steps of the wide loop over which the next k-step's loads are issued:
+// half in the first, half in the second, so the last of them still has three
+// sub-steps to arrive.  Measured at the 30B and 235B shapes against a quarter
+// in each sub-step (the last quarter had one sub-step: W1+SwiGLU 0.97 -> 0.89
+// ms and 3.22 -> 2.96 ms, W2 -3 to -6%), against all of them in the first
+// sub-step (-2 to -3% only) and against thirds, or halves in the first and third.
+constexpr int kWideIssueSub = 2;
+
 // Wide-row main loop: bf16 operands in 128-byte rows (64 k per step), two
 // stages.  Each step waits for its own loads and meets every wave at the
 // barrier (after which the other stage is free); its four 16-deep sub-steps
-// then each run their MFMAs while the next sub-step's fragments are read and a
-// quarter of the next step's loads is issued into the free stage.  A and B are
-// both k-contiguous.
+// then each run their MFMAs while the next sub-step's fragments are read, and
+// the first kWideIssueSub of them also issue a share of the next step's loads
+// into the free stage.  A and B are both k-contiguous.
 template <int BM, int BN, int WGM, int WGN, int ACT, class SA, class SB>
 __device__ __forceinline__ void mainloop_w(char* smem, const SA& sa, const SB& sb, int ktiles,
                                            f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int wave,
                                            int lane) {
   constexpr int WM = BM / WGM, WN = BN / WGN, WMT = WM / 32, WNT = WN / 32;
   constexpr int A_BYTES = BM * 128, STAGE = (BM + BN) * 128;
-  constexpr int NI = SA::NI + SB::NI, NQ = (NI + 3) / 4;  // DMA instructions per sub-step
+  constexpr int NI = SA::NI + SB::NI;
+  constexpr int NQW = (NI + kWideIssueSub - 1) / kWideIssueSub;  // DMA instructions per issuing sub-step
   static_assert(ACT >= 0 && ACT <= WMT, "active blocks within the wave tile");
   const int wm = wave / WGN, wn = wave % WGN;
   const uint32_t base = lds_addr(smem);
@@ -405,7 +414,8 @@ __device__ __forceinline__ void mainloop_w(char* smem, const SA& sa, const SB& s
     load(ta, 0, f[0]);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      if (next) issue((kt + 1) & 1, kt + 1, kk * NQ, (kk + 1) * NQ);
+      if (next && kk < kWideIssueSub)
+        issue((kt + 1) & 1, kt + 1, kk * NQW, kk + 1 == kWideIssueSub ? NI : (kk + 1) * NQW);
       if (kk < 3) load(ta, kk + 1, f[(kk + 1) & 1]);
       mma(f[kk & 1]);
       if (kk < 3) interleave_mfma_ds<NMF, NDS>();
