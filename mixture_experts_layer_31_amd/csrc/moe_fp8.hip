@@ -245,11 +245,7 @@ __global__ void __launch_bounds__(256) quant_tokens_kernel(QArgs p) {
   const int ctiles = p.cols / 128;
   const int rt = blockIdx.x / ctiles, ct = blockIdx.x % ctiles;
   if (rt >= p.tstart[p.E]) return;
-  int lo = 0, hi = p.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.tstart[mid] <= rt) lo = mid; else hi = mid;
-  }
+  const int lo = tile_expert(p.tstart, p.E, 1, rt);
   const int r0 = p.offsets[lo] + (rt - p.tstart[lo]) * 128;
   const int valid = min(128, p.offsets[lo + 1] - r0);
   const int slot0 = rt * 128, c0 = ct * 128;
@@ -608,12 +604,9 @@ __device__ __forceinline__ void f8_grouped_tile(const F8Args& p, int l, char* sm
   constexpr int BM = TL::BM, BN = TL::BN, WN = TL::WN, WAVES = TL::WAVES;
   static_assert(EPI != EPI_SWIGLU || TL::WNT % 2 == 0, "SwiGLU pairs gate/up sub-tiles");
   constexpr int ROWB = MX ? 128 : 64;  // MX: 128-element loop; blockwise: the 64-element ring
-  int mt_g, nt, lo = 0, hi = p.E;
+  int mt_g, nt, lo;
   if (p.nmajor) {  // expert e owns flat tiles [tstart[e] * ntn, tstart[e + 1] * ntn)
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.tstart[mid] * p.ntn <= l) lo = mid; else hi = mid;
-    }
+    lo = tile_expert(p.tstart, p.E, p.ntn, l);
     const int t0 = p.tstart[lo], mte = p.tstart[lo + 1] - t0;
     const int local = l - t0 * p.ntn;
     nt = local / mte;
@@ -621,10 +614,7 @@ __device__ __forceinline__ void f8_grouped_tile(const F8Args& p, int l, char* sm
   } else {
     mt_g = l / p.ntn;
     nt = l - mt_g * p.ntn;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.tstart[mid] <= mt_g) lo = mid; else hi = mid;
-    }
+    lo = tile_expert(p.tstart, p.E, 1, mt_g);
   }
   const int e = lo;
   const int e0 = p.offsets[e];

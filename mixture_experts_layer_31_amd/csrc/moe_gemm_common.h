@@ -62,6 +62,30 @@ __device__ __forceinline__ ExpertTile expert_tile(const int32_t* eorder, int l, 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
+// The expert of flat tile l is the last e in [0, E) with tile_start[e] * u <= key
+// (u = ntn, key = l for n-tiles outer; u = 1, key = the m-tile otherwise):
+// tile_start is non-decreasing from 0, so e = #{e : tile_start[e] * u <= key} - 1.
+// With E < 192 every lane loads its three entries at once and the wave counts
+// them with ballots: one memory round trip at each tile's start instead of a
+// chain of log2(E) dependent loads (30B W2 -2%, W1 dgrad -1%).  Called by whole
+// waves in uniform control flow.
+__device__ __forceinline__ int tile_expert(const int32_t* ts, int E, int u, int key) {
+  if (E < 192) {
+    const int lane = threadIdx.x & 63;
+    const int v0 = ts[min(lane, E)], v1 = ts[min(lane + 64, E)], v2 = ts[min(lane + 128, E)];
+    const int n = __popcll(__ballot(lane < E && v0 * u <= key)) +
+                  __popcll(__ballot(lane + 64 < E && v1 * u <= key)) +
+                  __popcll(__ballot(lane + 128 < E && v2 * u <= key));
+    return n - 1;
+  }
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (ts[mid] * u <= key) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 // Raw buffer resource over [base, base + bytes): loads at byte offsets >= bytes return 0.
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);

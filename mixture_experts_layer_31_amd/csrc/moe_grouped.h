@@ -36,12 +36,9 @@ struct TileCoord {
 template <int BM>
 __device__ __forceinline__ TileCoord decode_tile(const GroupedArgs& p, int l) {
   TileCoord c;
-  int lo = 0, hi = p.E;
+  int lo;
   if (p.nmajor) {  // expert e owns flat tiles [tile_start[e] * ntn, tile_start[e + 1] * ntn)
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.tile_start[mid] * p.ntn <= l) lo = mid; else hi = mid;
-    }
+    lo = tile_expert(p.tile_start, p.E, p.ntn, l);
     const int t0 = p.tile_start[lo], mte = p.tile_start[lo + 1] - t0;
     const int local = l - t0 * p.ntn;
     c.nt = local / mte;
@@ -49,10 +46,7 @@ __device__ __forceinline__ TileCoord decode_tile(const GroupedArgs& p, int l) {
   } else {
     c.mt_g = l / p.ntn;
     c.nt = l - c.mt_g * p.ntn;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.tile_start[mid] <= c.mt_g) lo = mid; else hi = mid;
-    }
+    lo = tile_expert(p.tile_start, p.E, 1, c.mt_g);
   }
   c.e = lo;
   c.e0 = p.offsets[c.e];
