@@ -60,7 +60,8 @@ constexpr int kXcds = 8;
 constexpr uint64_t kWaitTicks = 2000000;  // 20 ms of the 100 MHz real-time counter per wait
 constexpr uint64_t kTestWaitTicks = 100;  // 1 us
 enum : int { kItemChunk = 0, kItemW1 = 1, kItemW2 = 2 };
-using TileQ = Tile<256, 256, 2, 4, 5>;
+// the wide two-stage 128-byte-row loop of the per-step forward GEMMs
+using TileQ = Tile<256, 256, 2, 4, 2, true>;
 
 // ctrl words: tickets [8], totals [8], table bases [8], row bounds R [9],
 // dispatch-item bases CB [9]
