@@ -149,8 +149,13 @@ def clock_summary(args):
         by[d][r["Counter_Name"]] = float(r["Counter_Value"])
         meta[d] = r
     agg = collections.defaultdict(list)
-    for n, r in name_rows(list(meta.values())):
-        if n == "copyBuffer":
+    named = {int(r["Dispatch_Id"]): n for n, r in name_rows(list(meta.values()))}
+    for d, r in meta.items():
+        # kernels without a layer-step name (the FP8 GEMMs and quantisers) keep
+        # their own, without namespace and argument list
+        n = named.get(d) or "`" + re.sub(r"^void |moe::|\(anonymous namespace\)::|gemm::|\(.*\)$",
+                                         "", r["Kernel_Name"]) + "`"
+        if n == "copyBuffer" or "copyBuffer" in n:
             continue
         c = by[int(r["Dispatch_Id"])]
         dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
