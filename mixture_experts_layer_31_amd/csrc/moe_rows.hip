@@ -215,10 +215,14 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_wide_kernel(
 // wave + 4, ..., so each copy is written contiguously by one wave (235B
 // shape: 227 -> 218 us against every thread writing its chunk of every copy;
 // the 30B shape is unchanged).
-template <int CPL>
+// With QM (FP8 forward modes) every wave also quantises the row along D (a
+// 128-column group is 16 consecutive lanes' chunks) and writes the codes and
+// scale entries of its copies, as dispatch_kernel does.
+template <int CPL, int QM>
 __global__ void __launch_bounds__(kRowThreads) dispatch_rows_kernel(
     const uint16_t* __restrict__ rows, int T, int K, int D, const int32_t* __restrict__ pos,
-    const float* __restrict__ topk_w, float* __restrict__ wperm, uint16_t* __restrict__ dst) {
+    const float* __restrict__ topk_w, float* __restrict__ wperm, uint16_t* __restrict__ dst,
+    uint8_t* __restrict__ qcodes, uint32_t* __restrict__ qsc, int N) {
   constexpr int WAVES = kRowThreads / 64;
   const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (t >= T) return;
@@ -227,12 +231,30 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_rows_kernel(
   uint4 v[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) v[j] = src[64 * j];
+  uint2 codes[QM != QM_NONE ? CPL : 1];
+  uint32_t entry[QM != QM_NONE ? CPL : 1];
+  if constexpr (QM != QM_NONE) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      float f[8];
+      unpack8(v[j], f);
+      codes[j] = quantise8<QM>(f, lane, entry[j]);
+    }
+  }
   for (int k = wave; k < K; k += WAVES) {
     const int q = prow[k];
     if (q < 0) continue;
     uint4* d = reinterpret_cast<uint4*>(dst) + (size_t(q) * D) / 8 + lane;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) d[64 * j] = v[j];
+    if constexpr (QM != QM_NONE) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+        *reinterpret_cast<uint2*>(qcodes + size_t(q) * D + 8 * c) = codes[j];
+        if ((c & 15) == 0) qsc[size_t(c >> 4) * N + q] = entry[j];
+      }
+    }
     if (wperm != nullptr && lane == 0) wperm[q] = topk_w[size_t(t) * K + k];
   }
 }
@@ -454,6 +476,13 @@ int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool i
     ACT* dst = reinterpret_cast<ACT*>(scratch + dst_off);
     const int N = d.T * d.K;
     if constexpr (std::is_same<IO, uint16_t>::value && std::is_same<ACT, uint16_t>::value) {
+      if (qmode != 0 && d.D == 2048) {  // the FP8 forward modes at the 30B shape
+        if (qmode == 1)
+          dispatch_rows_kernel<4, QM_MX><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, topk_w, wperm, dst, qcodes, qsc, N);
+        else
+          dispatch_rows_kernel<4, QM_BLOCK><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, topk_w, wperm, dst, qcodes, qsc, N);
+        return 0;
+      }
       if (qmode == 1) {
         dispatch_kernel<IO, ACT, QM_MX><<<row_blocks(d), kRowThreads, 0, s>>>(
             src, d.T, d.K, d.D, pos, topk_w, wperm, dst, qcodes, qsc, N);
@@ -469,9 +498,9 @@ int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool i
     if constexpr (std::is_same<IO, uint16_t>::value && std::is_same<ACT, uint16_t>::value) {
       if (d.D == 2048 || d.D == 4096) {
         if (d.D == 2048)
-          dispatch_rows_kernel<4><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, topk_w, wperm, dst);
+          dispatch_rows_kernel<4, QM_NONE><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, topk_w, wperm, dst, nullptr, nullptr, N);
         else
-          dispatch_rows_kernel<8><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, topk_w, wperm, dst);
+          dispatch_rows_kernel<8, QM_NONE><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, topk_w, wperm, dst, nullptr, nullptr, N);
         return 0;
       }
     }
