@@ -160,31 +160,41 @@ def main():
     if status != moe.MOE_OK:
         raise RuntimeError(moe.strerror(status))
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    def timed_steps(profile: bool):
+        """K steps between a start and a stop event (fwd/bwd split by events between
+        them); with `profile`, the library also brackets every kernel with events."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        if profile:
+            moe.moe_profile_reset()
+            moe.moe_profile_enable(True)
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for a, b, c in ev:
+            a.record(stream)
+            L.fwd()
+            b.record(stream)
+            L.bwd()
+            c.record(stream)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        moe.moe_profile_enable(False)
+        kern = moe.moe_profile_collect() if profile else {}
+        status = L.check()
+        if status != moe.MOE_OK:
+            raise RuntimeError(moe.strerror(status))
+        return (start.elapsed_time(stop) / args.steps,
+                sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps,
+                sum(b.elapsed_time(c) for _, b, c in ev) / args.steps, kern)
+
+    # the step time is taken without per-kernel events (they add about 80 us to a
+    # 30B step); the same K steps then run again with them for the per-kernel
+    # durations behind the roofline entry
+    ms_step, fwd_ms, bwd_ms, _ = timed_steps(False)
+    kernels, ms_step_profiled = {}, None
     if not args.no_profile:
-        moe.moe_profile_reset()
-        moe.moe_profile_enable(True)
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for a, b, c in ev:
-        a.record(stream)
-        L.fwd()
-        b.record(stream)
-        L.bwd()
-        c.record(stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    moe.moe_profile_enable(False)
-    kernels = {} if args.no_profile else moe.moe_profile_collect()
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / args.steps
-    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
-    bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
-    status = L.check()
-    if status != moe.MOE_OK:
-        raise RuntimeError(moe.strerror(status))
+        ms_step_profiled, _, _, kernels = timed_steps(True)
 
     # the overlapped one-launch forward against the one-kernel-per-step forward
     f5 = None
@@ -282,6 +292,7 @@ def main():
         "peak_tflops": round(peak, 1),
         "frac_mfma_peak": round(tflops / peak, 4),
         "roofline": roof,
+        "ms_per_step_profiled": None if ms_step_profiled is None else round(ms_step_profiled, 4),
         "f5_overlap": f5,
         "router": router,
         "kernels": per_kernel,
