@@ -214,7 +214,8 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_wide_kernel(
 // come from the cache) and writes whole destination rows, copies k = wave,
 // wave + 4, ..., so each copy is written contiguously by one wave (235B
 // shape: 227 -> 218 us against every thread writing its chunk of every copy;
-// the 30B shape is unchanged).
+// the 30B shape is unchanged).  Used when every wave has a copy (K >= 4): with
+// one pair per token three waves of four would idle.
 // With QM (FP8 forward modes) every wave also quantises the row along D (a
 // 128-column group is 16 consecutive lanes' chunks) and writes the codes and
 // scale entries of its copies, as dispatch_kernel does.
@@ -476,7 +477,7 @@ int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool i
     ACT* dst = reinterpret_cast<ACT*>(scratch + dst_off);
     const int N = d.T * d.K;
     if constexpr (std::is_same<IO, uint16_t>::value && std::is_same<ACT, uint16_t>::value) {
-      if (qmode != 0 && d.D == 2048) {  // the FP8 forward modes at the 30B shape
+      if (qmode != 0 && d.D == 2048 && d.K >= kRowThreads / 64) {  // FP8 forward, 30B shape
         if (qmode == 1)
           dispatch_rows_kernel<4, QM_MX><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, topk_w, wperm, dst, qcodes, qsc, N);
         else
@@ -496,7 +497,7 @@ int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool i
     }
     if (qmode != 0) return int(MOE_EUNSUPPORTED);
     if constexpr (std::is_same<IO, uint16_t>::value && std::is_same<ACT, uint16_t>::value) {
-      if (d.D == 2048 || d.D == 4096) {
+      if ((d.D == 2048 || d.D == 4096) && d.K >= kRowThreads / 64) {
         if (d.D == 2048)
           dispatch_rows_kernel<4, QM_NONE><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, topk_w, wperm, dst, nullptr, nullptr, N);
         else
