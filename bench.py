@@ -49,10 +49,19 @@ def gemm_flops(cfg) -> dict:
 
 
 def row_bytes(cfg, b=2) -> dict:
-    """Algorithmic HBM bytes per launch of the row movers."""
+    """Algorithmic HBM bytes per launch of the row movers (bf16 rows).  In the FP8
+    forward modes the dispatch also writes the e4m3 row codes of x_perm and one
+    4-byte scale entry per 128 columns; in every FP8 mode the combine-backward
+    writes those of dYw."""
     T, N, D = cfg.T, cfg.N, cfg.D
-    return {"dispatch": T * D * b + N * D * b + 2 * N * 4 + N * 4,
+    codes = N * D + N * (D // 128) * 4
+    fwd_q = cfg.mode in (4, 5)   # MXFP8, blockwise FP8 in both passes
+    bwd_q = cfg.mode in (3, 4, 5)
+    return {"dispatch": T * D * b + N * D * b + 2 * N * 4 + N * 4 + (codes if fwd_q else 0),
             "combine": N * D * b + T * D * b + N * 8,
+            # dy once, each pair's expert-output row read and its w*dy row written,
+            # pos and topk_w read, dtopk_w written
+            "dispatch_dy": T * D * b + 2 * N * D * b + 3 * N * 4 + (codes if bwd_q else 0),
             "unpermute": N * D * b + T * D * b + N * 4}
 
 
