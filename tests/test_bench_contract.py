@@ -1,0 +1,47 @@
+"""Host-side checks of bench.py's contract that need no GPU: the refusal of more
+than one GPU (the layer's expert-parallel exchange is not part of this library),
+and the algorithmic byte counts behind the reported HBM rates."""
+import os
+import subprocess
+import sys
+
+import moe_inputs as mi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "--gpus must be 1" in r.stderr
+    assert r.stdout.strip() == ""  # no JSON line
+
+
+def _bench_module():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_for_test", os.path.join(ROOT, "bench.py"))
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+def test_row_mover_bytes_follow_the_definitions():
+    b = _bench_module()
+    cfg = mi.CONFIGS["30b"]
+    T, N, D = cfg.T, cfg.N, cfg.D
+    rb = b.row_bytes(cfg)
+    # dispatch: x once, every pair's row written, pos read, wperm written, topk_w read
+    assert rb["dispatch"] == 2 * T * D + 2 * N * D + 3 * N * 4
+    # combine / un-permute: every pair's row read, the token row written, indices (+ weights)
+    assert rb["combine"] == 2 * N * D + 2 * T * D + N * 8
+    assert rb["unpermute"] == 2 * N * D + 2 * T * D + N * 4
+    # combine-backward: dy once, pair rows read (O) and written (w * dy), 3 index/weight arrays
+    assert rb["dispatch_dy"] == 2 * T * D + 4 * N * D + 3 * N * 4
+    # the FP8 forward modes' dispatch also writes e4m3 codes and one 4-byte entry per 128 columns
+    mx = mi.CONFIGS["30b_mxfp8"]
+    assert b.row_bytes(mx)["dispatch"] - rb["dispatch"] == N * D + N * (D // 128) * 4
+    fb = mi.CONFIGS["235b_fp8bwd"]
+    assert b.row_bytes(fb)["dispatch"] == b.row_bytes(mi.CONFIGS["235b"])["dispatch"]
+    assert (b.row_bytes(fb)["dispatch_dy"] - b.row_bytes(mi.CONFIGS["235b"])["dispatch_dy"]
+            == fb.N * fb.D + fb.N * (fb.D // 128) * 4)
