@@ -147,10 +147,12 @@ int run_grouped(const moe_desc& d, const Layout& L, GroupedArgs a, int N, const 
   a.tile_start = reinterpret_cast<const int32_t*>(scratch + L.tiles[tile_index(TL::BM)]);
   a.E = d.E;
   a.ntn = N / TL::BN;
-  // n-tiles outer within an expert for the plain stores (W2, W1 dgrad: a round's
-  // tiles then span all of an expert's m-tiles and fewer n-tiles, 3-6% faster);
-  // m-tiles outer for the SwiGLU epilogues (as fast or faster)
-  a.nmajor = EPI == EPI_STORE;
+  // n-tiles outer within an expert for the plain stores and W1 + SwiGLU (W2, W1
+  // dgrad: a round's tiles then span all of an expert's m-tiles and fewer
+  // n-tiles, 3-6% faster; W1 + SwiGLU: 1% at the 235B shape since its loads go
+  // out in two sub-steps, equal at 30B); m-tiles outer for the SwiGLU backward
+  // (n-tiles outer measured -1.6% at 30B and +1.6% at 235B there)
+  a.nmajor = EPI == EPI_STORE || EPI == EPI_SWIGLU;
   const long long grid = (long long)max_mtiles(d, TL::BM) * a.ntn;
   if (grid <= 0) return MOE_OK;
   int resident;
