@@ -121,7 +121,7 @@ def stats_summary(args):
     tot = sum(float(r["TotalDurationNs"]) for r in rows)
     lines = [f"# {args.config} layer: per-kernel time", "",
              f"Workload: {args.workload or args.config}.", "",
-             "Commands (from the repository root on the GPU box):", ""]
+             "Commands (run from the repository root on the MI355X):", ""]
     lines += [f"    {c.strip()}" for c in args.commands.split(";") if c.strip()]
     lines += ["", "## Kernel statistics (rocprofv3 --kernel-trace --stats)", "",
               "Every launch of the run, warm-up included (the bench also times the overlapped "
@@ -163,7 +163,7 @@ def clock_summary(args):
                        c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)))
     lines = [f"# {args.config} layer: shader clock and MFMA busy per kernel", "",
              f"Workload: {args.workload or args.config}.", "",
-             "Commands (from the repository root on the GPU box):", ""]
+             "Commands (run from the repository root on the MI355X):", ""]
     lines += [f"    {c.strip()}" for c in args.commands.split(";") if c.strip()]
     lines += ["", "GRBM counters are summed over the 8 XCD instances, so the clock is "
               "GRBM_COUNT / 8 / duration; MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES / "
@@ -234,7 +234,7 @@ def main():
     lines = [f"# {args.config} layer, bf16: per-kernel time and HBM traffic", "",
              f"Workload: {args.workload or args.config}.  GEMM source hash (sha256 of "
              f"{', '.join(os.path.basename(p) for p in GEMM_SOURCES)}, first 16 hex digits): "
-             f"`{h}`.", "", "Commands (from the repository root on the GPU box):", ""]
+             f"`{h}`.", "", "Commands (run from the repository root on the MI355X):", ""]
     lines += [f"    {c.strip()}" for c in args.commands.split(";") if c.strip()]
     lines += ["", "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
               f"'timed avg' leaves out the first {args.skip} launches of each kernel (the bench's "
