@@ -135,7 +135,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's layer only: the expert-parallel exchange between "
-              "GPUs is outside this build, so --gpus must be 1", file=sys.stderr)
+              "GPUs is outside this library, so --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

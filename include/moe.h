@@ -78,7 +78,7 @@ enum moe_status {
   MOE_EINVAL = -1,       /* null pointer, non-positive or inconsistent sizes, bad mode */
   MOE_ESCRATCH = -2,     /* scratch_bytes / wprep_bytes smaller than required */
   MOE_EALIGN = -3,       /* a buffer is not 16-byte aligned */
-  MOE_EUNSUPPORTED = -4, /* valid request this build cannot run (mode or shape) */
+  MOE_EUNSUPPORTED = -4, /* valid request this library cannot run (mode or shape) */
   MOE_EHIP = -5,         /* a HIP launch or runtime call failed */
   MOE_EINDEX = -6,       /* (device) a topk_idx entry was outside [0, E) */
   MOE_ETIMEOUT = -7      /* (device) a bounded wait in a persistent kernel expired */

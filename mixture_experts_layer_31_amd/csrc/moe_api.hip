@@ -27,7 +27,7 @@ int check_desc(const moe_desc* d) {
   return MOE_OK;
 }
 
-// Modes whose kernels exist in this build, and their shape requirements.
+// Modes whose kernels exist in this library, and their shape requirements.
 int check_built(const moe_desc* d) {
   if (fp8_mode(d->mode) && (d->D % 256 != 0 || d->F % 256 != 0)) return MOE_EUNSUPPORTED;
   return MOE_OK;
@@ -125,7 +125,7 @@ const char* moe_strerror(int status) {
     case MOE_EINVAL: return "invalid argument (null pointer, bad sizes, bad mode or flags)";
     case MOE_ESCRATCH: return "scratch or wprep buffer smaller than required";
     case MOE_EALIGN: return "buffer not 16-byte aligned";
-    case MOE_EUNSUPPORTED: return "mode or shape not supported by this build";
+    case MOE_EUNSUPPORTED: return "mode or shape not supported by this library";
     case MOE_EHIP: return "HIP launch or runtime error";
     case MOE_EINDEX: return "topk_idx entry outside [0, E)";
     case MOE_ETIMEOUT: return "bounded wait in a persistent kernel expired";
