@@ -294,6 +294,18 @@ int launch_bwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, con
                 : run_wgrad_any<false>(d, L, a, "gemm_w2_wgrad", scratch, s);
     if (rc) return rc;
   }
+  {  // W1 wgrad: dW1[e] = sum_r dH[r] x_perm[r]^T (before the W1 dgrad, so that the
+     // un-permute reads dX_perm right after it is written)
+    WgradArgs a{};
+    a.M = 2 * F;
+    a.N = D;
+    a.A = reinterpret_cast<const uint16_t*>(scratch + L.dh);
+    a.B = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
+    a.C = dw1;
+    rc = dw_f32 ? run_wgrad_any<true>(d, L, a, "gemm_w1_wgrad", scratch, s)
+                : run_wgrad_any<false>(d, L, a, "gemm_w1_wgrad", scratch, s);
+    if (rc) return rc;
+  }
   {  // W1 dgrad: dX_perm = dH W1[e], W1[e] is [2F, D] = [K, N]
     GroupedArgs a{};
     a.K = 2 * F;
@@ -307,17 +319,6 @@ int launch_bwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, con
     a.out = reinterpret_cast<uint16_t*>(scratch + L.dxperm);
     a.ldo = D;
     rc = run_grouped_any<true, EPI_STORE>(d, L, a, D, "gemm_w1_dgrad", scratch, s);
-    if (rc) return rc;
-  }
-  {  // W1 wgrad: dW1[e] = sum_r dH[r] x_perm[r]^T
-    WgradArgs a{};
-    a.M = 2 * F;
-    a.N = D;
-    a.A = reinterpret_cast<const uint16_t*>(scratch + L.dh);
-    a.B = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
-    a.C = dw1;
-    rc = dw_f32 ? run_wgrad_any<true>(d, L, a, "gemm_w1_wgrad", scratch, s)
-                : run_wgrad_any<false>(d, L, a, "gemm_w1_wgrad", scratch, s);
     if (rc) return rc;
   }
   return MOE_OK;
