@@ -1123,43 +1123,59 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   rc = mx ? run_f8_wgrad<true>(d, L, w, "gemm_w2_wgrad", scratch, s)
           : run_f8_wgrad<false>(d, L, w, "gemm_w2_wgrad", scratch, s);
   if (rc) return rc;
-  // W1 dgrad on dH's row codes
-  F8Args b{};
-  b.K = 2 * F;
-  b.A = f.qrow;
-  b.SA = f.qrow_sc;
-  b.sa_ld = N;
-  b.sa_bytes = uint32_t(size_t(2 * F / 128) * N * 4);
-  b.B = reinterpret_cast<const uint8_t*>(wprep + W.w1t);
-  b.b_bstride = int64_t(D) * 2 * F;
-  b.SB = reinterpret_cast<const uint32_t*>(wprep + W.w1t_sc);
-  b.sb_ld = D;
-  b.sb_bstride = int64_t(2 * F / 128) * D;
-  b.sb_bytes = uint32_t(size_t(2 * F / 128) * D * 4);
-  b.F = F;
-  b.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.dxperm), D, nullptr, nullptr, F};
-  rc = mx ? run_f8_grouped<true, EPI_STORE>(d, L, b, D, "gemm_w1_dgrad", scratch, s)
-          : run_f8_grouped<false, EPI_STORE>(d, L, b, D, "gemm_w1_dgrad", scratch, s);
-  if (rc) return rc;
-  // W1 wgrad over tokens
-  if ((rc = quant_tokens(d, L, dh, 2 * F, mx, f.qt1, f.qt1_sc, "quant_dh_tokens", scratch, s))) return rc;
-  if ((rc = quant_tokens(d, L, xp, D, mx, f.qt2, f.qt2_sc, "quant_x_tokens", scratch, s))) return rc;
-  F8Args v{};
-  v.M = 2 * F;
-  v.N = D;
-  v.A = f.qt1;
-  v.lda = npad;
-  v.SA = f.qt1_sc;
-  v.sa_ld = 2 * F;
-  v.sa_bytes = uint32_t(f.qt_sc_bytes);
-  v.B = f.qt2;
-  v.ldb = npad;
-  v.SB = f.qt2_sc;
-  v.sb_ld = D;
-  v.sb_bytes = uint32_t(f.qt_sc_bytes);
-  v.C = dw1;
-  return mx ? run_f8_wgrad<true>(d, L, v, "gemm_w1_wgrad", scratch, s)
+  // W1 wgrad over tokens and W1 dgrad on dH's row codes.  Blockwise runs the
+  // wgrad first, so that the un-permute reads dX_perm right after it is written
+  // (235B fp8_bwd backward -0.8%; the token quantisers leave dH's row codes
+  // alone); MXFP8 keeps the dgrad first, right after the W2 dgrad wrote those
+  // codes (0.5% faster there).
+  auto w1_wgrad = [&]() -> int {
+    if ((rc = quant_tokens(d, L, dh, 2 * F, mx, f.qt1, f.qt1_sc, "quant_dh_tokens", scratch, s))) return rc;
+    if ((rc = quant_tokens(d, L, xp, D, mx, f.qt2, f.qt2_sc, "quant_x_tokens", scratch, s))) return rc;
+    F8Args v{};
+    v.M = 2 * F;
+    v.N = D;
+    v.A = f.qt1;
+    v.lda = npad;
+    v.SA = f.qt1_sc;
+    v.sa_ld = 2 * F;
+    v.sa_bytes = uint32_t(f.qt_sc_bytes);
+    v.B = f.qt2;
+    v.ldb = npad;
+    v.SB = f.qt2_sc;
+    v.sb_ld = D;
+    v.sb_bytes = uint32_t(f.qt_sc_bytes);
+    v.C = dw1;
+    rc = mx ? run_f8_wgrad<true>(d, L, v, "gemm_w1_wgrad", scratch, s)
             : run_f8_wgrad<false>(d, L, v, "gemm_w1_wgrad", scratch, s);
+    if (rc) return rc;
+    return MOE_OK;
+  };
+  auto w1_dgrad = [&]() -> int {
+    // W1 dgrad on dH's row codes
+    F8Args b{};
+    b.K = 2 * F;
+    b.A = f.qrow;
+    b.SA = f.qrow_sc;
+    b.sa_ld = N;
+    b.sa_bytes = uint32_t(size_t(2 * F / 128) * N * 4);
+    b.B = reinterpret_cast<const uint8_t*>(wprep + W.w1t);
+    b.b_bstride = int64_t(D) * 2 * F;
+    b.SB = reinterpret_cast<const uint32_t*>(wprep + W.w1t_sc);
+    b.sb_ld = D;
+    b.sb_bstride = int64_t(2 * F / 128) * D;
+    b.sb_bytes = uint32_t(size_t(2 * F / 128) * D * 4);
+    b.F = F;
+    b.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.dxperm), D, nullptr, nullptr, F};
+    rc = mx ? run_f8_grouped<true, EPI_STORE>(d, L, b, D, "gemm_w1_dgrad", scratch, s)
+            : run_f8_grouped<false, EPI_STORE>(d, L, b, D, "gemm_w1_dgrad", scratch, s);
+    return rc;
+  };
+  if (mx) {
+    if ((rc = w1_dgrad())) return rc;
+    return w1_wgrad();
+  }
+  if ((rc = w1_wgrad())) return rc;
+  return w1_dgrad();
 }
 
 }  // namespace moe
