@@ -268,6 +268,18 @@ int launch_bwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, con
                      void* dw1, void* dw2, bool dw_f32, char* scratch, hipStream_t s) {
   const int D = d.D, F = d.F;
   int rc;
+  {  // W2 wgrad: dW2[e] = sum_r dYw_perm[r] A[r]^T (first: the W2 dgrad after it then
+     // finds dYw in the caches, 5% faster at the 30B shape)
+    WgradArgs a{};
+    a.M = D;
+    a.N = F;
+    a.A = reinterpret_cast<const uint16_t*>(scratch + L.dyperm);
+    a.B = reinterpret_cast<const uint16_t*>(scratch + L.a);
+    a.C = dw2;
+    rc = dw_f32 ? run_wgrad_any<true>(d, L, a, "gemm_w2_wgrad", scratch, s)
+                : run_wgrad_any<false>(d, L, a, "gemm_w2_wgrad", scratch, s);
+    if (rc) return rc;
+  }
   {  // W2 dgrad (dA = dYw W2[e], W2[e] is [D, F] = [K, N]) with SwiGLU-backward epilogue
     GroupedArgs a{};
     a.K = D;
@@ -281,17 +293,6 @@ int launch_bwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, con
     a.out = reinterpret_cast<uint16_t*>(scratch + L.dh);
     a.hsave = reinterpret_cast<const uint16_t*>(scratch + L.h);
     rc = run_grouped_any<true, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s);
-    if (rc) return rc;
-  }
-  {  // W2 wgrad: dW2[e] = sum_r dYw_perm[r] A[r]^T
-    WgradArgs a{};
-    a.M = D;
-    a.N = F;
-    a.A = reinterpret_cast<const uint16_t*>(scratch + L.dyperm);
-    a.B = reinterpret_cast<const uint16_t*>(scratch + L.a);
-    a.C = dw2;
-    rc = dw_f32 ? run_wgrad_any<true>(d, L, a, "gemm_w2_wgrad", scratch, s)
-                : run_wgrad_any<false>(d, L, a, "gemm_w2_wgrad", scratch, s);
     if (rc) return rc;
   }
   {  // W1 wgrad: dW1[e] = sum_r dH[r] x_perm[r]^T (before the W1 dgrad, so that the
