@@ -102,12 +102,19 @@ def bf16(a) -> np.ndarray:
     return t.to(torch.bfloat16).to(torch.float64).numpy()
 
 
-def layer(mode, x, topk_idx, topk_w, dy, w1, w2, quantiser=None, store_bf16=True) -> dict:
+def layer(mode, x, topk_idx, topk_w, dy, w1, w2, quantiser=None, store_bf16=True,
+          experts=None) -> dict:
     """Forward and backward of the layer under `mode`'s FP8 recipe.
 
     Returns y [T, D], dx [T, D], dw1 [E, 2F, D], dw2 [E, D, F], dprob [T, K],
     and the permuted-order intermediates h, a, o, dh, dxp with the routing
     (offsets, src) they are ordered by.
+
+    `experts` (a list of expert ids) keeps only the rows routed to those experts
+    (checks at large sizes): every quantiser here works per row, per weight or
+    per expert segment, so those rows are unchanged; y, dx and dprob then hold
+    only those experts' contributions, and dw1, dw2 are [len(experts), ...] in
+    the order given.
     """
     if mode not in MODES:
         raise ValueError(f"mode must be one of {MODES}")
@@ -121,6 +128,13 @@ def layer(mode, x, topk_idx, topk_w, dy, w1, w2, quantiser=None, store_bf16=True
     K = topk_idx.shape[1]
     r = orc.route(topk_idx, E)
     off, src = r["offsets"], r["src"]
+    sel = list(range(E)) if experts is None else [int(e) for e in experts]
+    if experts is not None:
+        keep = np.zeros(E, bool)
+        keep[sel] = True
+        cnt = np.diff(off)
+        src = src[np.repeat(keep, cnt)]
+        off = np.concatenate([[0], np.cumsum(np.where(keep, cnt, 0))])
     tok = src // K
     wp = np.asarray(topk_w, np.float64).reshape(-1)[src]      # routing weight of each row
     N = len(src)
@@ -133,8 +147,8 @@ def layer(mode, x, topk_idx, topk_w, dy, w1, w2, quantiser=None, store_bf16=True
                 out[off[e]:off[e + 1]] = fn(e, slice(off[e], off[e + 1]))
         return out
 
-    W1 = [np.asarray(w1[e], np.float64) for e in range(E)]
-    W2 = [np.asarray(w2[e], np.float64) for e in range(E)]
+    W1 = {e: np.asarray(w1[e], np.float64) for e in sel}
+    W2 = {e: np.asarray(w2[e], np.float64) for e in sel}
     # forward
     xp = x[tok]
     xq = q("fwd_x", xp, "rows") if fwd_q else xp
@@ -164,11 +178,11 @@ def layer(mode, x, topk_idx, topk_w, dy, w1, w2, quantiser=None, store_bf16=True
     At = q("wgrad_a", A, "tokens", off)
     dHt = q("wgrad_dh", dH, "tokens", off)
     xt = q("wgrad_x", xp, "tokens", off)
-    dw1 = np.zeros((E, F2, D))
-    dw2 = np.zeros((E, D, F))
-    for e in range(E):
+    dw1 = np.zeros((len(sel), F2, D))
+    dw2 = np.zeros((len(sel), D, F))
+    for i, e in enumerate(sel):
         s = slice(off[e], off[e + 1])
-        dw2[e] = dYt[s].T @ At[s]
-        dw1[e] = dHt[s].T @ xt[s]
+        dw2[i] = dYt[s].T @ At[s]
+        dw1[i] = dHt[s].T @ xt[s]
     return dict(y=y, dx=dx, dw1=dw1, dw2=dw2, dprob=dprob.reshape(T, K),
                 h=H, a=A, o=O, dh=dH, dxp=dXp, offsets=off, src=src)

@@ -10,6 +10,8 @@
   [rows, contraction] with the contraction of its GEMM last.
 * bf16 storage: rounding the stored intermediates moves the outputs a little,
   but not by much.
+* Expert subsets: restricted to some experts, their rows and weight gradients
+  are bit-identical to the full run's.
 * Format bound: a product of two e4m3-quantised operands differs from the exact
   product by at most sum |a||eb| + |ea||b| + |ea||eb|, where an element's
   encoding error is at most 2^-4 of it (3 mantissa bits) plus half a subnormal
@@ -150,3 +152,15 @@ def test_recipe_stays_near_the_unquantised_layer(inp, mode):
             assert rel == 0.0, (mode, k)
         else:
             assert 1e-4 < rel < 0.2, (mode, k, rel)
+
+
+def test_expert_subset_keeps_those_rows_unchanged(inp):
+    full = _run(inp, "mxfp8", store_bf16=True)
+    sub = fl.layer("mxfp8", inp["x"], inp["topk_idx"], inp["topk_w"], inp["dy"], inp["w1"],
+                   inp["w2"], experts=[2, 0])
+    off = full["offsets"]
+    rows = np.r_[off[0]:off[1], off[2]:off[3]]
+    for k in ("h", "a", "o", "dh", "dxp"):
+        np.testing.assert_array_equal(sub[k], full[k][rows], err_msg=k)
+    np.testing.assert_array_equal(sub["dw1"], full["dw1"][[2, 0]])
+    np.testing.assert_array_equal(sub["dw2"], full["dw2"][[2, 0]])

@@ -287,13 +287,30 @@ def _full_size_fp8(name, ntok, nexp):
     dH = L.view(moe.MOE_VIEW_DH, C)[rows]
     rc, _ = f8.quant_rows(dH, 32 if mx else 128, mx)
     np.testing.assert_array_equal(codes, rc)
+    # two whole expert segments (the least-routed live expert and one other) against the
+    # oracle of the same FP8 recipe: dH and dX_perm rows, and both weight gradients
+    counts = np.bincount(inp["topk_idx"].ravel(), minlength=cfg.E)
+    live = np.nonzero(counts)[0]
+    ex = [int(live[np.argmin(counts[live])]), int(rng.choice(live))]
+    rec = fl.layer(RECIPE[cfg.mode], inp["x"], inp["topk_idx"], inp["topk_w"], inp["dy"],
+                   inp["w1"], inp["w2"], experts=ex)
+    off = r["offsets"]
+    rows = np.concatenate([np.arange(off[e], off[e + 1]) for e in sorted(ex)])
+    rerr = {"dh": rel_err(L.view(moe.MOE_VIEW_DH, C)[rows], rec["dh"]),
+            "dxp": rel_err(L.view(moe.MOE_VIEW_DXPERM, cfg.D)[rows], rec["dxp"])}
+    for i, e in enumerate(ex):
+        rerr[f"dw1[{e}]"] = rel_err(to_host(L.dw1[e]), rec["dw1"][i])
+        rerr[f"dw2[{e}]"] = rel_err(to_host(L.dw2[e]), rec["dw2"][i])
+    print(name, "recipe", counts[ex].tolist(), {k: round(v, 4) for k, v in rerr.items()},
+          flush=True)
+    for k, e in rerr.items():
+        assert e <= TOL_FP8, ("recipe", k, e)
     tok = np.sort(rng.choice(cfg.T, size=ntok, replace=False))
     ref = orc.backward_tokens(inp["dy"], inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"],
                               inp["w2"], tok)
     tt = torch.from_numpy(tok).cuda()
     errs = {k: rel_err(to_host(v), ref[k]) for k, v in
             (("y", L.y[tt]), ("dx", L.dx[tt]), ("dprob", L.dprob[tt]))}
-    counts = np.bincount(inp["topk_idx"].ravel(), minlength=cfg.E)
     for e in rng.choice(np.nonzero(counts)[0], size=nexp, replace=False):
         r1 = np.sort(rng.choice(2 * cfg.F, size=6, replace=False))
         r2 = np.sort(rng.choice(cfg.D, size=6, replace=False))
