@@ -112,7 +112,13 @@ enum moe_status {
 #define MOE_FLAG_RECOMPUTE 0x4u
 
 /* Layer descriptor, passed by host pointer.  Requirements: T >= 0; E, K >= 1;
- * K <= E; E <= 1024; D % 64 == 0 and F % 64 == 0; T * K < 2^31.  T = 0 is a
+ * K <= E; E <= 1024; D % 64 == 0 and F % 64 == 0; T * K < 2^31 (else
+ * MOE_EINVAL).  The kernels address one expert's rows and one expert's weight
+ * matrix through 32-bit buffer ranges, and an expert may receive every routed
+ * pair, so shapes with T * K * max(D, 2F) * s >= 2^31 or 2F * D * s >= 2^31
+ * (s = 4 bytes in MOE_FP32, else 2), or, in the FP8 modes, with
+ * 256 * Npad >= 2^31 (Npad = 128 * floor((T*K + 127*E) / 128)), give
+ * MOE_EUNSUPPORTED instead of wrapping; moe_scratch_bytes then returns 0.  T = 0 is a
  * layer with no tokens: moe_route and moe_fwd leave zero counts and offsets,
  * moe_bwd writes zero dw1 and dw2 (every expert has no tokens), and the [T, ...]
  * buffers (x, y, dy, dx, topk_idx, topk_w, dtopk_w) may be null. */
@@ -124,24 +130,36 @@ typedef struct moe_desc {
 
 /* Size in bytes of the scratch buffer for `d` (host call; 0 if `d` is invalid).
  * The scratch holds the routing metadata (the stable by-expert sort of the
- * routed pairs, the pages' "GPU sorts tokens" in "Why is MoE training
+ * routed pairs: the pages' sorting of tokens by expert, "Why is MoE training
  * communication-bound?") and the intermediates kept between forward and
- * backward (the pages' "GPU-only scratch buffers" instead of intermediate
- * tensors, "How does the fused kernel work?").  Its layout is private. */
+ * backward (the pages keep intermediates in scratch memory that only the GPU
+ * uses rather than in framework tensors, "How does the fused kernel work?").  Its layout is private. */
 size_t moe_scratch_bytes(const moe_desc* d);
 
 /* Size in bytes of the prepared-weight buffer: quantised weight copies for the
  * FP8 modes (each weight in the orientation of each GEMM that reads it), bf16
- * copies for MOE_FP32_BF16GEMM, 0 for MOE_BF16 (where `wprep` may be NULL). */
+ * copies for MOE_FP32_BF16GEMM, 0 for MOE_BF16 (where `wprep` may be NULL).
+ * The FP8 formats are the pages' blockwise FP8 and MXFP8 ("How does the fused
+ * kernel work?"), selected by the precision names of "How do developers use
+ * it?".  Host call; 0 if `d` is invalid. */
 size_t moe_wprep_bytes(const moe_desc* d);
 
 /* Fill `wprep` from w1/w2 (bf16 in the FP8 modes, fp32 in MOE_FP32_BF16GEMM; a
  * no-op returning MOE_OK in MOE_BF16).  Must be called again whenever the
- * weights change. */
+ * weights change.  FP8 modes: every weight is quantised to e4m3 in 128 x 128
+ * blocks (blockwise) or groups of 32 along the contraction (MXFP8), once per
+ * orientation a GEMM reads it in (the weight side of the pages' FP8 kernels,
+ * "How does the fused kernel work?").  w1, w2: [E, 2F, D] and [E, D, F] device
+ * buffers; wprep: device, wprep_bytes >= moe_wprep_bytes(d) (MOE_ESCRATCH).
+ * 16-byte alignment (MOE_EALIGN).  Asynchronous on `stream`. */
 int moe_prepare_weights(const moe_desc* d, const void* w1, const void* w2,
                         void* wprep, size_t wprep_bytes, void* stream);
 
-/* Routing metadata only (moe_fwd runs it itself).  For the flat pair index
+/* Routing metadata only (moe_fwd runs it itself): the pages' sort of the
+ * tokens by destination expert ("Why is MoE training communication-bound?",
+ * the tokens are sorted on the GPU before the exchange), here a stable
+ * counting sort of the routed pairs.  topk_idx: device int32 [T, K], 4-byte aligned; scratch as
+ * in moe_fwd.  For the flat pair index
  * p = t*K + k with expert e = topk_idx[p]:
  *   counts[e] = #{p : idx_p = e}; offsets = exclusive prefix sum, offsets[E]
  *   = number of valid pairs; pos[p] = offsets[e] + #{p' < p : idx_p' = e}
@@ -151,8 +169,11 @@ int moe_route(const moe_desc* d, const int32_t* topk_idx, void* scratch,
               size_t scratch_bytes, void* stream);
 
 /* Device pointers into `scratch` for counts [E], offsets [E+1], pos [T*K] and
- * src [T*K] (src entries past offsets[E] are unspecified).  Host arithmetic
- * only; any output pointer may be NULL. */
+ * src [T*K] (src entries past offsets[E] are unspecified): the routing
+ * metadata of moe_route ("Why is MoE training communication-bound?").  Host
+ * arithmetic only, nothing is read or launched; any output pointer may be
+ * NULL.  Takes the descriptor and scratch size to locate the regions and to
+ * check that the buffer holds them (MOE_ESCRATCH). */
 int moe_routing_view(const moe_desc* d, const void* scratch, size_t scratch_bytes,
                      int32_t** counts, int32_t** offsets, int32_t** pos, int32_t** src);
 
@@ -184,8 +205,11 @@ enum moe_view {
 int moe_scratch_view(const moe_desc* d, const void* scratch, size_t scratch_bytes,
                      int which, void** ptr, size_t* bytes);
 
-/* Forward pass.  Runs the routing step, the dispatch (x -> expert-contiguous
- * rows), expert linear 1 with SwiGLU fused into its epilogue, expert linear 2,
+/* Forward pass of the fused layer of the pages ("How does the fused kernel
+ * work?": dispatch, the two expert linear layers with SwiGLU, combine, with
+ * intermediates in scratch memory).  Runs the routing step, the dispatch
+ * (x -> expert-contiguous rows), expert linear 1 with SwiGLU fused into its
+ * epilogue, expert linear 2,
  * and the weighted combine y_t = sum_k w[t,k] o_{t,k} (an fp32 gather-reduce in
  * ascending k, rounded once).  Writes `y`; leaves the routing metadata and the
  * intermediates needed by moe_bwd in `scratch`.  `wprep` is ignored in the
@@ -194,8 +218,13 @@ int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const flo
             const void* w1, const void* w2, const void* wprep, void* y,
             void* scratch, size_t scratch_bytes, void* stream);
 
-/* Backward pass of the forward that last used `scratch` (which must be passed
- * back unmodified, with the same descriptor, topk_w and weights).  Steps:
+/* Backward pass of the fused layer (the training pass the pages add to the
+ * kernel: "How does the fused kernel work?", and the Russian page's
+ * "Объединённое ядро, дополненное для обучения"), for the forward that last
+ * used `scratch` (which must be passed back unmodified, with the same
+ * descriptor, topk_w and weights).  It reads that forward's routing, x_perm
+ * and saved intermediates from `scratch`, so it takes neither x nor topk_idx.
+ * Steps:
  * combine-backward (dispatch of w * dy to the expert rows, and the
  * routing-weight gradient dtopk_w[t,k] = <dy_t, o_{t,k}> from the saved expert
  * output, an fp32 dot product), the W2 dgrad with SwiGLU-backward fused into
@@ -236,7 +265,9 @@ int moe_router_bwd(const moe_desc* d, const int32_t* topk_idx, const float* topk
                    const float* dtopk_w, float* dlogits, void* stream);
 
 /* Synchronizes `stream`, returns the latched device error (MOE_OK, MOE_EINDEX
- * or MOE_ETIMEOUT) of `scratch` and clears it. */
+ * or MOE_ETIMEOUT) of `scratch` and clears it.  Error reporting of this
+ * library (the pages define no error interface): the descriptor and scratch
+ * size locate the error word and check the buffer (MOE_ESCRATCH). */
 int moe_check(const moe_desc* d, void* scratch, size_t scratch_bytes, void* stream);
 
 /* Text of a status code (static string, host). */

@@ -24,6 +24,21 @@ int check_desc(const moe_desc* d) {
   const long long widest = d->D > 2 * d->F ? d->D : 2 * d->F;
   if (N >= (1LL << 31) || N * widest >= (1LL << 46)) return MOE_EINVAL;
   if (d->D % 64 != 0 || d->F % 64 != 0) return MOE_EUNSUPPORTED;
+  // The GEMMs address one expert's rows, and one expert's weight matrix,
+  // through 32-bit buffer resources with int byte offsets.  An expert can hold
+  // every routed pair (ids need not be distinct for the kernels to stay in
+  // bounds), so every [N, widest] intermediate and every [2F, D] weight must
+  // stay below 2 GiB; larger shapes are refused rather than wrapped.
+  const long long eb = d->mode == MOE_FP32 ? 4 : 2;
+  if (N * widest * eb >= (1LL << 31) || 2LL * d->F * d->D * eb >= (1LL << 31))
+    return MOE_EUNSUPPORTED;
+  if (d->mode == MOE_FP8_BWD || d->mode == MOE_MXFP8 || d->mode == MOE_FP8) {
+    // token-quantised operands: [widest, npad] codes, read by the weight
+    // gradients with 256-row buffer ranges, and [npad / 128, widest] scales
+    const long long npad = (N + 127LL * d->E) / 128 * 128;
+    if (256 * npad >= (1LL << 31) || npad / 128 * widest * 4 >= (1LL << 31))
+      return MOE_EUNSUPPORTED;
+  }
   return MOE_OK;
 }
 

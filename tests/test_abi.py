@@ -190,3 +190,31 @@ def test_views_are_disjoint_regions_of_scratch():
     p, sz = vp(), ctypes.c_size_t()
     assert moe.lib().moe_scratch_view(ctypes.byref(d), FAKE, n, 8, ctypes.byref(p),
                                       ctypes.byref(sz)) == moe.MOE_EINVAL
+
+
+def test_segments_of_2_gib_are_refused():
+    """One expert may hold every routed pair, and the GEMMs address an expert's
+    rows and weight matrix through 32-bit buffer ranges: shapes where such a
+    segment or matrix reaches 2 GiB are refused instead of silently wrapping."""
+    L = moe.lib()
+    # E=1, K=1, T=262144, D=4096: one 2 GiB segment of bf16 rows
+    big = moe.make_desc(262144, 4096, 1024, 1, 1)
+    assert moe.moe_scratch_bytes(big) == 0
+    assert _fwd(big, nbytes=1 << 40) == moe.MOE_EUNSUPPORTED
+    assert _bwd(big, nbytes=1 << 40) == moe.MOE_EUNSUPPORTED
+    assert L.moe_route(ctypes.byref(big), FAKE, FAKE, 1 << 40, None) == moe.MOE_EUNSUPPORTED
+    # one row fewer fits (just under 2 GiB)
+    assert moe.moe_scratch_bytes(moe.make_desc(262143, 4096, 1024, 1, 1)) > 0
+    # fp32 storage halves the admissible rows
+    assert moe.moe_scratch_bytes(moe.make_desc(131072, 4096, 1024, 1, 1, moe.MOE_FP32)) == 0
+    assert moe.moe_scratch_bytes(moe.make_desc(131071, 4096, 1024, 1, 1, moe.MOE_FP32)) > 0
+    # top-8 counts every routed pair: T * K * widest * 2 bytes
+    assert moe.moe_scratch_bytes(moe.make_desc(32768, 4096, 1536, 128, 8)) == 0
+    assert moe.moe_scratch_bytes(moe.make_desc(16384, 4096, 1536, 128, 8)) > 0
+    # one expert's [2F, D] weight matrix at 2 GiB
+    assert moe.moe_scratch_bytes(moe.make_desc(64, 16384, 32768, 8, 2)) == 0
+    # the Qwen3-shaped workloads, FP8 modes included, stay admissible
+    for T, D, F, E, K in ((16384, 2048, 768, 128, 8), (16384, 4096, 1536, 128, 8),
+                          (131072, 4096, 1536, 16, 1)):
+        for mode in (moe.MOE_BF16, moe.MOE_FP8_BWD, moe.MOE_MXFP8, moe.MOE_FP8):
+            assert moe.moe_scratch_bytes(moe.make_desc(T, D, F, E, K, mode)) > 0
