@@ -224,13 +224,19 @@ def make_router_inputs(cfg: LayerConfig) -> dict:
     return {"logits": np.ascontiguousarray(z, np.float32), "dtopk_w": dw}
 
 
-def make_inputs(cfg: LayerConfig, threads: int = 8, with_dy: bool = True) -> dict:
+def make_inputs(cfg: LayerConfig, threads: int = 8, with_dy: bool = True,
+                experts=None) -> dict:
     """Seeded inputs of one layer workload.
 
     Returns float32 arrays x [T,D], w1 [E,2F,D], w2 [E,D,F], dy [T,D]; int32
     topk_idx [T,K]; float32 topk_w [T,K].  In bf16 storage modes the float
     tensors hold bf16-representable values (rounded once, ties to even), and
     both the GPU and the oracle consume exactly these values.
+
+    `experts` (a list of expert ids) draws only those experts' weights, each
+    equal to its draw in the full set (one child stream per expert); the other
+    experts' weights are left zero and their pages untouched, so checks of a
+    few experts at the full Qwen3 shapes stay cheap on the host.
     """
     ss = np.random.SeedSequence(cfg.seed)
     c_logits, c_perm, c_x, c_w1, c_w2, c_dy = ss.spawn(6)
@@ -239,8 +245,10 @@ def make_inputs(cfg: LayerConfig, threads: int = 8, with_dy: bool = True) -> dic
     rnd = cfg.mode != MODE_FP32 and cfg.mode != MODE_FP32_BF16GEMM
 
     x = _normal(np.random.Generator(np.random.PCG64(c_x)), (cfg.T, cfg.D), 1.0)
-    w1 = np.empty((cfg.E, 2 * cfg.F, cfg.D), np.float32)
-    w2 = np.empty((cfg.E, cfg.D, cfg.F), np.float32)
+    alloc = np.empty if experts is None else np.zeros
+    w1 = alloc((cfg.E, 2 * cfg.F, cfg.D), np.float32)
+    w2 = alloc((cfg.E, cfg.D, cfg.F), np.float32)
+    keep = set(range(cfg.E)) if experts is None else {int(e) for e in experts}
 
     def fill(args):
         arr, child, e = args
@@ -248,8 +256,8 @@ def make_inputs(cfg: LayerConfig, threads: int = 8, with_dy: bool = True) -> dic
         if rnd:
             bf16_round(arr[e])
 
-    jobs = [(w1, c, e) for e, c in enumerate(c_w1.spawn(cfg.E))]
-    jobs += [(w2, c, e) for e, c in enumerate(c_w2.spawn(cfg.E))]
+    jobs = [(w1, c, e) for e, c in enumerate(c_w1.spawn(cfg.E)) if e in keep]
+    jobs += [(w2, c, e) for e, c in enumerate(c_w2.spawn(cfg.E)) if e in keep]
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         list(ex.map(fill, jobs))
     out = dict(x=x, w1=w1, w2=w2, topk_idx=idx, topk_w=w)

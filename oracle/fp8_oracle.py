@@ -69,18 +69,12 @@ def block_scale(amax) -> np.ndarray:
 def e8m0_exponent(amax) -> np.ndarray:
     """Smallest integer X in [-127, 127] with amax <= 448 * 2^X (0 when amax == 0)."""
     amax = np.asarray(amax, dtype=np.float64)
-    out = np.zeros(amax.shape, dtype=np.int64)
-    flat = amax.reshape(-1)
-    res = out.reshape(-1)
-    for i, a in enumerate(flat):
-        if a == 0:
-            res[i] = 0
-            continue
-        X = -127
-        while X < 127 and a > E4M3_MAX * 2.0 ** X:
-            X += 1
-        res[i] = X
-    return out
+    # X starts at -127 and steps up once for every candidate X' < 127 whose
+    # 448 * 2^X' is still below amax: the first X with amax <= 448 * 2^X
+    X = np.full(amax.shape, -127, dtype=np.int64)
+    for cand in range(-127, 127):
+        X += amax > E4M3_MAX * 2.0 ** cand
+    return np.where(amax == 0, 0, X)
 
 
 def quant_block(x, scale) -> np.ndarray:

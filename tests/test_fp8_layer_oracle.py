@@ -164,3 +164,66 @@ def test_expert_subset_keeps_those_rows_unchanged(inp):
         np.testing.assert_array_equal(sub[k], full[k][rows], err_msg=k)
     np.testing.assert_array_equal(sub["dw1"], full["dw1"][[2, 0]])
     np.testing.assert_array_equal(sub["dw2"], full["dw2"][[2, 0]])
+
+
+def test_bf16_storage_points_are_the_stored_intermediates(inp, monkeypatch):
+    """The recipe rounds to bf16 exactly where the layer stores (A, H, O, y, w dy,
+    dH, dX_perm, dx, in that order), and every later step consumes the rounded
+    value: each rounding's argument is recomputed here, in float64 from the
+    previous rounded values, by the layer's definition, and must equal what the
+    oracle rounded.  A dropped, added or moved storage point changes the count,
+    the order or one of the arguments."""
+    seen = []
+    round_bf16 = fl.bf16
+
+    def spy(a):
+        seen.append(np.array(a, np.float64, copy=True))
+        return round_bf16(a)
+
+    monkeypatch.setattr(fl, "bf16", spy)
+    r = _run(inp, "fp8", fl.identity_quantiser, store_bf16=True)
+    monkeypatch.undo()
+    T, D, F, K = CFG.T, CFG.D, CFG.F, CFG.K
+    off, src = r["offsets"], r["src"]
+    N = len(src)
+    assert [a.shape for a in seen] == [(N, F), (N, 2 * F), (N, D), (T, D), (N, D), (N, 2 * F),
+                                        (N, D), (T, D)]
+    pre = dict(zip(("a", "h", "o", "y", "dyw", "dh", "dxp", "dx"), seen))
+    st = {k: fl.bf16(v) for k, v in pre.items()}
+    for k in ("a", "h", "o", "y", "dh", "dxp", "dx"):  # the returned values are the rounded ones
+        np.testing.assert_array_equal(r[k], st[k], err_msg=k)
+    tok = src // K
+    wp = np.asarray(inp["topk_w"], np.float64).reshape(-1)[src]
+    x = np.asarray(inp["x"], np.float64)
+    dy = np.asarray(inp["dy"], np.float64)
+    h_raw = np.zeros((N, 2 * F))
+    o_raw = np.zeros((N, D))
+    dA = np.zeros((N, F))
+    dxp_raw = np.zeros((N, D))
+    for e in range(CFG.E):
+        s = slice(off[e], off[e + 1])
+        W1 = np.asarray(inp["w1"][e], np.float64)
+        W2 = np.asarray(inp["w2"][e], np.float64)
+        h_raw[s] = x[tok[s]] @ W1.T
+        o_raw[s] = st["a"][s] @ W2.T            # O from the stored A
+        dA[s] = st["dyw"][s] @ W2                # dgrad from the stored w dy
+        dxp_raw[s] = st["dh"][s] @ W1            # dgrad from the stored dH
+    g, u = h_raw[:, :F], h_raw[:, F:]
+    a_raw = g / (1 + np.exp(-g)) * u             # A from the unrounded H
+    y_raw = np.zeros((T, D))
+    np.add.at(y_raw, tok, wp[:, None] * st["o"])  # y from the stored O
+    dyw_raw = wp[:, None] * dy[tok]
+    gs, us = st["h"][:, :F], st["h"][:, F:]      # SwiGLU backward at the stored H
+    sg = 1 / (1 + np.exp(-gs))
+    dh_raw = np.concatenate([dA * us * sg * (1 + gs * (1 - sg)), dA * gs * sg], axis=1)
+    dx_raw = np.zeros((T, D))
+    np.add.at(dx_raw, tok, st["dxp"])            # dx from the stored dX_perm
+    for k, want in (("a", a_raw), ("h", h_raw), ("o", o_raw), ("y", y_raw), ("dyw", dyw_raw),
+                    ("dh", dh_raw), ("dxp", dxp_raw), ("dx", dx_raw)):
+        np.testing.assert_allclose(pre[k], want, rtol=0, atol=1e-12 * np.abs(want).max(),
+                                   err_msg=k)
+    # the weight gradients contract the stored w dy, A, dH and the inputs
+    for e in range(CFG.E):
+        s = slice(off[e], off[e + 1])
+        np.testing.assert_allclose(r["dw2"][e], st["dyw"][s].T @ st["a"][s], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(r["dw1"][e], st["dh"][s].T @ x[tok[s]], rtol=0, atol=1e-12)

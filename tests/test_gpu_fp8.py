@@ -8,12 +8,15 @@ Three levels:
   (max|err|/max|ref| <= 1e-2: fp32 accumulation and bf16 output rounding only);
 * the whole layer against the float64 oracle of the same FP8 recipe
   (oracle/fp8_layer_oracle.py: both operands of every FP8 GEMM quantised with
-  the oracle's codecs, float64 elsewhere), to the requested bound
-  max|err|/max|ref| <= 5e-2;
-* the layer against the plain fp64 oracle (no quantisation).  e4m3's 3-bit
-  mantissa over two chained GEMMs gives 0.04-0.08 on these outputs, so the hard
-  gate there is 0.1 and the 5e-2 comparison is reported by a non-strict
-  expected-failure test.
+  the oracle's codecs, bf16 storage of the intermediates, float64 elsewhere),
+  max|err|/max|ref| <= 2e-2 (measured 0.012-0.017: fp32 accumulation, and e4m3
+  codes of stored values that differ in their last bf16 bit);
+* the layer against the plain fp64 oracle (no quantisation) at the requested
+  bound 5e-2.  The recipe itself, computed exactly on the CPU, is 0.052-0.08
+  from the plain oracle on these workloads (tests/test_fp8_recipe_bound.py:
+  e4m3's 3-bit mantissa on both operands of each GEMM), so no kernel of this
+  recipe can meet that bound: the comparison is a non-strict expected failure,
+  and a hard gate of 0.1 catches gross errors.
 """
 import numpy as np
 import pytest
@@ -28,7 +31,8 @@ from tests.layer_harness import Layer, rel_err, to_host
 
 pytestmark = pytest.mark.gpu
 
-TOL_FP8 = 5e-2      # requested bound
+TOL_FP8 = 5e-2      # requested bound, against the plain oracle
+TOL_RECIPE = 2e-2   # against the oracle of the same FP8 recipe
 GATE_FP8 = 1e-1     # format error of e4m3 over chained GEMMs stays below this
 
 
@@ -245,12 +249,12 @@ def test_fp8_layer_against_recipe_oracle(name):
     errs = {k: rel_err(out[k], ref[k]) for k in ("y", "dx", "dw1", "dw2", "dprob")}
     print(name, "recipe", {k: round(v, 4) for k, v in errs.items()}, flush=True)
     for k, e in errs.items():
-        assert e <= TOL_FP8, (k, e)
+        assert e <= TOL_RECIPE, (k, e)
 
 
-@pytest.mark.xfail(strict=False, reason="e4m3 format error over chained GEMMs exceeds 5e-2 on some "
-                                        "outputs (measured 0.04-0.08); kernels match the dequantised "
-                                        "products to 1e-2")
+@pytest.mark.xfail(strict=False, reason="the FP8 recipe itself, computed exactly, is 0.052-0.08 from "
+                                        "the plain oracle on these workloads (test_fp8_recipe_bound."
+                                        "py); the kernels match that recipe to 2e-2")
 @pytest.mark.parametrize("name", FP8_SMALL)
 def test_fp8_layer_literal_tolerance(name):
     _, errs = _layer_errors(name)
@@ -304,7 +308,7 @@ def _full_size_fp8(name, ntok, nexp):
     print(name, "recipe", counts[ex].tolist(), {k: round(v, 4) for k, v in rerr.items()},
           flush=True)
     for k, e in rerr.items():
-        assert e <= TOL_FP8, ("recipe", k, e)
+        assert e <= TOL_RECIPE, ("recipe", k, e)
     tok = np.sort(rng.choice(cfg.T, size=ntok, replace=False))
     ref = orc.backward_tokens(inp["dy"], inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"],
                               inp["w2"], tok)

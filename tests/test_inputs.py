@@ -53,3 +53,17 @@ def test_zipf_routing_is_skewed_with_eight_dead_experts():
     top16 = np.sort(counts)[::-1][:16].sum() / cfg.N
     assert top16 > 0.6
     assert counts.max() > 8 * cfg.N / cfg.E
+
+
+def test_expert_subset_draws_the_same_weights():
+    cfg = mi.CONFIGS["dead_bf16"]
+    full = mi.make_inputs(cfg)
+    sub = mi.make_inputs(cfg, experts=[7, 2])
+    for k in ("x", "dy", "topk_idx", "topk_w"):
+        np.testing.assert_array_equal(sub[k], full[k])
+    for e in range(cfg.E):
+        for k in ("w1", "w2"):
+            if e in (2, 7):
+                np.testing.assert_array_equal(sub[k][e], full[k][e])
+            else:
+                assert not sub[k][e].any()
