@@ -195,12 +195,16 @@ int moe_routing_view(const moe_desc* d, const void* scratch, size_t scratch_byte
  *                          tokens in columns 128*p[e] .. , p = prefix of ceil(count/128))
  *   MOE_VIEW_Q_TOK_A/B_SCALE [Npad/128, C] 4-byte scale entries
  * A 4-byte entry is an fp32 scale (blockwise) or four e8m0 bytes, one per 32
- * consecutive contraction elements of the 128-element step (MXFP8). */
+ * consecutive contraction elements of the 128-element step (MXFP8).
+ *   MOE_VIEW_QUEUE  the overlapped forward's schedule (MOE_FLAG_OVERLAP), as
+ *                   its last launch wrote it: int32 control words, dispatch
+ *                   flags, W1-done counters and per-XCD ticket tables. */
 enum moe_view {
   MOE_VIEW_XPERM = 0, MOE_VIEW_H = 1, MOE_VIEW_A = 2, MOE_VIEW_O = 3,
   MOE_VIEW_DYPERM = 4, MOE_VIEW_DH = 5, MOE_VIEW_DXPERM = 6, MOE_VIEW_WPERM = 7,
   MOE_VIEW_Q_ROWS = 8, MOE_VIEW_Q_ROWS_SCALE = 9, MOE_VIEW_Q_TOK_A = 10,
-  MOE_VIEW_Q_TOK_A_SCALE = 11, MOE_VIEW_Q_TOK_B = 12, MOE_VIEW_Q_TOK_B_SCALE = 13
+  MOE_VIEW_Q_TOK_A_SCALE = 11, MOE_VIEW_Q_TOK_B = 12, MOE_VIEW_Q_TOK_B_SCALE = 13,
+  MOE_VIEW_QUEUE = 14
 };
 int moe_scratch_view(const moe_desc* d, const void* scratch, size_t scratch_bytes,
                      int which, void** ptr, size_t* bytes);

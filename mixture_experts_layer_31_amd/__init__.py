@@ -22,7 +22,7 @@ MOE_FLAG_QUEUE_TIMEOUT_TEST = 0x2
 MOE_FLAG_RECOMPUTE = 0x4
 (MOE_VIEW_XPERM, MOE_VIEW_H, MOE_VIEW_A, MOE_VIEW_O, MOE_VIEW_DYPERM, MOE_VIEW_DH,
  MOE_VIEW_DXPERM, MOE_VIEW_WPERM, MOE_VIEW_Q_ROWS, MOE_VIEW_Q_ROWS_SCALE, MOE_VIEW_Q_TOK_A,
- MOE_VIEW_Q_TOK_A_SCALE, MOE_VIEW_Q_TOK_B, MOE_VIEW_Q_TOK_B_SCALE) = range(14)
+ MOE_VIEW_Q_TOK_A_SCALE, MOE_VIEW_Q_TOK_B, MOE_VIEW_Q_TOK_B_SCALE, MOE_VIEW_QUEUE) = range(15)
 
 # Exported symbols, in the order include/moe.h declares them.
 EXPORTS = (

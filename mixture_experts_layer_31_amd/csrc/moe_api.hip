@@ -227,6 +227,7 @@ int moe_scratch_view(const moe_desc* d, const void* scratch, size_t scratch_byte
     case MOE_VIEW_DH: off = L.dh; n = N * 2 * d->F * ab; break;
     case MOE_VIEW_DXPERM: off = L.dxperm; n = N * d->D * ab; break;
     case MOE_VIEW_WPERM: off = L.wperm; n = N * 4; break;
+    case MOE_VIEW_QUEUE: off = L.queue; n = queue_scratch_bytes(*d); break;
     default:
       if (!fp8_mode(d->mode) || which < MOE_VIEW_Q_ROWS || which > MOE_VIEW_Q_TOK_B_SCALE)
         return MOE_EINVAL;

@@ -218,3 +218,18 @@ def test_segments_of_2_gib_are_refused():
                           (131072, 4096, 1536, 16, 1)):
         for mode in (moe.MOE_BF16, moe.MOE_FP8_BWD, moe.MOE_MXFP8, moe.MOE_FP8):
             assert moe.moe_scratch_bytes(moe.make_desc(T, D, F, E, K, mode)) > 0
+
+
+def test_queue_view_matches_the_mirrored_region():
+    """MOE_VIEW_QUEUE spans the schedule region whose layout the host mirror of
+    the overlapped forward's tables (tests/queue_tables.py) reads."""
+    from tests import queue_tables as qt
+    for T, D, F, E, K in ((700, 512, 256, 8, 2), (16384, 2048, 768, 128, 8)):
+        d = moe.make_desc(T, D, F, E, K, moe.MOE_BF16, moe.MOE_FLAG_OVERLAP)
+        n = moe.moe_scratch_bytes(d)
+        p, sz = ctypes.c_void_p(), ctypes.c_size_t()
+        assert moe.lib().moe_scratch_view(ctypes.byref(d), FAKE, n, moe.MOE_VIEW_QUEUE,
+                                          ctypes.byref(p), ctypes.byref(sz)) == moe.MOE_OK
+        r = qt.region_offsets(T * K, E, 2 * F // 256, D // 256)
+        assert r["table"] + 4 * r["table_words"] <= sz.value
+        assert p.value + sz.value <= FAKE + n

@@ -232,12 +232,18 @@ def test_fp8_layer_against_oracle(name):
 RECIPE = {mi.MODE_FP8_BWD: "fp8_bwd", mi.MODE_FP8: "fp8", mi.MODE_MXFP8: "mxfp8"}
 
 
-@pytest.mark.parametrize("name", FP8_SMALL)
-def test_fp8_layer_against_recipe_oracle(name):
+# the default schedule, activation recompute, and (bf16-forward fp8_bwd only) the
+# overlapped forward, each against the recipe oracle
+RECIPE_CASES = ([(n, 0) for n in FP8_SMALL] + [(n, moe.MOE_FLAG_RECOMPUTE) for n in FP8_SMALL]
+                + [("fp8bwd_small", moe.MOE_FLAG_OVERLAP)])
+
+
+@pytest.mark.parametrize("name,flags", RECIPE_CASES)
+def test_fp8_layer_against_recipe_oracle(name, flags):
     cfg = mi.CONFIGS[name]
-    print(f"[case] recipe {name}", flush=True)
+    print(f"[case] recipe {name} flags={flags}", flush=True)
     inp = mi.make_inputs(cfg)
-    L = Layer(cfg, inp)
+    L = Layer(cfg, inp, flags=flags)
     L.prepare()
     L.fwd()
     L.bwd()

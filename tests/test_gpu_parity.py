@@ -13,14 +13,10 @@ import torch
 import mixture_experts_layer_31_amd as moe
 import moe_inputs as mi
 from oracle import moe_oracle as orc
-from tests.layer_harness import Layer, rel_err
+from tests.layer_harness import Layer
+from tests.oracle_parity import full_size_vs_oracle, layer_vs_oracle, routing_bitexact, run
 
 pytestmark = pytest.mark.gpu
-
-TOL_BF16 = 1e-2
-# fp32 storage and arithmetic against the float64 oracle: rounding of fp32 sums
-# over at most a few thousand terms stays orders of magnitude below this
-TOL_F32 = 1e-4
 
 SMALL = ["tiny", "tiny_bf16gemm", "small_bf16", "dead_bf16", "mid_bf16", "wide_bf16", "mid_f32io",
          "zipf_bf16", "rows4k_bf16", "rows8k_f32io"]
@@ -33,71 +29,19 @@ def _gpu():
     moe.lib()
 
 
-def _run(cfg, inp):
-    L = Layer(cfg, inp)
-    L.prepare()
-    L.fwd()
-    L.bwd()
-    assert L.check() == moe.MOE_OK
-    torch.cuda.synchronize()
-    return L
-
-
-def _routing_bitexact(L, idx):
-    got = L.routing()
-    ref = orc.route(idx, L.cfg.E)
-    np.testing.assert_array_equal(got["counts"], ref["counts"])
-    np.testing.assert_array_equal(got["offsets"], ref["offsets"])
-    np.testing.assert_array_equal(got["pos"], ref["pos"])
-    nv = int(ref["offsets"][-1])
-    np.testing.assert_array_equal(got["src"][:nv], ref["src"])
-    return ref
-
-
 @pytest.mark.parametrize("name", SMALL)
 def test_layer_matches_oracle(name):
     cfg = mi.CONFIGS[name]
     inp = mi.make_inputs(cfg)
     print(f"[case] {name} T={cfg.T} D={cfg.D} F={cfg.F} E={cfg.E} K={cfg.K} mode={cfg.mode}",
           flush=True)
-    L = _run(cfg, inp)
-    r = _routing_bitexact(L, inp["topk_idx"])
-    f = orc.forward(inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"], inp["w2"])
-    b = orc.backward(inp["dy"], inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"], inp["w2"], f)
-    out = L.outputs()
-    errs = {k: rel_err(out[k], ref) for k, ref in
-            (("y", f["y"]), ("dx", b["dx"]), ("dw1", b["dw1"]), ("dw2", b["dw2"]),
-             ("dprob", b["dprob"]))}
-    print(name, errs, flush=True)
-    tol = TOL_F32 if cfg.mode == mi.MODE_FP32 else TOL_BF16
-    for k, e in errs.items():
-        assert e <= tol, (k, e)
-
-    # intermediates, row r of a view is pair src[r]; fp32 in the fp32 mode, else bf16
-    K, F, D = cfg.K, cfg.F, cfg.D
-    act = torch.float32 if cfg.mode == mi.MODE_FP32 else torch.bfloat16
-    rnd = (lambda a: a) if cfg.mode == mi.MODE_FP32 else mi.bf16_round
-    src = r["src"]
-    t_of, k_of = src // K, src % K
-    xp = L.view(moe.MOE_VIEW_XPERM, D, act)
-    dyp = L.view(moe.MOE_VIEW_DYPERM, D, act)
-    wp = L.view(moe.MOE_VIEW_WPERM, 0, torch.float32)
-    # the dispatched gradient is w * dy (fp32 product, stored once)
-    dyw = rnd((inp["topk_w"][t_of, k_of][:, None] * inp["dy"][t_of]).astype(np.float32))
-    np.testing.assert_array_equal(dyp[:len(src)], dyw)
-    np.testing.assert_array_equal(xp, rnd(inp["x"][t_of].copy()))
-    np.testing.assert_array_equal(wp[:len(src)], inp["topk_w"][t_of, k_of])
-    for which, cols, ref in ((moe.MOE_VIEW_H, 2 * F, f["h"]), (moe.MOE_VIEW_A, F, f["a"]),
-                             (moe.MOE_VIEW_O, D, f["o"]), (moe.MOE_VIEW_DH, 2 * F, b["dh"])):
-        got = L.view(which, cols, act)[:len(src)]
-        e = rel_err(got, ref[t_of, k_of])
-        assert e <= tol, (which, e)
+    layer_vs_oracle(cfg, inp)
 
 
 def test_zero_token_experts_get_zero_wgrad():
     cfg = mi.CONFIGS["dead_bf16"]
     inp = mi.make_inputs(cfg)
-    L = _run(cfg, inp)
+    L = run(cfg, inp)
     counts = np.bincount(inp["topk_idx"].ravel(), minlength=cfg.E)
     dead = np.nonzero(counts == 0)[0]
     assert len(dead) == 4
@@ -109,7 +53,7 @@ def test_zero_token_experts_get_zero_wgrad():
 def test_run_to_run_bitwise_determinism():
     cfg = mi.CONFIGS["mid_bf16"]
     inp = mi.make_inputs(cfg)
-    L = _run(cfg, inp)
+    L = run(cfg, inp)
     first = L.outputs()
     for _ in range(3):
         L.fwd()
@@ -151,73 +95,30 @@ def test_routing_full_size_bitexact(name):
 
     L = Layer.__new__(Layer)
     L.cfg, L.desc, L.scratch = cfg, d, scratch
-    _routing_bitexact(L, idx)
-
-
-def _full_size(name, ntok, nexp):
-    cfg = mi.CONFIGS[name]
-    print(f"[case] full-size {name}", flush=True)
-    inp = mi.make_inputs(cfg, threads=16)
-    L = _run(cfg, inp)
-    _routing_bitexact(L, inp["topk_idx"])
-    rng = np.random.default_rng(0)
-    tok = np.sort(rng.choice(cfg.T, size=ntok, replace=False))
-    tok[0], tok[-1] = 0, cfg.T - 1
-    ref = orc.backward_tokens(inp["dy"], inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"],
-                              inp["w2"], tok)
-    tt = torch.from_numpy(tok).cuda()
-    out = dict(y=L.y[tt], dx=L.dx[tt], dprob=L.dprob[tt])
-    from tests.layer_harness import to_host
-    errs = {k: rel_err(to_host(v), ref[k]) for k, v in out.items()}
-    counts = np.bincount(inp["topk_idx"].ravel(), minlength=cfg.E)
-    for e in rng.choice(np.nonzero(counts)[0], size=nexp, replace=False):
-        r1 = np.sort(rng.choice(2 * cfg.F, size=6, replace=False))
-        r2 = np.sort(rng.choice(cfg.D, size=6, replace=False))
-        wr = orc.wgrad_rows(inp["dy"], inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"],
-                            inp["w2"], int(e), r1, r2)
-        errs[f"dw1[{e}]"] = rel_err(to_host(L.dw1[int(e)][torch.from_numpy(r1).cuda()]), wr["dw1"])
-        errs[f"dw2[{e}]"] = rel_err(to_host(L.dw2[int(e)][torch.from_numpy(r2).cuda()]), wr["dw2"])
-    print(name, errs, flush=True)
-    for k, e in errs.items():
-        assert e <= TOL_BF16, (k, e)
+    routing_bitexact(L, idx)
 
 
 @pytest.mark.timeout(600)
 def test_full_size_30b_sampled():
-    _full_size("30b", ntok=24, nexp=2)
+    full_size_vs_oracle("30b", ntok=24, nexp=2)
 
 
 @pytest.mark.timeout(900)
 def test_full_size_235b_sampled():
-    _full_size("235b", ntok=12, nexp=1)
+    full_size_vs_oracle("235b", ntok=12, nexp=1)
 
 
 @pytest.mark.timeout(600)
 def test_full_size_30b_ep_share_sampled():
     # one expert-parallel rank's share: 16 experts with about 8192 rows each
-    _full_size("30b_ep_share", ntok=24, nexp=1)
-
-
-def _check_layer(cfg, inp, tol=TOL_BF16):
-    L = _run(cfg, inp)
-    _routing_bitexact(L, inp["topk_idx"])
-    f = orc.forward(inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"], inp["w2"])
-    b = orc.backward(inp["dy"], inp["x"], inp["topk_idx"], inp["topk_w"], inp["w1"], inp["w2"], f)
-    out = L.outputs()
-    errs = {k: rel_err(out[k], ref) for k, ref in
-            (("y", f["y"]), ("dx", b["dx"]), ("dw1", b["dw1"]), ("dw2", b["dw2"]),
-             ("dprob", b["dprob"]))}
-    print(cfg.name, errs, flush=True)
-    for k, e in errs.items():
-        assert e <= tol, (k, e)
-    return L, out, b
+    full_size_vs_oracle("30b_ep_share", ntok=24, nexp=1)
 
 
 @pytest.mark.parametrize("name", ["one_token", "one_expert", "all_experts"])
 def test_degenerate_shapes(name):
     cfg = mi.CONFIGS[name]
     print(f"[case] {name} T={cfg.T} D={cfg.D} F={cfg.F} E={cfg.E} K={cfg.K}", flush=True)
-    _check_layer(cfg, mi.make_inputs(cfg))
+    layer_vs_oracle(cfg, mi.make_inputs(cfg))
 
 
 def test_all_pairs_on_two_experts():
@@ -229,7 +130,7 @@ def test_all_pairs_on_two_experts():
     idx[:, 1] = 1
     idx[::3] = idx[::3, ::-1]
     print("[case] mid_bf16 with all pairs on experts 0 and 1", flush=True)
-    L, out, b = _check_layer(cfg, dict(inp, topk_idx=idx))
+    L, out, b = layer_vs_oracle(cfg, dict(inp, topk_idx=idx))
     for e in range(2, cfg.E):
         assert np.all(out["dw1"][e] == 0) and np.all(out["dw2"][e] == 0)
 

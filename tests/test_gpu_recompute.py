@@ -4,7 +4,10 @@ the C ABI.
 With the flag the forward keeps no H and the backward rebuilds it with the
 forward's own W1 GEMM (same kernel, operands and accumulation order), so every
 output and every saved or backward intermediate must agree bit for bit with
-the default path, which test_gpu_parity.py checks against the oracle.
+the default path.  The recompute path is also checked against the CPU oracle
+directly: every output and intermediate within 1e-2 (1e-4 in the fp32 mode)
+on the small shapes, and sampled tokens and weight-gradient rows of the full
+30B layer.
 """
 from __future__ import annotations
 
@@ -15,6 +18,7 @@ import torch
 import mixture_experts_layer_31_amd as moe
 import moe_inputs as mi
 from tests.layer_harness import Layer
+from tests.oracle_parity import full_size_vs_oracle, layer_vs_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -89,3 +93,22 @@ def test_recompute_full_size_30b():
     base = {k: v.cpu() for k, v in base.items()}
     assert rc0 == moe.MOE_OK and rc1 == moe.MOE_OK
     _same(base, rec, cfg.N)
+
+
+@pytest.mark.parametrize("name", [c for c in CASES if mi.CONFIGS[c].mode in
+                                  (mi.MODE_FP32, mi.MODE_FP32_BF16GEMM, mi.MODE_BF16)])
+def test_recompute_matches_oracle(name):
+    cfg = mi.CONFIGS[name]
+    print(f"[case] recompute vs oracle {name}", flush=True)
+    layer_vs_oracle(cfg, mi.make_inputs(cfg), moe.MOE_FLAG_RECOMPUTE)
+
+
+def test_recompute_with_overlap_matches_oracle():
+    cfg = mi.CONFIGS["mid_bf16"]
+    print("[case] recompute + overlap vs oracle mid_bf16", flush=True)
+    layer_vs_oracle(cfg, mi.make_inputs(cfg), moe.MOE_FLAG_RECOMPUTE | moe.MOE_FLAG_OVERLAP)
+
+
+@pytest.mark.timeout(600)
+def test_recompute_full_size_30b_matches_oracle():
+    full_size_vs_oracle("30b", ntok=24, nexp=2, flags=moe.MOE_FLAG_RECOMPUTE)
