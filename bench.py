@@ -14,7 +14,11 @@ MoE news item, "How fast is Prime Mega MoE?").
 Prints one JSON line.  `value` is achieved TFLOP/s of the algorithmic fwd+bwd
 FLOPs (18 * T * K * D * F).  `roofline` covers the kernel with the largest
 share of the step, timed with HIP events on the stream it is launched on;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+`cpu_baseline` times the CPU oracle's forward and backward on a bounded sample
+of the same workload.  With the default 30B main line, the same run also times
+the Qwen3-235B-A22B-shaped layer in bf16 and in fp8_bwd, and the 30B shape in
+MXFP8 with Zipf routing, each under `configs` with its own step time, fwd/bwd
+split, kernel table and roofline entry (`--extra none` skips them).
 """
 from __future__ import annotations
 
@@ -83,32 +87,59 @@ def measured_traffic(cfg, kernel: str):
     return k["fetch_bytes"] + k["write_bytes"]
 
 
+def host_info() -> dict:
+    """CPU model, host memory and usable cores of the machine the oracle runs on."""
+    model, ram = "unknown", None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                ram = round(int(line.split()[1]) / 2 ** 20, 1)
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "ram_gib": ram, "cores": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(cfg, inp, budget_s: float) -> dict:
-    """Times the CPU oracle's fwd+bwd on the first S tokens of the workload."""
-    import numpy as np
+    """Times the CPU oracle's forward and backward, separately, on the first S
+    tokens of the workload (S sized so both take about budget_s), and scales
+    each to the whole layer's T tokens (the oracle's work is linear in T)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import moe_oracle as orc
 
-    cores = len(os.sched_getaffinity(0))
+    info = host_info()
+    cores = info["cores"]
 
     def run(S):
         sl = slice(0, S)
         t0 = time.perf_counter()
         f = orc.forward(inp["x"][sl], inp["topk_idx"][sl], inp["topk_w"][sl], inp["w1"], inp["w2"])
+        t1 = time.perf_counter()
         orc.backward(inp["dy"][sl], inp["x"][sl], inp["topk_idx"][sl], inp["topk_w"][sl],
                      inp["w1"], inp["w2"], f)
-        return time.perf_counter() - t0
+        return t1 - t0, time.perf_counter() - t1
 
     with threadpool_limits(limits=cores):
-        t_small = run(2)
+        t_small = sum(run(2))
         S = int(max(2, min(cfg.T, 2 * budget_s / max(t_small, 1e-3))))
         S = min(S, 512)
-        t = run(S)
+        tf, tb = run(S)
     flops = 18.0 * S * cfg.K * cfg.D * cfg.F
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"fwd+bwd of the first {S} of {cfg.T} tokens (all {cfg.K} routed pairs each), "
-                      f"numpy float64, {t:.1f} s"}
+    scale = cfg.T / S
+    return {"value": flops / (tf + tb) / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"forward and backward of the first {S} of {cfg.T} tokens (all {cfg.K} routed "
+                      f"pairs each), numpy float64, {tf:.1f} s + {tb:.1f} s",
+            "dtype": "float64", "tokens": S, "fwd_s": round(tf, 2), "bwd_s": round(tb, 2),
+            "fwd_tflops": round(6.0 * S * cfg.K * cfg.D * cfg.F / tf / 1e12, 5),
+            "bwd_tflops": round(12.0 * S * cfg.K * cfg.D * cfg.F / tb / 1e12, 5),
+            "fwd_ms_whole_layer_est": round(tf * scale * 1e3, 0),
+            "bwd_ms_whole_layer_est": round(tb * scale * 1e3, 0),
+            "cpu_model": info["cpu_model"], "ram_gib": info["ram_gib"]}
 
 
 def queue_capable(cfg) -> bool:
@@ -116,43 +147,35 @@ def queue_capable(cfg) -> bool:
     return cfg.mode in (1, 2, 3) and cfg.D % 256 == 0 and (2 * cfg.F) % 256 == 0
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=15)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="30b")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="run one device copy of this many MiB first (reference for HBM counters)")
-    ap.add_argument("--no-profile", action="store_true",
-                    help="time without per-kernel events (no roofline entry)")
-    ap.add_argument("--overlap", action="store_true",
-                    help="time the overlapped one-launch forward instead of one kernel per step")
-    ap.add_argument("--recompute", action="store_true",
-                    help="activation recompute: the forward keeps no H, the backward rebuilds it")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's layer only: the expert-parallel exchange between "
-              "GPUs is outside this library, so --gpus must be 1", file=sys.stderr)
-        sys.exit(2)
-
+def run_config(name: str, args, flags: int, main_line: bool) -> tuple:
+    """Times one workload: warm-up, then K steps without per-kernel events (the
+    step time), then K steps with them (kernel table and roofline entry).  The
+    main line also times the overlapped forward and the router.  Returns the
+    result dictionary and the host inputs (for the CPU baseline)."""
     import torch
 
     import mixture_experts_layer_31_amd as moe
     import moe_inputs as mi
     from tests.layer_harness import Layer, desc_of
 
-    cfg = mi.CONFIGS[args.config]
+    cfg = mi.CONFIGS[name]
     t0 = time.perf_counter()
     inp = mi.make_inputs(cfg, threads=16)
     gen_s = time.perf_counter() - t0
-    flags = (moe.MOE_FLAG_OVERLAP if args.overlap else 0) | (moe.MOE_FLAG_RECOMPUTE if args.recompute else 0)
     L = Layer(cfg, inp, flags=flags, device="cuda:0")
-    L.prepare()
     stream = torch.cuda.current_stream()
-    if args.calib_copy_mib:
+    # weight preparation (FP8 quantised copies) is timed on its own, outside the step
+    prep_ms = None
+    if L.wprep is not None:
+        L.prepare()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        L.prepare()
+        b.record(stream)
+        torch.cuda.synchronize()
+        prep_ms = round(a.elapsed_time(b), 4)
+    if main_line and args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
         dst = torch.empty_like(src)
@@ -167,7 +190,7 @@ def main():
     torch.cuda.synchronize()
     status = L.check()
     if status != moe.MOE_OK:
-        raise RuntimeError(moe.strerror(status))
+        raise RuntimeError(f"{name}: {moe.strerror(status)}")
 
     def timed_steps(profile: bool):
         """K steps between a start and a stop event (fwd/bwd split by events between
@@ -192,7 +215,7 @@ def main():
         kern = moe.moe_profile_collect() if profile else {}
         status = L.check()
         if status != moe.MOE_OK:
-            raise RuntimeError(moe.strerror(status))
+            raise RuntimeError(f"{name}: {moe.strerror(status)}")
         return (start.elapsed_time(stop) / args.steps,
                 sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps,
                 sum(b.elapsed_time(c) for _, b, c in ev) / args.steps, kern)
@@ -205,9 +228,9 @@ def main():
     if not args.no_profile:
         ms_step_profiled, _, _, kernels = timed_steps(True)
 
-    # the overlapped one-launch forward against the one-kernel-per-step forward
-    f5 = None
-    if queue_capable(cfg):
+    f5 = router = None
+    if main_line and queue_capable(cfg):
+        # the overlapped one-launch forward against the one-kernel-per-step forward
         f5 = {"reps": 10}
         for key, fl in (("fwd_ms_overlapped", moe.MOE_FLAG_OVERLAP), ("fwd_ms_per_step", 0)):
             L.desc = desc_of(cfg, fl | (flags & moe.MOE_FLAG_RECOMPUTE))
@@ -225,10 +248,9 @@ def main():
         if status != moe.MOE_OK:
             raise RuntimeError(moe.strerror(status))
 
-    # the router ahead of the layer (softmax -> top-k -> renormalise, and its
-    # backward to the logits), timed on its own: not part of the layer step
-    router = None
-    if cfg.E <= 512 and cfg.K <= 64:
+    if main_line and cfg.E <= 512 and cfg.K <= 64:
+        # the router ahead of the layer (softmax -> top-k -> renormalise, and its
+        # backward to the logits), timed on its own: not part of the layer step
         r = mi.make_router_inputs(cfg)
         rd = moe.make_desc(cfg.T, 0, 0, cfg.E, cfg.K)
         z = torch.from_numpy(r["logits"]).to("cuda:0")
@@ -267,16 +289,16 @@ def main():
     if kernels:
         gf = gemm_flops(cfg)
         rb = row_bytes(cfg)
-        for name, (ms, n) in kernels.items():
+        for kname, (ms, n) in kernels.items():
             avg = ms / n
             entry = {"avg_ms": round(avg, 4), "launches": n}
-            if name in gf:
-                entry["tflops"] = round(gf[name] / (avg * 1e-3) / 1e12, 1)
-                entry["frac_peak"] = round(gf[name] / (avg * 1e-3) / 1e12 / gemm_peak(cfg, name), 3)
-            if name in rb:
-                entry["gbs"] = round(rb[name] / (avg * 1e-3) / 1e9, 1)
-                entry["frac_hbm"] = round(rb[name] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)
-            per_kernel[name] = entry
+            if kname in gf:
+                entry["tflops"] = round(gf[kname] / (avg * 1e-3) / 1e12, 1)
+                entry["frac_peak"] = round(gf[kname] / (avg * 1e-3) / 1e12 / gemm_peak(cfg, kname), 3)
+            if kname in rb:
+                entry["gbs"] = round(rb[kname] / (avg * 1e-3) / 1e9, 1)
+                entry["frac_hbm"] = round(rb[kname] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)
+            per_kernel[kname] = entry
         dom = max((k for k in kernels if k in gf), key=lambda k: kernels[k][0])
         avg = kernels[dom][0] / kernels[dom][1]
         ach = gf[dom] / (avg * 1e-3) / 1e12
@@ -286,27 +308,88 @@ def main():
                 "traffic": measured_traffic(cfg, dom),
                 "flops_per_launch": gf[dom], "avg_ms": round(avg, 4)}
 
-    out = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
-        "data": "synthetic",
+    res = {
+        "value": round(tflops, 2), "ms_per_step": round(ms_step, 4), "dtype": dtype,
         "config": {"workload": f"{cfg.name}: Qwen3 MoE layer T={cfg.T} D={cfg.D} F={cfg.F} "
                                f"E={cfg.E} top-{cfg.K}, {cfg.routing} routing",
                    "T": cfg.T, "D": cfg.D, "F": cfg.F, "E": cfg.E, "K": cfg.K, "mode": cfg.mode,
-                   "recompute": bool(args.recompute)},
+                   "recompute": bool(flags & moe.MOE_FLAG_RECOMPUTE)},
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "fwd_tflops": round(cfg.fwd_flops() / (fwd_ms * 1e-3) / 1e12, 1),
         "bwd_tflops": round(cfg.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1),
         "peak_tflops": round(peak, 1),
         "frac_mfma_peak": round(tflops / peak, 4),
+        "weight_prep_ms": prep_ms,
         "roofline": roof,
         "ms_per_step_profiled": None if ms_step_profiled is None else round(ms_step_profiled, 4),
-        "f5_overlap": f5,
-        "router": router,
         "kernels": per_kernel,
         "input_gen_s": round(gen_s, 1),
     }
+    if main_line:
+        res["f5_overlap"] = f5
+        res["router"] = router
+    del L
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, inp
+
+
+# the other workloads of the metric, timed in the same run as extra entries
+EXTRA_CONFIGS = ("235b", "235b_fp8bwd", "30b_mxfp8")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=15)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="30b")
+    ap.add_argument("--extra", default=None,
+                    help="comma-separated extra workloads timed after the main one (default: "
+                         f"{','.join(EXTRA_CONFIGS)} with the 30b main line, none otherwise; 'none')")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (reference for HBM counters)")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="time without per-kernel events (no roofline entry)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="time the overlapped one-launch forward instead of one kernel per step")
+    ap.add_argument("--recompute", action="store_true",
+                    help="activation recompute: the forward keeps no H, the backward rebuilds it")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's layer only: the expert-parallel exchange between "
+              "GPUs is outside this library, so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import mixture_experts_layer_31_amd as moe
+    import moe_inputs as mi
+
+    cfg = mi.CONFIGS[args.config]
+    flags = (moe.MOE_FLAG_OVERLAP if args.overlap else 0) | (moe.MOE_FLAG_RECOMPUTE if args.recompute else 0)
+    if args.extra is None:
+        extra = list(EXTRA_CONFIGS) if args.config == "30b" and not flags else []
+    else:
+        extra = [] if args.extra == "none" else [e for e in args.extra.split(",") if e]
+    main_res, inp = run_config(args.config, args, flags, True)
+    print(f"[bench] {args.config}: {main_res['ms_per_step']} ms/step", file=sys.stderr, flush=True)
+    others = {}
+    for name in extra:
+        if name == args.config:
+            continue
+        others[name], _ = run_config(name, args, flags, False)
+        print(f"[bench] {name}: {others[name]['ms_per_step']} ms/step", file=sys.stderr, flush=True)
+
+    out = {
+        "metric": METRIC, "value": main_res["value"], "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": main_res["dtype"], "data": "synthetic",
+    }
+    out.update({k: v for k, v in main_res.items() if k not in ("value", "ms_per_step", "dtype")})
+    if others:
+        out["configs"] = others
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -63,6 +63,12 @@ def step_name(kernel: str) -> str | None:
     m = re.search(r"gather_reduce_kernel<[^>]*\b(true|false), \d+>", kernel)  # weighted, batch
     if m:
         return "combine" if m.group(1) == "true" else "unpermute"
+    # wide rows (D = 4096, 8192): <element type, weighted, chunks per thread, batch>
+    m = re.search(r"gather_reduce_wide_kernel<[^,>]*, (true|false),", kernel)
+    if m:
+        return "combine" if m.group(1) == "true" else "unpermute"
+    if "dispatch_rows_kernel" in kernel:  # whole rows per wave (D = 2048, 4096; K >= 4)
+        return "dispatch"
     for key, name in _PLAIN:
         if key in kernel:
             return name
