@@ -444,132 +444,80 @@ __device__ __forceinline__ void mainloop8(char* smem, const SA& sa, const SB& sb
   }
 }
 
-// fp8 fragment of a 64-element k-step (32 bytes: chunks (lane>>5) and
-// 2 + (lane>>5) of a 64-byte row, the operand layout of the 32x32x64 MFMA).
-__device__ __forceinline__ i32x8 frag64(const char* tile, int row, int lane) {
-  const int h = lane >> 5, sw = swz_row<64>(row);
-  const i32x4 a = *reinterpret_cast<const i32x4*>(tile + row * 64 + ((h ^ sw) << 4));
-  const i32x4 b = *reinterpret_cast<const i32x4*>(tile + row * 64 + (((2 + h) ^ sw) << 4));
-  const i32x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return r;
-}
-
-// The FP8 contraction ring: the bf16 kernels' pipeline (an LDS ring of STAGES
-// k-steps filled by direct-to-LDS loads STAGES-1 steps ahead, one barrier per
-// k-step) with 64-element k-steps, so a k-step moves the same 64-byte rows as
-// a bf16 k-step and issues one 32x32x64 MFMA per 32x32 block instead of two
-// 32x32x16 ones.  Each stage also holds the k-step's scale entries (1 KB per
-// operand, staged by waves 0 and 1).  A k-step's MFMAs run in two halves (the
-// first and second half of the wave's m-blocks); the second half's A
-// fragments are read while the first half multiplies, and the next k-step's
-// B and first-half A fragments are read across the barrier while the second
-// half multiplies (into a second B register set, moved at the step's end).
-// It serves the blockwise token-grouped GEMMs: each step's product (unit
-// scales) is promoted into the accumulator with its 128-block's fp32 scales,
-// acc += part * s_a * s_b, s_b uniform over each 32-column block (weights in
-// 128 x 128 blocks).
+// The blockwise token-grouped loop on 128-element k-steps (one scale block
+// per step) in two LDS stages of 128-byte rows, as the MX loop: a 32x32
+// block's two 64-deep MFMAs accumulate into a partial that is promoted once
+// per step, acc += part * s_a[row] * s_b[block] (s_b uniform over a 32-column
+// block: weights in 128 x 128 blocks), one scale product and 16 FMAs per block
+// and step.  The step's B fragments and scales stay in registers while the A
+// fragments stream one 32-row block at a time (the next block's are read while
+// the current one multiplies), which keeps the loop inside 256 registers.
 template <class TL, class SA, class SB>
-__device__ __forceinline__ void ring8(char* smem, const SA& sa, const SB& sb,
-                                      const ScaleStager& ssa, const ScaleStager& ssb, int ktiles,
-                                      f32x16 (&acc)[TL::WMT][TL::WNT], int wave, int lane) {
+__device__ __forceinline__ void block8(char* smem, const SA& sa, const SB& sb,
+                                       const ScaleStager& ssa, const ScaleStager& ssb, int ktiles,
+                                       f32x16 (&acc)[TL::WMT][TL::WNT], int wave, int lane) {
   constexpr int BM = TL::BM, BN = TL::BN, WM = TL::WM, WN = TL::WN;
-  constexpr int WMT = TL::WMT, WNT = TL::WNT, STAGES = TL::STAGES, H = WMT / 2;
-  constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64, STAGE = A_BYTES + B_BYTES + 2048;
-  constexpr int NI = SA::NI + SB::NI;
-  static_assert(WMT % 2 == 0, "two halves of m-blocks");
-  static_assert(STAGES >= 3 && STAGES - 2 <= 3, "ring of 3 to 5 k-steps");
-  const bool scw = wave < 2;  // waves 0 and 1 stage the scale entries too
+  constexpr int WMT = TL::WMT, WNT = TL::WNT;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES + 2048;
+  static_assert(TL::STAGES == 2, "two stages");
   const int wm = wave / TL::WGN, wn = wave % TL::WGN;
   const uint32_t base = lds_addr(smem);
-
-  auto issue = [&](int kt, int j0, int j1) __attribute__((always_inline)) {
-    const uint32_t st = base + uint32_t(kt % STAGES) * STAGE;
-    if (j0 == 0) {
-      ssa.issue(st + A_BYTES + B_BYTES, kt >> 1);
-      ssb.issue(st + A_BYTES + B_BYTES + 1024, kt >> 1);
-    }
-    sa.issue(st, wave, kt, j0, j1);
-    sb.issue(st + A_BYTES, wave, kt, j0 - SA::NI, j1 - SA::NI);
+  auto issue = [&](int s, int kt) {
+    const uint32_t st = base + s * STAGE;
+    sa.issue(st, wave, kt);
+    sb.issue(st + A_BYTES, wave, kt);
+    ssa.issue(st + A_BYTES + B_BYTES, kt);
+    ssb.issue(st + A_BYTES + B_BYTES + 1024, kt);
   };
-  auto wait_steps = [&](int n) __attribute__((always_inline)) {  // at most n k-steps of this wave's loads outstanding
-    if (scw) wait_vmcnt_n<NI + 1>(n);
-    else wait_vmcnt_n<NI>(n);
-  };
-  auto stage_of = [&](int kt) __attribute__((always_inline)) { return smem + (kt % STAGES) * STAGE; };
-  // per-lane scale operands of k-step kt
-  auto scale_a = [&](int kt, int i) __attribute__((always_inline)) {
-    return __uint_as_float(reinterpret_cast<const uint32_t*>(stage_of(kt) + A_BYTES + B_BYTES)
-                               [wm * WM + i * 32 + (lane & 31)]);
-  };
-  auto scale_b = [&](int kt, int j) __attribute__((always_inline)) {
-    return __uint_as_float(reinterpret_cast<const uint32_t*>(stage_of(kt) + A_BYTES + B_BYTES + 1024)
-                               [wn * WN + j * 32]);
-  };
-  struct Half { i32x8 a[H]; float s[H]; };
-  struct Bset { i32x8 b[WNT]; float s[WNT]; };
-  auto load_a = [&](int kt, int h, Half& f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < H; ++i) {
-      f.a[i] = frag64(stage_of(kt), wm * WM + (h * H + i) * 32 + (lane & 31), lane);
-      f.s[i] = scale_a(kt, h * H + i);
-    }
-  };
-  auto load_b = [&](int kt, Bset& f) __attribute__((always_inline)) {
+  if (ktiles > 0) issue(0, 0);
+  for (int kt = 0; kt < ktiles; ++kt) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + 1 < ktiles) issue((kt + 1) & 1, kt + 1);
+    const char* ta = smem + (kt & 1) * STAGE;
+    const char* tb = ta + A_BYTES;
+    const uint32_t* sca = reinterpret_cast<const uint32_t*>(tb + B_BYTES);
+    const uint32_t* scb = sca + 256;
+    i32x8 b0[WNT], b1[WNT];
+    float sbv[WNT];
 #pragma unroll
     for (int j = 0; j < WNT; ++j) {
-      f.b[j] = frag64(stage_of(kt) + A_BYTES, wn * WN + j * 32 + (lane & 31), lane);
-      f.s[j] = scale_b(kt, j);
+      const int n = wn * WN + j * 32;
+      b0[j] = frag8(tb, n + (lane & 31), 0, lane);
+      b1[j] = frag8(tb, n + (lane & 31), 1, lane);
+      sbv[j] = __uint_as_float(scb[n]);
     }
-  };
-  auto mma = [&](int h, const Half& fa, const Bset& fb) __attribute__((always_inline)) {
+    const int r0 = wm * WM + (lane & 31);
+    i32x8 a0 = frag8(ta, r0, 0, lane), a1 = frag8(ta, r0, 1, lane);
+    float sav = __uint_as_float(sca[r0]);
 #pragma unroll
-    for (int i = 0; i < H; ++i)
+    for (int i = 0; i < WMT; ++i) {
+      i32x8 n0, n1;
+      float nsa = 0.f;
+      if (i + 1 < WMT) {
+        n0 = frag8(ta, r0 + (i + 1) * 32, 0, lane);
+        n1 = frag8(ta, r0 + (i + 1) * 32, 1, lane);
+        nsa = __uint_as_float(sca[r0 + (i + 1) * 32]);
+      }
+      f32x16 part[WNT];
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) part[j] = mfma8<0>(b0[j], a0, f32x16{}, 127, 127);
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) part[j] = mfma8<0>(b1[j], a1, part[j], 127, 127);
 #pragma unroll
       for (int j = 0; j < WNT; ++j) {
-        f32x16& c = acc[h * H + i][j];
-        const f32x16 part = mfma8<0>(fb.b[j], fa.a[i], f32x16{}, 127, 127);
-        const float sc = fa.s[i] * fb.s[j];
+        const float sc = sav * sbv[j];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) c[r] = __builtin_fmaf(part[r], sc, c[r]);
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[j][r], sc, acc[i][j][r]);
       }
-  };
-  constexpr int NH = NI / 2;
-
-  const int pre = min(STAGES - 1, ktiles);
-#pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
-    if (st < pre) issue(st, 0, NI);
-  wait_steps(pre - 1);
-  __builtin_amdgcn_s_barrier();
-  Half f0, f1;
-  Bset bx, by;
-  load_a(0, 0, f0);
-  load_b(0, bx);
-
-  auto step = [&](int kt, auto dma_on) __attribute__((always_inline)) {
-    constexpr bool DMA = decltype(dma_on)::value;
-    const int kn = kt + STAGES - 1;
-    load_a(kt, 1, f1);
-    if constexpr (DMA) issue(kn, 0, NH);
-    mma(0, f0, bx);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (DMA) issue(kn, NH, NI);
-    const bool more = DMA || kt + 1 < ktiles;
-    if (more) {
-      wait_steps(DMA ? STAGES - 2 : ktiles - 2 - kt);
-      wait_lgkm0();
-      __builtin_amdgcn_s_barrier();
-      load_a(kt + 1, 0, f0);
-      load_b(kt + 1, by);
+      if (i + 1 < WMT) {
+        a0 = n0;
+        a1 = n1;
+        sav = nsa;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    mma(1, f1, bx);
-    __builtin_amdgcn_sched_barrier(0);
-    bx = by;  // the next step's B fragments (register renaming across an unrolled pair)
-  };
-  const int kmain = ktiles - (STAGES - 1);
-  int kt = 0;
-  for (; kt < kmain; ++kt) step(kt, std::true_type{});
-  for (; kt < ktiles; ++kt) step(kt, std::false_type{});
+  }
 }
 
 struct F8Args {
@@ -597,13 +545,13 @@ struct F8Args {
 // Token-grouped FP8 GEMM: rows of expert e times B[e]^T ([N, K] codes).
 template <class TL, bool MX>
 constexpr int f8_grouped_lds() {
-  return TL::STAGES * ((TL::BM + TL::BN) * (MX ? 128 : 64) + 2048);
+  return TL::STAGES * ((TL::BM + TL::BN) * 128 + 2048);
 }
 template <class TL, bool MX, int EPI>
 __device__ __forceinline__ void f8_grouped_tile(const F8Args& p, int l, char* smem) {
   constexpr int BM = TL::BM, BN = TL::BN, WN = TL::WN, WAVES = TL::WAVES;
   static_assert(EPI != EPI_SWIGLU || TL::WNT % 2 == 0, "SwiGLU pairs gate/up sub-tiles");
-  constexpr int ROWB = MX ? 128 : 64;  // MX: 128-element loop; blockwise: the 64-element ring
+  constexpr int ROWB = 128;  // 128-element k-steps (one MX or blockwise scale step)
   int mt_g, nt, lo;
   if (p.nmajor) {  // expert e owns flat tiles [tstart[e] * ntn, tstart[e + 1] * ntn)
     lo = tile_expert(p.tstart, p.E, p.ntn, l);
@@ -647,7 +595,7 @@ __device__ __forceinline__ void f8_grouped_tile(const F8Args& p, int l, char* sm
   f32x16 acc[TL::WMT][TL::WNT];
   zero(acc);
   if constexpr (MX) mainloop8<TL, true, false>(smem, sa, sb, ssa, ssb, p.K / 128, acc, wave, lane);
-  else ring8<TL>(smem, sa, sb, ssa, ssb, p.K / 64, acc, wave, lane);
+  else block8<TL>(smem, sa, sb, ssa, ssb, p.K / 128, acc, wave, lane);
   static_assert(f8_grouped_lds<TL, MX>() >= grouped_epi_lds<TL, EPI>(), "epilogue staging exceeds LDS");
   grouped_epilogue<TL, EPI>(p.epi, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane, smem, threadIdx.x);
 }
@@ -716,10 +664,14 @@ using namespace gemm;
 
 // Tiles, measured on the 235B fp8_bwd and 30B MXFP8 layers:
 //  * MXFP8 (scales applied by the matrix core): 256 x 256, eight waves, the
-//    two-stage 128-element loop (about 10% faster than the 64-element ring:
-//    half the barriers, scales read once per 128 elements);
-//  * blockwise token-grouped GEMMs: 256 x 256, eight waves, the four-stage
-//    64-element ring (about 30% faster than four waves of 128 x 64);
+//    two-stage 128-element loop (about 10% faster than a four-stage ring of
+//    64-element steps: half the barriers, scales read once per 128 elements);
+//  * blockwise token-grouped GEMMs: the same tiles and stages with the
+//    promoting loop block8 (one promotion per 128-element scale block).  The
+//    four-stage ring of 64-element steps it replaced promoted every 64
+//    elements, twice per scale block, and spilled registers; block8 cut the
+//    235B W1 dgrad from 2.42 to 1.95 ms and the W2 dgrad + SwiGLU-backward
+//    from 1.93 to 1.69 ms (30B blockwise step 4.98 -> 4.69 ms);
 //  * blockwise weight-gradient GEMMs, whose scales vary along both output
 //    axes (a scale product per output element and 128-token block): the
 //    promoting 128-element loop on 256 x 128 tiles of eight 64 x 64 waves,
@@ -728,10 +680,9 @@ using namespace gemm;
 //    promotion overlaps the other's MFMAs (about 30% faster than four waves
 //    of 128 x 64, one per SIMD).
 using TileF8 = Tile<256, 256, 2, 4, 2>;
-using TileF8R = Tile<256, 256, 2, 4, 4>;
 using TileF8B = Tile<256, 128, 4, 2, 3>;
-template <bool MX> using F8GrTile = typename std::conditional<MX, TileF8, TileF8R>::type;
-static_assert(TileF8::BN % 128 == 0 && TileF8R::BN % 128 == 0,
+template <bool MX> using F8GrTile = TileF8;
+static_assert(TileF8::BN % 128 == 0,
               "the SwiGLU-backward epilogue quantises whole 128-column groups of dH");
 template <bool MX> using F8WgTile = typename std::conditional<MX, TileF8, TileF8B>::type;
 
