@@ -241,6 +241,27 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w,
             void* dx, void* dw1, void* dw2, float* dtopk_w,
             void* scratch, size_t scratch_bytes, void* stream);
 
+/* moe_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * forward with the same kernels and results as moe_fwd, run in a scratch
+ * buffer the library owns instead of the caller's.  That buffer is a device
+ * array of MOE_NOALLOC_SCRATCH_BYTES; each GPU the library runs on holds its
+ * own copy from the first call on that device until the process ends.  The
+ * call allocates nothing (make the first call on a device outside graph
+ * capture: it resolves the array's address).  Descriptors whose
+ * moe_scratch_bytes exceeds MOE_NOALLOC_SCRATCH_BYTES return MOE_ESCRATCH (at
+ * the Qwen3-30B shape, about 1,300 tokens at top-8); invalid ones return what
+ * moe_fwd returns.  Arguments, layouts and the other errors are moe_fwd's.
+ * The saved state stays in the library's buffer, so moe_bwd cannot follow this
+ * call (it is a forward for inference), and an expert id out of range is
+ * skipped as in moe_fwd but not reported (moe_check needs the scratch).  Every
+ * call on a GPU shares that GPU's buffer and keeps the last call's contents:
+ * calls that overlap on one GPU (different streams or threads) race. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int moe_fwd_noalloc(const moe_desc* d, const void* x, const int32_t* topk_idx,
+                    const float* topk_w, const void* w1, const void* w2, const void* wprep,
+                    void* y, void* stream);
+
 /* Router ahead of the layer (the step that makes the top-k routing decision the
  * layer consumes: Prime Mega MoE news item, "TL;DR", 128 experts with top-8
  * routing, and "Why is MoE training communication-bound?", each token goes to a

@@ -20,6 +20,7 @@ MOE_OK, MOE_EINVAL, MOE_ESCRATCH, MOE_EALIGN, MOE_EUNSUPPORTED, MOE_EHIP, MOE_EI
 MOE_FLAG_OVERLAP = 0x1
 MOE_FLAG_QUEUE_TIMEOUT_TEST = 0x2
 MOE_FLAG_RECOMPUTE = 0x4
+MOE_NOALLOC_SCRATCH_BYTES = 256 << 20
 (MOE_VIEW_XPERM, MOE_VIEW_H, MOE_VIEW_A, MOE_VIEW_O, MOE_VIEW_DYPERM, MOE_VIEW_DH,
  MOE_VIEW_DXPERM, MOE_VIEW_WPERM, MOE_VIEW_Q_ROWS, MOE_VIEW_Q_ROWS_SCALE, MOE_VIEW_Q_TOK_A,
  MOE_VIEW_Q_TOK_A_SCALE, MOE_VIEW_Q_TOK_B, MOE_VIEW_Q_TOK_B_SCALE, MOE_VIEW_QUEUE) = range(15)
@@ -27,7 +28,7 @@ MOE_FLAG_RECOMPUTE = 0x4
 # Exported symbols, in the order include/moe.h declares them.
 EXPORTS = (
     "moe_scratch_bytes", "moe_wprep_bytes", "moe_prepare_weights", "moe_route",
-    "moe_routing_view", "moe_scratch_view", "moe_fwd", "moe_bwd", "moe_router_fwd",
+    "moe_routing_view", "moe_scratch_view", "moe_fwd", "moe_bwd", "moe_fwd_noalloc", "moe_router_fwd",
     "moe_router_bwd", "moe_check", "moe_strerror", "moe_abi_version", "moe_profile_enable", "moe_profile_collect",
     "moe_profile_get", "moe_profile_reset",
 )
@@ -64,6 +65,7 @@ def lib() -> ctypes.CDLL:
             "moe_scratch_view": (_i32, [_dp, _vp, _sz, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_sz)]),
             "moe_fwd": (_i32, [_dp] + [_vp] * 8 + [_sz, _vp]),
             "moe_bwd": (_i32, [_dp] + [_vp] * 10 + [_sz, _vp]),
+            "moe_fwd_noalloc": (_i32, [_dp] + [_vp] * 8),
             "moe_router_fwd": (_i32, [_dp, _vp, _vp, _vp, _vp]),
             "moe_router_bwd": (_i32, [_dp, _vp, _vp, _vp, _vp, _vp]),
             "moe_check": (_i32, [_dp, _vp, _sz, _vp]),
@@ -163,6 +165,11 @@ def moe_scratch_view(desc, scratch, which: int) -> tuple:
 def moe_fwd(desc, x, topk_idx, topk_w, w1, w2, wprep, y, scratch, stream=None) -> int:
     return lib().moe_fwd(ctypes.byref(desc), _p(x), _p(topk_idx), _p(topk_w), _p(w1), _p(w2),
                          _p(wprep), _p(y), _p(scratch), _nbytes(scratch), _stream(stream))
+
+
+def moe_fwd_noalloc(desc, x, topk_idx, topk_w, w1, w2, wprep, y, stream=None) -> int:
+    return lib().moe_fwd_noalloc(ctypes.byref(desc), _p(x), _p(topk_idx), _p(topk_w), _p(w1),
+                                 _p(w2), _p(wprep), _p(y), _stream(stream))
 
 
 def moe_bwd(desc, dy, topk_w, w1, w2, wprep, dx, dw1, dw2, dtopk_w, scratch, stream=None) -> int:

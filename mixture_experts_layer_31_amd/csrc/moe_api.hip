@@ -242,6 +242,17 @@ int moe_scratch_view(const moe_desc* d, const void* scratch, size_t scratch_byte
 int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const float* topk_w,
             const void* w1, const void* w2, const void* wprep, void* y, void* scratch,
             size_t scratch_bytes, void* stream) {
+  return forward(d, x, topk_idx, topk_w, w1, w2, wprep, y, scratch, scratch_bytes,
+                 static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// The forward behind moe_fwd and moe_fwd_noalloc (which passes the library's
+// own scratch).
+int moe::forward(const moe_desc* d, const void* x, const int32_t* topk_idx, const float* topk_w,
+                 const void* w1, const void* w2, const void* wprep, void* y, void* scratch,
+                 size_t scratch_bytes, hipStream_t s) {
   int rc = check_desc(d);
   if (rc) return rc;
   if ((rc = check_built(d))) return rc;
@@ -255,7 +266,6 @@ int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const flo
   if ((rc = gemm_weights(*d, w1, w2, wprep, &g1, &g2))) return rc;
   const Layout L = make_layout(*d);
   char* sc = static_cast<char*>(scratch);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const bool io_f32 = d->mode == MOE_FP32 || d->mode == MOE_FP32_BF16GEMM;
   if ((rc = launch_route(*d, L, topk_idx, sc, s))) return rc;
   if (d->T == 0) return MOE_OK;  // routing metadata of no pairs; y is empty
@@ -284,6 +294,8 @@ int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const flo
   if (rc) return rc;
   return launch_combine(*d, L, topk_w, y, io_f32, sc, s);
 }
+
+extern "C" {
 
 int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* w1,
             const void* w2, const void* wprep, void* dx, void* dw1, void* dw2, float* dtopk_w,

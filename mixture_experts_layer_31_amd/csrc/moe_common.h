@@ -87,6 +87,12 @@ inline Layout make_layout(const moe_desc& d) {
 // Tile heights for which the routing step writes per-expert m-tile prefix sums.
 constexpr int kTileRows[3] = {64, 128, 256};
 
+// The whole forward (validation, routing, dispatch, GEMMs, combine) into the
+// given scratch; moe_fwd and moe_fwd_noalloc (moe_noalloc.hip) call it.
+int forward(const moe_desc* d, const void* x, const int32_t* topk_idx, const float* topk_w,
+            const void* w1, const void* w2, const void* wprep, void* y, void* scratch,
+            size_t scratch_bytes, hipStream_t s);
+
 // ---- launch helpers (host), implemented in moe_api.hip ----
 // Every kernel launch goes through these so the opt-in profiler can bracket it.
 void prof_begin(const char* name, hipStream_t s);

@@ -233,3 +233,17 @@ def test_queue_view_matches_the_mirrored_region():
         r = qt.region_offsets(T * K, E, 2 * F // 256, D // 256)
         assert r["table"] + 4 * r["table_words"] <= sz.value
         assert p.value + sz.value <= FAKE + n
+
+
+def test_noalloc_forward_validation():
+    """moe_fwd_noalloc refuses a layer whose scratch exceeds its own buffer and
+    returns moe_fwd's validation error for an invalid descriptor, before any
+    GPU call."""
+    L = moe.lib()
+    big = moe.make_desc(16384, 2048, 768, 128, 8)
+    assert moe.moe_scratch_bytes(big) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None)
+    assert L.moe_fwd_noalloc(ctypes.byref(big), *args) == moe.MOE_ESCRATCH
+    assert L.moe_fwd_noalloc(ctypes.byref(moe.make_desc(64, 100, 64, 8, 2)), *args) == moe.MOE_EUNSUPPORTED
+    assert L.moe_fwd_noalloc(ctypes.byref(moe.make_desc(-1, 128, 64, 8, 2)), *args) == moe.MOE_EINVAL
+    assert L.moe_fwd_noalloc(None, *args) == moe.MOE_EINVAL
