@@ -49,7 +49,9 @@ def gemm_flops(cfg) -> dict:
     """Algorithmic FLOPs per launch of each GEMM kernel (2 per multiply-add)."""
     ndf = float(cfg.N) * cfg.D * cfg.F
     return {"gemm_w1_swiglu": 4 * ndf, "gemm_w2": 2 * ndf, "gemm_w2_dgrad_dswiglu": 2 * ndf,
-            "gemm_w2_wgrad": 2 * ndf, "gemm_w1_dgrad": 4 * ndf, "gemm_w1_wgrad": 4 * ndf}
+            "gemm_w2_wgrad": 2 * ndf, "gemm_w1_dgrad": 4 * ndf, "gemm_w1_wgrad": 4 * ndf,
+            # paired backward launches: each dgrad with its weight gradient
+            "pair_w2": 4 * ndf, "pair_w1": 8 * ndf}
 
 
 def row_bytes(cfg, b=2) -> dict:
@@ -357,6 +359,11 @@ def main():
                     help="time the overlapped one-launch forward instead of one kernel per step")
     ap.add_argument("--recompute", action="store_true",
                     help="activation recompute: the forward keeps no H, the backward rebuilds it")
+    ap.add_argument("--overlap-bwd", action="store_true",
+                    help="backward with each dgrad beside its weight gradient in one launch "
+                         "(the default in bf16)")
+    ap.add_argument("--serial-bwd", action="store_true",
+                    help="backward with one kernel per GEMM")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's layer only: the expert-parallel exchange between "
@@ -367,7 +374,10 @@ def main():
     import moe_inputs as mi
 
     cfg = mi.CONFIGS[args.config]
-    flags = (moe.MOE_FLAG_OVERLAP if args.overlap else 0) | (moe.MOE_FLAG_RECOMPUTE if args.recompute else 0)
+    flags = ((moe.MOE_FLAG_OVERLAP if args.overlap else 0) |
+             (moe.MOE_FLAG_RECOMPUTE if args.recompute else 0) |
+             (moe.MOE_FLAG_OVERLAP_BWD if args.overlap_bwd else 0) |
+             (moe.MOE_FLAG_SERIAL_BWD if args.serial_bwd else 0))
     if args.extra is None:
         extra = list(EXTRA_CONFIGS) if args.config == "30b" and not flags else []
     else:

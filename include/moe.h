@@ -110,6 +110,21 @@ enum moe_status {
  * output is bit-identical to the default; the backward does 4*T*K*D*F more
  * flops.  MOE_VIEW_H is not available (MOE_EINVAL).  All modes. */
 #define MOE_FLAG_RECOMPUTE 0x4u
+/* Backward with each dgrad and its weight gradient in one launch: W2 dgrad +
+ * SwiGLU-backward beside the W2 weight gradient, then the W1 dgrad beside the
+ * W1 weight gradient, their tiles taken from shared per-XCD queues, so that
+ * one GEMM's tiles fill the other's tail and their epilogues fall between the
+ * other's main loops (the single-GPU form of the overlapping backward the
+ * pages add to the fused kernel: Prime Mega MoE news item, "How does the fused
+ * kernel work?").  Needs D % 256 == 0, F % 256 == 0 and E <= 256, in MOE_BF16
+ * and the FP8 modes.  It is the default for MOE_BF16, where it measured 0.7-0.9%
+ * faster on MI355X at the Qwen3 shapes; MOE_FLAG_OVERLAP_BWD selects it in the
+ * FP8 modes too (there it measured 2-3% slower), MOE_FLAG_SERIAL_BWD selects
+ * one kernel per GEMM in every mode, and setting both is MOE_EINVAL.  Results
+ * are bit-identical either way (the same tile code in the same accumulation
+ * order). */
+#define MOE_FLAG_OVERLAP_BWD 0x8u
+#define MOE_FLAG_SERIAL_BWD 0x10u
 
 /* Layer descriptor, passed by host pointer.  Requirements: T >= 0; E, K >= 1;
  * K <= E; E <= 1024; D % 64 == 0 and F % 64 == 0; T * K < 2^31 (else

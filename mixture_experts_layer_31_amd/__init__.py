@@ -20,6 +20,8 @@ MOE_OK, MOE_EINVAL, MOE_ESCRATCH, MOE_EALIGN, MOE_EUNSUPPORTED, MOE_EHIP, MOE_EI
 MOE_FLAG_OVERLAP = 0x1
 MOE_FLAG_QUEUE_TIMEOUT_TEST = 0x2
 MOE_FLAG_RECOMPUTE = 0x4
+MOE_FLAG_OVERLAP_BWD = 0x8
+MOE_FLAG_SERIAL_BWD = 0x10
 MOE_NOALLOC_SCRATCH_BYTES = 256 << 20
 (MOE_VIEW_XPERM, MOE_VIEW_H, MOE_VIEW_A, MOE_VIEW_O, MOE_VIEW_DYPERM, MOE_VIEW_DH,
  MOE_VIEW_DXPERM, MOE_VIEW_WPERM, MOE_VIEW_Q_ROWS, MOE_VIEW_Q_ROWS_SCALE, MOE_VIEW_Q_TOK_A,

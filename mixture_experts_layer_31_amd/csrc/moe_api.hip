@@ -18,8 +18,10 @@ int check_desc(const moe_desc* d) {
   if (d->T < 0 || d->D <= 0 || d->F <= 0 || d->E <= 0 || d->K <= 0) return MOE_EINVAL;
   if (d->K > d->E || d->E > 1024) return MOE_EINVAL;
   if (d->mode < MOE_FP32 || d->mode > MOE_FP8) return MOE_EINVAL;
-  if ((d->flags & ~int32_t(MOE_FLAG_OVERLAP | MOE_FLAG_QUEUE_TIMEOUT_TEST | MOE_FLAG_RECOMPUTE)) != 0)
+  if ((d->flags & ~int32_t(MOE_FLAG_OVERLAP | MOE_FLAG_QUEUE_TIMEOUT_TEST | MOE_FLAG_RECOMPUTE |
+                           MOE_FLAG_OVERLAP_BWD | MOE_FLAG_SERIAL_BWD)) != 0)
     return MOE_EINVAL;
+  if ((d->flags & MOE_FLAG_OVERLAP_BWD) && (d->flags & MOE_FLAG_SERIAL_BWD)) return MOE_EINVAL;
   const long long N = (long long)d->T * d->K;
   const long long widest = d->D > 2 * d->F ? d->D : 2 * d->F;
   if (N >= (1LL << 31) || N * widest >= (1LL << 46)) return MOE_EINVAL;

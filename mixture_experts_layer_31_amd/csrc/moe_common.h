@@ -36,7 +36,7 @@ constexpr int kRouteThreads = 256;
 // starts on a 256-byte boundary.  The layout depends only on the descriptor.
 struct Layout {
   size_t err, counts, offsets, tiles[3], eorder, chunk_cnt, chunk_bad, pos, src, wperm;
-  size_t xperm, h, a, o, dyperm, dh, dxperm, fp8, queue, total;
+  size_t xperm, h, a, o, dyperm, dh, dxperm, fp8, queue, pair, total;
   bool recompute;   // MOE_FLAG_RECOMPUTE: no H region; H is rebuilt in the dH region
   int nchunks;      // routing chunks
   int act_bytes;    // bytes per intermediate element
@@ -80,6 +80,7 @@ inline Layout make_layout(const moe_desc& d) {
   if (L.recompute) L.h = L.dh;  // written by the backward's recompute, then overwritten by dH
   L.fp8 = take(fp8_scratch_bytes(d));
   L.queue = take(queue_scratch_bytes(d));
+  L.pair = take(2 * 8 * 4);  // ticket counters of the paired backward launches
   L.total = o;
   return L;
 }
@@ -133,6 +134,9 @@ int launch_fwd_gemms_f32(const moe_desc& d, const Layout& L, const float* w1, co
                          char* scratch, hipStream_t s);
 int launch_bwd_gemms_f32(const moe_desc& d, const Layout& L, const float* w1, const float* w2,
                          float* dw1, float* dw2, char* scratch, hipStream_t s);
+// Backward GEMMs in pairs (each dgrad beside its weight gradient in one
+// launch, moe_pair.h): when the descriptor and shapes allow it.
+bool pair_capable(const moe_desc& d);
 // Persistent forward (dispatch + W1 + SwiGLU + W2 in one launch); see moe_queue.hip.
 bool queue_capable(const moe_desc& d);
 int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_f32,

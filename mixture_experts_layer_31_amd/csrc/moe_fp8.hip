@@ -30,6 +30,7 @@
 
 #include "moe_fp8_codec.h"
 #include "moe_gemm_common.h"
+#include "moe_pair.h"
 
 namespace moe {
 namespace {
@@ -652,6 +653,27 @@ __global__ void __launch_bounds__(TL::THREADS, 1) f8_wgrad_kernel(F8Args p) {
   f8_wgrad_tile<TL, MX, OUT_F32>(p, expert_tile_start(p.eorder, p.E), smem);
 }
 
+// A token-grouped FP8 GEMM (TLA) and an FP8 weight gradient (TLB) in one
+// launch over the paired schedule of moe_pair.h.
+template <class TLA, bool MX, int EPI, class TLB>
+__global__ void __launch_bounds__(TLA::THREADS, 1) f8_pair_kernel(F8Args a, F8Args b, PairSched ps) {
+  static_assert(TLA::THREADS == TLB::THREADS, "one workgroup shape for both GEMMs");
+  constexpr int LA = f8_grouped_lds<TLA, MX>(), LB = f8_wgrad_lds<TLB>();
+  constexpr int PIPE = LA > LB ? LA : LB;
+  __shared__ __attribute__((aligned(1024))) char smem[PIPE + sizeof(PairLds)];
+  PairLds& L = *reinterpret_cast<PairLds*>(smem + PIPE);
+  pair_setup<TLA::THREADS>(ps, L);
+  int q = blockIdx.x % kPairQueues;
+  for (;;) {
+    const int g = pair_next(ps, L, &q);
+    if (g < 0) break;
+    const PairItem it = pair_decode(ps, L, g);
+    if (it.is_a) f8_grouped_tile<TLA, MX, EPI>(a, it.l, smem);
+    else f8_wgrad_tile<TLB, MX, false>(b, it.l, smem);
+    __syncthreads();  // the next item's loads overwrite this one's epilogue staging
+  }
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -815,6 +837,42 @@ int run_f8_wgrad(const moe_desc& d, const Layout& L, F8Args a, const char* name,
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
+// The token-grouped GEMM a (operands set) and the weight gradient b (operands
+// set) in one paired launch.
+template <bool MX, int EPI>
+int run_f8_pair(const moe_desc& d, const Layout& L, F8Args a, int N, F8Args b, int* ctr,
+                const char* name, char* scratch, hipStream_t s) {
+  using TA = F8GrTile<MX>;
+  using TB = F8WgTile<MX>;
+  a.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
+  a.tstart = reinterpret_cast<const int32_t*>(scratch + L.tiles[2]);  // 256-row m-tiles
+  a.E = d.E;
+  a.ntn = N / TA::BN;
+  a.N = N;
+  a.nmajor = EPI == EPI_STORE;
+  b.offsets = a.offsets;
+  b.tstart = reinterpret_cast<const int32_t*>(scratch + L.tiles[1]);  // 128-token steps
+  b.eorder = reinterpret_cast<const int32_t*>(scratch + L.eorder);
+  b.E = d.E;
+  b.tm = b.M / TB::BM;
+  b.tn = b.N / TB::BN;
+  PairSched ps{};
+  ps.offsets = a.offsets;
+  ps.tstart = a.tstart;
+  ps.eorder = b.eorder;
+  ps.E = d.E;
+  ps.ntn = a.ntn;
+  ps.per_b = b.tm * b.tn;
+  ps.cost_a = a.K;
+  ps.ctr = ctr;
+  int resident;
+  if (int rc = resident_grid<f8_pair_kernel<TA, MX, EPI, TB>>(TA::THREADS, &resident)) return rc;
+  prof_begin(name, s);
+  f8_pair_kernel<TA, MX, EPI, TB><<<unsigned(resident), TA::THREADS, 0, s>>>(a, b, ps);
+  prof_end(s);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
 // Regions of the prepared-weight buffer.
 struct WLayout {
   size_t w1f, w1f_sc, w2f, w2f_sc, w2t, w2t_sc, w1t, w1t_sc, total;
@@ -855,8 +913,11 @@ size_t fp8_scratch_bytes(const moe_desc& d) {
   size_t o = 0;
   o = align256(o + N * C);                 // row-quantised codes
   o = align256(o + (C / 128) * N * 4);     // their scale entries
-  for (int i = 0; i < 2; ++i) {
-    o = align256(o + C * npad);            // token-quantised codes
+  // token-quantised codes and scales: two buffers, a third for the paired
+  // backward (dYw's token codes, while the W2 dgrad still reads its row codes)
+  const int nt = pair_capable(d) ? 3 : 2;
+  for (int i = 0; i < nt; ++i) {
+    o = align256(o + C * npad);
     o = align256(o + (npad / 128) * C * 4);
   }
   return o;
@@ -885,8 +946,8 @@ int fp8_prepare_weights(const moe_desc& d, const uint16_t* w1, const uint16_t* w
 
 // Scratch regions of the FP8 operands (after the bf16 layout).
 struct F8Scratch {
-  uint8_t *qrow, *qt1, *qt2;
-  uint32_t *qrow_sc, *qt1_sc, *qt2_sc;
+  uint8_t *qrow, *qt1, *qt2, *qt3;
+  uint32_t *qrow_sc, *qt1_sc, *qt2_sc, *qt3_sc;
   size_t qrow_sc_bytes, qt_sc_bytes;
 };
 
@@ -909,6 +970,12 @@ static F8Scratch f8scratch(const moe_desc& d, const Layout& L, char* scratch) {
   f.qt2 = reinterpret_cast<uint8_t*>(b + o);
   o = align256(o + C * npad);
   f.qt2_sc = reinterpret_cast<uint32_t*>(b + o);
+  o = align256(o + f.qt_sc_bytes);
+  if (pair_capable(d)) {
+    f.qt3 = reinterpret_cast<uint8_t*>(b + o);
+    o = align256(o + C * npad);
+    f.qt3_sc = reinterpret_cast<uint32_t*>(b + o);
+  }
   return f;
 }
 
@@ -1025,6 +1092,7 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   const WLayout W = wlayout(d);
   const F8Scratch f = f8scratch(d, L, scratch);
   const bool mx = d.mode == MOE_MXFP8;
+  const bool paired = pair_capable(d);
   const int D = d.D, F = d.F, N = d.T * d.K;
   const int64_t npad = int64_t(max_steps128(d)) * 128;
   const auto* dyw = reinterpret_cast<const uint16_t*>(scratch + L.dyperm);
@@ -1032,7 +1100,8 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   const auto* dh = reinterpret_cast<const uint16_t*>(scratch + L.dh);
   const auto* xp = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
   int rc;
-  // W2 dgrad + SwiGLU-backward; its epilogue also writes dH's row codes for the W1 dgrad
+  // W2 dgrad + SwiGLU-backward on dYw's row codes (in the first token-code
+  // buffer); its epilogue also writes dH's row codes for the W1 dgrad
   if (!dyw_quantised && (rc = quant_rows(d, dyw, D, mx, f.qt1, f.qt1_sc, "quant_dyw_rows", s)))
     return rc;
   F8Args a{};
@@ -1051,18 +1120,17 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   a.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.dh), 0, nullptr,
                   reinterpret_cast<const uint16_t*>(scratch + L.h), F, f.qrow, f.qrow_sc, N,
                   mx ? QM_MX : QM_BLOCK};
-  rc = mx ? run_f8_grouped<true, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s)
-          : run_f8_grouped<false, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s);
-  if (rc) return rc;
-  // W2 wgrad over tokens
-  if ((rc = quant_tokens(d, L, dyw, D, mx, f.qt1, f.qt1_sc, "quant_dyw_tokens", scratch, s))) return rc;
-  if ((rc = quant_tokens(d, L, act, F, mx, f.qt2, f.qt2_sc, "quant_a_tokens", scratch, s))) return rc;
+  // W2 wgrad over tokens: dYw's token codes (in the first buffer once the W2
+  // dgrad is done with the row codes there; in the third when both run in one
+  // launch) and A's (in the second)
+  uint8_t* dyt = paired ? f.qt3 : f.qt1;
+  uint32_t* dyt_sc = paired ? f.qt3_sc : f.qt1_sc;
   F8Args w{};
   w.M = D;
   w.N = F;
-  w.A = f.qt1;
+  w.A = dyt;
   w.lda = npad;
-  w.SA = f.qt1_sc;
+  w.SA = dyt_sc;
   w.sa_ld = D;
   w.sa_bytes = uint32_t(f.qt_sc_bytes);
   w.B = f.qt2;
@@ -1071,55 +1139,72 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   w.sb_ld = F;
   w.sb_bytes = uint32_t(f.qt_sc_bytes);
   w.C = dw2;
+  // W1 wgrad over tokens: dH's token codes (first buffer) and x_perm's (second)
+  F8Args v{};
+  v.M = 2 * F;
+  v.N = D;
+  v.A = f.qt1;
+  v.lda = npad;
+  v.SA = f.qt1_sc;
+  v.sa_ld = 2 * F;
+  v.sa_bytes = uint32_t(f.qt_sc_bytes);
+  v.B = f.qt2;
+  v.ldb = npad;
+  v.SB = f.qt2_sc;
+  v.sb_ld = D;
+  v.sb_bytes = uint32_t(f.qt_sc_bytes);
+  v.C = dw1;
+  // W1 dgrad on dH's row codes
+  F8Args b{};
+  b.K = 2 * F;
+  b.A = f.qrow;
+  b.SA = f.qrow_sc;
+  b.sa_ld = N;
+  b.sa_bytes = uint32_t(size_t(2 * F / 128) * N * 4);
+  b.B = reinterpret_cast<const uint8_t*>(wprep + W.w1t);
+  b.b_bstride = int64_t(D) * 2 * F;
+  b.SB = reinterpret_cast<const uint32_t*>(wprep + W.w1t_sc);
+  b.sb_ld = D;
+  b.sb_bstride = int64_t(2 * F / 128) * D;
+  b.sb_bytes = uint32_t(size_t(2 * F / 128) * D * 4);
+  b.F = F;
+  b.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.dxperm), D, nullptr, nullptr, F};
+
+  if (paired) {  // each dgrad beside its weight gradient, one launch per pair
+    int* ctr = reinterpret_cast<int*>(scratch + L.pair);
+    if ((rc = launch_zero(ctr, 2 * kPairQueues * sizeof(int), s))) return rc;
+    if ((rc = quant_tokens(d, L, dyw, D, mx, f.qt3, f.qt3_sc, "quant_dyw_tokens", scratch, s))) return rc;
+    if ((rc = quant_tokens(d, L, act, F, mx, f.qt2, f.qt2_sc, "quant_a_tokens", scratch, s))) return rc;
+    rc = mx ? run_f8_pair<true, EPI_DSWIGLU>(d, L, a, F, w, ctr, "pair_w2", scratch, s)
+            : run_f8_pair<false, EPI_DSWIGLU>(d, L, a, F, w, ctr, "pair_w2", scratch, s);
+    if (rc) return rc;
+    if ((rc = quant_tokens(d, L, dh, 2 * F, mx, f.qt1, f.qt1_sc, "quant_dh_tokens", scratch, s))) return rc;
+    if ((rc = quant_tokens(d, L, xp, D, mx, f.qt2, f.qt2_sc, "quant_x_tokens", scratch, s))) return rc;
+    return mx ? run_f8_pair<true, EPI_STORE>(d, L, b, D, v, ctr + kPairQueues, "pair_w1", scratch, s)
+              : run_f8_pair<false, EPI_STORE>(d, L, b, D, v, ctr + kPairQueues, "pair_w1", scratch, s);
+  }
+
+  rc = mx ? run_f8_grouped<true, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s)
+          : run_f8_grouped<false, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s);
+  if (rc) return rc;
+  if ((rc = quant_tokens(d, L, dyw, D, mx, f.qt1, f.qt1_sc, "quant_dyw_tokens", scratch, s))) return rc;
+  if ((rc = quant_tokens(d, L, act, F, mx, f.qt2, f.qt2_sc, "quant_a_tokens", scratch, s))) return rc;
   rc = mx ? run_f8_wgrad<true>(d, L, w, "gemm_w2_wgrad", scratch, s)
           : run_f8_wgrad<false>(d, L, w, "gemm_w2_wgrad", scratch, s);
   if (rc) return rc;
-  // W1 wgrad over tokens and W1 dgrad on dH's row codes.  Blockwise runs the
-  // wgrad first, so that the un-permute reads dX_perm right after it is written
-  // (235B fp8_bwd backward -0.8%; the token quantisers leave dH's row codes
-  // alone); MXFP8 keeps the dgrad first, right after the W2 dgrad wrote those
-  // codes (0.5% faster there).
+  // W1 wgrad and W1 dgrad.  Blockwise runs the wgrad first, so that the
+  // un-permute reads dX_perm right after it is written (235B fp8_bwd backward
+  // -0.8%; the token quantisers leave dH's row codes alone); MXFP8 keeps the
+  // dgrad first, right after the W2 dgrad wrote those codes (0.5% faster there).
   auto w1_wgrad = [&]() -> int {
     if ((rc = quant_tokens(d, L, dh, 2 * F, mx, f.qt1, f.qt1_sc, "quant_dh_tokens", scratch, s))) return rc;
     if ((rc = quant_tokens(d, L, xp, D, mx, f.qt2, f.qt2_sc, "quant_x_tokens", scratch, s))) return rc;
-    F8Args v{};
-    v.M = 2 * F;
-    v.N = D;
-    v.A = f.qt1;
-    v.lda = npad;
-    v.SA = f.qt1_sc;
-    v.sa_ld = 2 * F;
-    v.sa_bytes = uint32_t(f.qt_sc_bytes);
-    v.B = f.qt2;
-    v.ldb = npad;
-    v.SB = f.qt2_sc;
-    v.sb_ld = D;
-    v.sb_bytes = uint32_t(f.qt_sc_bytes);
-    v.C = dw1;
-    rc = mx ? run_f8_wgrad<true>(d, L, v, "gemm_w1_wgrad", scratch, s)
-            : run_f8_wgrad<false>(d, L, v, "gemm_w1_wgrad", scratch, s);
-    if (rc) return rc;
-    return MOE_OK;
+    return mx ? run_f8_wgrad<true>(d, L, v, "gemm_w1_wgrad", scratch, s)
+              : run_f8_wgrad<false>(d, L, v, "gemm_w1_wgrad", scratch, s);
   };
   auto w1_dgrad = [&]() -> int {
-    // W1 dgrad on dH's row codes
-    F8Args b{};
-    b.K = 2 * F;
-    b.A = f.qrow;
-    b.SA = f.qrow_sc;
-    b.sa_ld = N;
-    b.sa_bytes = uint32_t(size_t(2 * F / 128) * N * 4);
-    b.B = reinterpret_cast<const uint8_t*>(wprep + W.w1t);
-    b.b_bstride = int64_t(D) * 2 * F;
-    b.SB = reinterpret_cast<const uint32_t*>(wprep + W.w1t_sc);
-    b.sb_ld = D;
-    b.sb_bstride = int64_t(2 * F / 128) * D;
-    b.sb_bytes = uint32_t(size_t(2 * F / 128) * D * 4);
-    b.F = F;
-    b.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.dxperm), D, nullptr, nullptr, F};
-    rc = mx ? run_f8_grouped<true, EPI_STORE>(d, L, b, D, "gemm_w1_dgrad", scratch, s)
-            : run_f8_grouped<false, EPI_STORE>(d, L, b, D, "gemm_w1_dgrad", scratch, s);
-    return rc;
+    return mx ? run_f8_grouped<true, EPI_STORE>(d, L, b, D, "gemm_w1_dgrad", scratch, s)
+              : run_f8_grouped<false, EPI_STORE>(d, L, b, D, "gemm_w1_dgrad", scratch, s);
   };
   if (mx) {
     if ((rc = w1_dgrad())) return rc;

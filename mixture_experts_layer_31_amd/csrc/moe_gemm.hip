@@ -53,6 +53,7 @@
 // consecutive tiles of one expert land on the same XCD (hardware dispatch is
 // round-robin over the 8 XCDs) and share its L2.
 #include "moe_grouped.h"
+#include "moe_pair.h"
 
 namespace moe {
 namespace {
@@ -128,6 +129,28 @@ template <class TL, bool OUT_F32>
 __global__ void __launch_bounds__(TL::THREADS, 1) wgrad_gemm_kernel(WgradArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
   wgrad_tile<TL, OUT_F32>(p, expert_tile_start(p.eorder, p.E), smem);
+}
+
+// A token-grouped GEMM (TLA, B_T, EPI) and a weight gradient (TLB) in one
+// launch over the paired schedule of moe_pair.h: a grid of resident
+// workgroups takes items until every queue is exhausted.
+template <class TLA, bool B_T, int EPI, class TLB, bool OUT_F32>
+__global__ void __launch_bounds__(TLA::THREADS, 1) pair_kernel(GroupedArgs a, WgradArgs b,
+                                                               PairSched ps) {
+  static_assert(TLA::THREADS == TLB::THREADS, "one workgroup shape for both GEMMs");
+  constexpr int PIPE = TLA::LDS > TLB::LDS ? TLA::LDS : TLB::LDS;
+  __shared__ __attribute__((aligned(1024))) char smem[PIPE + sizeof(PairLds)];
+  PairLds& L = *reinterpret_cast<PairLds*>(smem + PIPE);
+  pair_setup<TLA::THREADS>(ps, L);
+  int q = blockIdx.x % kPairQueues;
+  for (;;) {
+    const int g = pair_next(ps, L, &q);
+    if (g < 0) break;
+    const PairItem it = pair_decode(ps, L, g);
+    if (it.is_a) grouped_tile<TLA, B_T, EPI>(a, decode_tile<TLA::BM>(a, it.l), smem);
+    else wgrad_tile<TLB, OUT_F32>(b, it.l, smem);
+    __syncthreads();  // the next item's loads overwrite this one's epilogue staging
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -213,6 +236,40 @@ int run_wgrad_any(const moe_desc& d, const Layout& L, WgradArgs a, const char* n
   return run_wgrad<TileWg64x64, OUT_F32>(d, L, a, name, scratch, s);
 }
 
+// The token-grouped GEMM a (fully set up except for the routing pointers) and
+// the weight gradient b in one paired launch; both on 256 x 256 tiles.
+template <bool B_T, int EPI, bool OUT_F32>
+int run_pair(const moe_desc& d, const Layout& L, GroupedArgs a, int N, WgradArgs b, int* ctr,
+             const char* name, char* scratch, hipStream_t s) {
+  using TA = TileBig;
+  using TB = TileBig;
+  a.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
+  a.tile_start = reinterpret_cast<const int32_t*>(scratch + L.tiles[tile_index(TA::BM)]);
+  a.E = d.E;
+  a.ntn = N / TA::BN;
+  a.nmajor = EPI == EPI_STORE;  // as the grouped GEMM launched alone
+  b.offsets = a.offsets;
+  b.eorder = reinterpret_cast<const int32_t*>(scratch + L.eorder);
+  b.E = d.E;
+  b.tm = b.M / TB::BM;
+  b.tn = b.N / TB::BN;
+  PairSched ps{};
+  ps.offsets = a.offsets;
+  ps.tstart = a.tile_start;
+  ps.eorder = b.eorder;
+  ps.E = d.E;
+  ps.ntn = a.ntn;
+  ps.per_b = b.tm * b.tn;
+  ps.cost_a = a.K;
+  ps.ctr = ctr;
+  int resident;
+  if (int rc = resident_grid<pair_kernel<TA, B_T, EPI, TB, OUT_F32>>(TA::THREADS, &resident)) return rc;
+  prof_begin(name, s);
+  pair_kernel<TA, B_T, EPI, TB, OUT_F32><<<unsigned(resident), TA::THREADS, 0, s>>>(a, b, ps);
+  prof_end(s);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
 // Expert linear 1 with the SwiGLU epilogue; W1[e] is [2F, D].  Stores H into
 // `h` and A into `act` (either may be null: the recompute forward skips H, the
 // backward's recompute skips A).
@@ -264,65 +321,82 @@ int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, con
   return MOE_OK;
 }
 
+// Paired by default in bf16 (measured 0.7-0.9% faster at the 30B and 235B
+// shapes), on request in the FP8 modes (measured 2-3% slower there: their
+// quantisers already sit between the GEMMs, and the paired launch needs the
+// larger of the two tiles' LDS).
+bool pair_capable(const moe_desc& d) {
+  if (d.flags & MOE_FLAG_SERIAL_BWD) return false;
+  const bool want = (d.flags & MOE_FLAG_OVERLAP_BWD) || d.mode == MOE_BF16;
+  return want && (d.mode == MOE_BF16 || fp8_mode(d.mode)) && d.D % 256 == 0 &&
+         d.F % 256 == 0 && d.E <= kPairMaxE;
+}
+
 int launch_bwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
                      void* dw1, void* dw2, bool dw_f32, char* scratch, hipStream_t s) {
   const int D = d.D, F = d.F;
   int rc;
-  {  // W2 wgrad: dW2[e] = sum_r dYw_perm[r] A[r]^T (first: the W2 dgrad after it then
-     // finds dYw in the caches, 5% faster at the 30B shape)
-    WgradArgs a{};
-    a.M = D;
-    a.N = F;
-    a.A = reinterpret_cast<const uint16_t*>(scratch + L.dyperm);
-    a.B = reinterpret_cast<const uint16_t*>(scratch + L.a);
-    a.C = dw2;
-    rc = dw_f32 ? run_wgrad_any<true>(d, L, a, "gemm_w2_wgrad", scratch, s)
-                : run_wgrad_any<false>(d, L, a, "gemm_w2_wgrad", scratch, s);
-    if (rc) return rc;
+  // W2 wgrad: dW2[e] = sum_r dYw_perm[r] A[r]^T
+  WgradArgs w2g{};
+  w2g.M = D;
+  w2g.N = F;
+  w2g.A = reinterpret_cast<const uint16_t*>(scratch + L.dyperm);
+  w2g.B = reinterpret_cast<const uint16_t*>(scratch + L.a);
+  w2g.C = dw2;
+  // W2 dgrad (dA = dYw W2[e], W2[e] is [D, F] = [K, N]) with SwiGLU-backward epilogue
+  GroupedArgs w2d{};
+  w2d.K = D;
+  w2d.F = F;
+  w2d.A = reinterpret_cast<const uint16_t*>(scratch + L.dyperm);
+  w2d.lda = D;
+  w2d.B = w2;
+  w2d.bstride = int64_t(D) * F;
+  w2d.ldb = F;
+  w2d.brows = D;
+  w2d.out = reinterpret_cast<uint16_t*>(scratch + L.dh);
+  w2d.hsave = reinterpret_cast<const uint16_t*>(scratch + L.h);
+  // W1 wgrad: dW1[e] = sum_r dH[r] x_perm[r]^T
+  WgradArgs w1g{};
+  w1g.M = 2 * F;
+  w1g.N = D;
+  w1g.A = reinterpret_cast<const uint16_t*>(scratch + L.dh);
+  w1g.B = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
+  w1g.C = dw1;
+  // W1 dgrad: dX_perm = dH W1[e], W1[e] is [2F, D] = [K, N]
+  GroupedArgs w1d{};
+  w1d.K = 2 * F;
+  w1d.F = F;
+  w1d.A = reinterpret_cast<const uint16_t*>(scratch + L.dh);
+  w1d.lda = 2 * F;
+  w1d.B = w1;
+  w1d.bstride = int64_t(2) * F * D;
+  w1d.ldb = D;
+  w1d.brows = 2 * F;
+  w1d.out = reinterpret_cast<uint16_t*>(scratch + L.dxperm);
+  w1d.ldo = D;
+
+  if (pair_capable(d) && !dw_f32) {
+    // each dgrad beside its weight gradient, one launch per pair
+    int* ctr = reinterpret_cast<int*>(scratch + L.pair);
+    if ((rc = launch_zero(ctr, 2 * kPairQueues * sizeof(int), s))) return rc;
+    if ((rc = run_pair<true, EPI_DSWIGLU, false>(d, L, w2d, F, w2g, ctr, "pair_w2", scratch, s)))
+      return rc;
+    return run_pair<true, EPI_STORE, false>(d, L, w1d, D, w1g, ctr + kPairQueues, "pair_w1",
+                                            scratch, s);
   }
-  {  // W2 dgrad (dA = dYw W2[e], W2[e] is [D, F] = [K, N]) with SwiGLU-backward epilogue
-    GroupedArgs a{};
-    a.K = D;
-    a.F = F;
-    a.A = reinterpret_cast<const uint16_t*>(scratch + L.dyperm);
-    a.lda = D;
-    a.B = w2;
-    a.bstride = int64_t(D) * F;
-    a.ldb = F;
-    a.brows = D;
-    a.out = reinterpret_cast<uint16_t*>(scratch + L.dh);
-    a.hsave = reinterpret_cast<const uint16_t*>(scratch + L.h);
-    rc = run_grouped_any<true, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s);
-    if (rc) return rc;
-  }
-  {  // W1 wgrad: dW1[e] = sum_r dH[r] x_perm[r]^T (before the W1 dgrad, so that the
-     // un-permute reads dX_perm right after it is written)
-    WgradArgs a{};
-    a.M = 2 * F;
-    a.N = D;
-    a.A = reinterpret_cast<const uint16_t*>(scratch + L.dh);
-    a.B = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
-    a.C = dw1;
-    rc = dw_f32 ? run_wgrad_any<true>(d, L, a, "gemm_w1_wgrad", scratch, s)
-                : run_wgrad_any<false>(d, L, a, "gemm_w1_wgrad", scratch, s);
-    if (rc) return rc;
-  }
-  {  // W1 dgrad: dX_perm = dH W1[e], W1[e] is [2F, D] = [K, N]
-    GroupedArgs a{};
-    a.K = 2 * F;
-    a.F = F;
-    a.A = reinterpret_cast<const uint16_t*>(scratch + L.dh);
-    a.lda = 2 * F;
-    a.B = w1;
-    a.bstride = int64_t(2) * F * D;
-    a.ldb = D;
-    a.brows = 2 * F;
-    a.out = reinterpret_cast<uint16_t*>(scratch + L.dxperm);
-    a.ldo = D;
-    rc = run_grouped_any<true, EPI_STORE>(d, L, a, D, "gemm_w1_dgrad", scratch, s);
-    if (rc) return rc;
-  }
-  return MOE_OK;
+  // one kernel per GEMM.  The W2 weight gradient runs first (the W2 dgrad after
+  // it then finds dYw in the caches, 5% faster at the 30B shape), and the W1
+  // weight gradient before the W1 dgrad (so that the un-permute reads dX_perm
+  // right after it is written)
+  rc = dw_f32 ? run_wgrad_any<true>(d, L, w2g, "gemm_w2_wgrad", scratch, s)
+              : run_wgrad_any<false>(d, L, w2g, "gemm_w2_wgrad", scratch, s);
+  if (rc) return rc;
+  if ((rc = run_grouped_any<true, EPI_DSWIGLU>(d, L, w2d, F, "gemm_w2_dgrad_dswiglu", scratch, s)))
+    return rc;
+  rc = dw_f32 ? run_wgrad_any<true>(d, L, w1g, "gemm_w1_wgrad", scratch, s)
+              : run_wgrad_any<false>(d, L, w1g, "gemm_w1_wgrad", scratch, s);
+  if (rc) return rc;
+  return run_grouped_any<true, EPI_STORE>(d, L, w1d, D, "gemm_w1_dgrad", scratch, s);
 }
 
 }  // namespace moe

@@ -55,6 +55,10 @@ def sources_hash() -> str:
 
 
 def step_name(kernel: str) -> str | None:
+    # paired backward launches: <A tile, B_T or MX, epilogue, B tile...>
+    m = re.search(r"pair_kernel<[^,]*Tile<[^>]*>, (true|false), (\d),", kernel)
+    if m:
+        return {"2": "pair_w2", "0": "pair_w1"}.get(m.group(2))
     m = re.search(r"grouped_gemm_kernel<.*Tile<[^>]*>, (true|false), (\d)>", kernel)
     if m:
         return _GROUPED.get((m.group(1), m.group(2)))

@@ -106,6 +106,10 @@ CONFIGS = {
                              mode=MODE_FP32_BF16GEMM, seed=2005),
     "zipf_bf16": LayerConfig("zipf_bf16", T=900, D=256, F=128, E=16, K=4, routing="zipf",
                              seed=2006),
+    # skewed routing with dead experts at a shape the paired backward takes
+    # (D % 256 == 0, F % 256 == 0)
+    "zipf_wide_bf16": LayerConfig("zipf_wide_bf16", T=1500, D=512, F=256, E=16, K=4,
+                                  routing="zipf", seed=2009),
     # token rows of 512 and 1024 16-byte chunks (the row movers give each thread
     # several chunks of a row), top-8, bf16 I/O and fp32 I/O
     "rows4k_bf16": LayerConfig("rows4k_bf16", T=96, D=4096, F=128, E=12, K=8, seed=2007),

@@ -50,7 +50,9 @@ def test_scratch_bytes():
     assert moe.moe_scratch_bytes(moe.make_desc(0, 128, 64, 8, 2)) > 0
     for bad in (moe.make_desc(-1, 128, 64, 8, 2), moe.make_desc(64, 128, 64, 8, 9),
                 moe.make_desc(64, 128, 64, 2000, 2), moe.make_desc(64, 128, 64, 8, 2, 7),
-                moe.make_desc(64, 128, 64, 8, 2, 2, 0x10)):
+                moe.make_desc(64, 128, 64, 8, 2, 2, 0x20),
+                # paired and one-kernel-per-GEMM backward at once
+                moe.make_desc(64, 128, 64, 8, 2, 2, moe.MOE_FLAG_OVERLAP_BWD | moe.MOE_FLAG_SERIAL_BWD)):
         assert moe.moe_scratch_bytes(bad) == 0
 
 
