@@ -353,16 +353,19 @@ __device__ __forceinline__ f32x16 mfma8(i32x8 b, i32x8 a, f32x16 c, int sb, int 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, SEL, sb, SEL, sa);
 }
 
-template <class TL, bool MX, bool SB_COL, class SA, class SB>
+// The MXFP8 loop: 128-element k-steps in two LDS stages of 128-byte rows; the
+// matrix core applies the e8m0 scales (the lane's row and column entries,
+// shifted so that op_sel 0 and 2 pick the lane's 32-group of each 64-deep
+// half).
+template <class TL, class SA, class SB>
 __device__ __forceinline__ void mainloop8(char* smem, const SA& sa, const SB& sb,
                                           const ScaleStager& ssa, const ScaleStager& ssb,
                                           int ktiles, f32x16 (&acc)[TL::WMT][TL::WNT], int wave,
                                           int lane) {
   constexpr int BM = TL::BM, BN = TL::BN, WM = TL::WM, WN = TL::WN;
-  constexpr int WMT = TL::WMT, WNT = TL::WNT, STAGES = TL::STAGES;
+  constexpr int WMT = TL::WMT, WNT = TL::WNT;
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES + 2048;
-  constexpr int NI = SA::NI + SB::NI;
-  static_assert(STAGES == 2 || STAGES == 3, "two or three stages");
+  static_assert(TL::STAGES == 2, "two stages");
   const int wm = wave / TL::WGN, wn = wave % TL::WGN;
   const uint32_t base = lds_addr(smem);
   auto issue = [&](int s, int kt) {
@@ -372,23 +375,12 @@ __device__ __forceinline__ void mainloop8(char* smem, const SA& sa, const SB& sb
     ssa.issue(st + A_BYTES + B_BYTES, kt);
     ssb.issue(st + A_BYTES + B_BYTES + 1024, kt);
   };
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < ktiles) issue(s, s);
-
+  if (ktiles > 0) issue(0, 0);
   for (int kt = 0; kt < ktiles; ++kt) {
-    if constexpr (STAGES == 3) {
-      if (kt + 1 < ktiles) {
-        if (wave < 2) wait_vmcnt<NI + 1>(); else wait_vmcnt<NI>();
-      } else {
-        wait_vmcnt<0>();
-      }
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (kt + STAGES - 1 < ktiles) issue((kt + STAGES - 1) % STAGES, kt + STAGES - 1);
-    const char* ta = smem + (kt % STAGES) * STAGE;
+    if (kt + 1 < ktiles) issue((kt + 1) & 1, kt + 1);
+    const char* ta = smem + (kt & 1) * STAGE;
     const char* tb = ta + A_BYTES;
     const uint32_t* sca = reinterpret_cast<const uint32_t*>(tb + B_BYTES);
     const uint32_t* scb = sca + 256;
@@ -400,60 +392,35 @@ __device__ __forceinline__ void mainloop8(char* smem, const SA& sa, const SB& sb
 #pragma unroll
       for (int j = 0; j < WNT; ++j) bfr[kk][j] = frag8(tb, wn * WN + j * 32 + (lane & 31), kk, lane);
     }
-    if constexpr (MX) {
-      const int sh = 8 * (lane >> 5);
-      int sa_w[WMT], sb_w[WNT];
+    const int sh = 8 * (lane >> 5);
+    int sa_w[WMT], sb_w[WNT];
 #pragma unroll
-      for (int i = 0; i < WMT; ++i) sa_w[i] = int(sca[wm * WM + i * 32 + (lane & 31)] >> sh);
+    for (int i = 0; i < WMT; ++i) sa_w[i] = int(sca[wm * WM + i * 32 + (lane & 31)] >> sh);
 #pragma unroll
-      for (int j = 0; j < WNT; ++j) sb_w[j] = int(scb[wn * WN + j * 32 + (lane & 31)] >> sh);
+    for (int j = 0; j < WNT; ++j) sb_w[j] = int(scb[wn * WN + j * 32 + (lane & 31)] >> sh);
 #pragma unroll
-      for (int i = 0; i < WMT; ++i)
-#pragma unroll
-        for (int j = 0; j < WNT; ++j) {
-          acc[i][j] = mfma8<0>(bfr[0][j], af[0][i], acc[i][j], sb_w[j], sa_w[i]);
-          acc[i][j] = mfma8<2>(bfr[1][j], af[1][i], acc[i][j], sb_w[j], sa_w[i]);
-        }
-    } else {
-      float s_a[WMT];
-#pragma unroll
-      for (int i = 0; i < WMT; ++i) s_a[i] = __uint_as_float(sca[wm * WM + i * 32 + (lane & 31)]);
+    for (int i = 0; i < WMT; ++i)
 #pragma unroll
       for (int j = 0; j < WNT; ++j) {
-        float s_b[16];
-        if constexpr (SB_COL) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const float4 v4 = *reinterpret_cast<const float4*>(scb + wn * WN + j * 32 + acc_col(g, lane));
-            s_b[4 * g] = v4.x; s_b[4 * g + 1] = v4.y; s_b[4 * g + 2] = v4.z; s_b[4 * g + 3] = v4.w;
-          }
-        } else {
-          const float v = __uint_as_float(scb[wn * WN + j * 32]);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s_b[r] = v;
-        }
-#pragma unroll
-        for (int i = 0; i < WMT; ++i) {
-          f32x16 part = {};
-          part = mfma8<0>(bfr[0][j], af[0][i], part, 127, 127);
-          part = mfma8<0>(bfr[1][j], af[1][i], part, 127, 127);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[r], s_a[i] * s_b[r], acc[i][j][r]);
-        }
+        acc[i][j] = mfma8<0>(bfr[0][j], af[0][i], acc[i][j], sb_w[j], sa_w[i]);
+        acc[i][j] = mfma8<2>(bfr[1][j], af[1][i], acc[i][j], sb_w[j], sa_w[i]);
       }
-    }
   }
 }
 
-// The blockwise token-grouped loop on 128-element k-steps (one scale block
-// per step) in two LDS stages of 128-byte rows, as the MX loop: a 32x32
-// block's two 64-deep MFMAs accumulate into a partial that is promoted once
-// per step, acc += part * s_a[row] * s_b[block] (s_b uniform over a 32-column
-// block: weights in 128 x 128 blocks), one scale product and 16 FMAs per block
-// and step.  The step's B fragments and scales stay in registers while the A
-// fragments stream one 32-row block at a time (the next block's are read while
-// the current one multiplies), which keeps the loop inside 256 registers.
-template <class TL, class SA, class SB>
+// The blockwise loop on 128-element k-steps (one scale block per step) in two
+// LDS stages of 128-byte rows, as the MX loop: a 32x32 block's two 64-deep
+// MFMAs accumulate into a partial that is promoted once per step,
+// acc += part * s_a[row] * s_b[col].  Token-grouped GEMMs (SB_COL false): s_b
+// is uniform over a 32-column block (weights in 128 x 128 blocks), one scale
+// product and 16 FMAs per block and step.  Weight gradients (SB_COL true):
+// both operands are scaled per 128-token block along an output axis, so each
+// of the lane's 16 columns has its own s_b, read from LDS right before the
+// promotion (16 products and 16 FMAs).  The step's B fragments stay in
+// registers while the A fragments stream one 32-row block at a time (the next
+// block's are read while the current one multiplies), which keeps the loop
+// inside 256 registers.
+template <class TL, bool SB_COL, class SA, class SB>
 __device__ __forceinline__ void block8(char* smem, const SA& sa, const SB& sb,
                                        const ScaleStager& ssa, const ScaleStager& ssb, int ktiles,
                                        f32x16 (&acc)[TL::WMT][TL::WNT], int wave, int lane) {
@@ -507,9 +474,21 @@ __device__ __forceinline__ void block8(char* smem, const SA& sa, const SB& sb,
       for (int j = 0; j < WNT; ++j) part[j] = mfma8<0>(b1[j], a1, part[j], 127, 127);
 #pragma unroll
       for (int j = 0; j < WNT; ++j) {
-        const float sc = sav * sbv[j];
+        if constexpr (SB_COL) {  // one scale per output column: the lane's 16 columns
+          float sbc[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[j][r], sc, acc[i][j][r]);
+          for (int g = 0; g < 4; ++g) {
+            const float4 v4 = *reinterpret_cast<const float4*>(scb + wn * WN + j * 32 + acc_col(g, lane));
+            sbc[4 * g] = v4.x; sbc[4 * g + 1] = v4.y; sbc[4 * g + 2] = v4.z; sbc[4 * g + 3] = v4.w;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[i][j][r] = __builtin_fmaf(part[j][r], sav * sbc[r], acc[i][j][r]);
+        } else {
+          const float sc = sav * sbv[j];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[j][r], sc, acc[i][j][r]);
+        }
       }
       if (i + 1 < WMT) {
         a0 = n0;
@@ -595,8 +574,8 @@ __device__ __forceinline__ void f8_grouped_tile(const F8Args& p, int l, char* sm
 
   f32x16 acc[TL::WMT][TL::WNT];
   zero(acc);
-  if constexpr (MX) mainloop8<TL, true, false>(smem, sa, sb, ssa, ssb, p.K / 128, acc, wave, lane);
-  else block8<TL>(smem, sa, sb, ssa, ssb, p.K / 128, acc, wave, lane);
+  if constexpr (MX) mainloop8<TL>(smem, sa, sb, ssa, ssb, p.K / 128, acc, wave, lane);
+  else block8<TL, false>(smem, sa, sb, ssa, ssb, p.K / 128, acc, wave, lane);
   static_assert(f8_grouped_lds<TL, MX>() >= grouped_epi_lds<TL, EPI>(), "epilogue staging exceeds LDS");
   grouped_epilogue<TL, EPI>(p.epi, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane, smem, threadIdx.x);
 }
@@ -640,7 +619,8 @@ __device__ __forceinline__ void f8_wgrad_tile(const F8Args& p, int l, char* smem
                     int(p.sa_ld * 4), wave == 0};
     ScaleStager ssb{make_rsrc(p.SB, p.sb_bytes), int((size_t(s0) * p.sb_ld + nt * BN + 4 * lane) * 4),
                     int(p.sb_ld * 4), wave == 1};
-    mainloop8<TL, MX, true>(smem, sa, sb, ssa, ssb, ksteps, acc, wave, lane);
+    if constexpr (MX) mainloop8<TL>(smem, sa, sb, ssa, ssb, ksteps, acc, wave, lane);
+    else block8<TL, true>(smem, sa, sb, ssa, ssb, ksteps, acc, wave, lane);
   }
   static_assert(f8_wgrad_lds<TL>() >= wgrad_epi_lds<TL, OUT_F32>(), "epilogue staging exceeds LDS");
   wgrad_epilogue<TL, OUT_F32>(p.C, p.M, p.N, e, mt, nt, acc, wm, wn, lane, smem, threadIdx.x);
@@ -695,18 +675,19 @@ using namespace gemm;
 //    235B W1 dgrad from 2.42 to 1.95 ms and the W2 dgrad + SwiGLU-backward
 //    from 1.93 to 1.69 ms (30B blockwise step 4.98 -> 4.69 ms);
 //  * blockwise weight-gradient GEMMs, whose scales vary along both output
-//    axes (a scale product per output element and 128-token block): the
-//    promoting 128-element loop on 256 x 128 tiles of eight 64 x 64 waves,
-//    three stages.  The accumulators, partials, fragments and each column's
-//    scales fit in about 190 registers, so two waves share a SIMD and one's
-//    promotion overlaps the other's MFMAs (about 30% faster than four waves
-//    of 128 x 64, one per SIMD).
+//    axes (a scale product per output element and 128-token block): the same
+//    256 x 256 tiles with block8's per-column-scale path (each column's 16
+//    scales read from LDS right before its promotion, so the streaming loop
+//    still fits 256 registers).  An expert's tile covers only n_e / 128 steps
+//    (8 at the Qwen3 shapes), so the halved prologue and epilogue cost per
+//    flop pays: against 256 x 128 tiles of eight 64 x 64 waves in three
+//    stages, 235B W1 wgrad 3.50 -> 2.92 ms, W2 wgrad 1.56 -> 1.38 ms (fp8_bwd
+//    backward 10.59 -> 9.84 ms), 30B fp8 W1 wgrad 0.81 -> 0.69 ms.
 using TileF8 = Tile<256, 256, 2, 4, 2>;
-using TileF8B = Tile<256, 128, 4, 2, 3>;
 template <bool MX> using F8GrTile = TileF8;
 static_assert(TileF8::BN % 128 == 0,
               "the SwiGLU-backward epilogue quantises whole 128-column groups of dH");
-template <bool MX> using F8WgTile = typename std::conditional<MX, TileF8, TileF8B>::type;
+template <bool MX> using F8WgTile = TileF8;
 
 inline int max_steps128(const moe_desc& d) {
   const long long N = (long long)d.T * d.K;
