@@ -38,6 +38,7 @@ GEMM_SOURCES = [
     "mixture_experts_layer_31_amd/csrc/moe_gemm_common.h",
     "mixture_experts_layer_31_amd/csrc/moe_fp8_codec.h",
     "mixture_experts_layer_31_amd/csrc/moe_grouped.h",
+    "mixture_experts_layer_31_amd/csrc/moe_pair.h",
 ]
 _GROUPED = {("false", "1"): "gemm_w1_swiglu", ("false", "0"): "gemm_w2",
             ("true", "2"): "gemm_w2_dgrad_dswiglu", ("true", "0"): "gemm_w1_dgrad"}
