@@ -1082,7 +1082,12 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   const auto* xp = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
   int rc;
   // W2 dgrad + SwiGLU-backward on dYw's row codes (in the first token-code
-  // buffer); its epilogue also writes dH's row codes for the W1 dgrad
+  // buffer).  dH's row codes for the W1 dgrad: in MXFP8 the epilogue writes
+  // them as it stores dH; blockwise, a separate pass over the stored dH is
+  // cheaper (its quotients and 128-lane maxima made the epilogue 0.16 ms
+  // slower at the 30B shape, 0.33 ms at 235B, against a 0.11 / 0.22 ms pass,
+  // while MXFP8's power-of-two scales cost the epilogue less than the pass)
+  const bool dh_pass = !mx;
   if (!dyw_quantised && (rc = quant_rows(d, dyw, D, mx, f.qt1, f.qt1_sc, "quant_dyw_rows", s)))
     return rc;
   F8Args a{};
@@ -1100,7 +1105,7 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   a.F = F;
   a.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.dh), 0, nullptr,
                   reinterpret_cast<const uint16_t*>(scratch + L.h), F, f.qrow, f.qrow_sc, N,
-                  mx ? QM_MX : QM_BLOCK};
+                  dh_pass ? QM_NONE : QM_MX};
   // W2 wgrad over tokens: dYw's token codes (in the first buffer once the W2
   // dgrad is done with the row codes there; in the third when both run in one
   // launch) and A's (in the second)
@@ -1159,6 +1164,8 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
     rc = mx ? run_f8_pair<true, EPI_DSWIGLU>(d, L, a, F, w, ctr, "pair_w2", scratch, s)
             : run_f8_pair<false, EPI_DSWIGLU>(d, L, a, F, w, ctr, "pair_w2", scratch, s);
     if (rc) return rc;
+    if (dh_pass && (rc = quant_rows(d, dh, 2 * F, false, f.qrow, f.qrow_sc, "quant_dh_rows", s)))
+      return rc;
     if ((rc = quant_tokens(d, L, dh, 2 * F, mx, f.qt1, f.qt1_sc, "quant_dh_tokens", scratch, s))) return rc;
     if ((rc = quant_tokens(d, L, xp, D, mx, f.qt2, f.qt2_sc, "quant_x_tokens", scratch, s))) return rc;
     return mx ? run_f8_pair<true, EPI_STORE>(d, L, b, D, v, ctr + kPairQueues, "pair_w1", scratch, s)
@@ -1168,6 +1175,8 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   rc = mx ? run_f8_grouped<true, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s)
           : run_f8_grouped<false, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s);
   if (rc) return rc;
+  if (dh_pass && (rc = quant_rows(d, dh, 2 * F, false, f.qrow, f.qrow_sc, "quant_dh_rows", s)))
+    return rc;
   if ((rc = quant_tokens(d, L, dyw, D, mx, f.qt1, f.qt1_sc, "quant_dyw_tokens", scratch, s))) return rc;
   if ((rc = quant_tokens(d, L, act, F, mx, f.qt2, f.qt2_sc, "quant_a_tokens", scratch, s))) return rc;
   rc = mx ? run_f8_wgrad<true>(d, L, w, "gemm_w2_wgrad", scratch, s)
