@@ -194,11 +194,15 @@ int moe_routing_view(const moe_desc* d, const void* scratch, size_t scratch_byte
 
 /* Intermediates in scratch, for tests and tools (row r is the r-th routed pair
  * in expert order, i.e. pair src[r]):
- *   MOE_VIEW_XPERM  [T*K, D]   dispatched tokens (bf16; fp32 in MOE_FP32)
+ *   MOE_VIEW_XPERM  [T*K, D]   dispatched tokens (bf16; fp32 in MOE_FP32).  Not
+ *                              stored in MOE_MXFP8 and MOE_FP8 without
+ *                              MOE_FLAG_RECOMPUTE (only their FP8 codes are)
  *   MOE_VIEW_H      [T*K, 2F]  linear-1 output: gate | up
  *   MOE_VIEW_A      [T*K, F]   SwiGLU output
  *   MOE_VIEW_O      [T*K, D]   linear-2 output (unweighted)
- *   MOE_VIEW_DYPERM [T*K, D]   dispatched upstream gradient (unweighted)
+ *   MOE_VIEW_DYPERM [T*K, D]   dispatched upstream gradient times the routing
+ *                              weight, w * dy (fp32 product, stored once).  Not
+ *                              stored in the FP8 modes (only its FP8 codes are)
  *   MOE_VIEW_DH     [T*K, 2F]  gradient wrt linear-1 output
  *   MOE_VIEW_DXPERM [T*K, D]   gradient wrt dispatched tokens
  *   MOE_VIEW_WPERM  [T*K] fp32 routing weight of each routed pair
@@ -207,7 +211,8 @@ int moe_routing_view(const moe_desc* d, const void* scratch, size_t scratch_byte
  *   MOE_VIEW_Q_ROWS        [T*K, C] e4m3 codes of an activation quantised along its rows
  *   MOE_VIEW_Q_ROWS_SCALE  [C/128, T*K] 4-byte scale entries
  *   MOE_VIEW_Q_TOK_A/B     [C, Npad] e4m3 codes quantised along tokens (expert e's
- *                          tokens in columns 128*p[e] .. , p = prefix of ceil(count/128))
+ *                          tokens in columns 128*p[e] .. , p = prefix of ceil(count/128));
+ *                          after moe_bwd, A holds dH's and B x_perm's
  *   MOE_VIEW_Q_TOK_A/B_SCALE [Npad/128, C] 4-byte scale entries
  * A 4-byte entry is an fp32 scale (blockwise) or four e8m0 bytes, one per 32
  * consecutive contraction elements of the 128-element step (MXFP8).

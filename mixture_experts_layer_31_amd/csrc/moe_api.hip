@@ -276,13 +276,18 @@ int moe::forward(const moe_desc* d, const void* x, const int32_t* topk_idx, cons
     return launch_combine(*d, L, topk_w, y, io_f32, sc, s);
   }
   const bool fwd_q = fp8_mode(d->mode) && d->mode != MOE_FP8_BWD;
-  if (fwd_q) {  // the dispatch also quantises x's rows for the W1 GEMM
+  if (fwd_q) {
+    // the dispatch quantises x's rows for the W1 GEMM (and stores the bf16 rows
+    // only for the recompute, which quantises them again); x's token codes for
+    // the W1 weight gradient are gathered from x here, so the backward needs no
+    // dispatched rows
     uint8_t* qc;
     uint32_t* qs;
     fp8_row_codes(*d, L, sc, &qc, &qs);
     if ((rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s,
-                              d->mode == MOE_MXFP8 ? 1 : 2, qc, qs)))
+                              d->mode == MOE_MXFP8 ? 1 : 2, qc, qs, L.recompute)))
       return rc;
+    if ((rc = fp8_x_tokens(*d, L, x, sc, s))) return rc;
   } else if ((rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s))) {
     return rc;
   }
@@ -333,12 +338,13 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
       rc = launch_recompute_h(*d, L, g1, sc, s);
     if (rc) return rc;
   }
-  if (fp8_mode(d->mode)) {  // the combine-backward also quantises dYw's rows for the W2 dgrad
+  if (fp8_mode(d->mode)) {  // the combine-backward quantises dYw's rows for the W2 dgrad,
+                            // without storing them in bf16
     uint8_t* qc;
     uint32_t* qs;
     fp8_dyw_codes(*d, L, sc, &qc, &qs);
     if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s,
-                                 d->mode == MOE_MXFP8 ? 1 : 2, qc, qs)))
+                                 d->mode == MOE_MXFP8 ? 1 : 2, qc, qs, false)))
       return rc;
   } else if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s))) {
     return rc;
@@ -347,7 +353,7 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
     rc = launch_bwd_gemms_f32(*d, L, static_cast<const float*>(w1), static_cast<const float*>(w2),
                               static_cast<float*>(dw1), static_cast<float*>(dw2), sc, s);
   else if (fp8_mode(d->mode))
-    rc = fp8_bwd_gemms(*d, L, static_cast<const char*>(wprep), dw1, dw2, sc, s, true);
+    rc = fp8_bwd_gemms(*d, L, static_cast<const char*>(wprep), dy, topk_w, dw1, dw2, sc, s);
   else
     rc = launch_bwd_gemms(*d, L, g1, g2, dw1, dw2, io_f32, sc, s);
   if (rc) return rc;

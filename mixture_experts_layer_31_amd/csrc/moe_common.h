@@ -106,9 +106,12 @@ int launch_clear_err(char* scratch, const Layout& L, hipStream_t s);
 
 // Row gathers/scatters: dispatch (x -> expert-contiguous rows), combine and the
 // un-permute reduction.  `in_f32`/`out_f32` select fp32 instead of bf16 I/O.
+// With qmode (FP8 forward modes) the dispatch also writes the rows' e4m3
+// quantisation along D; store_rows = false then skips the bf16 rows themselves.
 int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool in_f32,
                     const float* topk_w, char* scratch, size_t dst_off, hipStream_t s,
-                    int qmode = 0, uint8_t* qcodes = nullptr, uint32_t* qsc = nullptr);
+                    int qmode = 0, uint8_t* qcodes = nullptr, uint32_t* qsc = nullptr,
+                    bool store_rows = true);
 int launch_combine(const moe_desc& d, const Layout& L, const float* topk_w, void* y,
                    bool out_f32, const char* scratch, hipStream_t s);
 int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
@@ -116,9 +119,11 @@ int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
 // Combine-backward: dYw_perm rows (w * dy, bf16) and dtopk_w = <dy, o>.  With
 // qmode 1 (MX) or 2 (blockwise) it also writes the rows' e4m3 quantisation
 // along D (codes [N, D], scale entries [D/128][N]); bf16 rows only.
+// store_rows = false (with qmode) skips the bf16 dYw rows.
 int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool in_f32,
                        const float* topk_w, float* dtopk_w, char* scratch, hipStream_t s,
-                       int qmode = 0, uint8_t* qcodes = nullptr, uint32_t* qsc = nullptr);
+                       int qmode = 0, uint8_t* qcodes = nullptr, uint32_t* qsc = nullptr,
+                       bool store_rows = true);
 int launch_zero(void* p, size_t bytes, hipStream_t s);  // bytes % 16 == 0
 int launch_convert_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
 // Router ahead of the layer (moe_router.hip): softmax -> top-K -> renormalise,
@@ -157,10 +162,14 @@ int fp8_prepare_weights(const moe_desc& d, const uint16_t* w1, const uint16_t* w
 // x_quantised: the dispatch already wrote x_perm's row quantisation (fp8_row_codes).
 int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,
                   hipStream_t s, bool x_quantised = false);
-// The FP8 backward; dyw_quantised: the combine-backward already wrote dYw's row
-// quantisation (fp8_dyw_codes).
-int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* dw1, void* dw2,
-                  char* scratch, hipStream_t s, bool dyw_quantised = false);
+// MXFP8 and FP8 forward: x's token codes for the W1 weight gradient, gathered
+// from x (the dispatch stores only x's row codes in these modes).
+int fp8_x_tokens(const moe_desc& d, const Layout& L, const void* x, char* scratch, hipStream_t s);
+// The FP8 backward, after the combine-backward wrote dYw's row codes
+// (fp8_dyw_codes) and no bf16 dYw rows: dYw's token codes are gathered from dy
+// (bf16 [T, D]) and topk_w.
+int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const void* dy,
+                  const float* topk_w, void* dw1, void* dw2, char* scratch, hipStream_t s);
 // Where the dispatch writes x_perm's row codes, and the combine-backward dYw's.
 void fp8_row_codes(const moe_desc& d, const Layout& L, char* scratch, uint8_t** codes,
                    uint32_t** scales);

@@ -65,6 +65,9 @@ struct QArgs {
   int64_t sc_ld, sc_bstride;
   const int32_t* offsets;  // token quantiser: [E+1] expert row offsets
   const int32_t* tstart;   // token quantiser: [E+1] prefix of ceil(count / 128)
+  const int32_t* src;      // gathering token quantiser: [N] pair of each permuted row
+  const float* topk_w;     // TOK_GATHER_W: [T*K] routing weight of each pair
+  int K;                   // gathering token quantiser: pairs per token
   int E;
   int ntr;                 // weights: r-steps per expert
   int total_rows;          // row quantiser: rows of the input
@@ -228,99 +231,161 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(QArgs p) {
   }
 }
 
+// Where the token quantiser's rows come from:
+//   TOK_PERM      row q of the permuted activations `in` [N, C] (read once:
+//                 streaming loads);
+//   TOK_GATHER    the dispatched token itself, row src[q] / K of `in` [T, C]
+//                 (x: the dispatched rows need not be stored at all);
+//   TOK_GATHER_W  the combine-backward's row w * dy: row src[q] / K of `in`
+//                 (dy) times the pair's routing weight, the fp32 product
+//                 rounded to bf16 as the combine-backward rounds it.
+// A token's row is gathered once per routed pair (K times), mostly from the
+// caches: plain loads.
+enum TokSrc { TOK_PERM = 0, TOK_GATHER = 1, TOK_GATHER_W = 2 };
+
+// Eight bf16 values times w, each fp32 product rounded to bf16 (RNE).
+__device__ __forceinline__ uint4 scale_bf16x8(const uint4& v, float w) {
+  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float lo = w * __uint_as_float(in[k] << 16), hi = w * __uint_as_float(in[k] & 0xffff0000u);
+    out[k] = uint32_t(__builtin_bit_cast(uint16_t, (__bf16)lo)) |
+             (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)hi)) << 16);
+  }
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 // Token quantiser for activations contracted over tokens (the weight-gradient
-// operands): one workgroup per 128-token step of an expert segment x 128
-// columns.  The tile is loaded with whole 256-byte row segments per sixteen
-// lanes into LDS (streaming loads: each input row is read once), its 32-byte
-// column blocks XOR-swizzled by row; then each thread takes one column and 64
-// consecutive tokens, four tokens per ds_read_b64_tr_b16 (a sixteen-lane group
-// reads a 4-token x 16-column block and lane i receives column i).  The other
-// 64 tokens of the column are in lane ^ 16, so the 128-token amax is one
-// shuffle away.  The codes go back through the same LDS tile as 128 rows of
-// 128 bytes (one per column, 16-byte chunks XOR-swizzled by row), so each
-// wave's store covers eight whole 128-byte output rows instead of 16-byte
-// pieces of 32 rows.
-template <bool MX>
+// operands): one workgroup per 128-token step of an expert segment x NCT
+// column tiles of 128.  A tile is loaded with whole 256-byte row segments per
+// sixteen lanes into LDS, its 32-byte column blocks XOR-swizzled by row; then
+// each thread takes one column and 64 consecutive tokens, four tokens per
+// ds_read_b64_tr_b16 (a sixteen-lane group reads a 4-token x 16-column block
+// and lane i receives column i).  The other 64 tokens of the column are in
+// lane ^ 16, so the 128-token amax is one shuffle away.  The codes go back
+// through the same LDS tile as 128 rows of 128 bytes (one per column, 16-byte
+// chunks XOR-swizzled by row), so each wave's store covers eight whole
+// 128-byte output rows instead of 16-byte pieces of 32 rows.  With NCT > 1 the
+// next tile's rows are loaded into registers as soon as the current tile is
+// in LDS, so they arrive while it is quantised and stored, and a gathered
+// row's index and weight are looked up once for all NCT tiles.
+template <bool MX, int SRC, int NCT>
 __global__ void __launch_bounds__(256) quant_tokens_kernel(QArgs p) {
   __shared__ __attribute__((aligned(16))) char tile[128 * 256];
-  const int ctiles = p.cols / 128;
-  const int rt = blockIdx.x / ctiles, ct = blockIdx.x % ctiles;
+  const int groups = p.cols / (128 * NCT);
+  const int rt = blockIdx.x / groups, cg = blockIdx.x % groups;
   if (rt >= p.tstart[p.E]) return;
   const int lo = tile_expert(p.tstart, p.E, 1, rt);
   const int r0 = p.offsets[lo] + (rt - p.tstart[lo]) * 128;
   const int valid = min(128, p.offsets[lo + 1] - r0);
-  const int slot0 = rt * 128, c0 = ct * 128;
+  const int slot0 = rt * 128;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15;
   auto at = [&](int r, int cb) { return r * 256 + ((cb ^ (r & 7)) << 5); };  // 32-byte block cb of row r
-  {
-    uint4 raw[8];
-    const int rw = w * 4 + (lane >> 4);
+  auto oat = [&](int row, int ch) { return row * 128 + ((ch ^ (row & 7)) << 4); };
+  // this thread's 8 rows (16 apart): the input row each comes from (-1: past
+  // the segment's end, zeros)
+  const int rw = w * 4 + (lane >> 4);
+  int row[8];
+  float wt[SRC == TOK_GATHER_W ? 8 : 1];
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int r = it * 16 + rw;
-      raw[it] = r < valid ? load16_nt(p.in + size_t(r0 + r) * p.cols + c0 + 8 * l16)
-                          : make_uint4(0, 0, 0, 0);
+  for (int it = 0; it < 8; ++it) {
+    const int r = it * 16 + rw;
+    row[it] = -1;
+    if constexpr (SRC == TOK_GATHER_W) wt[it] = 0.f;
+    if (r < valid) {
+      if constexpr (SRC == TOK_PERM) {
+        row[it] = r0 + r;
+      } else {
+        const int pr = p.src[r0 + r];
+        row[it] = pr / p.K;
+        if constexpr (SRC == TOK_GATHER_W) wt[it] = p.topk_w[pr];
+      }
     }
+  }
+  uint4 raw[8];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      raw[it] = make_uint4(0, 0, 0, 0);
+      if (row[it] >= 0) {
+        const uint16_t* a = p.in + size_t(row[it]) * p.cols + c0 + 8 * l16;
+        if constexpr (SRC == TOK_PERM) raw[it] = load16_nt(a);
+        else raw[it] = *reinterpret_cast<const uint4*>(a);
+      }
+    }
+  };
+  load(cg * NCT * 128);
+  for (int k = 0; k < NCT; ++k) {
+    const int c0 = (cg * NCT + k) * 128;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int r = it * 16 + rw;
+      if constexpr (SRC == TOK_GATHER_W) raw[it] = scale_bf16x8(raw[it], wt[it]);
       *reinterpret_cast<uint4*>(tile + at(r, l16 >> 1) + (l16 & 1) * 16) = raw[it];
     }
-  }
-  __syncthreads();
-  const int g = lane >> 4, h = g & 1, cb = 2 * w + (g >> 1);
-  const int q = 16 * cb + l16;  // this thread's column; tokens 64h .. 64h + 63
-  float v[64];
+    if (k + 1 < NCT) load(c0 + 128);  // in flight while this tile is quantised and stored
+    __syncthreads();
+    const int g = lane >> 4, h = g & 1, cb = 2 * w + (g >> 1);
+    const int q = 16 * cb + l16;  // this thread's column; tokens 64h .. 64h + 63
+    float v[64];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = 64 * h + 4 * j + (l16 >> 2);
-    const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)AS3(tile + at(r, cb) + (l16 & 3) * 8));
+    for (int j = 0; j < 16; ++j) {
+      const int r = 64 * h + 4 * j + (l16 >> 2);
+      const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)AS3(tile + at(r, cb) + (l16 & 3) * 8));
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[4 * j + k] = __uint_as_float(uint32_t(uint16_t(x[k])) << 16);
-  }
-  float am[2] = {0.f, 0.f};  // amax of the two 32-token groups
-#pragma unroll
-  for (int i = 0; i < 64; ++i) am[i >> 5] = fmaxf(am[i >> 5], fabsf(v[i]));
-  uint32_t packed[16], entry;
-  if constexpr (MX) {
-    const int X0 = e8m0_exponent(am[0]), X1 = e8m0_exponent(am[1]);
-    const float mul[2] = {ldexpf(1.f, -X0), ldexpf(1.f, -X1)};
-    const uint32_t mine = uint32_t(X0 + 127) | (uint32_t(X1 + 127) << 8);
-    entry = mine | (__shfl_xor(mine, 16, 64) << 16);  // meaningful in the h == 0 lane
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float m = mul[i >> 3];
-      packed[i] = pack_e4m3x4(v[4 * i] * m, v[4 * i + 1] * m, v[4 * i + 2] * m, v[4 * i + 3] * m);
+      for (int e = 0; e < 4; ++e) v[4 * j + e] = __uint_as_float(uint32_t(uint16_t(x[e])) << 16);
     }
-  } else {
-    float amax = fmaxf(am[0], am[1]);
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    const float sc = amax == 0.f ? 1.f : amax / 448.f;
-    const float rc = 1.f / sc;
-    entry = __float_as_uint(sc);
+    float am[2] = {0.f, 0.f};  // amax of the two 32-token groups
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float y[8];
-      block_quotients(v + 8 * i, sc, rc, y);
-      packed[2 * i] = pack_e4m3x4(y[0], y[1], y[2], y[3]);
-      packed[2 * i + 1] = pack_e4m3x4(y[4], y[5], y[6], y[7]);
+    for (int i = 0; i < 64; ++i) am[i >> 5] = fmaxf(am[i >> 5], fabsf(v[i]));
+    uint32_t packed[16], entry;
+    if constexpr (MX) {
+      const int X0 = e8m0_exponent(am[0]), X1 = e8m0_exponent(am[1]);
+      const float mul[2] = {ldexpf(1.f, -X0), ldexpf(1.f, -X1)};
+      const uint32_t mine = uint32_t(X0 + 127) | (uint32_t(X1 + 127) << 8);
+      entry = mine | (__shfl_xor(mine, 16, 64) << 16);  // meaningful in the h == 0 lane
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float m = mul[i >> 3];
+        packed[i] = pack_e4m3x4(v[4 * i] * m, v[4 * i + 1] * m, v[4 * i + 2] * m, v[4 * i + 3] * m);
+      }
+    } else {
+      float amax = fmaxf(am[0], am[1]);
+      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+      const float sc = amax == 0.f ? 1.f : amax / 448.f;
+      const float rc = 1.f / sc;
+      entry = __float_as_uint(sc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float y[8];
+        block_quotients(v + 8 * i, sc, rc, y);
+        packed[2 * i] = pack_e4m3x4(y[0], y[1], y[2], y[3]);
+        packed[2 * i + 1] = pack_e4m3x4(y[4], y[5], y[6], y[7]);
+      }
     }
-  }
-  if (h == 0) p.sc[size_t(slot0 / 128) * p.sc_ld + c0 + q] = entry;
-  // codes of column q, tokens 64h .. 64h + 63: chunks 4h .. 4h + 3 of LDS row q
-  auto oat = [&](int row, int ch) { return row * 128 + ((ch ^ (row & 7)) << 4); };
-  __syncthreads();  // every wave is done reading the input tile
+    if (h == 0) p.sc[size_t(slot0 / 128) * p.sc_ld + c0 + q] = entry;
+    // codes of column q, tokens 64h .. 64h + 63: chunks 4h .. 4h + 3 of LDS row q
+    __syncthreads();  // every wave is done reading the input tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint4*>(tile + oat(q, 4 * h + i)) =
-        make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
-  __syncthreads();
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(tile + oat(q, 4 * h + i)) =
+          make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+    __syncthreads();
+    // 128 rows of 128 bytes, eight lanes per row.  The gathering forms store
+    // with streaming stores, which keep the re-read token rows in the caches
+    // (235B dYw 0.44 -> 0.43 ms); the permuted form keeps plain stores (the
+    // 30B MXFP8 dH pass measured 0.107 ms with them, 0.125 streaming)
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {  // 128 rows x 8 chunks, eight lanes per row
-    const int id = threadIdx.x + 256 * u, row = id >> 3, ch = id & 7;
-    *reinterpret_cast<uint4*>(p.out + size_t(c0 + row) * p.out_ld + slot0 + 16 * ch) =
-        *reinterpret_cast<const uint4*>(tile + oat(row, ch));
+    for (int u = 0; u < 4; ++u) {
+      const int id = threadIdx.x + 256 * u, row = id >> 3, ch = id & 7;
+      uint8_t* dst = p.out + size_t(c0 + row) * p.out_ld + slot0 + 16 * ch;
+      const uint4 val = *reinterpret_cast<const uint4*>(tile + oat(row, ch));
+      if constexpr (SRC == TOK_PERM) *reinterpret_cast<uint4*>(dst) = val;
+      else store16_nt(dst, val);
+    }
+    __syncthreads();  // the next tile's rows overwrite the staged codes
   }
 }
 
@@ -731,10 +796,13 @@ int quant_rows(const moe_desc& d, const uint16_t* in, int C, bool mx, uint8_t* o
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-// Quantise permuted activations [N, C] along tokens within expert segments,
-// transposed to [C, Npad] (row stride npad) with scale entries [step][C].
+// Quantise activations along tokens within expert segments, transposed to
+// [C, Npad] (row stride npad) with scale entries [step][C].  `in` is the
+// permuted rows [N, C] (TOK_PERM) or the per-token rows [T, C] the permuted
+// rows are gathered from (TOK_GATHER, TOK_GATHER_W with the weights topk_w).
 int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, bool mx,
-                 uint8_t* out, uint32_t* sc, const char* name, const char* scratch, hipStream_t s) {
+                 uint8_t* out, uint32_t* sc, const char* name, const char* scratch, hipStream_t s,
+                 int src = TOK_PERM, const float* topk_w = nullptr) {
   QArgs a{};
   a.in = in;
   a.cols = C;
@@ -744,12 +812,29 @@ int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, 
   a.sc_ld = C;
   a.offsets = reinterpret_cast<const int32_t*>(scratch + L.offsets);
   a.tstart = reinterpret_cast<const int32_t*>(scratch + L.tiles[1]);
+  a.src = reinterpret_cast<const int32_t*>(scratch + L.src);
+  a.topk_w = topk_w;
+  a.K = d.K;
   a.E = d.E;
-  const int blocks = max_steps128(d) * (C / 128);
+  if (src == TOK_GATHER_W && topk_w == nullptr) return MOE_EINVAL;
+  // column tiles per workgroup: the gathering forms pipeline the next tile's
+  // row loads behind the current tile's quantisation (at the 30B shape x
+  // 0.19 -> 0.17 ms and dYw 0.21 -> 0.19 ms, at 235B dYw 0.43 -> 0.38 ms);
+  // the permuted form, whose rows stream from consecutive addresses, is
+  // faster at one tile per workgroup and the occupancy that leaves
+  const int nct = src == TOK_PERM ? 1 : (C / 128) % 4 == 0 ? 4 : (C / 128) % 2 == 0 ? 2 : 1;
+  const int blocks = max_steps128(d) * (C / 128 / nct);
   if (blocks <= 0) return MOE_OK;
   prof_begin(name, s);
-  if (mx) quant_tokens_kernel<true><<<unsigned(blocks), 256, 0, s>>>(a);
-  else quant_tokens_kernel<false><<<unsigned(blocks), 256, 0, s>>>(a);
+#define MOE_QT(S, W) \
+  (mx ? quant_tokens_kernel<true, S, W><<<unsigned(blocks), 256, 0, s>>>(a) \
+      : quant_tokens_kernel<false, S, W><<<unsigned(blocks), 256, 0, s>>>(a))
+#define MOE_QTW(S) (nct == 4 ? MOE_QT(S, 4) : nct == 2 ? MOE_QT(S, 2) : MOE_QT(S, 1))
+  if (src == TOK_GATHER) MOE_QTW(TOK_GATHER);
+  else if (src == TOK_GATHER_W) MOE_QTW(TOK_GATHER_W);
+  else MOE_QT(TOK_PERM, 1);
+#undef MOE_QTW
+#undef MOE_QT
   prof_end(s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
@@ -887,21 +972,61 @@ bool fp8_mode(int mode) { return mode == MOE_FP8_BWD || mode == MOE_MXFP8 || mod
 
 size_t fp8_wprep_bytes(const moe_desc& d) { return fp8_mode(d.mode) ? wlayout(d).total : 0; }
 
-size_t fp8_scratch_bytes(const moe_desc& d) {
-  if (!fp8_mode(d.mode)) return 0;
+// Regions of the FP8 operands in scratch (after the bf16 layout), as offsets
+// from its FP8 region: the row codes of one activation, and three (paired
+// backward: four) buffers of token codes:
+//   qt1  A's row codes in the forward (MXFP8 epilogue, or quant_rows), then
+//        dYw's row codes, dYw's token codes (one-GEMM-per-launch backward),
+//        dH's token codes;
+//   qt2  x's token codes: written by the forward in MXFP8 and FP8 (gathered
+//        from x), by the backward in fp8_bwd (from the dispatched rows);
+//   qta  A's token codes: their own buffer when the forward fills qt2 (F
+//        columns), else qt2 itself, which the W2 weight gradient has read
+//        before x's token codes replace them;
+//   qt3  the paired backward's dYw token codes (the W2 dgrad still reads the
+//        row codes in qt1 in the same launch).
+struct F8Offsets {
+  size_t qrow, qrow_sc, qt1, qt1_sc, qt2, qt2_sc, qta, qta_sc, qt3, qt3_sc, total;
+  size_t qrow_sc_bytes, qt_sc_bytes, qta_sc_bytes;
+  bool own_qta, has_qt3;
+};
+
+static F8Offsets f8offsets(const moe_desc& d) {
+  F8Offsets f{};
   const size_t N = size_t(d.T) * d.K, C = d.D > 2 * d.F ? d.D : 2 * d.F;
   const size_t npad = size_t(max_steps128(d)) * 128;
   size_t o = 0;
-  o = align256(o + N * C);                 // row-quantised codes
-  o = align256(o + (C / 128) * N * 4);     // their scale entries
-  // token-quantised codes and scales: two buffers, a third for the paired
-  // backward (dYw's token codes, while the W2 dgrad still reads its row codes)
-  const int nt = pair_capable(d) ? 3 : 2;
-  for (int i = 0; i < nt; ++i) {
-    o = align256(o + C * npad);
-    o = align256(o + (npad / 128) * C * 4);
+  auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
+  f.qrow_sc_bytes = (C / 128) * N * 4;
+  f.qt_sc_bytes = (npad / 128) * C * 4;
+  f.qrow = take(N * C);
+  f.qrow_sc = take(f.qrow_sc_bytes);
+  f.qt1 = take(C * npad);
+  f.qt1_sc = take(f.qt_sc_bytes);
+  f.qt2 = take(C * npad);
+  f.qt2_sc = take(f.qt_sc_bytes);
+  f.own_qta = fp8_fwd(d.mode);
+  if (f.own_qta) {
+    f.qta_sc_bytes = (npad / 128) * size_t(d.F) * 4;
+    f.qta = take(size_t(d.F) * npad);
+    f.qta_sc = take(f.qta_sc_bytes);
+  } else {
+    f.qta_sc_bytes = f.qt_sc_bytes;
+    f.qta = f.qt2;
+    f.qta_sc = f.qt2_sc;
   }
-  return o;
+  f.has_qt3 = pair_capable(d);
+  if (f.has_qt3) {
+    f.qt3 = take(C * npad);
+    f.qt3_sc = take(f.qt_sc_bytes);
+  }
+  f.total = o;
+  return f;
+}
+
+size_t fp8_scratch_bytes(const moe_desc& d) {
+  if (!fp8_mode(d.mode)) return 0;
+  return f8offsets(d).total;
 }
 
 int fp8_prepare_weights(const moe_desc& d, const uint16_t* w1, const uint16_t* w2, char* wprep,
@@ -925,38 +1050,34 @@ int fp8_prepare_weights(const moe_desc& d, const uint16_t* w1, const uint16_t* w
                        reinterpret_cast<uint32_t*>(wprep + W.w1t_sc), "quant_w1_t", s);
 }
 
-// Scratch regions of the FP8 operands (after the bf16 layout).
+// Pointers to the FP8 regions of one scratch buffer.
 struct F8Scratch {
-  uint8_t *qrow, *qt1, *qt2, *qt3;
-  uint32_t *qrow_sc, *qt1_sc, *qt2_sc, *qt3_sc;
-  size_t qrow_sc_bytes, qt_sc_bytes;
+  uint8_t *qrow, *qt1, *qt2, *qta, *qt3;
+  uint32_t *qrow_sc, *qt1_sc, *qt2_sc, *qta_sc, *qt3_sc;
+  size_t qrow_sc_bytes, qt_sc_bytes, qta_sc_bytes;
 };
 
 static F8Scratch f8scratch(const moe_desc& d, const Layout& L, char* scratch) {
-  const size_t N = size_t(d.T) * d.K, C = d.D > 2 * d.F ? d.D : 2 * d.F;
-  const size_t npad = size_t(max_steps128(d)) * 128;
+  const F8Offsets o = f8offsets(d);
   char* b = scratch + L.fp8;
+  auto u8 = [&](size_t off) { return reinterpret_cast<uint8_t*>(b + off); };
+  auto u32 = [&](size_t off) { return reinterpret_cast<uint32_t*>(b + off); };
   F8Scratch f{};
-  size_t o = 0;
-  f.qrow = reinterpret_cast<uint8_t*>(b + o);
-  o = align256(o + N * C);
-  f.qrow_sc = reinterpret_cast<uint32_t*>(b + o);
-  f.qrow_sc_bytes = (C / 128) * N * 4;
-  o = align256(o + f.qrow_sc_bytes);
-  f.qt_sc_bytes = (npad / 128) * C * 4;
-  f.qt1 = reinterpret_cast<uint8_t*>(b + o);
-  o = align256(o + C * npad);
-  f.qt1_sc = reinterpret_cast<uint32_t*>(b + o);
-  o = align256(o + f.qt_sc_bytes);
-  f.qt2 = reinterpret_cast<uint8_t*>(b + o);
-  o = align256(o + C * npad);
-  f.qt2_sc = reinterpret_cast<uint32_t*>(b + o);
-  o = align256(o + f.qt_sc_bytes);
-  if (pair_capable(d)) {
-    f.qt3 = reinterpret_cast<uint8_t*>(b + o);
-    o = align256(o + C * npad);
-    f.qt3_sc = reinterpret_cast<uint32_t*>(b + o);
+  f.qrow = u8(o.qrow);
+  f.qrow_sc = u32(o.qrow_sc);
+  f.qt1 = u8(o.qt1);
+  f.qt1_sc = u32(o.qt1_sc);
+  f.qt2 = u8(o.qt2);
+  f.qt2_sc = u32(o.qt2_sc);
+  f.qta = u8(o.qta);
+  f.qta_sc = u32(o.qta_sc);
+  if (o.has_qt3) {
+    f.qt3 = u8(o.qt3);
+    f.qt3_sc = u32(o.qt3_sc);
   }
+  f.qrow_sc_bytes = o.qrow_sc_bytes;
+  f.qt_sc_bytes = o.qt_sc_bytes;
+  f.qta_sc_bytes = o.qta_sc_bytes;
   return f;
 }
 
@@ -1068,28 +1189,34 @@ void fp8_dyw_codes(const moe_desc& d, const Layout& L, char* scratch, uint8_t** 
   *scales = f.qt1_sc;
 }
 
-int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* dw1, void* dw2,
-                  char* scratch, hipStream_t s, bool dyw_quantised) {
+int fp8_x_tokens(const moe_desc& d, const Layout& L, const void* x, char* scratch, hipStream_t s) {
+  const F8Scratch f = f8scratch(d, L, scratch);
+  return quant_tokens(d, L, static_cast<const uint16_t*>(x), d.D, d.mode == MOE_MXFP8, f.qt2,
+                      f.qt2_sc, "quant_x_tokens", scratch, s, TOK_GATHER);
+}
+
+int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const void* dy,
+                  const float* topk_w, void* dw1, void* dw2, char* scratch, hipStream_t s) {
   const WLayout W = wlayout(d);
   const F8Scratch f = f8scratch(d, L, scratch);
   const bool mx = d.mode == MOE_MXFP8;
   const bool paired = pair_capable(d);
+  // MXFP8 and FP8: the forward already wrote x's token codes (fp8_x_tokens)
+  const bool x_tokens = !fp8_fwd(d.mode);
   const int D = d.D, F = d.F, N = d.T * d.K;
   const int64_t npad = int64_t(max_steps128(d)) * 128;
-  const auto* dyw = reinterpret_cast<const uint16_t*>(scratch + L.dyperm);
+  const auto* dyg = static_cast<const uint16_t*>(dy);
   const auto* act = reinterpret_cast<const uint16_t*>(scratch + L.a);
   const auto* dh = reinterpret_cast<const uint16_t*>(scratch + L.dh);
   const auto* xp = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
   int rc;
-  // W2 dgrad + SwiGLU-backward on dYw's row codes (in the first token-code
-  // buffer).  dH's row codes for the W1 dgrad: in MXFP8 the epilogue writes
+  // W2 dgrad + SwiGLU-backward on dYw's row codes, which the combine-backward
+  // wrote into the first token-code buffer.  dH's row codes for the W1 dgrad: in MXFP8 the epilogue writes
   // them as it stores dH; blockwise, a separate pass over the stored dH is
   // cheaper (its quotients and 128-lane maxima made the epilogue 0.16 ms
   // slower at the 30B shape, 0.33 ms at 235B, against a 0.11 / 0.22 ms pass,
   // while MXFP8's power-of-two scales cost the epilogue less than the pass)
   const bool dh_pass = !mx;
-  if (!dyw_quantised && (rc = quant_rows(d, dyw, D, mx, f.qt1, f.qt1_sc, "quant_dyw_rows", s)))
-    return rc;
   F8Args a{};
   a.K = D;
   a.A = f.qt1;
@@ -1108,7 +1235,8 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
                   dh_pass ? QM_NONE : QM_MX};
   // W2 wgrad over tokens: dYw's token codes (in the first buffer once the W2
   // dgrad is done with the row codes there; in the third when both run in one
-  // launch) and A's (in the second)
+  // launch) and A's.  dYw's are gathered from dy (the combine-backward stores
+  // no bf16 dYw rows in the FP8 modes).
   uint8_t* dyt = paired ? f.qt3 : f.qt1;
   uint32_t* dyt_sc = paired ? f.qt3_sc : f.qt1_sc;
   F8Args w{};
@@ -1119,11 +1247,11 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   w.SA = dyt_sc;
   w.sa_ld = D;
   w.sa_bytes = uint32_t(f.qt_sc_bytes);
-  w.B = f.qt2;
+  w.B = f.qta;
   w.ldb = npad;
-  w.SB = f.qt2_sc;
+  w.SB = f.qta_sc;
   w.sb_ld = F;
-  w.sb_bytes = uint32_t(f.qt_sc_bytes);
+  w.sb_bytes = uint32_t(f.qta_sc_bytes);
   w.C = dw2;
   // W1 wgrad over tokens: dH's token codes (first buffer) and x_perm's (second)
   F8Args v{};
@@ -1159,15 +1287,19 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   if (paired) {  // each dgrad beside its weight gradient, one launch per pair
     int* ctr = reinterpret_cast<int*>(scratch + L.pair);
     if ((rc = launch_zero(ctr, 2 * kPairQueues * sizeof(int), s))) return rc;
-    if ((rc = quant_tokens(d, L, dyw, D, mx, f.qt3, f.qt3_sc, "quant_dyw_tokens", scratch, s))) return rc;
-    if ((rc = quant_tokens(d, L, act, F, mx, f.qt2, f.qt2_sc, "quant_a_tokens", scratch, s))) return rc;
+    if ((rc = quant_tokens(d, L, dyg, D, mx, f.qt3, f.qt3_sc, "quant_dyw_tokens", scratch, s,
+                           TOK_GATHER_W, topk_w)))
+      return rc;
+    if ((rc = quant_tokens(d, L, act, F, mx, f.qta, f.qta_sc, "quant_a_tokens", scratch, s))) return rc;
     rc = mx ? run_f8_pair<true, EPI_DSWIGLU>(d, L, a, F, w, ctr, "pair_w2", scratch, s)
             : run_f8_pair<false, EPI_DSWIGLU>(d, L, a, F, w, ctr, "pair_w2", scratch, s);
     if (rc) return rc;
     if (dh_pass && (rc = quant_rows(d, dh, 2 * F, false, f.qrow, f.qrow_sc, "quant_dh_rows", s)))
       return rc;
     if ((rc = quant_tokens(d, L, dh, 2 * F, mx, f.qt1, f.qt1_sc, "quant_dh_tokens", scratch, s))) return rc;
-    if ((rc = quant_tokens(d, L, xp, D, mx, f.qt2, f.qt2_sc, "quant_x_tokens", scratch, s))) return rc;
+    if (x_tokens &&
+        (rc = quant_tokens(d, L, xp, D, mx, f.qt2, f.qt2_sc, "quant_x_tokens", scratch, s)))
+      return rc;
     return mx ? run_f8_pair<true, EPI_STORE>(d, L, b, D, v, ctr + kPairQueues, "pair_w1", scratch, s)
               : run_f8_pair<false, EPI_STORE>(d, L, b, D, v, ctr + kPairQueues, "pair_w1", scratch, s);
   }
@@ -1177,8 +1309,10 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   if (rc) return rc;
   if (dh_pass && (rc = quant_rows(d, dh, 2 * F, false, f.qrow, f.qrow_sc, "quant_dh_rows", s)))
     return rc;
-  if ((rc = quant_tokens(d, L, dyw, D, mx, f.qt1, f.qt1_sc, "quant_dyw_tokens", scratch, s))) return rc;
-  if ((rc = quant_tokens(d, L, act, F, mx, f.qt2, f.qt2_sc, "quant_a_tokens", scratch, s))) return rc;
+  if ((rc = quant_tokens(d, L, dyg, D, mx, f.qt1, f.qt1_sc, "quant_dyw_tokens", scratch, s,
+                         TOK_GATHER_W, topk_w)))
+    return rc;
+  if ((rc = quant_tokens(d, L, act, F, mx, f.qta, f.qta_sc, "quant_a_tokens", scratch, s))) return rc;
   rc = mx ? run_f8_wgrad<true>(d, L, w, "gemm_w2_wgrad", scratch, s)
           : run_f8_wgrad<false>(d, L, w, "gemm_w2_wgrad", scratch, s);
   if (rc) return rc;
@@ -1188,7 +1322,9 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, void* d
   // dgrad first, right after the W2 dgrad wrote those codes (0.5% faster there).
   auto w1_wgrad = [&]() -> int {
     if ((rc = quant_tokens(d, L, dh, 2 * F, mx, f.qt1, f.qt1_sc, "quant_dh_tokens", scratch, s))) return rc;
-    if ((rc = quant_tokens(d, L, xp, D, mx, f.qt2, f.qt2_sc, "quant_x_tokens", scratch, s))) return rc;
+    if (x_tokens &&
+        (rc = quant_tokens(d, L, xp, D, mx, f.qt2, f.qt2_sc, "quant_x_tokens", scratch, s)))
+      return rc;
     return mx ? run_f8_wgrad<true>(d, L, v, "gemm_w1_wgrad", scratch, s)
               : run_f8_wgrad<false>(d, L, v, "gemm_w1_wgrad", scratch, s);
   };

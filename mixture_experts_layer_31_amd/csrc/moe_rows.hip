@@ -94,7 +94,8 @@ __device__ __forceinline__ void store8(float* p, size_t i8, const float (&f)[8])
 // bf16 rows) the token's row is also quantised along D once and its codes
 // written with every copy: codes [N, D], scale entries [D/128][N], as the
 // standalone row quantiser writes them (a token's chunks sit on consecutive
-// threads, so the groups are aligned lanes when D / 8 is a multiple of 16).
+// threads, so the groups are aligned lanes when D / 8 is a multiple of 16);
+// with dst null only the codes are written.
 template <typename IO, typename ACT, int QM>
 __global__ void __launch_bounds__(kRowThreads) dispatch_kernel(
     const IO* __restrict__ rows, int T, int K, int D, const int32_t* __restrict__ pos,
@@ -119,7 +120,7 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_kernel(
         for (int k = 0; k < K; ++k) {
           const int q = prow[k];
           if (q >= 0) {
-            reinterpret_cast<uint4*>(dst)[(size_t(q) * D) / 8 + c] = v;
+            if (dst != nullptr) reinterpret_cast<uint4*>(dst)[(size_t(q) * D) / 8 + c] = v;
             *reinterpret_cast<uint2*>(qcodes + size_t(q) * D + 8 * c) = codes;
             if ((c & 15) == 0) qsc[size_t(c >> 4) * N + q] = entry;
           }
@@ -218,7 +219,8 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_wide_kernel(
 // one pair per token three waves of four would idle.
 // With QM (FP8 forward modes) every wave also quantises the row along D (a
 // 128-column group is 16 consecutive lanes' chunks) and writes the codes and
-// scale entries of its copies, as dispatch_kernel does.
+// scale entries of its copies, as dispatch_kernel does; with dst null it
+// writes only those.
 template <int CPL, int QM>
 __global__ void __launch_bounds__(kRowThreads) dispatch_rows_kernel(
     const uint16_t* __restrict__ rows, int T, int K, int D, const int32_t* __restrict__ pos,
@@ -245,9 +247,11 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_rows_kernel(
   for (int k = wave; k < K; k += WAVES) {
     const int q = prow[k];
     if (q < 0) continue;
-    uint4* d = reinterpret_cast<uint4*>(dst) + (size_t(q) * D) / 8 + lane;
+    if (QM == QM_NONE || dst != nullptr) {  // FP8 modes may keep only the codes
+      uint4* d = reinterpret_cast<uint4*>(dst) + (size_t(q) * D) / 8 + lane;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) d[64 * j] = v[j];
+      for (int j = 0; j < CPL; ++j) d[64 * j] = v[j];
+    }
     if constexpr (QM != QM_NONE) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
@@ -326,7 +330,8 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_kernel(
 // same bf16-rounded values it stores: QM_BLOCK, an fp32 scale per 128 columns
 // (a group is 16 consecutive lanes' chunks); QM_MX, an e8m0 scale per 32 (4
 // lanes).  Codes are [N, D] bytes, scale entries [D/128][N], as the standalone
-// row quantiser writes them.  D / 8 must be a multiple of 16 so a group never
+// row quantiser writes them.  With QM and dst null the bf16 rows are not stored
+// (the FP8 backward's token quantiser gathers w * dy itself).  D / 8 must be a multiple of 16 so a group never
 // straddles active and idle lanes.
 constexpr int kSplitMaxK = 64;  // K up to this many slots may split a row over waves
 
@@ -374,7 +379,7 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_dy_kernel(
             dot = __builtin_fmaf(v[j][i], o[i], dot);
             sc[i] = w * v[j][i];
           }
-          store8(dst, (size_t(q) * D) / 8 + c, sc);
+          if (QM == QM_NONE || dst != nullptr) store8(dst, (size_t(q) * D) / 8 + c, sc);
         }
         if constexpr (QM != QM_NONE) {
           // quantise the stored (bf16-rounded) values; idle lanes join the reductions with 0
@@ -466,7 +471,8 @@ static int with_types(const moe_desc& d, bool io_f32, F f) {
 
 int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool in_f32,
                     const float* topk_w, char* scratch, size_t dst_off, hipStream_t s,
-                    int qmode, uint8_t* qcodes, uint32_t* qsc) {
+                    int qmode, uint8_t* qcodes, uint32_t* qsc, bool store_rows) {
+  if (!store_rows && qmode == 0) return MOE_EINVAL;
   const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
   auto* wperm = topk_w ? reinterpret_cast<float*>(scratch + L.wperm) : nullptr;
   prof_begin("dispatch", s);
@@ -474,7 +480,7 @@ int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool i
     using IO = decltype(io);
     using ACT = decltype(act);
     const IO* src = static_cast<const IO*>(rows);
-    ACT* dst = reinterpret_cast<ACT*>(scratch + dst_off);
+    ACT* dst = store_rows ? reinterpret_cast<ACT*>(scratch + dst_off) : nullptr;
     const int N = d.T * d.K;
     if constexpr (std::is_same<IO, uint16_t>::value && std::is_same<ACT, uint16_t>::value) {
       if (qmode != 0 && d.D == 2048 && d.K >= kRowThreads / 64) {  // FP8 forward, 30B shape
@@ -564,7 +570,8 @@ static int dispatch_dy_cpl(const moe_desc& d, const IO* dy, const int32_t* pos,
 
 int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool in_f32,
                        const float* topk_w, float* dtopk_w, char* scratch, hipStream_t s,
-                       int qmode, uint8_t* qcodes, uint32_t* qsc) {
+                       int qmode, uint8_t* qcodes, uint32_t* qsc, bool store_rows) {
+  if (!store_rows && qmode == 0) return MOE_EINVAL;
   const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
   prof_begin("dispatch_dy", s);
   const int rc = with_types(d, in_f32, [&](auto io, auto act) {
@@ -572,7 +579,7 @@ int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool 
     using ACT = decltype(act);
     const IO* src = static_cast<const IO*>(dy);
     const ACT* o = reinterpret_cast<const ACT*>(scratch + L.o);
-    ACT* dst = reinterpret_cast<ACT*>(scratch + L.dyperm);
+    ACT* dst = store_rows ? reinterpret_cast<ACT*>(scratch + L.dyperm) : nullptr;
     if constexpr (std::is_same<ACT, uint16_t>::value) {
       if (qmode == 1)
         return dispatch_dy_cpl<IO, ACT, QM_MX>(d, src, pos, topk_w, o, dst, dtopk_w, qcodes, qsc, s);

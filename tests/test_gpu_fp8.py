@@ -123,8 +123,12 @@ def test_fp8_quantisers_and_gemms(name):
     src = r["src"]
     e_of = np.repeat(np.arange(cfg.E), np.diff(offsets))
     D, F = cfg.D, cfg.F
+    # the dispatched rows x_perm and the combine-backward's w * dy rows, built on the host
+    # from the routing (the FP8 modes store only their codes; x and dy are bf16 values)
+    t_of, k_of = src // cfg.K, src % cfg.K
+    xp = inp["x"][t_of]
+    dYw = mi.bf16_round((inp["topk_w"][t_of, k_of][:, None] * inp["dy"][t_of]).astype(np.float32))
     if fwd_q:  # x_perm's rows were quantised by the dispatch: H = quantised x times quantised W1
-        xp = L.view(moe.MOE_VIEW_XPERM, D)[:len(src)]
         qc, qs = f8.quant_rows(xp, 32 if mx else 128, mx)
         xdq = f8.dequant_rows(qc, qs, 32 if mx else 128, mx)
         Hg = L.view(moe.MOE_VIEW_H, 2 * F)[:len(src)]
@@ -148,7 +152,6 @@ def test_fp8_quantisers_and_gemms(name):
     assert L.check() == moe.MOE_OK
     # the W2 dgrad consumed dYw's row codes written by the combine-backward: its SwiGLU-backward
     # output must equal the oracle's row quantisation of the dYw rows times the quantised W2
-    dYw = L.view(moe.MOE_VIEW_DYPERM, D)[:len(src)]
     qc, qs = f8.quant_rows(dYw, 32 if mx else 128, mx)
     dYdq = f8.dequant_rows(qc, qs, 32 if mx else 128, mx)
     H = L.view(moe.MOE_VIEW_H, 2 * F)[:len(src)].astype(np.float64)
@@ -163,7 +166,6 @@ def test_fp8_quantisers_and_gemms(name):
     assert rel_err(dH_gpu, dH_ref) <= 1e-2, ("dH from fused dYw codes", rel_err(dH_gpu, dH_ref))
     # the backward's last quantised operands: dH rows (W1 dgrad), dH and x_perm along tokens (W1 wgrad)
     dH = L.view(moe.MOE_VIEW_DH, 2 * F)[:len(src)]
-    xp = L.view(moe.MOE_VIEW_XPERM, D)[:len(src)]
     dHdq = _check_rows(L, dH, mx)
     dXp = L.view(moe.MOE_VIEW_DXPERM, D)[:len(src)]
     ref = np.zeros_like(dXp, dtype=np.float64)
@@ -171,7 +173,7 @@ def test_fp8_quantisers_and_gemms(name):
         rows = slice(offsets[e], offsets[e + 1])
         ref[rows] = dHdq[rows] @ _w_deq(inp["w1"][e], True, mx)
     assert rel_err(dXp, ref) <= 1e-2, ("dX_perm", rel_err(dXp, ref))
-    # the W2 weight gradient: dYw (built from dy by the token quantiser) and A along tokens
+    # the W2 weight gradient: dYw (gathered from dy by the token quantiser) and A along tokens
     A = L.view(moe.MOE_VIEW_A, F)[:len(src)]
     rc1, rs1, poff = f8.quant_tokens(dYw, offsets, 32 if mx else 128, mx)
     rc2, rs2, _ = f8.quant_tokens(A, offsets, 32 if mx else 128, mx)
