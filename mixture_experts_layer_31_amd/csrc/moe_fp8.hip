@@ -421,7 +421,13 @@ __device__ __forceinline__ f32x16 mfma8(i32x8 b, i32x8 a, f32x16 c, int sb, int 
 // The MXFP8 loop: 128-element k-steps in two LDS stages of 128-byte rows; the
 // matrix core applies the e8m0 scales (the lane's row and column entries,
 // shifted so that op_sel 0 and 2 pick the lane's 32-group of each 64-deep
-// half).
+// half).  Each step waits for its stage, meets every wave at the barrier and
+// issues the next step's loads into the other stage; then a half-step's two B
+// fragments stay in registers while its A fragments stream one 32-row block
+// ahead of the MFMAs that use them (the second half's B fragments are read
+// beside the first half's last blocks), so only the step's first three
+// fragments are read in front of the matrix core.  All branches stay at the
+// top of the step, before the MFMAs.
 template <class TL, class SA, class SB>
 __device__ __forceinline__ void mainloop8(char* smem, const SA& sa, const SB& sb,
                                           const ScaleStager& ssa, const ScaleStager& ssb,
@@ -431,6 +437,7 @@ __device__ __forceinline__ void mainloop8(char* smem, const SA& sa, const SB& sb
   constexpr int WMT = TL::WMT, WNT = TL::WNT;
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES + 2048;
   static_assert(TL::STAGES == 2, "two stages");
+  static_assert(WMT >= 2 && WNT == 2, "the second half's B fragments go beside the last two A blocks");
   const int wm = wave / TL::WGN, wn = wave % TL::WGN;
   const uint32_t base = lds_addr(smem);
   auto issue = [&](int s, int kt) {
@@ -440,6 +447,7 @@ __device__ __forceinline__ void mainloop8(char* smem, const SA& sa, const SB& sb
     ssa.issue(st + A_BYTES + B_BYTES, kt);
     ssb.issue(st + A_BYTES + B_BYTES + 1024, kt);
   };
+  const int sh = 8 * (lane >> 5);
   if (ktiles > 0) issue(0, 0);
   for (int kt = 0; kt < ktiles; ++kt) {
     wait_vmcnt<0>();
@@ -447,29 +455,47 @@ __device__ __forceinline__ void mainloop8(char* smem, const SA& sa, const SB& sb
     if (kt + 1 < ktiles) issue((kt + 1) & 1, kt + 1);
     const char* ta = smem + (kt & 1) * STAGE;
     const char* tb = ta + A_BYTES;
+    auto fa = [&](int h, int i) { return frag8(ta, wm * WM + i * 32 + (lane & 31), h, lane); };
+    auto fb = [&](int h, int j) { return frag8(tb, wn * WN + j * 32 + (lane & 31), h, lane); };
     const uint32_t* sca = reinterpret_cast<const uint32_t*>(tb + B_BYTES);
     const uint32_t* scb = sca + 256;
-    i32x8 af[2][WMT], bfr[2][WNT];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int i = 0; i < WMT; ++i) af[kk][i] = frag8(ta, wm * WM + i * 32 + (lane & 31), kk, lane);
-#pragma unroll
-      for (int j = 0; j < WNT; ++j) bfr[kk][j] = frag8(tb, wn * WN + j * 32 + (lane & 31), kk, lane);
-    }
-    const int sh = 8 * (lane >> 5);
     int sa_w[WMT], sb_w[WNT];
 #pragma unroll
     for (int i = 0; i < WMT; ++i) sa_w[i] = int(sca[wm * WM + i * 32 + (lane & 31)] >> sh);
 #pragma unroll
     for (int j = 0; j < WNT; ++j) sb_w[j] = int(scb[wn * WN + j * 32 + (lane & 31)] >> sh);
+    i32x8 bc[WNT], bn[WNT], ac, an;
 #pragma unroll
-    for (int i = 0; i < WMT; ++i)
+    for (int j = 0; j < WNT; ++j) bc[j] = fb(0, j);
+    ac = fa(0, 0);
+    auto half = [&](auto H) {
+      constexpr int h = decltype(H)::value;
 #pragma unroll
-      for (int j = 0; j < WNT; ++j) {
-        acc[i][j] = mfma8<0>(bfr[0][j], af[0][i], acc[i][j], sb_w[j], sa_w[i]);
-        acc[i][j] = mfma8<2>(bfr[1][j], af[1][i], acc[i][j], sb_w[j], sa_w[i]);
+      for (int i = 0; i < WMT; ++i) {
+        if (i + 1 < WMT) an = fa(h, i + 1);
+        if constexpr (h == 0) {
+          if (i == WMT - 2) bn[0] = fb(1, 0);
+          if (i == WMT - 1) {
+            bn[1] = fb(1, 1);
+            an = fa(1, 0);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < WNT; ++j)
+          acc[i][j] = mfma8<2 * h>(bc[j], ac, acc[i][j], sb_w[j], sa_w[i]);
+        // the reads first, so they have both MFMAs (and the other wave's) to return
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, WNT, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        ac = an;
       }
+      if constexpr (h == 0) {
+#pragma unroll
+        for (int j = 0; j < WNT; ++j) bc[j] = bn[j];
+      }
+    };
+    half(std::integral_constant<int, 0>{});
+    half(std::integral_constant<int, 1>{});
   }
 }
 
@@ -642,7 +668,8 @@ __device__ __forceinline__ void f8_grouped_tile(const F8Args& p, int l, char* sm
   if constexpr (MX) mainloop8<TL>(smem, sa, sb, ssa, ssb, p.K / 128, acc, wave, lane);
   else block8<TL, false>(smem, sa, sb, ssa, ssb, p.K / 128, acc, wave, lane);
   static_assert(f8_grouped_lds<TL, MX>() >= grouped_epi_lds<TL, EPI>(), "epilogue staging exceeds LDS");
-  grouped_epilogue<TL, EPI>(p.epi, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane, smem, threadIdx.x);
+  grouped_epilogue<TL, EPI, false, f8_grouped_lds<TL, MX>()>(p.epi, acc, size_t(e0) + m0, rows_valid,
+                                                               nt, wm, wn, lane, smem, threadIdx.x);
 }
 
 // The tiles from a grid of resident workgroups, in rounds of gridDim.x (an XCD

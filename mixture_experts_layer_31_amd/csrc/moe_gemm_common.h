@@ -546,6 +546,31 @@ __device__ __forceinline__ void band_store(const BandTile<ES>& t, int rows, int 
   }
 }
 
+// Whole-tile form of band_store: ROWS staged rows of CH 16-byte chunks (row
+// stride CH * 16 bytes, chunks XOR-swizzled by row as in BandTile) to global
+// rows dst(row), the first `valid` of them.  Every thread reads all of its
+// chunks from LDS before it issues any store, so its stores leave back to back
+// instead of each behind its own LDS round trip.
+template <int THREADS, int ROWS, int CH, class Dst>
+__device__ __forceinline__ void tile_store(const char* base, int valid, Dst dst) {
+  constexpr int N = ROWS * CH / THREADS;
+  constexpr int SW = (CH < 32 ? CH : 32) - 1;
+  static_assert(N * THREADS == ROWS * CH, "chunks split evenly over the threads");
+  // per-thread offsets recomputed here, not hoisted out of a persistent tile loop
+  const int tid = opaque_tid();
+  uint4 v[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int i = tid + k * THREADS, r = i / CH, c = i % CH;
+    v[k] = *reinterpret_cast<const uint4*>(base + r * CH * 16 + ((c ^ (r & SW)) << 4));
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int i = tid + k * THREADS, r = i / CH, c = i % CH;
+    if (r < valid) *reinterpret_cast<uint4*>(dst(r) + c * 16) = v[k];
+  }
+}
+
 // Cooperative copy of global rows src(row) into a band tile (zeros for rows >= valid).
 template <int THREADS, int ES, class Src>
 __device__ __forceinline__ void band_load(const BandTile<ES>& t, int rows, int valid, int tid, Src src) {
@@ -687,8 +712,10 @@ __device__ __forceinline__ void dswiglu_epilogue(const EpiArgs& p,
 // Epilogue of a token-grouped GEMM.  Lane owns row (lane & 31) of each 32-row
 // block and, per group g of four registers, four consecutive columns starting
 // at acc_col(g).  grow0 is the tile's first row in the permuted buffers; smem is
-// the (now free) pipeline LDS.
-template <class TL, int EPI, bool COH2 = false>
+// the (now free) pipeline LDS, AVAIL bytes of it.  A plain store stages the
+// whole bf16 tile at once when AVAIL holds it (one barrier, every store of a
+// thread issued back to back), else one band at a time.
+template <class TL, int EPI, bool COH2 = false, int AVAIL = 0>
 __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
                                                  f32x16 (&acc)[TL::WMT][TL::WNT], size_t grow0,
                                                  int rows_valid, int nt, int wm, int wn, int lane,
@@ -699,6 +726,24 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
   __syncthreads();  // every wave is done reading the pipeline stages
   if constexpr (EPI == EPI_DSWIGLU) {
     dswiglu_epilogue<TL>(p, acc, grow0, rows_valid, nt, wm, wn, lane, smem);
+    return;
+  }
+  if constexpr (EPI == EPI_STORE && AVAIL >= TL::BM * BN * 2) {
+    BandTile<2> t{smem, BN};
+#pragma unroll
+    for (int i = 0; i < WMT; ++i)
+#pragma unroll
+      for (int j = 0; j < WNT; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& a = acc[i][j];
+          *reinterpret_cast<uint2*>(t.at(wm * WM + i * 32 + (lane & 31), wn * WN + j * 32 + acc_col(g, lane))) =
+              pack4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+        }
+    __syncthreads();
+    tile_store<TL::THREADS, TL::BM, BN * 2 / 16>(smem, rows_valid, [&](int r) {
+      return reinterpret_cast<char*>(p.out + (grow0 + r) * p.ldo + nt * BN);
+    });
     return;
   }
 #pragma unroll
@@ -772,7 +817,9 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
   }
 }
 
-// Epilogue of a per-expert weight-gradient GEMM: dW[e] tile (mt, nt) of [M, N].
+// Epilogue of a per-expert weight-gradient GEMM: dW[e] tile (mt, nt) of [M, N],
+// one band at a time (the whole-tile staging of the token-grouped store made
+// these GEMMs slower: 30B blockwise FP8 wgrads +20%, MXFP8 W1 wgrad +2%).
 template <class TL, bool OUT_F32>
 __device__ __forceinline__ void wgrad_epilogue(void* C, int M, int N, int e, int mt, int nt,
                                                f32x16 (&acc)[TL::WMT][TL::WNT], int wm, int wn,

@@ -117,7 +117,8 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoo
   }
 
   EpiArgs ea{p.out, p.ldo, p.out2, p.hsave, p.F};
-  grouped_epilogue<TL, EPI, COH2>(ea, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane, smem, tid);
+  grouped_epilogue<TL, EPI, COH2, TL::LDS>(ea, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane,
+                                           smem, tid);
 }
 
 }  // namespace gemm
