@@ -54,20 +54,22 @@ def gemm_flops(cfg) -> dict:
             "pair_w2": 4 * ndf, "pair_w1": 8 * ndf}
 
 
-def row_bytes(cfg, b=2) -> dict:
+def row_bytes(cfg, b=2, recompute=False) -> dict:
     """Algorithmic HBM bytes per launch of the row movers (bf16 rows).  In the FP8
-    forward modes the dispatch also writes the e4m3 row codes of x_perm and one
-    4-byte scale entry per 128 columns; in every FP8 mode the combine-backward
-    writes those of dYw."""
+    forward modes (MXFP8, blockwise FP8) the dispatch writes the e4m3 row codes
+    of x_perm and one 4-byte scale entry per 128 columns instead of the bf16
+    rows (which it writes too under activation recompute); in every FP8 mode
+    the combine-backward writes those of dYw instead of its bf16 rows."""
     T, N, D = cfg.T, cfg.N, cfg.D
     codes = N * D + N * (D // 128) * 4
     fwd_q = cfg.mode in (4, 5)   # MXFP8, blockwise FP8 in both passes
     bwd_q = cfg.mode in (3, 4, 5)
-    return {"dispatch": T * D * b + N * D * b + 2 * N * 4 + N * 4 + (codes if fwd_q else 0),
+    xrows = N * D * b if (not fwd_q or recompute) else 0
+    return {"dispatch": T * D * b + xrows + 2 * N * 4 + N * 4 + (codes if fwd_q else 0),
             "combine": N * D * b + T * D * b + N * 8,
-            # dy once, each pair's expert-output row read and its w*dy row written,
-            # pos and topk_w read, dtopk_w written
-            "dispatch_dy": T * D * b + 2 * N * D * b + 3 * N * 4 + (codes if bwd_q else 0),
+            # dy once, each pair's expert-output row read and (bf16 modes) its w*dy
+            # row written, pos and topk_w read, dtopk_w written
+            "dispatch_dy": T * D * b + N * D * b + (codes if bwd_q else N * D * b) + 3 * N * 4,
             "unpermute": N * D * b + T * D * b + N * 4}
 
 
@@ -290,7 +292,7 @@ def run_config(name: str, args, flags: int, main_line: bool) -> tuple:
     per_kernel = {}
     if kernels:
         gf = gemm_flops(cfg)
-        rb = row_bytes(cfg)
+        rb = row_bytes(cfg, recompute=bool(flags & moe.MOE_FLAG_RECOMPUTE))
         for kname, (ms, n) in kernels.items():
             avg = ms / n
             entry = {"avg_ms": round(avg, 4), "launches": n}

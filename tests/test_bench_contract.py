@@ -38,10 +38,16 @@ def test_row_mover_bytes_follow_the_definitions():
     assert rb["unpermute"] == 2 * N * D + 2 * T * D + N * 4
     # combine-backward: dy once, pair rows read (O) and written (w * dy), 3 index/weight arrays
     assert rb["dispatch_dy"] == 2 * T * D + 4 * N * D + 3 * N * 4
-    # the FP8 forward modes' dispatch also writes e4m3 codes and one 4-byte entry per 128 columns
+    # the FP8 forward modes' dispatch writes e4m3 codes and one 4-byte entry per 128 columns
+    # instead of the bf16 rows (both under activation recompute)
+    codes = N * D + N * (D // 128) * 4
     mx = mi.CONFIGS["30b_mxfp8"]
-    assert b.row_bytes(mx)["dispatch"] - rb["dispatch"] == N * D + N * (D // 128) * 4
+    assert b.row_bytes(mx)["dispatch"] - rb["dispatch"] == codes - 2 * N * D
+    assert b.row_bytes(mx, recompute=True)["dispatch"] - rb["dispatch"] == codes
+    # every FP8 mode's combine-backward writes dYw's codes instead of its bf16 rows
+    assert b.row_bytes(mx)["dispatch_dy"] - rb["dispatch_dy"] == codes - 2 * N * D
     fb = mi.CONFIGS["235b_fp8bwd"]
+    fcodes = fb.N * fb.D + fb.N * (fb.D // 128) * 4
     assert b.row_bytes(fb)["dispatch"] == b.row_bytes(mi.CONFIGS["235b"])["dispatch"]
     assert (b.row_bytes(fb)["dispatch_dy"] - b.row_bytes(mi.CONFIGS["235b"])["dispatch_dy"]
-            == fb.N * fb.D + fb.N * (fb.D // 128) * 4)
+            == fcodes - 2 * fb.N * fb.D)
