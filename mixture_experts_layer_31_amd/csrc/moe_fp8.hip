@@ -68,6 +68,9 @@ struct QArgs {
   const int32_t* src;      // gathering token quantiser: [N] pair of each permuted row
   const float* topk_w;     // TOK_GATHER_W: [T*K] routing weight of each pair
   int K;                   // gathering token quantiser: pairs per token
+  uint8_t* rcodes;         // token quantiser with ROWQ: the rows' own codes [N, cols]
+  uint32_t* rsc;           //   and their scale entries [cols / 128][rsc_ld]
+  int64_t rsc_ld;
   int E;
   int ntr;                 // weights: r-steps per expert
   int total_rows;          // row quantiser: rows of the input
@@ -270,7 +273,7 @@ __device__ __forceinline__ uint4 scale_bf16x8(const uint4& v, float w) {
 // next tile's rows are loaded into registers as soon as the current tile is
 // in LDS, so they arrive while it is quantised and stored, and a gathered
 // row's index and weight are looked up once for all NCT tiles.
-template <bool MX, int SRC, int NCT>
+template <bool MX, int SRC, int NCT, bool ROWQ = false>
 __global__ void __launch_bounds__(256) quant_tokens_kernel(QArgs p) {
   __shared__ __attribute__((aligned(16))) char tile[128 * 256];
   const int groups = p.cols / (128 * NCT);
@@ -323,6 +326,27 @@ __global__ void __launch_bounds__(256) quant_tokens_kernel(QArgs p) {
       const int r = it * 16 + rw;
       if constexpr (SRC == TOK_GATHER_W) raw[it] = scale_bf16x8(raw[it], wt[it]);
       *reinterpret_cast<uint4*>(tile + at(r, l16 >> 1) + (l16 & 1) * 16) = raw[it];
+    }
+    if constexpr (ROWQ) {
+      // the same rows quantised along their columns, as quant_rows_kernel does
+      // (sixteen lanes per row): one read of the input for both operands
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = it * 16 + rw;
+        const uint32_t wd[4] = {raw[it].x, raw[it].y, raw[it].z, raw[it].w};
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = __uint_as_float(wd[e] << 16);
+          f[2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
+        }
+        uint32_t ent;
+        const uint2 codes = quantise8<MX ? QM_MX : QM_BLOCK>(f, lane, ent);
+        if (r < valid) {
+          *reinterpret_cast<uint2*>(p.rcodes + size_t(r0 + r) * p.cols + c0 + 8 * l16) = codes;
+          if (l16 == 0) p.rsc[size_t(c0 / 128) * p.rsc_ld + r0 + r] = ent;
+        }
+      }
     }
     if (k + 1 < NCT) load(c0 + 128);  // in flight while this tile is quantised and stored
     __syncthreads();
@@ -827,9 +851,13 @@ int quant_rows(const moe_desc& d, const uint16_t* in, int C, bool mx, uint8_t* o
 // [C, Npad] (row stride npad) with scale entries [step][C].  `in` is the
 // permuted rows [N, C] (TOK_PERM) or the per-token rows [T, C] the permuted
 // rows are gathered from (TOK_GATHER, TOK_GATHER_W with the weights topk_w).
+// With rcodes (permuted rows only) the same pass also writes the rows' own
+// quantisation along C, as quant_rows does: codes [N, C] into rcodes, scale
+// entries [C/128][N] into rsc.
 int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, bool mx,
                  uint8_t* out, uint32_t* sc, const char* name, const char* scratch, hipStream_t s,
-                 int src = TOK_PERM, const float* topk_w = nullptr) {
+                 int src = TOK_PERM, const float* topk_w = nullptr, uint8_t* rcodes = nullptr,
+                 uint32_t* rsc = nullptr) {
   QArgs a{};
   a.in = in;
   a.cols = C;
@@ -843,7 +871,11 @@ int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, 
   a.topk_w = topk_w;
   a.K = d.K;
   a.E = d.E;
+  a.rcodes = rcodes;
+  a.rsc = rsc;
+  a.rsc_ld = int64_t(d.T) * d.K;
   if (src == TOK_GATHER_W && topk_w == nullptr) return MOE_EINVAL;
+  if (rcodes != nullptr && (src != TOK_PERM || rsc == nullptr)) return MOE_EINVAL;
   // column tiles per workgroup: the gathering forms pipeline the next tile's
   // row loads behind the current tile's quantisation (at the 30B shape x
   // 0.19 -> 0.17 ms and dYw 0.21 -> 0.19 ms, at 235B dYw 0.43 -> 0.38 ms);
@@ -859,6 +891,9 @@ int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, 
 #define MOE_QTW(S) (nct == 4 ? MOE_QT(S, 4) : nct == 2 ? MOE_QT(S, 2) : MOE_QT(S, 1))
   if (src == TOK_GATHER) MOE_QTW(TOK_GATHER);
   else if (src == TOK_GATHER_W) MOE_QTW(TOK_GATHER_W);
+  else if (rcodes != nullptr)
+    (mx ? quant_tokens_kernel<true, TOK_PERM, 1, true><<<unsigned(blocks), 256, 0, s>>>(a)
+        : quant_tokens_kernel<false, TOK_PERM, 1, true><<<unsigned(blocks), 256, 0, s>>>(a));
   else MOE_QT(TOK_PERM, 1);
 #undef MOE_QTW
 #undef MOE_QT
@@ -1238,12 +1273,13 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   const auto* xp = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
   int rc;
   // W2 dgrad + SwiGLU-backward on dYw's row codes, which the combine-backward
-  // wrote into the first token-code buffer.  dH's row codes for the W1 dgrad: in MXFP8 the epilogue writes
-  // them as it stores dH; blockwise, a separate pass over the stored dH is
-  // cheaper (its quotients and 128-lane maxima made the epilogue 0.16 ms
-  // slower at the 30B shape, 0.33 ms at 235B, against a 0.11 / 0.22 ms pass,
-  // while MXFP8's power-of-two scales cost the epilogue less than the pass)
-  const bool dh_pass = !mx;
+  // wrote into the first token-code buffer.  dH's row codes for the W1 dgrad: in
+  // MXFP8 the epilogue writes them as it stores dH; blockwise, the pass that
+  // quantises the stored dH over tokens writes them too (in the epilogue, the
+  // quotients and 128-lane maxima cost 0.16 ms at the 30B shape and 0.33 ms at
+  // 235B, more than a pass over dH; MXFP8's power-of-two scales cost less)
+  uint8_t* dh_rows = mx ? nullptr : f.qrow;
+  uint32_t* dh_rows_sc = mx ? nullptr : f.qrow_sc;
   F8Args a{};
   a.K = D;
   a.A = f.qt1;
@@ -1259,7 +1295,7 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   a.F = F;
   a.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.dh), 0, nullptr,
                   reinterpret_cast<const uint16_t*>(scratch + L.h), F, f.qrow, f.qrow_sc, N,
-                  dh_pass ? QM_NONE : QM_MX};
+                  mx ? QM_MX : QM_NONE};
   // W2 wgrad over tokens: dYw's token codes (in the first buffer once the W2
   // dgrad is done with the row codes there; in the third when both run in one
   // launch) and A's.  dYw's are gathered from dy (the combine-backward stores
@@ -1321,9 +1357,9 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
     rc = mx ? run_f8_pair<true, EPI_DSWIGLU>(d, L, a, F, w, ctr, "pair_w2", scratch, s)
             : run_f8_pair<false, EPI_DSWIGLU>(d, L, a, F, w, ctr, "pair_w2", scratch, s);
     if (rc) return rc;
-    if (dh_pass && (rc = quant_rows(d, dh, 2 * F, false, f.qrow, f.qrow_sc, "quant_dh_rows", s)))
+    if ((rc = quant_tokens(d, L, dh, 2 * F, mx, f.qt1, f.qt1_sc, "quant_dh_tokens", scratch, s,
+                           TOK_PERM, nullptr, dh_rows, dh_rows_sc)))
       return rc;
-    if ((rc = quant_tokens(d, L, dh, 2 * F, mx, f.qt1, f.qt1_sc, "quant_dh_tokens", scratch, s))) return rc;
     if (x_tokens &&
         (rc = quant_tokens(d, L, xp, D, mx, f.qt2, f.qt2_sc, "quant_x_tokens", scratch, s)))
       return rc;
@@ -1334,8 +1370,6 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   rc = mx ? run_f8_grouped<true, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s)
           : run_f8_grouped<false, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s);
   if (rc) return rc;
-  if (dh_pass && (rc = quant_rows(d, dh, 2 * F, false, f.qrow, f.qrow_sc, "quant_dh_rows", s)))
-    return rc;
   if ((rc = quant_tokens(d, L, dyg, D, mx, f.qt1, f.qt1_sc, "quant_dyw_tokens", scratch, s,
                          TOK_GATHER_W, topk_w)))
     return rc;
@@ -1343,12 +1377,15 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   rc = mx ? run_f8_wgrad<true>(d, L, w, "gemm_w2_wgrad", scratch, s)
           : run_f8_wgrad<false>(d, L, w, "gemm_w2_wgrad", scratch, s);
   if (rc) return rc;
-  // W1 wgrad and W1 dgrad.  Blockwise runs the wgrad first, so that the
-  // un-permute reads dX_perm right after it is written (235B fp8_bwd backward
-  // -0.8%; the token quantisers leave dH's row codes alone); MXFP8 keeps the
-  // dgrad first, right after the W2 dgrad wrote those codes (0.5% faster there).
+  // W1 wgrad and W1 dgrad.  Blockwise runs the wgrad first: its dH token pass
+  // also writes the row codes the dgrad reads, and the un-permute then reads
+  // dX_perm right after it is written (235B fp8_bwd backward -0.8%); MXFP8
+  // keeps the dgrad first, right after the W2 dgrad wrote those codes (0.5%
+  // faster there).
   auto w1_wgrad = [&]() -> int {
-    if ((rc = quant_tokens(d, L, dh, 2 * F, mx, f.qt1, f.qt1_sc, "quant_dh_tokens", scratch, s))) return rc;
+    if ((rc = quant_tokens(d, L, dh, 2 * F, mx, f.qt1, f.qt1_sc, "quant_dh_tokens", scratch, s,
+                           TOK_PERM, nullptr, dh_rows, dh_rows_sc)))
+      return rc;
     if (x_tokens &&
         (rc = quant_tokens(d, L, xp, D, mx, f.qt2, f.qt2_sc, "quant_x_tokens", scratch, s)))
       return rc;
