@@ -1042,9 +1042,10 @@ size_t fp8_wprep_bytes(const moe_desc& d) { return fp8_mode(d.mode) ? wlayout(d)
 //        dH's token codes;
 //   qt2  x's token codes: written by the forward in MXFP8 and FP8 (gathered
 //        from x), by the backward in fp8_bwd (from the dispatched rows);
-//   qta  A's token codes: their own buffer when the forward fills qt2 (F
-//        columns), else qt2 itself, which the W2 weight gradient has read
-//        before x's token codes replace them;
+//   qta  A's token codes (written by the forward in FP8, beside A's row
+//        codes, else by the backward): their own buffer when the forward
+//        fills qt2 (F columns), else qt2 itself, which the W2 weight gradient
+//        has read before x's token codes replace them;
 //   qt3  the paired backward's dYw token codes (the W2 dgrad still reads the
 //        row codes in qt1 in the same launch).
 struct F8Offsets {
@@ -1211,9 +1212,12 @@ int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* s
                          reinterpret_cast<uint16_t*>(scratch + L.a), "gemm_w1_swiglu", scratch, s,
                          x_quantised);
   if (rc) return rc;
-  // expert linear 2, on A's row codes (MXFP8: from the W1 epilogue)
-  if (!mx && (rc = quant_rows(d, reinterpret_cast<const uint16_t*>(scratch + L.a), F, false,
-                              f.qt1, f.qt1_sc, "quant_a_rows", s)))
+  // expert linear 2, on A's row codes (MXFP8: from the W1 epilogue).
+  // Blockwise, one pass over A writes them and A's token codes for the W2
+  // weight gradient (into their own buffer, which the backward leaves alone)
+  if (!mx && (rc = quant_tokens(d, L, reinterpret_cast<const uint16_t*>(scratch + L.a), F, false,
+                                f.qta, f.qta_sc, "quant_a", scratch, s, TOK_PERM, nullptr, f.qt1,
+                                f.qt1_sc)))
     return rc;
   F8Args b{};
   b.K = F;
@@ -1263,8 +1267,10 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   const F8Scratch f = f8scratch(d, L, scratch);
   const bool mx = d.mode == MOE_MXFP8;
   const bool paired = pair_capable(d);
-  // MXFP8 and FP8: the forward already wrote x's token codes (fp8_x_tokens)
+  // MXFP8 and FP8: the forward already wrote x's token codes (fp8_x_tokens);
+  // FP8 also A's (beside A's row codes)
   const bool x_tokens = !fp8_fwd(d.mode);
+  const bool a_tokens = d.mode != MOE_FP8;
   const int D = d.D, F = d.F, N = d.T * d.K;
   const int64_t npad = int64_t(max_steps128(d)) * 128;
   const auto* dyg = static_cast<const uint16_t*>(dy);
@@ -1353,7 +1359,9 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
     if ((rc = quant_tokens(d, L, dyg, D, mx, f.qt3, f.qt3_sc, "quant_dyw_tokens", scratch, s,
                            TOK_GATHER_W, topk_w)))
       return rc;
-    if ((rc = quant_tokens(d, L, act, F, mx, f.qta, f.qta_sc, "quant_a_tokens", scratch, s))) return rc;
+    if (a_tokens &&
+        (rc = quant_tokens(d, L, act, F, mx, f.qta, f.qta_sc, "quant_a_tokens", scratch, s)))
+      return rc;
     rc = mx ? run_f8_pair<true, EPI_DSWIGLU>(d, L, a, F, w, ctr, "pair_w2", scratch, s)
             : run_f8_pair<false, EPI_DSWIGLU>(d, L, a, F, w, ctr, "pair_w2", scratch, s);
     if (rc) return rc;
@@ -1373,7 +1381,9 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   if ((rc = quant_tokens(d, L, dyg, D, mx, f.qt1, f.qt1_sc, "quant_dyw_tokens", scratch, s,
                          TOK_GATHER_W, topk_w)))
     return rc;
-  if ((rc = quant_tokens(d, L, act, F, mx, f.qta, f.qta_sc, "quant_a_tokens", scratch, s))) return rc;
+  if (a_tokens &&
+      (rc = quant_tokens(d, L, act, F, mx, f.qta, f.qta_sc, "quant_a_tokens", scratch, s)))
+    return rc;
   rc = mx ? run_f8_wgrad<true>(d, L, w, "gemm_w2_wgrad", scratch, s)
           : run_f8_wgrad<false>(d, L, w, "gemm_w2_wgrad", scratch, s);
   if (rc) return rc;
