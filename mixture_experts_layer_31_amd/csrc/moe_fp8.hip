@@ -801,8 +801,6 @@ using namespace gemm;
 //    backward 10.59 -> 9.84 ms), 30B fp8 W1 wgrad 0.81 -> 0.69 ms.
 using TileF8 = Tile<256, 256, 2, 4, 2>;
 template <bool MX> using F8GrTile = TileF8;
-static_assert(TileF8::BN % 128 == 0,
-              "the SwiGLU-backward epilogue quantises whole 128-column groups of dH");
 template <bool MX> using F8WgTile = TileF8;
 
 inline int max_steps128(const moe_desc& d) {
@@ -1037,13 +1035,13 @@ size_t fp8_wprep_bytes(const moe_desc& d) { return fp8_mode(d.mode) ? wlayout(d)
 // Regions of the FP8 operands in scratch (after the bf16 layout), as offsets
 // from its FP8 region: the row codes of one activation, and three (paired
 // backward: four) buffers of token codes:
-//   qt1  A's row codes in the forward (MXFP8 epilogue, or quant_rows), then
+//   qt1  A's row codes in the forward (from the pass over A), then
 //        dYw's row codes, dYw's token codes (one-GEMM-per-launch backward),
 //        dH's token codes;
 //   qt2  x's token codes: written by the forward in MXFP8 and FP8 (gathered
 //        from x), by the backward in fp8_bwd (from the dispatched rows);
-//   qta  A's token codes (written by the forward in FP8, beside A's row
-//        codes, else by the backward): their own buffer when the forward
+//   qta  A's token codes (written by the forward in MXFP8 and FP8, beside A's
+//        row codes, else by the backward): their own buffer when the forward
 //        fills qt2 (F columns), else qt2 itself, which the W2 weight gradient
 //        has read before x's token codes replace them;
 //   qt3  the paired backward's dYw token codes (the W2 dgrad still reads the
@@ -1161,10 +1159,10 @@ int fp8_view(const moe_desc& d, const Layout& L, char* scratch, int which, void*
 }
 
 // Expert linear 1 + SwiGLU on the quantised x rows: stores H into `h` and A
-// into `act` (either may be null, as in the bf16 path).  MXFP8: the epilogue
-// also writes A's row codes for the W2 GEMM, into the first token-code buffer
-// (free until the backward); the blockwise quotients cost the epilogue more
-// than a separate pass over A, so blockwise A is quantised by quant_rows.
+// into `act` (either may be null, as in the bf16 path).  A's codes come from a
+// pass over the stored A (fp8_fwd_gemms): the epilogue runs while the matrix
+// cores idle, so quantising there costs more than that pass (30B MXFP8: the
+// epilogue 36 us slower, against a pass that also writes A's token codes).
 static int fp8_w1_swiglu(const moe_desc& d, const Layout& L, const char* wprep, uint16_t* h,
                          uint16_t* act, const char* name, char* scratch, hipStream_t s,
                          bool x_quantised = false) {
@@ -1190,7 +1188,7 @@ static int fp8_w1_swiglu(const moe_desc& d, const Layout& L, const char* wprep, 
   a.sb_bstride = int64_t(D / 128) * 2 * F;
   a.sb_bytes = uint32_t(size_t(D / 128) * 2 * F * 4);
   a.F = F;
-  a.epi = EpiArgs{h, 0, act, nullptr, F, f.qt1, f.qt1_sc, N, mx ? QM_MX : QM_NONE};
+  a.epi = EpiArgs{h, 0, act, nullptr, F};
   return mx ? run_f8_grouped<true, EPI_SWIGLU>(d, L, a, 2 * F, name, scratch, s)
             : run_f8_grouped<false, EPI_SWIGLU>(d, L, a, 2 * F, name, scratch, s);
 }
@@ -1212,12 +1210,11 @@ int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* s
                          reinterpret_cast<uint16_t*>(scratch + L.a), "gemm_w1_swiglu", scratch, s,
                          x_quantised);
   if (rc) return rc;
-  // expert linear 2, on A's row codes (MXFP8: from the W1 epilogue).
-  // Blockwise, one pass over A writes them and A's token codes for the W2
-  // weight gradient (into their own buffer, which the backward leaves alone)
-  if (!mx && (rc = quant_tokens(d, L, reinterpret_cast<const uint16_t*>(scratch + L.a), F, false,
-                                f.qta, f.qta_sc, "quant_a", scratch, s, TOK_PERM, nullptr, f.qt1,
-                                f.qt1_sc)))
+  // expert linear 2, on A's row codes: one pass over A writes them and A's
+  // token codes for the W2 weight gradient (into their own buffer, which the
+  // backward leaves alone)
+  if ((rc = quant_tokens(d, L, reinterpret_cast<const uint16_t*>(scratch + L.a), F, mx, f.qta,
+                         f.qta_sc, "quant_a", scratch, s, TOK_PERM, nullptr, f.qt1, f.qt1_sc)))
     return rc;
   F8Args b{};
   b.K = F;
@@ -1245,9 +1242,7 @@ void fp8_row_codes(const moe_desc& d, const Layout& L, char* scratch, uint8_t** 
 }
 
 // dYw's row codes live in the first token-code buffer: the W2 dgrad reads them
-// before the W2 weight gradient quantises dYw over tokens into that buffer, and
-// the row-code buffer meanwhile receives dH's row codes from the W2 dgrad's
-// epilogue.
+// before the W2 weight gradient quantises dYw over tokens into that buffer.
 void fp8_dyw_codes(const moe_desc& d, const Layout& L, char* scratch, uint8_t** codes,
                    uint32_t** scales) {
   const F8Scratch f = f8scratch(d, L, scratch);
@@ -1270,7 +1265,7 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   // MXFP8 and FP8: the forward already wrote x's token codes (fp8_x_tokens);
   // FP8 also A's (beside A's row codes)
   const bool x_tokens = !fp8_fwd(d.mode);
-  const bool a_tokens = d.mode != MOE_FP8;
+  const bool a_tokens = !fp8_fwd(d.mode);
   const int D = d.D, F = d.F, N = d.T * d.K;
   const int64_t npad = int64_t(max_steps128(d)) * 128;
   const auto* dyg = static_cast<const uint16_t*>(dy);
@@ -1279,13 +1274,13 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   const auto* xp = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
   int rc;
   // W2 dgrad + SwiGLU-backward on dYw's row codes, which the combine-backward
-  // wrote into the first token-code buffer.  dH's row codes for the W1 dgrad: in
-  // MXFP8 the epilogue writes them as it stores dH; blockwise, the pass that
-  // quantises the stored dH over tokens writes them too (in the epilogue, the
-  // quotients and 128-lane maxima cost 0.16 ms at the 30B shape and 0.33 ms at
-  // 235B, more than a pass over dH; MXFP8's power-of-two scales cost less)
-  uint8_t* dh_rows = mx ? nullptr : f.qrow;
-  uint32_t* dh_rows_sc = mx ? nullptr : f.qrow_sc;
+  // wrote into the first token-code buffer.  dH's row codes for the W1 dgrad
+  // come from the pass that quantises the stored dH over tokens: quantising in
+  // the epilogue, which runs while the matrix cores idle, cost more (blockwise
+  // 0.16 ms at the 30B shape and 0.33 ms at 235B; MXFP8 62 us against the
+  // pass's 40 us more)
+  uint8_t* dh_rows = f.qrow;
+  uint32_t* dh_rows_sc = f.qrow_sc;
   F8Args a{};
   a.K = D;
   a.A = f.qt1;
@@ -1300,8 +1295,7 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   a.sb_bytes = uint32_t(size_t(D / 128) * F * 4);
   a.F = F;
   a.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.dh), 0, nullptr,
-                  reinterpret_cast<const uint16_t*>(scratch + L.h), F, f.qrow, f.qrow_sc, N,
-                  mx ? QM_MX : QM_NONE};
+                  reinterpret_cast<const uint16_t*>(scratch + L.h), F};
   // W2 wgrad over tokens: dYw's token codes (in the first buffer once the W2
   // dgrad is done with the row codes there; in the third when both run in one
   // launch) and A's.  dYw's are gathered from dy (the combine-backward stores
@@ -1387,11 +1381,9 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   rc = mx ? run_f8_wgrad<true>(d, L, w, "gemm_w2_wgrad", scratch, s)
           : run_f8_wgrad<false>(d, L, w, "gemm_w2_wgrad", scratch, s);
   if (rc) return rc;
-  // W1 wgrad and W1 dgrad.  Blockwise runs the wgrad first: its dH token pass
-  // also writes the row codes the dgrad reads, and the un-permute then reads
-  // dX_perm right after it is written (235B fp8_bwd backward -0.8%); MXFP8
-  // keeps the dgrad first, right after the W2 dgrad wrote those codes (0.5%
-  // faster there).
+  // W1 wgrad, then W1 dgrad: the wgrad's dH token pass also writes the row
+  // codes the dgrad reads, and the un-permute then reads dX_perm right after
+  // it is written.
   auto w1_wgrad = [&]() -> int {
     if ((rc = quant_tokens(d, L, dh, 2 * F, mx, f.qt1, f.qt1_sc, "quant_dh_tokens", scratch, s,
                            TOK_PERM, nullptr, dh_rows, dh_rows_sc)))
@@ -1406,10 +1398,6 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
     return mx ? run_f8_grouped<true, EPI_STORE>(d, L, b, D, "gemm_w1_dgrad", scratch, s)
               : run_f8_grouped<false, EPI_STORE>(d, L, b, D, "gemm_w1_dgrad", scratch, s);
   };
-  if (mx) {
-    if ((rc = w1_dgrad())) return rc;
-    return w1_wgrad();
-  }
   if ((rc = w1_wgrad())) return rc;
   return w1_dgrad();
 }

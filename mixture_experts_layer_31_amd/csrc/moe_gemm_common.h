@@ -497,12 +497,6 @@ struct EpiArgs {
   const uint16_t* hsave;  // DSWIGLU: H [rows, 2F]; may equal out (each tile reads its H band
                           // into LDS before it stores the same band's dH)
   int F;
-  // FP8 paths (qmode QM_MX or QM_BLOCK): the e4m3 row quantisation of the
-  // stored rows, dH along 2F (DSWIGLU) or A along F (SWIGLU): codes with the
-  // rows' element pitch, scale entries [columns/128][qn]
-  uint8_t* qcodes;
-  uint32_t* qsc;
-  int qn, qmode;
 };
 
 // Epilogues stage the output through LDS, one band of 32-row blocks (one per
@@ -584,35 +578,16 @@ __device__ __forceinline__ void band_load(const BandTile<ES>& t, int rows, int v
 }
 
 // Rows [0, n) of a 32-row slice of a band tile of CH 16-byte chunks per row to
-// the bf16 rows out + (row0 + r) * ld + col0, and, when q.qmode is set, their
-// e4m3 row codes at q.qcodes with the same element pitch, one scale entry per
-// 128 columns at q.qsc[(column / 128) * q.qn + row].  A row's chunks are
-// consecutive threads, so a 128-column group is 16 aligned lanes (an MX group
-// of 32 columns is 4), as quantise8 needs; slices narrower than 16 chunks never
-// quantise (the FP8 tiles are wide enough).
-template <int THREADS, int CH, class Q>
+// the bf16 rows out + (row0 + r) * ld + col0.  (Reading all of a thread's
+// chunks before storing any made the SwiGLU-backward epilogue slower.)
+template <int THREADS, int CH>
 __device__ __forceinline__ void slice_store(const BandTile<2>& t, int n, size_t row0, int col0,
-                                            uint16_t* out, int ld, const Q& q, int tid, int lane) {
+                                            uint16_t* out, int ld, int tid) {
   static_assert(CH <= 32, "one swizzle period per row");
   for (int k = tid; k < 32 * CH; k += THREADS) {
     const int r = k / CH, c = k - r * CH;
     const uint4 v = *reinterpret_cast<const uint4*>(t.base + r * CH * 16 + ((c ^ (r & (CH - 1))) << 4));
-    const size_t row = row0 + r;
-    const int col = col0 + 8 * c;
-    if (r < n) *reinterpret_cast<uint4*>(out + row * ld + col) = v;
-    if (CH % 16 == 0 && q.qmode != QM_NONE) {
-      const float f[8] = {__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                          __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u),
-                          __uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u),
-                          __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u)};
-      uint32_t entry;
-      const uint2 codes = q.qmode == QM_MX ? quantise8<QM_MX>(f, lane, entry)
-                                           : quantise8<QM_BLOCK>(f, lane, entry);
-      if (r < n) {
-        *reinterpret_cast<uint2*>(q.qcodes + row * ld + col) = codes;
-        if ((c & 15) == 0) q.qsc[size_t(col >> 7) * q.qn + row] = entry;
-      }
-    }
+    if (r < n) *reinterpret_cast<uint4*>(out + (row0 + r) * ld + col0 + 8 * c) = v;
   }
 }
 
@@ -700,11 +675,11 @@ __device__ __forceinline__ void dswiglu_epilogue(const EpiArgs& p,
     for (int w = 0; w < TL::WGM; ++w) {
       const int first = w * WM + i * 32, n = min(32, rows_valid - first);
       if (n <= 0) continue;
-      // dH, and in the FP8 backward its row codes for the W1 dgrad
+      // dH (its FP8 codes come from a pass over the stored rows)
       slice_store<TL::THREADS, CH>(BandTile<2>{buf + w * 32 * BN * 2, BN}, n, grow0 + first, f0,
-                                   p.out, 2 * F, p, tid, lane);
+                                   p.out, 2 * F, tid);
       slice_store<TL::THREADS, CH>(BandTile<2>{buf + TILE + w * 32 * BN * 2, BN}, n, grow0 + first,
-                                   F + f0, p.out, 2 * F, p, tid, lane);
+                                   F + f0, p.out, 2 * F, tid);
     }
   }
 }
@@ -807,9 +782,9 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
                                              tid, [&](int r) {
               return reinterpret_cast<char*>(p.out2 + (grow0 + first + r) * F + f0);
             });
-          else  // and in the FP8 forward A's row codes for the W2 GEMM
+          else
             slice_store<TL::THREADS, BN / 16>(BandTile<2>{smem + 2 * RB * BN + off, BN / 2}, n,
-                                              grow0 + first, f0, p.out2, F, p, tid, lane);
+                                              grow0 + first, f0, p.out2, F, tid);
         }
       }
     }
