@@ -277,17 +277,24 @@ int moe::forward(const moe_desc* d, const void* x, const int32_t* topk_idx, cons
   }
   const bool fwd_q = fp8_mode(d->mode) && d->mode != MOE_FP8_BWD;
   if (fwd_q) {
-    // the dispatch quantises x's rows for the W1 GEMM (and stores the bf16 rows
-    // only for the recompute, which quantises them again); x's token codes for
-    // the W1 weight gradient are gathered from x here, so the backward needs no
-    // dispatched rows
-    uint8_t* qc;
-    uint32_t* qs;
-    fp8_row_codes(*d, L, sc, &qc, &qs);
-    if ((rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s,
-                              d->mode == MOE_MXFP8 ? 1 : 2, qc, qs, L.recompute)))
-      return rc;
-    if ((rc = fp8_x_tokens(*d, L, x, sc, s))) return rc;
+    // Nothing stores the dispatched bf16 rows (except under recompute, whose
+    // backward quantises them again): x's token codes (the W1 weight gradient's
+    // operand) come from a pass gathered from x.  In MXFP8 that pass also writes
+    // x's row codes (the W1 GEMM's operand) and w_perm, and no dispatch runs
+    // (30B: 0.17 ms against 0.09 + 0.12); blockwise, whose row quotients cost
+    // that pass more than the dispatch (0.31 against 0.09 + 0.17 ms), the
+    // dispatch writes them.
+    const bool mx = d->mode == MOE_MXFP8;
+    const bool rows_in_pass = mx && !L.recompute;
+    if (!rows_in_pass) {
+      uint8_t* qc;
+      uint32_t* qs;
+      fp8_row_codes(*d, L, sc, &qc, &qs);
+      if ((rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s, mx ? 1 : 2, qc, qs,
+                                L.recompute)))
+        return rc;
+    }
+    if ((rc = fp8_x_tokens(*d, L, x, topk_w, rows_in_pass, sc, s))) return rc;
   } else if ((rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s))) {
     return rc;
   }

@@ -163,8 +163,10 @@ int fp8_prepare_weights(const moe_desc& d, const uint16_t* w1, const uint16_t* w
 int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,
                   hipStream_t s, bool x_quantised = false);
 // MXFP8 and FP8 forward: x's token codes for the W1 weight gradient, gathered
-// from x (the dispatch stores only x's row codes in these modes).
-int fp8_x_tokens(const moe_desc& d, const Layout& L, const void* x, char* scratch, hipStream_t s);
+// from x; with rows, also x's row codes for the W1 GEMM and w_perm (what the
+// dispatch writes in these modes, which then need no dispatch).
+int fp8_x_tokens(const moe_desc& d, const Layout& L, const void* x, const float* topk_w,
+                 bool rows, char* scratch, hipStream_t s);
 // The FP8 backward, after the combine-backward wrote dYw's row codes
 // (fp8_dyw_codes) and no bf16 dYw rows: dYw's token codes are gathered from dy
 // (bf16 [T, D]) and topk_w.

@@ -71,6 +71,7 @@ struct QArgs {
   uint8_t* rcodes;         // token quantiser with ROWQ: the rows' own codes [N, cols]
   uint32_t* rsc;           //   and their scale entries [cols / 128][rsc_ld]
   int64_t rsc_ld;
+  float* wperm;            // TOK_GATHER (optional): [N] routing weight of each permuted row
   int E;
   int ntr;                 // weights: r-steps per expert
   int total_rows;          // row quantiser: rows of the input
@@ -303,6 +304,8 @@ __global__ void __launch_bounds__(256) quant_tokens_kernel(QArgs p) {
         const int pr = p.src[r0 + r];
         row[it] = pr / p.K;
         if constexpr (SRC == TOK_GATHER_W) wt[it] = p.topk_w[pr];
+        if constexpr (SRC == TOK_GATHER)  // the dispatch's w_perm, when it does not run
+          if (p.wperm != nullptr && cg == 0 && l16 == 0) p.wperm[r0 + r] = p.topk_w[pr];
       }
     }
   }
@@ -849,13 +852,14 @@ int quant_rows(const moe_desc& d, const uint16_t* in, int C, bool mx, uint8_t* o
 // [C, Npad] (row stride npad) with scale entries [step][C].  `in` is the
 // permuted rows [N, C] (TOK_PERM) or the per-token rows [T, C] the permuted
 // rows are gathered from (TOK_GATHER, TOK_GATHER_W with the weights topk_w).
-// With rcodes (permuted rows only) the same pass also writes the rows' own
-// quantisation along C, as quant_rows does: codes [N, C] into rcodes, scale
-// entries [C/128][N] into rsc.
+// With rcodes the same pass also writes the rows' own quantisation along C,
+// as quant_rows does: codes [N, C] into rcodes, scale entries [C/128][N] into
+// rsc (permuted rows, or gathered rows without weights).  With wperm
+// (TOK_GATHER) it writes each permuted row's routing weight.
 int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, bool mx,
                  uint8_t* out, uint32_t* sc, const char* name, const char* scratch, hipStream_t s,
                  int src = TOK_PERM, const float* topk_w = nullptr, uint8_t* rcodes = nullptr,
-                 uint32_t* rsc = nullptr) {
+                 uint32_t* rsc = nullptr, float* wperm = nullptr) {
   QArgs a{};
   a.in = in;
   a.cols = C;
@@ -872,8 +876,10 @@ int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, 
   a.rcodes = rcodes;
   a.rsc = rsc;
   a.rsc_ld = int64_t(d.T) * d.K;
+  a.wperm = wperm;
   if (src == TOK_GATHER_W && topk_w == nullptr) return MOE_EINVAL;
-  if (rcodes != nullptr && (src != TOK_PERM || rsc == nullptr)) return MOE_EINVAL;
+  if (rcodes != nullptr && (src == TOK_GATHER_W || rsc == nullptr)) return MOE_EINVAL;
+  if (wperm != nullptr && (src != TOK_GATHER || topk_w == nullptr)) return MOE_EINVAL;
   // column tiles per workgroup: the gathering forms pipeline the next tile's
   // row loads behind the current tile's quantisation (at the 30B shape x
   // 0.19 -> 0.17 ms and dYw 0.21 -> 0.19 ms, at 235B dYw 0.43 -> 0.38 ms);
@@ -887,12 +893,18 @@ int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, 
   (mx ? quant_tokens_kernel<true, S, W><<<unsigned(blocks), 256, 0, s>>>(a) \
       : quant_tokens_kernel<false, S, W><<<unsigned(blocks), 256, 0, s>>>(a))
 #define MOE_QTW(S) (nct == 4 ? MOE_QT(S, 4) : nct == 2 ? MOE_QT(S, 2) : MOE_QT(S, 1))
-  if (src == TOK_GATHER) MOE_QTW(TOK_GATHER);
+#define MOE_QTR(W) \
+  (mx ? quant_tokens_kernel<true, TOK_GATHER, W, true><<<unsigned(blocks), 256, 0, s>>>(a) \
+      : quant_tokens_kernel<false, TOK_GATHER, W, true><<<unsigned(blocks), 256, 0, s>>>(a))
+  if (src == TOK_GATHER && rcodes != nullptr)
+    (nct == 4 ? MOE_QTR(4) : nct == 2 ? MOE_QTR(2) : MOE_QTR(1));
+  else if (src == TOK_GATHER) MOE_QTW(TOK_GATHER);
   else if (src == TOK_GATHER_W) MOE_QTW(TOK_GATHER_W);
   else if (rcodes != nullptr)
     (mx ? quant_tokens_kernel<true, TOK_PERM, 1, true><<<unsigned(blocks), 256, 0, s>>>(a)
         : quant_tokens_kernel<false, TOK_PERM, 1, true><<<unsigned(blocks), 256, 0, s>>>(a));
   else MOE_QT(TOK_PERM, 1);
+#undef MOE_QTR
 #undef MOE_QTW
 #undef MOE_QT
   prof_end(s);
@@ -1250,10 +1262,13 @@ void fp8_dyw_codes(const moe_desc& d, const Layout& L, char* scratch, uint8_t** 
   *scales = f.qt1_sc;
 }
 
-int fp8_x_tokens(const moe_desc& d, const Layout& L, const void* x, char* scratch, hipStream_t s) {
+int fp8_x_tokens(const moe_desc& d, const Layout& L, const void* x, const float* topk_w,
+                 bool rows, char* scratch, hipStream_t s) {
   const F8Scratch f = f8scratch(d, L, scratch);
   return quant_tokens(d, L, static_cast<const uint16_t*>(x), d.D, d.mode == MOE_MXFP8, f.qt2,
-                      f.qt2_sc, "quant_x_tokens", scratch, s, TOK_GATHER);
+                      f.qt2_sc, rows ? "quant_x" : "quant_x_tokens", scratch, s, TOK_GATHER, topk_w,
+                      rows ? f.qrow : nullptr, rows ? f.qrow_sc : nullptr,
+                      rows ? reinterpret_cast<float*>(scratch + L.wperm) : nullptr);
 }
 
 int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const void* dy,

@@ -128,7 +128,13 @@ def test_fp8_quantisers_and_gemms(name):
     t_of, k_of = src // cfg.K, src % cfg.K
     xp = inp["x"][t_of]
     dYw = mi.bf16_round((inp["topk_w"][t_of, k_of][:, None] * inp["dy"][t_of]).astype(np.float32))
-    if fwd_q:  # x_perm's rows were quantised by the dispatch: H = quantised x times quantised W1
+    if fwd_q:
+        # x's row codes (written by the pass gathered from x, bit for bit the oracle's codec of
+        # the dispatched rows) and w_perm, which that pass writes in place of the dispatch
+        _check_rows(L, xp, mx)
+        wp = L.view(moe.MOE_VIEW_WPERM, 0, torch.float32)[:len(src)]
+        np.testing.assert_array_equal(wp, inp["topk_w"][t_of, k_of])
+    if fwd_q:  # H = quantised x times quantised W1
         qc, qs = f8.quant_rows(xp, 32 if mx else 128, mx)
         xdq = f8.dequant_rows(qc, qs, 32 if mx else 128, mx)
         Hg = L.view(moe.MOE_VIEW_H, 2 * F)[:len(src)]
