@@ -345,13 +345,16 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
       rc = launch_recompute_h(*d, L, g1, sc, s);
     if (rc) return rc;
   }
-  if (fp8_mode(d->mode)) {  // the combine-backward quantises dYw's rows for the W2 dgrad,
-                            // without storing them in bf16
+  if (d->mode == MOE_MXFP8) {  // dtopk_w only: the pass gathered from dy writes dYw's codes
+    if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s, 0, nullptr, nullptr,
+                                 false)))
+      return rc;
+  } else if (fp8_mode(d->mode)) {  // the combine-backward quantises dYw's rows for the W2
+                                   // dgrad, without storing them in bf16
     uint8_t* qc;
     uint32_t* qs;
     fp8_dyw_codes(*d, L, sc, &qc, &qs);
-    if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s,
-                                 d->mode == MOE_MXFP8 ? 1 : 2, qc, qs, false)))
+    if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s, 2, qc, qs, false)))
       return rc;
   } else if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s))) {
     return rc;

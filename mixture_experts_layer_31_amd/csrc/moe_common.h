@@ -119,7 +119,7 @@ int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
 // Combine-backward: dYw_perm rows (w * dy, bf16) and dtopk_w = <dy, o>.  With
 // qmode 1 (MX) or 2 (blockwise) it also writes the rows' e4m3 quantisation
 // along D (codes [N, D], scale entries [D/128][N]); bf16 rows only.
-// store_rows = false (with qmode) skips the bf16 dYw rows.
+// store_rows = false skips the bf16 dYw rows (with qmode 0: dtopk_w only).
 int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool in_f32,
                        const float* topk_w, float* dtopk_w, char* scratch, hipStream_t s,
                        int qmode = 0, uint8_t* qcodes = nullptr, uint32_t* qsc = nullptr,

@@ -878,7 +878,7 @@ int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, 
   a.rsc_ld = int64_t(d.T) * d.K;
   a.wperm = wperm;
   if (src == TOK_GATHER_W && topk_w == nullptr) return MOE_EINVAL;
-  if (rcodes != nullptr && (src == TOK_GATHER_W || rsc == nullptr)) return MOE_EINVAL;
+  if (rcodes != nullptr && rsc == nullptr) return MOE_EINVAL;
   if (wperm != nullptr && (src != TOK_GATHER || topk_w == nullptr)) return MOE_EINVAL;
   // column tiles per workgroup: the gathering forms pipeline the next tile's
   // row loads behind the current tile's quantisation (at the 30B shape x
@@ -893,11 +893,14 @@ int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, 
   (mx ? quant_tokens_kernel<true, S, W><<<unsigned(blocks), 256, 0, s>>>(a) \
       : quant_tokens_kernel<false, S, W><<<unsigned(blocks), 256, 0, s>>>(a))
 #define MOE_QTW(S) (nct == 4 ? MOE_QT(S, 4) : nct == 2 ? MOE_QT(S, 2) : MOE_QT(S, 1))
-#define MOE_QTR(W) \
-  (mx ? quant_tokens_kernel<true, TOK_GATHER, W, true><<<unsigned(blocks), 256, 0, s>>>(a) \
-      : quant_tokens_kernel<false, TOK_GATHER, W, true><<<unsigned(blocks), 256, 0, s>>>(a))
+#define MOE_QTR(S, W) \
+  (mx ? quant_tokens_kernel<true, S, W, true><<<unsigned(blocks), 256, 0, s>>>(a) \
+      : quant_tokens_kernel<false, S, W, true><<<unsigned(blocks), 256, 0, s>>>(a))
   if (src == TOK_GATHER && rcodes != nullptr)
-    (nct == 4 ? MOE_QTR(4) : nct == 2 ? MOE_QTR(2) : MOE_QTR(1));
+    (nct == 4 ? MOE_QTR(TOK_GATHER, 4) : nct == 2 ? MOE_QTR(TOK_GATHER, 2) : MOE_QTR(TOK_GATHER, 1));
+  else if (src == TOK_GATHER_W && rcodes != nullptr)
+    (nct == 4 ? MOE_QTR(TOK_GATHER_W, 4)
+              : nct == 2 ? MOE_QTR(TOK_GATHER_W, 2) : MOE_QTR(TOK_GATHER_W, 1));
   else if (src == TOK_GATHER) MOE_QTW(TOK_GATHER);
   else if (src == TOK_GATHER_W) MOE_QTW(TOK_GATHER_W);
   else if (rcodes != nullptr)
@@ -1056,8 +1059,9 @@ size_t fp8_wprep_bytes(const moe_desc& d) { return fp8_mode(d.mode) ? wlayout(d)
 //        row codes, else by the backward): their own buffer when the forward
 //        fills qt2 (F columns), else qt2 itself, which the W2 weight gradient
 //        has read before x's token codes replace them;
-//   qt3  the paired backward's dYw token codes (the W2 dgrad still reads the
-//        row codes in qt1 in the same launch).
+//   qt3  dYw's token codes when the W2 dgrad still reads dYw's row codes in
+//        qt1: in the paired backward (same launch), and in MXFP8, where one
+//        pass writes both before the W2 dgrad.
 struct F8Offsets {
   size_t qrow, qrow_sc, qt1, qt1_sc, qt2, qt2_sc, qta, qta_sc, qt3, qt3_sc, total;
   size_t qrow_sc_bytes, qt_sc_bytes, qta_sc_bytes;
@@ -1088,7 +1092,7 @@ static F8Offsets f8offsets(const moe_desc& d) {
     f.qta = f.qt2;
     f.qta_sc = f.qt2_sc;
   }
-  f.has_qt3 = pair_capable(d);
+  f.has_qt3 = pair_capable(d) || d.mode == MOE_MXFP8;
   if (f.has_qt3) {
     f.qt3 = take(C * npad);
     f.qt3_sc = take(f.qt_sc_bytes);
@@ -1288,8 +1292,9 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   const auto* dh = reinterpret_cast<const uint16_t*>(scratch + L.dh);
   const auto* xp = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
   int rc;
-  // W2 dgrad + SwiGLU-backward on dYw's row codes, which the combine-backward
-  // wrote into the first token-code buffer.  dH's row codes for the W1 dgrad
+  // W2 dgrad + SwiGLU-backward on dYw's row codes, in the first token-code
+  // buffer (written by the combine-backward, or in MXFP8 by the pass below
+  // that also writes dYw's token codes).  dH's row codes for the W1 dgrad
   // come from the pass that quantises the stored dH over tokens: quantising in
   // the epilogue, which runs while the matrix cores idle, cost more (blockwise
   // 0.16 ms at the 30B shape and 0.33 ms at 235B; MXFP8 62 us against the
@@ -1315,8 +1320,8 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   // dgrad is done with the row codes there; in the third when both run in one
   // launch) and A's.  dYw's are gathered from dy (the combine-backward stores
   // no bf16 dYw rows in the FP8 modes).
-  uint8_t* dyt = paired ? f.qt3 : f.qt1;
-  uint32_t* dyt_sc = paired ? f.qt3_sc : f.qt1_sc;
+  uint8_t* dyt = paired || mx ? f.qt3 : f.qt1;
+  uint32_t* dyt_sc = paired || mx ? f.qt3_sc : f.qt1_sc;
   F8Args w{};
   w.M = D;
   w.N = F;
@@ -1362,11 +1367,18 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   b.F = F;
   b.epi = EpiArgs{reinterpret_cast<uint16_t*>(scratch + L.dxperm), D, nullptr, nullptr, F};
 
+  // MXFP8: one pass gathered from dy and the routing weights writes dYw's row
+  // codes (the W2 dgrad's operand, in the first buffer) and its token codes
+  // (the W2 weight gradient's, in the third); the combine-backward computed
+  // only dtopk_w
+  if (mx && (rc = quant_tokens(d, L, dyg, D, true, f.qt3, f.qt3_sc, "quant_dyw", scratch, s,
+                               TOK_GATHER_W, topk_w, f.qt1, f.qt1_sc)))
+    return rc;
   if (paired) {  // each dgrad beside its weight gradient, one launch per pair
     int* ctr = reinterpret_cast<int*>(scratch + L.pair);
     if ((rc = launch_zero(ctr, 2 * kPairQueues * sizeof(int), s))) return rc;
-    if ((rc = quant_tokens(d, L, dyg, D, mx, f.qt3, f.qt3_sc, "quant_dyw_tokens", scratch, s,
-                           TOK_GATHER_W, topk_w)))
+    if (!mx && (rc = quant_tokens(d, L, dyg, D, mx, f.qt3, f.qt3_sc, "quant_dyw_tokens", scratch, s,
+                                  TOK_GATHER_W, topk_w)))
       return rc;
     if (a_tokens &&
         (rc = quant_tokens(d, L, act, F, mx, f.qta, f.qta_sc, "quant_a_tokens", scratch, s)))
@@ -1387,8 +1399,8 @@ int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const v
   rc = mx ? run_f8_grouped<true, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s)
           : run_f8_grouped<false, EPI_DSWIGLU>(d, L, a, F, "gemm_w2_dgrad_dswiglu", scratch, s);
   if (rc) return rc;
-  if ((rc = quant_tokens(d, L, dyg, D, mx, f.qt1, f.qt1_sc, "quant_dyw_tokens", scratch, s,
-                         TOK_GATHER_W, topk_w)))
+  if (!mx && (rc = quant_tokens(d, L, dyg, D, mx, f.qt1, f.qt1_sc, "quant_dyw_tokens", scratch, s,
+                                TOK_GATHER_W, topk_w)))
     return rc;
   if (a_tokens &&
       (rc = quant_tokens(d, L, act, F, mx, f.qta, f.qta_sc, "quant_a_tokens", scratch, s)))

@@ -330,8 +330,9 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_kernel(
 // same bf16-rounded values it stores: QM_BLOCK, an fp32 scale per 128 columns
 // (a group is 16 consecutive lanes' chunks); QM_MX, an e8m0 scale per 32 (4
 // lanes).  Codes are [N, D] bytes, scale entries [D/128][N], as the standalone
-// row quantiser writes them.  With QM and dst null the bf16 rows are not stored
-// (the FP8 backward's token quantiser gathers w * dy itself).  D / 8 must be a multiple of 16 so a group never
+// row quantiser writes them.  With dst null the bf16 rows are not stored (the
+// FP8 backward's token quantiser gathers w * dy itself; in MXFP8 it also writes
+// the row codes, and this kernel computes only dtopk_w).  D / 8 must be a multiple of 16 so a group never
 // straddles active and idle lanes.
 constexpr int kSplitMaxK = 64;  // K up to this many slots may split a row over waves
 
@@ -379,7 +380,7 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_dy_kernel(
             dot = __builtin_fmaf(v[j][i], o[i], dot);
             sc[i] = w * v[j][i];
           }
-          if (QM == QM_NONE || dst != nullptr) store8(dst, (size_t(q) * D) / 8 + c, sc);
+          if (dst != nullptr) store8(dst, (size_t(q) * D) / 8 + c, sc);
         }
         if constexpr (QM != QM_NONE) {
           // quantise the stored (bf16-rounded) values; idle lanes join the reductions with 0
@@ -571,7 +572,6 @@ static int dispatch_dy_cpl(const moe_desc& d, const IO* dy, const int32_t* pos,
 int launch_dispatch_dy(const moe_desc& d, const Layout& L, const void* dy, bool in_f32,
                        const float* topk_w, float* dtopk_w, char* scratch, hipStream_t s,
                        int qmode, uint8_t* qcodes, uint32_t* qsc, bool store_rows) {
-  if (!store_rows && qmode == 0) return MOE_EINVAL;
   const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
   prof_begin("dispatch_dy", s);
   const int rc = with_types(d, in_f32, [&](auto io, auto act) {
