@@ -58,18 +58,20 @@ def row_bytes(cfg, b=2, recompute=False) -> dict:
     """Algorithmic HBM bytes per launch of the row movers (bf16 rows).  In the FP8
     forward modes (MXFP8, blockwise FP8) the dispatch writes the e4m3 row codes
     of x_perm and one 4-byte scale entry per 128 columns instead of the bf16
-    rows (which it writes too under activation recompute); in every FP8 mode
-    the combine-backward writes those of dYw instead of its bf16 rows."""
+    rows (which it writes too under activation recompute; in MXFP8 without
+    recompute no dispatch runs).  The combine-backward writes dYw's codes in
+    blockwise FP8 and fp8_bwd instead of its bf16 rows, and in MXFP8 neither
+    (it computes only dtopk_w)."""
     T, N, D = cfg.T, cfg.N, cfg.D
     codes = N * D + N * (D // 128) * 4
     fwd_q = cfg.mode in (4, 5)   # MXFP8, blockwise FP8 in both passes
-    bwd_q = cfg.mode in (3, 4, 5)
+    dyw_out = {4: 0, 3: codes, 5: codes}.get(cfg.mode, N * D * b)
     xrows = N * D * b if (not fwd_q or recompute) else 0
     return {"dispatch": T * D * b + xrows + 2 * N * 4 + N * 4 + (codes if fwd_q else 0),
             "combine": N * D * b + T * D * b + N * 8,
-            # dy once, each pair's expert-output row read and (bf16 modes) its w*dy
-            # row written, pos and topk_w read, dtopk_w written
-            "dispatch_dy": T * D * b + N * D * b + (codes if bwd_q else N * D * b) + 3 * N * 4,
+            # dy once, each pair's expert-output row read and its w*dy row (or its
+            # codes) written, pos and topk_w read, dtopk_w written
+            "dispatch_dy": T * D * b + N * D * b + dyw_out + 3 * N * 4,
             "unpermute": N * D * b + T * D * b + N * 4}
 
 

@@ -44,8 +44,10 @@ def test_row_mover_bytes_follow_the_definitions():
     mx = mi.CONFIGS["30b_mxfp8"]
     assert b.row_bytes(mx)["dispatch"] - rb["dispatch"] == codes - 2 * N * D
     assert b.row_bytes(mx, recompute=True)["dispatch"] - rb["dispatch"] == codes
-    # every FP8 mode's combine-backward writes dYw's codes instead of its bf16 rows
-    assert b.row_bytes(mx)["dispatch_dy"] - rb["dispatch_dy"] == codes - 2 * N * D
+    # the blockwise combine-backward writes dYw's codes instead of its bf16 rows; the MXFP8
+    # one neither (it computes only dtopk_w)
+    assert b.row_bytes(mi.CONFIGS["30b_fp8"])["dispatch_dy"] - rb["dispatch_dy"] == codes - 2 * N * D
+    assert b.row_bytes(mx)["dispatch_dy"] - rb["dispatch_dy"] == -2 * N * D
     fb = mi.CONFIGS["235b_fp8bwd"]
     fcodes = fb.N * fb.D + fb.N * (fb.D // 128) * 4
     assert b.row_bytes(fb)["dispatch"] == b.row_bytes(mi.CONFIGS["235b"])["dispatch"]
