@@ -117,10 +117,12 @@ enum moe_status {
  * other's main loops (the single-GPU form of the overlapping backward the
  * pages add to the fused kernel: Prime Mega MoE news item, "How does the fused
  * kernel work?").  Needs D % 256 == 0, F % 256 == 0 and E <= 256, in MOE_BF16
- * and the FP8 modes.  It is the default for MOE_BF16, where it measured 0.7-0.9%
- * faster on MI355X at the Qwen3 shapes; MOE_FLAG_OVERLAP_BWD selects it in the
- * FP8 modes too (there it measured 2-3% slower), MOE_FLAG_SERIAL_BWD selects
- * one kernel per GEMM in every mode, and setting both is MOE_EINVAL.  Results
+ * and the FP8 modes.  It is the default for MOE_BF16 when T*K <= 4096*E (at
+ * most 4096 routed pairs per expert on average), where it measured 0.7-0.9%
+ * faster on MI355X at the Qwen3 shapes (with 8192 per expert it measured up to
+ * 8% slower); MOE_FLAG_OVERLAP_BWD selects it in every mode (in the FP8 modes
+ * it measured 4-10% slower), MOE_FLAG_SERIAL_BWD selects one kernel per GEMM
+ * in every mode, and setting both is MOE_EINVAL.  Results
  * are bit-identical either way (the same tile code in the same accumulation
  * order). */
 #define MOE_FLAG_OVERLAP_BWD 0x8u

@@ -325,9 +325,18 @@ int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, con
 // shapes), on request in the FP8 modes (measured 2-3% slower there: their
 // quantisers already sit between the GEMMs, and the paired launch needs the
 // larger of the two tiles' LDS).
+// The paired backward is the bf16 default only where experts are small on
+// average (at most kPairDefaultTokens routed pairs each): at the Qwen3 shapes
+// (1024 per expert) it gained 0.7-0.9%, but with 8192 per expert (the 16-expert
+// EP-share workloads) it lost 8% at D = 4096 (an expert's dgrad and weight-
+// gradient operands, tens of MB each, then thrash one XCD's L2 together) and
+// 0.2% at D = 2048.
+constexpr long long kPairDefaultTokens = 4096;
+
 bool pair_capable(const moe_desc& d) {
   if (d.flags & MOE_FLAG_SERIAL_BWD) return false;
-  const bool want = (d.flags & MOE_FLAG_OVERLAP_BWD) || d.mode == MOE_BF16;
+  const bool small_experts = (long long)d.T * d.K <= kPairDefaultTokens * d.E;
+  const bool want = (d.flags & MOE_FLAG_OVERLAP_BWD) || (d.mode == MOE_BF16 && small_experts);
   return want && (d.mode == MOE_BF16 || fp8_mode(d.mode)) && d.D % 256 == 0 &&
          d.F % 256 == 0 && d.E <= kPairMaxE;
 }

@@ -110,6 +110,9 @@ CONFIGS = {
     # (D % 256 == 0, F % 256 == 0)
     "zipf_wide_bf16": LayerConfig("zipf_wide_bf16", T=1500, D=512, F=256, E=16, K=4,
                                   routing="zipf", seed=2009),
+    # two experts of about 4200 rows each (above the mean expert size up to
+    # which bf16 pairs its backward GEMMs by default)
+    "deep_bf16": LayerConfig("deep_bf16", T=8400, D=256, F=256, E=2, K=1, seed=2010),
     # token rows of 512 and 1024 16-byte chunks (the row movers give each thread
     # several chunks of a row), top-8, bf16 I/O and fp32 I/O
     "rows4k_bf16": LayerConfig("rows4k_bf16", T=96, D=4096, F=128, E=12, K=8, seed=2007),

@@ -22,7 +22,7 @@ from tests.oracle_parity import full_size_vs_oracle, layer_vs_oracle
 
 pytestmark = pytest.mark.gpu
 
-CASES = ["mid_bf16", "wide_bf16", "zipf_wide_bf16"]
+CASES = ["mid_bf16", "wide_bf16", "zipf_wide_bf16", "deep_bf16"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -145,11 +145,12 @@ def test_paired_fp8_backward_is_bitwise_the_default_and_the_recipe(name):
         assert e <= 2e-2, (k, e)
 
 
-@pytest.mark.parametrize("name,paired", [("mid_bf16", True), ("fp8bwd_small", False),
-                                         ("mxfp8_small", False)])
+@pytest.mark.parametrize("name,paired", [("mid_bf16", True), ("deep_bf16", False),
+                                         ("fp8bwd_small", False), ("mxfp8_small", False)])
 def test_default_backward_schedule(name, paired):
-    """bf16 pairs its backward GEMMs by default; the FP8 modes launch one kernel
-    per GEMM unless asked (the kernels the opt-in profiler saw)."""
+    """bf16 pairs its backward GEMMs by default while experts average at most
+    4096 routed rows; larger experts and the FP8 modes launch one kernel per
+    GEMM unless asked (the kernels the opt-in profiler saw)."""
     cfg = mi.CONFIGS[name]
     L = Layer(cfg, mi.make_inputs(cfg))
     L.prepare()

@@ -19,7 +19,7 @@ from tests.oracle_parity import full_size_vs_oracle, layer_vs_oracle, routing_bi
 pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny", "tiny_bf16gemm", "small_bf16", "dead_bf16", "mid_bf16", "wide_bf16", "mid_f32io",
-         "zipf_bf16", "rows4k_bf16", "rows8k_f32io"]
+         "zipf_bf16", "rows4k_bf16", "rows8k_f32io", "deep_bf16"]
 
 
 @pytest.fixture(scope="module", autouse=True)
