@@ -198,7 +198,10 @@ int moe_routing_view(const moe_desc* d, const void* scratch, size_t scratch_byte
  * in expert order, i.e. pair src[r]):
  *   MOE_VIEW_XPERM  [T*K, D]   dispatched tokens (bf16; fp32 in MOE_FP32).  Not
  *                              stored in MOE_MXFP8 and MOE_FP8 without
- *                              MOE_FLAG_RECOMPUTE (only their FP8 codes are)
+ *                              MOE_FLAG_RECOMPUTE (only their FP8 codes are).  In
+ *                              MOE_BF16 at D % 64 == 0 and 2F % 256 == 0 no
+ *                              dispatch kernel runs: the linear-1 GEMM gathers
+ *                              the token rows and writes these (and WPERM)
  *   MOE_VIEW_H      [T*K, 2F]  linear-1 output: gate | up
  *   MOE_VIEW_A      [T*K, F]   SwiGLU output
  *   MOE_VIEW_O      [T*K, D]   linear-2 output (unweighted)

@@ -295,7 +295,7 @@ int moe::forward(const moe_desc* d, const void* x, const int32_t* topk_idx, cons
         return rc;
     }
     if ((rc = fp8_x_tokens(*d, L, x, topk_w, rows_in_pass, sc, s))) return rc;
-  } else if ((rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s))) {
+  } else if (!w1_gathers(*d) && (rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s))) {
     return rc;
   }
   if (d->mode == MOE_FP32)
@@ -304,7 +304,8 @@ int moe::forward(const moe_desc* d, const void* x, const int32_t* topk_idx, cons
   else if (fp8_mode(d->mode) && d->mode != MOE_FP8_BWD)
     rc = fp8_fwd_gemms(*d, L, static_cast<const char*>(wprep), sc, s, true);
   else
-    rc = launch_fwd_gemms(*d, L, g1, g2, sc, s);
+    rc = launch_fwd_gemms(*d, L, g1, g2, sc, s,
+                          w1_gathers(*d) ? static_cast<const uint16_t*>(x) : nullptr, topk_w);
   if (rc) return rc;
   return launch_combine(*d, L, topk_w, y, io_f32, sc, s);
 }

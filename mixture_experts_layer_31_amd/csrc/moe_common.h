@@ -147,8 +147,14 @@ bool queue_capable(const moe_desc& d);
 int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_f32,
                      const float* topk_w, const uint16_t* w1, const uint16_t* w2, char* scratch,
                      hipStream_t s);
+// bf16 at shapes the wide-row W1 loop takes: no dispatch kernel; the W1 GEMM
+// gathers x's rows itself and its tiles also write the dispatched rows and
+// weights (x_perm, w_perm) for the backward, from the rows they staged.
+bool w1_gathers(const moe_desc& d);
+// x and topk_w: the token rows and routing weights when w1_gathers(d), else null.
 int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
-                     char* scratch, hipStream_t s);
+                     char* scratch, hipStream_t s, const uint16_t* x = nullptr,
+                     const float* topk_w = nullptr);
 // MOE_FLAG_RECOMPUTE: the forward's W1 GEMM again, storing only H (into L.h,
 // the dH region), with the same kernels and operands as the forward.
 int launch_recompute_h(const moe_desc& d, const Layout& L, const uint16_t* w1, char* scratch,

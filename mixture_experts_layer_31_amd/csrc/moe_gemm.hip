@@ -274,11 +274,22 @@ int run_pair(const moe_desc& d, const Layout& L, GroupedArgs a, int N, WgradArgs
 // `h` and A into `act` (either may be null: the recompute forward skips H, the
 // backward's recompute skips A).
 int run_w1_swiglu(const moe_desc& d, const Layout& L, const uint16_t* w1, uint16_t* h,
-                  uint16_t* act, const char* name, char* scratch, hipStream_t s) {
+                  uint16_t* act, const char* name, char* scratch, hipStream_t s,
+                  const uint16_t* x = nullptr, const float* topk_w = nullptr) {
   GroupedArgs a{};
   a.K = d.D;
   a.F = d.F;
   a.A = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
+  if (x != nullptr) {
+    if (!w1_gathers(d) || topk_w == nullptr) return MOE_EINVAL;
+    a.A = x;
+    a.gather = reinterpret_cast<const int32_t*>(scratch + L.src);
+    a.gK = d.K;
+    a.gT = d.T;
+    a.xcopy = reinterpret_cast<uint16_t*>(scratch + L.xperm);
+    a.wcopy = reinterpret_cast<float*>(scratch + L.wperm);
+    a.gw = topk_w;
+  }
   a.lda = d.D;
   a.B = w1;
   a.bstride = int64_t(2) * d.F * d.D;
@@ -297,11 +308,17 @@ int launch_recompute_h(const moe_desc& d, const Layout& L, const uint16_t* w1, c
                        "gemm_w1_recompute", scratch, s);
 }
 
+bool w1_gathers(const moe_desc& d) {
+  // the condition under which run_grouped_any takes the wide-row loop for W1
+  return d.mode == MOE_BF16 && (2 * d.F) % 256 == 0 && d.D % 64 == 0;
+}
+
 int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
-                     char* scratch, hipStream_t s) {
+                     char* scratch, hipStream_t s, const uint16_t* x, const float* topk_w) {
   const int D = d.D, F = d.F;
   int rc = run_w1_swiglu(d, L, w1, L.recompute ? nullptr : reinterpret_cast<uint16_t*>(scratch + L.h),
-                         reinterpret_cast<uint16_t*>(scratch + L.a), "gemm_w1_swiglu", scratch, s);
+                         reinterpret_cast<uint16_t*>(scratch + L.a), "gemm_w1_swiglu", scratch, s, x,
+                         topk_w);
   if (rc) return rc;
   {  // expert linear 2: O.  W2[e] is [D, F].
     GroupedArgs a{};

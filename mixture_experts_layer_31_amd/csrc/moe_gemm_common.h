@@ -397,10 +397,16 @@ constexpr int kWideIssueSub = 2;
 // then each run their MFMAs while the next sub-step's fragments are read, and
 // the first kWideIssueSub of them also issue a share of the next step's loads
 // into the free stage.  A and B are both k-contiguous.
-template <int BM, int BN, int WGM, int WGN, int ACT, class SA, class SB>
+struct NoStepHook {
+  __device__ void operator()(int, const char*) const {}
+};
+
+// hook(kt, a) runs once per k-step after the barrier, with a pointing at the
+// stage's A rows (BM rows of 128 bytes, chunks swizzled as swz_row<128>).
+template <int BM, int BN, int WGM, int WGN, int ACT, class SA, class SB, class Hook = NoStepHook>
 __device__ __forceinline__ void mainloop_w(char* smem, const SA& sa, const SB& sb, int ktiles,
                                            f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int wave,
-                                           int lane) {
+                                           int lane, Hook hook = {}) {
   constexpr int WM = BM / WGM, WN = BN / WGN, WMT = WM / 32, WNT = WN / 32;
   constexpr int A_BYTES = BM * 128, STAGE = (BM + BN) * 128;
   constexpr int NI = SA::NI + SB::NI;
@@ -436,6 +442,7 @@ __device__ __forceinline__ void mainloop_w(char* smem, const SA& sa, const SB& s
     const char* ta = smem + (kt & 1) * STAGE;
     Frags f[2];
     load(ta, 0, f[0]);
+    hook(kt, ta);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (next && kk < kWideIssueSub)

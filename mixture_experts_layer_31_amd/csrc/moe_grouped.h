@@ -22,6 +22,13 @@ struct GroupedArgs {
   uint16_t* out2;             // SWIGLU: A [rows, F] or null
   const uint16_t* hsave;      // DSWIGLU: H [rows, 2F] (may equal out: read before written, per tile)
   int nmajor;                 // tile order within an expert: n-tiles outer (1) or m-tiles outer (0)
+  const int32_t* gather;      // null: A holds the permuted rows; else A is [T, lda] token rows and
+  int gK;                     //   permuted row q reads token row gather[q] / gK (wide-row loop only)
+  int gT;                     //   token rows in A
+  uint16_t* xcopy;            // gather (SwiGLU epilogue only): the permuted rows [N, lda], k-step
+                              //   kt of an m-tile written by its n-tile kt % ntn
+  float* wcopy;               // gather: routing weight of each permuted row [N], by n-tile 0
+  const float* gw;            //   from the routing weights [T, gK]
 };
 
 // Where flat tile l sits: experts in order, and within an expert either
@@ -75,8 +82,20 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoo
   constexpr int ROWB = TL::WIDE ? 128 : kBK * 2;  // bytes of a k-step's row
   static_assert(!TL::WIDE || !B_T, "the wide-row loop takes k-contiguous operands");
   KStager<BM, WAVES, ROWB> sa;
-  sa.init(make_rsrc(p.A + size_t(e0) * p.lda, uint32_t(ne) * p.lda * 2),
-          [&](int r) { return r < rows_valid ? (m0 + r) * p.lda * 2 : -1; }, wave, lane);
+  constexpr bool CAN_GATHER = TL::WIDE && EPI == EPI_SWIGLU;
+  const bool gathered = CAN_GATHER && p.gather != nullptr;
+  if (gathered) {
+    const int32_t* g = p.gather + e0 + m0;
+    sa.init(make_rsrc(p.A, uint32_t(p.gT) * p.lda * 2),
+            [&](int r) { return r < rows_valid ? (g[r] / p.gK) * p.lda * 2 : -1; }, wave, lane);
+    if (nt == 0) {  // this tile's rows also leave as the dispatched rows and weights
+      const int tid = opaque_tid();
+      if (tid < rows_valid) p.wcopy[e0 + m0 + tid] = p.gw[g[tid]];
+    }
+  } else {
+    sa.init(make_rsrc(p.A + size_t(e0) * p.lda, uint32_t(ne) * p.lda * 2),
+            [&](int r) { return r < rows_valid ? (m0 + r) * p.lda * 2 : -1; }, wave, lane);
+  }
   const uint16_t* Be = p.B + size_t(e) * p.bstride;
   const uint32_t bbytes = uint32_t(p.brows) * p.ldb * 2;
   f32x16 acc[WMT][WNT];
@@ -107,9 +126,33 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoo
             },
             wave, lane);
     with_active<WMT>(act, [&](auto a) {
-      if constexpr (TL::WIDE)
-        mainloop_w<BM, BN, TL::WGM, TL::WGN, decltype(a)::value>(smem, sa, sb, ktiles, acc, wave,
-                                                                 lane);
+      if constexpr (TL::WIDE) {
+        bool copy = false;
+        if constexpr (CAN_GATHER) copy = gathered;
+        if (copy) {
+          if constexpr (CAN_GATHER) {
+            // k-step kt's 128-byte row segments of A, from LDS to the permuted rows, by the
+            // n-tile kt % ntn (the m-tile's n-tiles share the copy evenly)
+            uint16_t* xc = p.xcopy + (size_t(e0) + m0) * p.lda;
+            const int lda = p.lda, ntn = p.ntn;
+            mainloop_w<BM, BN, TL::WGM, TL::WGN, decltype(a)::value>(
+                smem, sa, sb, ktiles, acc, wave, lane, [&](int kt, const char* ta) {
+                  if (kt % ntn != nt) return;
+                  const int tid = wave * 64 + lane;
+#pragma unroll
+                  for (int i = 0; i < BM * 8 / TL::THREADS; ++i) {
+                    const int c = tid + i * TL::THREADS, r = c >> 3, ch = c & 7;
+                    if (r < rows_valid)
+                      *reinterpret_cast<uint4*>(xc + size_t(r) * lda + kt * 64 + ch * 8) =
+                          *reinterpret_cast<const uint4*>(ta + r * 128 + ((ch ^ swz_row<128>(r)) << 4));
+                  }
+                });
+          }
+        } else {
+          mainloop_w<BM, BN, TL::WGM, TL::WGN, decltype(a)::value>(smem, sa, sb, ktiles, acc,
+                                                                   wave, lane);
+        }
+      }
       else
         mainloop<BM, BN, TL::WGM, TL::WGN, TL::STAGES, false, false, decltype(a)::value>(
             smem, sa, sb, ktiles, acc, wave, lane);
