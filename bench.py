@@ -54,6 +54,12 @@ def gemm_flops(cfg) -> dict:
             "pair_w2": 4 * ndf, "pair_w1": 8 * ndf}
 
 
+def weights_in_gemms(cfg) -> bool:
+    """bf16 at the shapes whose GEMMs carry the routing weights and the dispatch
+    (the library's own condition: 2F % 256 == 0 and D % 64 == 0)."""
+    return cfg.mode == 2 and (2 * cfg.F) % 256 == 0 and cfg.D % 64 == 0
+
+
 def row_bytes(cfg, b=2, recompute=False) -> dict:
     """Algorithmic HBM bytes per launch of the row movers (bf16 rows).  In the FP8
     forward modes (MXFP8, blockwise FP8) the dispatch writes the e4m3 row codes
@@ -61,12 +67,21 @@ def row_bytes(cfg, b=2, recompute=False) -> dict:
     rows (which it writes too under activation recompute; in MXFP8 without
     recompute no dispatch runs).  The combine-backward writes dYw's codes in
     blockwise FP8 and fp8_bwd instead of its bf16 rows, and in MXFP8 neither
-    (it computes only dtopk_w)."""
+    (it computes only dtopk_w).  Where the GEMMs carry the routing weights (bf16
+    at the wide shapes) no forward dispatch runs, the combine is an unweighted
+    sum, the backward's dispatch copies dy unscaled and dtopk_w is the sum of
+    the W2 dgrad's partials (F / 64 per row)."""
     T, N, D = cfg.T, cfg.N, cfg.D
     codes = N * D + N * (D // 128) * 4
     fwd_q = cfg.mode in (4, 5)   # MXFP8, blockwise FP8 in both passes
     dyw_out = {4: 0, 3: codes, 5: codes}.get(cfg.mode, N * D * b)
     xrows = N * D * b if (not fwd_q or recompute) else 0
+    if weights_in_gemms(cfg):
+        return {"combine": N * D * b + T * D * b + N * 4,
+                # dy once, each pair's row written, pos read
+                "dispatch_dy": T * D * b + N * D * b + N * 4,
+                "dprob_reduce": N * 4 + N * (cfg.F // 64) * 4 + N * 4,
+                "unpermute": N * D * b + T * D * b + N * 4}
     return {"dispatch": T * D * b + xrows + 2 * N * 4 + N * 4 + (codes if fwd_q else 0),
             "combine": N * D * b + T * D * b + N * 8,
             # dy once, each pair's expert-output row read and its w*dy row (or its

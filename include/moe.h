@@ -208,6 +208,10 @@ int moe_routing_view(const moe_desc* d, const void* scratch, size_t scratch_byte
  *   MOE_VIEW_DYPERM [T*K, D]   dispatched upstream gradient times the routing
  *                              weight, w * dy (fp32 product, stored once).  Not
  *                              stored in the FP8 modes (only its FP8 codes are)
+ *   In MOE_BF16 at D % 64 == 0 and 2F % 256 == 0 the GEMMs carry the routing
+ *   weights instead: A holds w * A (rounded once), O holds w * O, DYPERM holds
+ *   dy itself, and dtopk_w comes from the W2 dgrad (sum over f of its fp32
+ *   dy W2^T against the SwiGLU output recomputed from H).
  *   MOE_VIEW_DH     [T*K, 2F]  gradient wrt linear-1 output
  *   MOE_VIEW_DXPERM [T*K, D]   gradient wrt dispatched tokens
  *   MOE_VIEW_WPERM  [T*K] fp32 routing weight of each routed pair

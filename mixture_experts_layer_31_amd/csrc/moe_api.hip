@@ -269,11 +269,11 @@ int moe::forward(const moe_desc* d, const void* x, const int32_t* topk_idx, cons
   const Layout L = make_layout(*d);
   char* sc = static_cast<char*>(scratch);
   const bool io_f32 = d->mode == MOE_FP32 || d->mode == MOE_FP32_BF16GEMM;
-  if ((rc = launch_route(*d, L, topk_idx, sc, s))) return rc;
+  if ((rc = launch_route(*d, L, topk_idx, sc, s, topk_w))) return rc;
   if (d->T == 0) return MOE_OK;  // routing metadata of no pairs; y is empty
   if (queue_capable(*d)) {
     if ((rc = launch_fwd_queue(*d, L, x, io_f32, topk_w, g1, g2, sc, s))) return rc;
-    return launch_combine(*d, L, topk_w, y, io_f32, sc, s);
+    return launch_combine(*d, L, topk_w, y, io_f32, sc, s, !bf16_wide(*d));
   }
   const bool fwd_q = fp8_mode(d->mode) && d->mode != MOE_FP8_BWD;
   if (fwd_q) {
@@ -295,7 +295,7 @@ int moe::forward(const moe_desc* d, const void* x, const int32_t* topk_idx, cons
         return rc;
     }
     if ((rc = fp8_x_tokens(*d, L, x, topk_w, rows_in_pass, sc, s))) return rc;
-  } else if (!w1_gathers(*d) && (rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s))) {
+  } else if (!bf16_wide(*d) && (rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s))) {
     return rc;
   }
   if (d->mode == MOE_FP32)
@@ -305,9 +305,9 @@ int moe::forward(const moe_desc* d, const void* x, const int32_t* topk_idx, cons
     rc = fp8_fwd_gemms(*d, L, static_cast<const char*>(wprep), sc, s, true);
   else
     rc = launch_fwd_gemms(*d, L, g1, g2, sc, s,
-                          w1_gathers(*d) ? static_cast<const uint16_t*>(x) : nullptr, topk_w);
+                          bf16_wide(*d) ? static_cast<const uint16_t*>(x) : nullptr, topk_w);
   if (rc) return rc;
-  return launch_combine(*d, L, topk_w, y, io_f32, sc, s);
+  return launch_combine(*d, L, topk_w, y, io_f32, sc, s, !bf16_wide(*d));
 }
 
 extern "C" {
@@ -357,6 +357,10 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
     fp8_dyw_codes(*d, L, sc, &qc, &qs);
     if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s, 2, qc, qs, false)))
       return rc;
+  } else if (bf16_wide(*d)) {  // dy unscaled: w and dtopk_w come from the W2 dgrad
+    if ((rc = launch_dispatch(*d, L, dy, false, nullptr, sc, L.dyperm, s, 0, nullptr, nullptr,
+                              true, "dispatch_dy")))
+      return rc;
   } else if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s))) {
     return rc;
   }
@@ -368,6 +372,7 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
   else
     rc = launch_bwd_gemms(*d, L, g1, g2, dw1, dw2, io_f32, sc, s);
   if (rc) return rc;
+  if (bf16_wide(*d) && (rc = launch_dprob_reduce(*d, L, dtopk_w, sc, s))) return rc;
   return launch_unpermute(*d, L, dx, io_f32, sc, s);
 }
 

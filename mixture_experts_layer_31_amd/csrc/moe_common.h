@@ -36,13 +36,28 @@ constexpr int kRouteThreads = 256;
 // starts on a 256-byte boundary.  The layout depends only on the descriptor.
 struct Layout {
   size_t err, counts, offsets, tiles[3], eorder, chunk_cnt, chunk_bad, pos, src, wperm;
-  size_t xperm, h, a, o, dyperm, dh, dxperm, fp8, queue, pair, total;
+  size_t xperm, h, a, o, dyperm, dh, dxperm, dpart, fp8, queue, pair, total;
   bool recompute;   // MOE_FLAG_RECOMPUTE: no H region; H is rebuilt in the dH region
   int nchunks;      // routing chunks
   int act_bytes;    // bytes per intermediate element
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// bf16 at the shapes whose W1 GEMM takes the 128-byte-row loop (2F % 256 == 0,
+// D % 64 == 0).  There the GEMMs carry the routing weights and the dispatch:
+// - the W1 GEMM gathers x's rows itself (no dispatch kernel) and writes x_perm
+//   and w_perm for the backward;
+// - its SwiGLU epilogue stores A_w = w * A, so W2 yields O_w = w * O and the
+//   combine is an unweighted sum;
+// - the backward dispatches dy unscaled, the W2 dgrad's epilogue applies w and
+//   writes dProb partials (its accumulators G = dy W2^T against the SwiGLU
+//   output recomputed from H), and the W2 weight gradient pairs dy with A_w.
+inline bool bf16_wide(const moe_desc& d) {
+  return d.mode == MOE_BF16 && (2 * d.F) % 256 == 0 && d.D % 64 == 0;
+}
+// dProb partials per routed row: one per 64 columns of F
+inline int dprob_parts(const moe_desc& d) { return d.F / 64; }
 
 // FP8 modes (moe_fp8.hip): extra scratch for quantised operands, prepared
 // weight sizes, weight preparation and the quantised GEMM sequences.
@@ -77,6 +92,7 @@ inline Layout make_layout(const moe_desc& d) {
   L.dyperm = take(N * D * ab);
   L.dh = take(N * 2 * F * ab);
   L.dxperm = take(N * D * ab);
+  L.dpart = bf16_wide(d) ? take(N * size_t(dprob_parts(d)) * 4) : 0;
   if (L.recompute) L.h = L.dh;  // written by the backward's recompute, then overwritten by dH
   L.fp8 = take(fp8_scratch_bytes(d));
   L.queue = take(queue_scratch_bytes(d));
@@ -100,8 +116,9 @@ void prof_begin(const char* name, hipStream_t s);
 void prof_end(hipStream_t s);
 
 // ---- kernel launchers (host) ----
+// topk_w (optional): also w_perm[pos[p]] = topk_w[p]
 int launch_route(const moe_desc& d, const Layout& L, const int32_t* idx, char* scratch,
-                 hipStream_t s);
+                 hipStream_t s, const float* topk_w = nullptr);
 int launch_clear_err(char* scratch, const Layout& L, hipStream_t s);
 
 // Row gathers/scatters: dispatch (x -> expert-contiguous rows), combine and the
@@ -111,9 +128,14 @@ int launch_clear_err(char* scratch, const Layout& L, hipStream_t s);
 int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool in_f32,
                     const float* topk_w, char* scratch, size_t dst_off, hipStream_t s,
                     int qmode = 0, uint8_t* qcodes = nullptr, uint32_t* qsc = nullptr,
-                    bool store_rows = true);
+                    bool store_rows = true, const char* name = "dispatch");
+// weighted = false: y_t = sum_k O[pos] (the rows already carry their weights)
 int launch_combine(const moe_desc& d, const Layout& L, const float* topk_w, void* y,
-                   bool out_f32, const char* scratch, hipStream_t s);
+                   bool out_f32, const char* scratch, hipStream_t s, bool weighted = true);
+// dtopk_w[p] = sum of row pos[p]'s dProb partials, in column order (0 for pairs
+// without a row)
+int launch_dprob_reduce(const moe_desc& d, const Layout& L, float* dtopk_w, const char* scratch,
+                        hipStream_t s);
 int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
                      const char* scratch, hipStream_t s);
 // Combine-backward: dYw_perm rows (w * dy, bf16) and dtopk_w = <dy, o>.  With
@@ -147,11 +169,7 @@ bool queue_capable(const moe_desc& d);
 int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_f32,
                      const float* topk_w, const uint16_t* w1, const uint16_t* w2, char* scratch,
                      hipStream_t s);
-// bf16 at shapes the wide-row W1 loop takes: no dispatch kernel; the W1 GEMM
-// gathers x's rows itself and its tiles also write the dispatched rows and
-// weights (x_perm, w_perm) for the backward, from the rows they staged.
-bool w1_gathers(const moe_desc& d);
-// x and topk_w: the token rows and routing weights when w1_gathers(d), else null.
+// x and topk_w: the token rows and routing weights when bf16_wide(d), else null.
 int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
                      char* scratch, hipStream_t s, const uint16_t* x = nullptr,
                      const float* topk_w = nullptr);

@@ -281,14 +281,13 @@ int run_w1_swiglu(const moe_desc& d, const Layout& L, const uint16_t* w1, uint16
   a.F = d.F;
   a.A = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
   if (x != nullptr) {
-    if (!w1_gathers(d) || topk_w == nullptr) return MOE_EINVAL;
+    if (!bf16_wide(d) || topk_w == nullptr) return MOE_EINVAL;
     a.A = x;
     a.gather = reinterpret_cast<const int32_t*>(scratch + L.src);
     a.gK = d.K;
     a.gT = d.T;
     a.xcopy = reinterpret_cast<uint16_t*>(scratch + L.xperm);
-    a.wcopy = reinterpret_cast<float*>(scratch + L.wperm);
-    a.gw = topk_w;
+    a.rw = reinterpret_cast<const float*>(scratch + L.wperm);  // A_w = w A (routing wrote w_perm)
   }
   a.lda = d.D;
   a.B = w1;
@@ -306,11 +305,6 @@ int launch_recompute_h(const moe_desc& d, const Layout& L, const uint16_t* w1, c
                        hipStream_t s) {
   return run_w1_swiglu(d, L, w1, reinterpret_cast<uint16_t*>(scratch + L.h), nullptr,
                        "gemm_w1_recompute", scratch, s);
-}
-
-bool w1_gathers(const moe_desc& d) {
-  // the condition under which run_grouped_any takes the wide-row loop for W1
-  return d.mode == MOE_BF16 && (2 * d.F) % 256 == 0 && d.D % 64 == 0;
 }
 
 int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
@@ -360,6 +354,8 @@ bool pair_capable(const moe_desc& d) {
 
 int launch_bwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
                      void* dw1, void* dw2, bool dw_f32, char* scratch, hipStream_t s) {
+  // bf16_wide: dYw_perm holds dy unscaled, A holds A_w = w A; the W2 dgrad applies w
+  // (from w_perm) and writes the dProb partials
   const int D = d.D, F = d.F;
   int rc;
   // W2 wgrad: dW2[e] = sum_r dYw_perm[r] A[r]^T
@@ -381,6 +377,10 @@ int launch_bwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, con
   w2d.brows = D;
   w2d.out = reinterpret_cast<uint16_t*>(scratch + L.dh);
   w2d.hsave = reinterpret_cast<const uint16_t*>(scratch + L.h);
+  if (bf16_wide(d)) {
+    w2d.rw = reinterpret_cast<const float*>(scratch + L.wperm);
+    w2d.dpart = reinterpret_cast<float*>(scratch + L.dpart);
+  }
   // W1 wgrad: dW1[e] = sum_r dH[r] x_perm[r]^T
   WgradArgs w1g{};
   w1g.M = 2 * F;

@@ -504,6 +504,16 @@ struct EpiArgs {
   const uint16_t* hsave;  // DSWIGLU: H [rows, 2F]; may equal out (each tile reads its H band
                           // into LDS before it stores the same band's dH)
   int F;
+  // Routing weights carried by the GEMMs (epilogues instantiated with WS):
+  // SWIGLU stores A_w = w * A, with wrow[i] the weight of the lane's row in
+  // 32-row block i of its wave's share (loaded ahead of the main loop); DSWIGLU
+  // takes dA = w * G, loading row r's weight wp[r] itself, and writes dProb
+  // partials.  Null wp / wscale false: no weights.
+  bool wscale;
+  float wrow[4];
+  const float* wp;        // DSWIGLU: [rows] routing weight of each permuted row
+  float* dpart;           // DSWIGLU: dProb partials [rows, F / 64], the wave's 64 columns of
+                          // sum_f G[r, f] * A[r, f] (A recomputed from the saved H)
 };
 
 // Epilogues stage the output through LDS, one band of 32-row blocks (one per
@@ -615,7 +625,7 @@ constexpr int wgrad_epi_lds() { return TL::WGM * 32 * TL::BN * (OUT_F32 ? 4 : 2)
 // arrives by direct-to-LDS loads (into the XOR-swizzled band layout) while
 // band i is computed in place and stored, so the H loads overlap the previous
 // band's work instead of preceding it.
-template <class TL>
+template <class TL, bool WS>
 __device__ __forceinline__ void dswiglu_epilogue(const EpiArgs& p,
                                                  f32x16 (&acc)[TL::WMT][TL::WNT], size_t grow0,
                                                  int rows_valid, int nt, int wm, int wn, int lane,
@@ -650,8 +660,19 @@ __device__ __forceinline__ void dswiglu_epilogue(const EpiArgs& p,
   };
   const int tid = wave * 64 + lane;
   issue(0, 0);
+  // the lane's rows' routing weights arrive with band 0's H
+  float wr[WMT];
+  const bool ws = WS && p.wp != nullptr;
+  if constexpr (WS) {
+#pragma unroll
+    for (int i = 0; i < WMT; ++i) {
+      const int trow = wm * WM + i * 32 + (lane & 31);
+      wr[i] = ws && trow < rows_valid ? p.wp[grow0 + trow] : 1.f;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < WMT; ++i) {
+    float part = 0.f;
     const int b = i & 1;
     wait_vmcnt<0>();   // band i's H (and the previous band's stores)
     __syncthreads();   // ... for every wave; buffer b ^ 1 is free again
@@ -670,14 +691,31 @@ __device__ __forceinline__ void dswiglu_epilogue(const EpiArgs& p,
         unpack4(*pu, uv);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float dA = acc[i][j][4 * g + q];
+          const float G = acc[i][j][4 * g + q];
           const float sg = 1.f / (1.f + __expf(-gv[q]));
-          dg[q] = dA * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
-          du[q] = dA * gv[q] * sg;
+          if constexpr (WS) {
+            const float s = gv[q] * sg, dA = G * wr[i];
+            part += G * (s * uv[q]);
+            asm volatile("" : "+v"(part));  // keeps the compiler from spilling here
+            dg[q] = dA * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
+            du[q] = dA * s;
+          } else {
+            const float dA = G;
+            dg[q] = dA * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
+            du[q] = dA * gv[q] * sg;
+          }
         }
         *pg = pack4(dg[0], dg[1], dg[2], dg[3]);
         *pu = pack4(du[0], du[1], du[2], du[3]);
       }
+    if constexpr (WS) {
+      if (ws && p.dpart != nullptr) {  // the row's other 32 columns of this wave sit in lane ^ 32
+        part += __shfl_xor(part, 32);
+        const int trow = wm * WM + i * 32 + (lane & 31);
+        if (lane < 32 && trow < rows_valid)
+          p.dpart[(grow0 + trow) * (F / 64) + (f0 + wn * WN) / 64] = part;
+      }
+    }
     __syncthreads();
     for (int w = 0; w < TL::WGM; ++w) {
       const int first = w * WM + i * 32, n = min(32, rows_valid - first);
@@ -697,7 +735,7 @@ __device__ __forceinline__ void dswiglu_epilogue(const EpiArgs& p,
 // the (now free) pipeline LDS, AVAIL bytes of it.  A plain store stages the
 // whole bf16 tile at once when AVAIL holds it (one barrier, every store of a
 // thread issued back to back), else one band at a time.
-template <class TL, int EPI, bool COH2 = false, int AVAIL = 0>
+template <class TL, int EPI, bool COH2 = false, int AVAIL = 0, bool WS = false>
 __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
                                                  f32x16 (&acc)[TL::WMT][TL::WNT], size_t grow0,
                                                  int rows_valid, int nt, int wm, int wn, int lane,
@@ -707,7 +745,7 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
   const int rr = wm * 32 + (lane & 31);
   __syncthreads();  // every wave is done reading the pipeline stages
   if constexpr (EPI == EPI_DSWIGLU) {
-    dswiglu_epilogue<TL>(p, acc, grow0, rows_valid, nt, wm, wn, lane, smem);
+    dswiglu_epilogue<TL, WS>(p, acc, grow0, rows_valid, nt, wm, wn, lane, smem);
     return;
   }
   if constexpr (EPI == EPI_STORE && AVAIL >= TL::BM * BN * 2) {
@@ -764,6 +802,7 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
             gv[q] = acc[i][j][4 * g + q];
             uv[q] = acc[i][j + WNT / 2][4 * g + q];
             av[q] = gv[q] / (1.f + __expf(-gv[q])) * uv[q];
+            if constexpr (WS) if (p.wscale) av[q] *= p.wrow[i];
           }
           *reinterpret_cast<uint2*>(tg.at(rr, c)) = pack4(gv[0], gv[1], gv[2], gv[3]);
           *reinterpret_cast<uint2*>(tu.at(rr, c)) = pack4(uv[0], uv[1], uv[2], uv[3]);

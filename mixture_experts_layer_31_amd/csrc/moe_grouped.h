@@ -25,10 +25,12 @@ struct GroupedArgs {
   const int32_t* gather;      // null: A holds the permuted rows; else A is [T, lda] token rows and
   int gK;                     //   permuted row q reads token row gather[q] / gK (wide-row loop only)
   int gT;                     //   token rows in A
+  const float* rw;            // routing weights carried by the epilogue (SWIGLU: A_w = w A,
+  const int32_t* rsrc;        //   row r's weight rw[rsrc[r]], or rw[r] if rsrc is null;
+                              //   DSWIGLU: dA = w G with row r's weight rw[r]); null: none
+  float* dpart;               // DSWIGLU with rw: dProb partials [rows, F / 64]
   uint16_t* xcopy;            // gather (SwiGLU epilogue only): the permuted rows [N, lda], k-step
                               //   kt of an m-tile written by its n-tile kt % ntn
-  float* wcopy;               // gather: routing weight of each permuted row [N], by n-tile 0
-  const float* gw;            //   from the routing weights [T, gK]
 };
 
 // Where flat tile l sits: experts in order, and within an expert either
@@ -88,16 +90,28 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoo
     const int32_t* g = p.gather + e0 + m0;
     sa.init(make_rsrc(p.A, uint32_t(p.gT) * p.lda * 2),
             [&](int r) { return r < rows_valid ? (g[r] / p.gK) * p.lda * 2 : -1; }, wave, lane);
-    if (nt == 0) {  // this tile's rows also leave as the dispatched rows and weights
-      const int tid = opaque_tid();
-      if (tid < rows_valid) p.wcopy[e0 + m0 + tid] = p.gw[g[tid]];
-    }
   } else {
     sa.init(make_rsrc(p.A + size_t(e0) * p.lda, uint32_t(ne) * p.lda * 2),
             [&](int r) { return r < rows_valid ? (m0 + r) * p.lda * 2 : -1; }, wave, lane);
   }
   const uint16_t* Be = p.B + size_t(e) * p.bstride;
   const uint32_t bbytes = uint32_t(p.brows) * p.ldb * 2;
+  EpiArgs ea{p.out, p.ldo, p.out2, p.hsave, p.F};
+  if constexpr (EPI == EPI_SWIGLU) {  // the routing weights of the lane's rows, ahead of the main loop
+    static_assert(WMT <= 4, "one routing weight per 32-row block");
+    if (p.rw != nullptr) {
+      ea.wscale = true;
+#pragma unroll
+      for (int i = 0; i < WMT; ++i) {
+        const int trow = wm * TL::WM + i * 32 + (lane & 31);
+        const int r = e0 + m0 + trow;
+        ea.wrow[i] = trow < rows_valid ? p.rw[p.rsrc != nullptr ? p.rsrc[r] : r] : 0.f;
+      }
+    }
+  } else if constexpr (EPI == EPI_DSWIGLU) {  // loaded by the epilogue (rsrc unused)
+    ea.wp = p.rw;
+    ea.dpart = p.dpart;
+  }
   f32x16 acc[WMT][WNT];
   zero(acc);
   const int ktiles = p.K / (ROWB / 2);
@@ -159,8 +173,7 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoo
     });
   }
 
-  EpiArgs ea{p.out, p.ldo, p.out2, p.hsave, p.F};
-  grouped_epilogue<TL, EPI, COH2, TL::LDS>(ea, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane,
+  grouped_epilogue<TL, EPI, COH2, TL::LDS, true>(ea, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane,
                                            smem, tid);
 }
 

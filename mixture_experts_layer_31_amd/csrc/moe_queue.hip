@@ -357,6 +357,8 @@ int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_
   q.w1.brows = 2 * d.F;
   q.w1.out = L.recompute ? nullptr : reinterpret_cast<uint16_t*>(scratch + L.h);
   q.w1.out2 = reinterpret_cast<uint16_t*>(scratch + L.a);
+  if (bf16_wide(d))  // A_w = w A, as the per-step forward stores it (routing wrote w_perm)
+    q.w1.rw = reinterpret_cast<const float*>(scratch + L.wperm);
   q.w2.offsets = b.offsets;
   q.w2.tile_start = b.tile256;
   q.w2.E = d.E;

@@ -122,7 +122,8 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(
 __global__ void __launch_bounds__(kRouteThreads) route_scatter_kernel(
     const int32_t* __restrict__ idx, int N, int E, int nbits,
     const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ pos, int32_t* __restrict__ src) {
+    int32_t* __restrict__ pos, int32_t* __restrict__ src, const float* __restrict__ topk_w,
+    float* __restrict__ wperm) {
   constexpr int kWaves = kRouteThreads / 64;
   __shared__ int base[1024];
   __shared__ int wcnt[kWaves][1024];
@@ -152,6 +153,7 @@ __global__ void __launch_bounds__(kRouteThreads) route_scatter_kernel(
       for (int w = 0; w < wave; ++w) q += wcnt[w][e];
       pos[p] = q;
       src[q] = p;
+      if (topk_w != nullptr) wperm[q] = topk_w[p];
     } else if (p < N) {
       pos[p] = -1;
     }
@@ -180,7 +182,7 @@ int launch_clear_err(char* scratch, const Layout& L, hipStream_t s) {
 }
 
 int launch_route(const moe_desc& d, const Layout& L, const int32_t* idx, char* scratch,
-                 hipStream_t s) {
+                 hipStream_t s, const float* topk_w) {
   const int N = d.T * d.K, E = d.E;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
@@ -206,7 +208,8 @@ int launch_route(const moe_desc& d, const Layout& L, const int32_t* idx, char* s
     prof_begin("route_scatter", s);
     route_scatter_kernel<<<L.nchunks, kRouteThreads, 0, s>>>(
         idx, N, E, nbits, chunk, reinterpret_cast<const int32_t*>(scratch + L.offsets),
-        reinterpret_cast<int32_t*>(scratch + L.pos), reinterpret_cast<int32_t*>(scratch + L.src));
+        reinterpret_cast<int32_t*>(scratch + L.pos), reinterpret_cast<int32_t*>(scratch + L.src),
+        topk_w, reinterpret_cast<float*>(scratch + L.wperm));
     prof_end(s);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;

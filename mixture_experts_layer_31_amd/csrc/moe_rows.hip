@@ -472,11 +472,11 @@ static int with_types(const moe_desc& d, bool io_f32, F f) {
 
 int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool in_f32,
                     const float* topk_w, char* scratch, size_t dst_off, hipStream_t s,
-                    int qmode, uint8_t* qcodes, uint32_t* qsc, bool store_rows) {
+                    int qmode, uint8_t* qcodes, uint32_t* qsc, bool store_rows, const char* name) {
   if (!store_rows && qmode == 0) return MOE_EINVAL;
   const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
   auto* wperm = topk_w ? reinterpret_cast<float*>(scratch + L.wperm) : nullptr;
-  prof_begin("dispatch", s);
+  prof_begin(name, s);
   const int rc = with_types(d, in_f32, [&](auto io, auto act) {
     using IO = decltype(io);
     using ACT = decltype(act);
@@ -522,14 +522,18 @@ int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool i
 }
 
 int launch_combine(const moe_desc& d, const Layout& L, const float* topk_w, void* y,
-                   bool out_f32, const char* scratch, hipStream_t s) {
+                   bool out_f32, const char* scratch, hipStream_t s, bool weighted) {
   const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
   prof_begin("combine", s);
   with_types(d, out_f32, [&](auto io, auto act) {
     using IO = decltype(io);
     using ACT = decltype(act);
-    launch_gather_reduce<ACT, IO, true>(d, reinterpret_cast<const ACT*>(scratch + L.o), pos,
-                                        topk_w, static_cast<IO*>(y), s);
+    if (weighted)
+      launch_gather_reduce<ACT, IO, true>(d, reinterpret_cast<const ACT*>(scratch + L.o), pos,
+                                          topk_w, static_cast<IO*>(y), s);
+    else
+      launch_gather_reduce<ACT, IO, false>(d, reinterpret_cast<const ACT*>(scratch + L.o), pos,
+                                           nullptr, static_cast<IO*>(y), s);
     return 0;
   });
   prof_end(s);
@@ -547,6 +551,32 @@ int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
                                          pos, nullptr, static_cast<IO*>(dx), s);
     return 0;
   });
+  prof_end(s);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// dtopk_w[p] = sum over j of part[pos[p] * J + j], j ascending (pairs without a
+// row: 0).  One thread per pair.
+__global__ void __launch_bounds__(256) dprob_reduce_kernel(const int32_t* __restrict__ pos,
+                                                           const float* __restrict__ part, int J,
+                                                           float* __restrict__ dtopk_w, int N) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= N) return;
+  const int q = pos[p];
+  float s = 0.f;
+  if (q >= 0)
+    for (int j = 0; j < J; ++j) s += part[size_t(q) * J + j];
+  dtopk_w[p] = s;
+}
+
+int launch_dprob_reduce(const moe_desc& d, const Layout& L, float* dtopk_w, const char* scratch,
+                        hipStream_t s) {
+  const int N = d.T * d.K;
+  if (N == 0) return MOE_OK;
+  prof_begin("dprob_reduce", s);
+  dprob_reduce_kernel<<<unsigned((N + 255) / 256), 256, 0, s>>>(
+      reinterpret_cast<const int32_t*>(scratch + L.pos),
+      reinterpret_cast<const float*>(scratch + L.dpart), dprob_parts(d), dtopk_w, N);
   prof_end(s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }

@@ -7,6 +7,11 @@ Integer routing arrays must be bit-exact; floating-point outputs and
 intermediates must meet max|err| / max|ref| <= tol against the float64 oracle
 on the same inputs.  Dispatch copies (x_perm, dY_perm) and the permuted
 routing weights are bit-exact copies.
+
+In bf16 at the shapes whose GEMMs carry the routing weights (2F % 256 == 0,
+D % 64 == 0) the saved A and O rows are w * A and w * O, and the dispatched
+upstream gradient is dy itself (w enters in the W2 dgrad); elsewhere A and O
+are unweighted and the dispatched gradient is w * dy.
 """
 from __future__ import annotations
 
@@ -22,6 +27,11 @@ TOL_BF16 = 1e-2
 # fp32 storage and arithmetic against the float64 oracle: rounding of fp32 sums
 # over at most a few thousand terms stays orders of magnitude below this
 TOL_F32 = 1e-4
+
+
+def weights_in_gemms(cfg):
+    """Whether the library applies the routing weights inside the GEMMs."""
+    return cfg.mode == mi.MODE_BF16 and (2 * cfg.F) % 256 == 0 and cfg.D % 64 == 0
 
 
 def run(cfg, inp, flags=0):
@@ -66,12 +76,19 @@ def layer_vs_oracle(cfg, inp, flags=0):
     xp = L.view(moe.MOE_VIEW_XPERM, D, act)
     dyp = L.view(moe.MOE_VIEW_DYPERM, D, act)
     wp = L.view(moe.MOE_VIEW_WPERM, 0, torch.float32)
-    # the dispatched gradient is w * dy (fp32 product, stored once)
-    dyw = rnd((inp["topk_w"][t_of, k_of][:, None] * inp["dy"][t_of]).astype(np.float32))
-    np.testing.assert_array_equal(dyp[:len(src)], dyw)
+    w = inp["topk_w"][t_of, k_of]
+    if weights_in_gemms(cfg):
+        # dy itself; the saved A and O carry the weights
+        np.testing.assert_array_equal(dyp[:len(src)], rnd(inp["dy"][t_of].copy()))
+        a_ref, o_ref = f["a"] * inp["topk_w"][..., None], f["o"] * inp["topk_w"][..., None]
+    else:
+        # the dispatched gradient is w * dy (fp32 product, stored once)
+        dyw = rnd((w[:, None] * inp["dy"][t_of]).astype(np.float32))
+        np.testing.assert_array_equal(dyp[:len(src)], dyw)
+        a_ref, o_ref = f["a"], f["o"]
     np.testing.assert_array_equal(xp[:len(src)], rnd(inp["x"][t_of].copy()))
-    np.testing.assert_array_equal(wp[:len(src)], inp["topk_w"][t_of, k_of])
-    views = [(moe.MOE_VIEW_A, F, f["a"], "a"), (moe.MOE_VIEW_O, D, f["o"], "o"),
+    np.testing.assert_array_equal(wp[:len(src)], w)
+    views = [(moe.MOE_VIEW_A, F, a_ref, "a"), (moe.MOE_VIEW_O, D, o_ref, "o"),
              (moe.MOE_VIEW_DH, 2 * F, b["dh"], "dh")]
     if not flags & moe.MOE_FLAG_RECOMPUTE:  # the forward keeps no H under recompute
         views.append((moe.MOE_VIEW_H, 2 * F, f["h"], "h"))

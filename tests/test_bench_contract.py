@@ -30,7 +30,18 @@ def test_row_mover_bytes_follow_the_definitions():
     b = _bench_module()
     cfg = mi.CONFIGS["30b"]
     T, N, D = cfg.T, cfg.N, cfg.D
-    rb = b.row_bytes(cfg)
+    # bf16 at the 30B shape: the GEMMs carry the routing weights and the dispatch
+    assert b.weights_in_gemms(cfg)
+    wide = b.row_bytes(cfg)
+    assert "dispatch" not in wide
+    # unweighted combine: every pair's row read, the token row written, pos read
+    assert wide["combine"] == 2 * N * D + 2 * T * D + N * 4
+    # the backward's dispatch of dy: dy once, every pair's row written, pos read
+    assert wide["dispatch_dy"] == 2 * T * D + 2 * N * D + N * 4
+    assert wide["dprob_reduce"] == N * 4 * (2 + cfg.F // 64)
+    # the same shape where the weights stay in the row movers (fp32 I/O with bf16 GEMMs)
+    rb = b.row_bytes(mi.LayerConfig("30b_io", T=T, D=D, F=cfg.F, E=cfg.E, K=cfg.K,
+                                    mode=mi.MODE_FP32_BF16GEMM))
     # dispatch: x once, every pair's row written, pos read, wperm written, topk_w read
     assert rb["dispatch"] == 2 * T * D + 2 * N * D + 3 * N * 4
     # combine / un-permute: every pair's row read, the token row written, indices (+ weights)
@@ -50,6 +61,7 @@ def test_row_mover_bytes_follow_the_definitions():
     assert b.row_bytes(mx)["dispatch_dy"] - rb["dispatch_dy"] == -2 * N * D
     fb = mi.CONFIGS["235b_fp8bwd"]
     fcodes = fb.N * fb.D + fb.N * (fb.D // 128) * 4
-    assert b.row_bytes(fb)["dispatch"] == b.row_bytes(mi.CONFIGS["235b"])["dispatch"]
-    assert (b.row_bytes(fb)["dispatch_dy"] - b.row_bytes(mi.CONFIGS["235b"])["dispatch_dy"]
-            == fcodes - 2 * fb.N * fb.D)
+    io = b.row_bytes(mi.LayerConfig("235b_io", T=fb.T, D=fb.D, F=fb.F, E=fb.E, K=fb.K,
+                                    mode=mi.MODE_FP32_BF16GEMM))
+    assert b.row_bytes(fb)["dispatch"] == io["dispatch"]
+    assert b.row_bytes(fb)["dispatch_dy"] - io["dispatch_dy"] == fcodes - 2 * fb.N * fb.D
