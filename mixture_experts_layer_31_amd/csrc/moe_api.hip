@@ -272,7 +272,7 @@ int moe::forward(const moe_desc* d, const void* x, const int32_t* topk_idx, cons
   if ((rc = launch_route(*d, L, topk_idx, sc, s, topk_w))) return rc;
   if (d->T == 0) return MOE_OK;  // routing metadata of no pairs; y is empty
   if (queue_capable(*d)) {
-    if ((rc = launch_fwd_queue(*d, L, x, io_f32, topk_w, g1, g2, sc, s))) return rc;
+    if ((rc = launch_fwd_queue(*d, L, x, io_f32, g1, g2, sc, s))) return rc;
     return launch_combine(*d, L, topk_w, y, io_f32, sc, s, !bf16_wide(*d));
   }
   const bool fwd_q = fp8_mode(d->mode) && d->mode != MOE_FP8_BWD;
@@ -280,7 +280,7 @@ int moe::forward(const moe_desc* d, const void* x, const int32_t* topk_idx, cons
     // Nothing stores the dispatched bf16 rows (except under recompute, whose
     // backward quantises them again): x's token codes (the W1 weight gradient's
     // operand) come from a pass gathered from x.  In MXFP8 that pass also writes
-    // x's row codes (the W1 GEMM's operand) and w_perm, and no dispatch runs
+    // x's row codes (the W1 GEMM's operand), and no dispatch runs
     // (30B: 0.17 ms against 0.09 + 0.12); blockwise, whose row quotients cost
     // that pass more than the dispatch (0.31 against 0.09 + 0.17 ms), the
     // dispatch writes them.
@@ -290,12 +290,12 @@ int moe::forward(const moe_desc* d, const void* x, const int32_t* topk_idx, cons
       uint8_t* qc;
       uint32_t* qs;
       fp8_row_codes(*d, L, sc, &qc, &qs);
-      if ((rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s, mx ? 1 : 2, qc, qs,
+      if ((rc = launch_dispatch(*d, L, x, io_f32, sc, L.xperm, s, mx ? 1 : 2, qc, qs,
                                 L.recompute)))
         return rc;
     }
-    if ((rc = fp8_x_tokens(*d, L, x, topk_w, rows_in_pass, sc, s))) return rc;
-  } else if (!bf16_wide(*d) && (rc = launch_dispatch(*d, L, x, io_f32, topk_w, sc, L.xperm, s))) {
+    if ((rc = fp8_x_tokens(*d, L, x, rows_in_pass, sc, s))) return rc;
+  } else if (!bf16_wide(*d) && (rc = launch_dispatch(*d, L, x, io_f32, sc, L.xperm, s))) {
     return rc;
   }
   if (d->mode == MOE_FP32)
@@ -358,8 +358,8 @@ int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w, const void* 
     if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s, 2, qc, qs, false)))
       return rc;
   } else if (bf16_wide(*d)) {  // dy unscaled: w and dtopk_w come from the W2 dgrad
-    if ((rc = launch_dispatch(*d, L, dy, false, nullptr, sc, L.dyperm, s, 0, nullptr, nullptr,
-                              true, "dispatch_dy")))
+    if ((rc = launch_dispatch(*d, L, dy, false, sc, L.dyperm, s, 0, nullptr, nullptr, true,
+                              "dispatch_dy")))
       return rc;
   } else if ((rc = launch_dispatch_dy(*d, L, dy, io_f32, topk_w, dtopk_w, sc, s))) {
     return rc;

@@ -126,14 +126,14 @@ int launch_clear_err(char* scratch, const Layout& L, hipStream_t s);
 // With qmode (FP8 forward modes) the dispatch also writes the rows' e4m3
 // quantisation along D; store_rows = false then skips the bf16 rows themselves.
 int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool in_f32,
-                    const float* topk_w, char* scratch, size_t dst_off, hipStream_t s,
-                    int qmode = 0, uint8_t* qcodes = nullptr, uint32_t* qsc = nullptr,
-                    bool store_rows = true, const char* name = "dispatch");
+                    char* scratch, size_t dst_off, hipStream_t s, int qmode = 0,
+                    uint8_t* qcodes = nullptr, uint32_t* qsc = nullptr, bool store_rows = true,
+                    const char* name = "dispatch");
 // weighted = false: y_t = sum_k O[pos] (the rows already carry their weights)
 int launch_combine(const moe_desc& d, const Layout& L, const float* topk_w, void* y,
                    bool out_f32, const char* scratch, hipStream_t s, bool weighted = true);
 // dtopk_w[p] = sum of row pos[p]'s dProb partials, in column order (0 for pairs
-// without a row)
+// without a row); offsets[E] rows hold partials
 int launch_dprob_reduce(const moe_desc& d, const Layout& L, float* dtopk_w, const char* scratch,
                         hipStream_t s);
 int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
@@ -167,8 +167,7 @@ bool pair_capable(const moe_desc& d);
 // Persistent forward (dispatch + W1 + SwiGLU + W2 in one launch); see moe_queue.hip.
 bool queue_capable(const moe_desc& d);
 int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_f32,
-                     const float* topk_w, const uint16_t* w1, const uint16_t* w2, char* scratch,
-                     hipStream_t s);
+                     const uint16_t* w1, const uint16_t* w2, char* scratch, hipStream_t s);
 // x and topk_w: the token rows and routing weights when bf16_wide(d), else null.
 int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
                      char* scratch, hipStream_t s, const uint16_t* x = nullptr,
@@ -187,10 +186,10 @@ int fp8_prepare_weights(const moe_desc& d, const uint16_t* w1, const uint16_t* w
 int fp8_fwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, char* scratch,
                   hipStream_t s, bool x_quantised = false);
 // MXFP8 and FP8 forward: x's token codes for the W1 weight gradient, gathered
-// from x; with rows, also x's row codes for the W1 GEMM and w_perm (what the
-// dispatch writes in these modes, which then need no dispatch).
-int fp8_x_tokens(const moe_desc& d, const Layout& L, const void* x, const float* topk_w,
-                 bool rows, char* scratch, hipStream_t s);
+// from x; with rows, also x's row codes for the W1 GEMM (what the dispatch
+// writes in these modes, which then need no dispatch).
+int fp8_x_tokens(const moe_desc& d, const Layout& L, const void* x, bool rows, char* scratch,
+                 hipStream_t s);
 // The FP8 backward, after the combine-backward wrote dYw's row codes
 // (fp8_dyw_codes) and no bf16 dYw rows: dYw's token codes are gathered from dy
 // (bf16 [T, D]) and topk_w.

@@ -71,7 +71,6 @@ struct QArgs {
   uint8_t* rcodes;         // token quantiser with ROWQ: the rows' own codes [N, cols]
   uint32_t* rsc;           //   and their scale entries [cols / 128][rsc_ld]
   int64_t rsc_ld;
-  float* wperm;            // TOK_GATHER (optional): [N] routing weight of each permuted row
   int E;
   int ntr;                 // weights: r-steps per expert
   int total_rows;          // row quantiser: rows of the input
@@ -304,8 +303,6 @@ __global__ void __launch_bounds__(256) quant_tokens_kernel(QArgs p) {
         const int pr = p.src[r0 + r];
         row[it] = pr / p.K;
         if constexpr (SRC == TOK_GATHER_W) wt[it] = p.topk_w[pr];
-        if constexpr (SRC == TOK_GATHER)  // the dispatch's w_perm, when it does not run
-          if (p.wperm != nullptr && cg == 0 && l16 == 0) p.wperm[r0 + r] = p.topk_w[pr];
       }
     }
   }
@@ -854,12 +851,11 @@ int quant_rows(const moe_desc& d, const uint16_t* in, int C, bool mx, uint8_t* o
 // rows are gathered from (TOK_GATHER, TOK_GATHER_W with the weights topk_w).
 // With rcodes the same pass also writes the rows' own quantisation along C,
 // as quant_rows does: codes [N, C] into rcodes, scale entries [C/128][N] into
-// rsc (permuted rows, or gathered rows without weights).  With wperm
-// (TOK_GATHER) it writes each permuted row's routing weight.
+// rsc (permuted rows, or gathered rows without weights).
 int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, bool mx,
                  uint8_t* out, uint32_t* sc, const char* name, const char* scratch, hipStream_t s,
                  int src = TOK_PERM, const float* topk_w = nullptr, uint8_t* rcodes = nullptr,
-                 uint32_t* rsc = nullptr, float* wperm = nullptr) {
+                 uint32_t* rsc = nullptr) {
   QArgs a{};
   a.in = in;
   a.cols = C;
@@ -876,10 +872,8 @@ int quant_tokens(const moe_desc& d, const Layout& L, const uint16_t* in, int C, 
   a.rcodes = rcodes;
   a.rsc = rsc;
   a.rsc_ld = int64_t(d.T) * d.K;
-  a.wperm = wperm;
   if (src == TOK_GATHER_W && topk_w == nullptr) return MOE_EINVAL;
   if (rcodes != nullptr && rsc == nullptr) return MOE_EINVAL;
-  if (wperm != nullptr && (src != TOK_GATHER || topk_w == nullptr)) return MOE_EINVAL;
   // column tiles per workgroup: the gathering forms pipeline the next tile's
   // row loads behind the current tile's quantisation (at the 30B shape x
   // 0.19 -> 0.17 ms and dYw 0.21 -> 0.19 ms, at 235B dYw 0.43 -> 0.38 ms);
@@ -1266,13 +1260,12 @@ void fp8_dyw_codes(const moe_desc& d, const Layout& L, char* scratch, uint8_t** 
   *scales = f.qt1_sc;
 }
 
-int fp8_x_tokens(const moe_desc& d, const Layout& L, const void* x, const float* topk_w,
-                 bool rows, char* scratch, hipStream_t s) {
+int fp8_x_tokens(const moe_desc& d, const Layout& L, const void* x, bool rows, char* scratch,
+                 hipStream_t s) {
   const F8Scratch f = f8scratch(d, L, scratch);
   return quant_tokens(d, L, static_cast<const uint16_t*>(x), d.D, d.mode == MOE_MXFP8, f.qt2,
-                      f.qt2_sc, rows ? "quant_x" : "quant_x_tokens", scratch, s, TOK_GATHER, topk_w,
-                      rows ? f.qrow : nullptr, rows ? f.qrow_sc : nullptr,
-                      rows ? reinterpret_cast<float*>(scratch + L.wperm) : nullptr);
+                      f.qt2_sc, rows ? "quant_x" : "quant_x_tokens", scratch, s, TOK_GATHER,
+                      nullptr, rows ? f.qrow : nullptr, rows ? f.qrow_sc : nullptr);
 }
 
 int fp8_bwd_gemms(const moe_desc& d, const Layout& L, const char* wprep, const void* dy,

@@ -12,7 +12,9 @@
 //   bwd  W2 wgrad     dW2[e] = sum_r dYw_perm[r] A[r]^T                 (per-expert, TN)
 //   bwd  W1 wgrad     dW1[e] = sum_r dH[r] x_perm[r]^T                  (per-expert, TN)
 // (dYw_perm holds the dispatched upstream gradient already multiplied by the
-// pair's routing weight.)
+// pair's routing weight; in bf16 at the shapes whose W1 GEMM gathers x's rows,
+// A holds w * A instead, dYw_perm holds dy itself, and the W2 dgrad's epilogue
+// applies w, so the same products carry the weights.)
 //
 // Work decomposition: a workgroup of WGM x WGN wave64s owns one BM x BN output
 // tile (256 x 256 with a 2 x 4 grid of waves on the large shapes, smaller

@@ -191,8 +191,6 @@ struct QueueArgs {
   const void* x;           // [T, D] bf16, or fp32 when in_f32
   int in_f32, K, D;
   const int32_t* src;      // [N] pair of each permuted row
-  const float* topk_w;     // [T*K]
-  float* wperm;            // [N]
   uint16_t* xperm;         // [N, D]
   int* ctrl;
   int* flags;
@@ -253,7 +251,6 @@ __device__ __forceinline__ void dispatch_rows(const QueueArgs& q, int r0, int r1
     for (int u = 0; u < U; ++u)
       if (rr[u] >= 0) {
         store16_coherent(reinterpret_cast<char*>(q.xperm + size_t(rr[u]) * q.D + cc[u] * 8), v[u]);
-        if (cc[u] == 0) q.wperm[rr[u]] = q.topk_w[q.src[rr[u]]];
       }
   }
 }
@@ -320,8 +317,7 @@ bool queue_capable(const moe_desc& d) {
 }
 
 int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_f32,
-                     const float* topk_w, const uint16_t* w1, const uint16_t* w2, char* scratch,
-                     hipStream_t s) {
+                     const uint16_t* w1, const uint16_t* w2, char* scratch, hipStream_t s) {
   const QLayout Q = qlayout(d);
   char* qbase = scratch + L.queue;
   BuildArgs b{};
@@ -378,8 +374,6 @@ int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_
   q.K = d.K;
   q.D = d.D;
   q.src = reinterpret_cast<const int32_t*>(scratch + L.src);
-  q.topk_w = topk_w;
-  q.wperm = reinterpret_cast<float*>(scratch + L.wperm);
   q.xperm = reinterpret_cast<uint16_t*>(scratch + L.xperm);
   q.ctrl = b.ctrl;
   q.flags = b.flags;

@@ -99,7 +99,7 @@ __device__ __forceinline__ void store8(float* p, size_t i8, const float (&f)[8])
 template <typename IO, typename ACT, int QM>
 __global__ void __launch_bounds__(kRowThreads) dispatch_kernel(
     const IO* __restrict__ rows, int T, int K, int D, const int32_t* __restrict__ pos,
-    const float* __restrict__ topk_w, float* __restrict__ wperm, ACT* __restrict__ dst,
+    ACT* __restrict__ dst,
     uint8_t* __restrict__ qcodes, uint32_t* __restrict__ qsc, int N) {
   const int chunks = D / 8;
   const int tpr = chunks < kRowThreads ? chunks : kRowThreads;
@@ -138,12 +138,6 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_kernel(
         const int q = prow[k];
         if (q >= 0) store8(dst, (size_t(q) * D) / 8 + c, f);
       }
-    }
-  }
-  if (wperm != nullptr) {
-    for (int k = c0; k < K; k += tpr) {
-      const int q = prow[k];
-      if (q >= 0) wperm[q] = topk_w[size_t(t) * K + k];
     }
   }
 }
@@ -224,7 +218,7 @@ __global__ void __launch_bounds__(kRowThreads) gather_reduce_wide_kernel(
 template <int CPL, int QM>
 __global__ void __launch_bounds__(kRowThreads) dispatch_rows_kernel(
     const uint16_t* __restrict__ rows, int T, int K, int D, const int32_t* __restrict__ pos,
-    const float* __restrict__ topk_w, float* __restrict__ wperm, uint16_t* __restrict__ dst,
+    uint16_t* __restrict__ dst,
     uint8_t* __restrict__ qcodes, uint32_t* __restrict__ qsc, int N) {
   constexpr int WAVES = kRowThreads / 64;
   const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -260,7 +254,6 @@ __global__ void __launch_bounds__(kRowThreads) dispatch_rows_kernel(
         if ((c & 15) == 0) qsc[size_t(c >> 4) * N + q] = entry[j];
       }
     }
-    if (wperm != nullptr && lane == 0) wperm[q] = topk_w[size_t(t) * K + k];
   }
 }
 
@@ -471,11 +464,10 @@ static int with_types(const moe_desc& d, bool io_f32, F f) {
 }
 
 int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool in_f32,
-                    const float* topk_w, char* scratch, size_t dst_off, hipStream_t s,
-                    int qmode, uint8_t* qcodes, uint32_t* qsc, bool store_rows, const char* name) {
+                    char* scratch, size_t dst_off, hipStream_t s, int qmode, uint8_t* qcodes,
+                    uint32_t* qsc, bool store_rows, const char* name) {
   if (!store_rows && qmode == 0) return MOE_EINVAL;
   const auto* pos = reinterpret_cast<const int32_t*>(scratch + L.pos);
-  auto* wperm = topk_w ? reinterpret_cast<float*>(scratch + L.wperm) : nullptr;
   prof_begin(name, s);
   const int rc = with_types(d, in_f32, [&](auto io, auto act) {
     using IO = decltype(io);
@@ -486,19 +478,19 @@ int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool i
     if constexpr (std::is_same<IO, uint16_t>::value && std::is_same<ACT, uint16_t>::value) {
       if (qmode != 0 && d.D == 2048 && d.K >= kRowThreads / 64) {  // FP8 forward, 30B shape
         if (qmode == 1)
-          dispatch_rows_kernel<4, QM_MX><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, topk_w, wperm, dst, qcodes, qsc, N);
+          dispatch_rows_kernel<4, QM_MX><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, dst, qcodes, qsc, N);
         else
-          dispatch_rows_kernel<4, QM_BLOCK><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, topk_w, wperm, dst, qcodes, qsc, N);
+          dispatch_rows_kernel<4, QM_BLOCK><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, dst, qcodes, qsc, N);
         return 0;
       }
       if (qmode == 1) {
         dispatch_kernel<IO, ACT, QM_MX><<<row_blocks(d), kRowThreads, 0, s>>>(
-            src, d.T, d.K, d.D, pos, topk_w, wperm, dst, qcodes, qsc, N);
+            src, d.T, d.K, d.D, pos, dst, qcodes, qsc, N);
         return 0;
       }
       if (qmode == 2) {
         dispatch_kernel<IO, ACT, QM_BLOCK><<<row_blocks(d), kRowThreads, 0, s>>>(
-            src, d.T, d.K, d.D, pos, topk_w, wperm, dst, qcodes, qsc, N);
+            src, d.T, d.K, d.D, pos, dst, qcodes, qsc, N);
         return 0;
       }
     }
@@ -506,14 +498,14 @@ int launch_dispatch(const moe_desc& d, const Layout& L, const void* rows, bool i
     if constexpr (std::is_same<IO, uint16_t>::value && std::is_same<ACT, uint16_t>::value) {
       if ((d.D == 2048 || d.D == 4096) && d.K >= kRowThreads / 64) {
         if (d.D == 2048)
-          dispatch_rows_kernel<4, QM_NONE><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, topk_w, wperm, dst, nullptr, nullptr, N);
+          dispatch_rows_kernel<4, QM_NONE><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, dst, nullptr, nullptr, N);
         else
-          dispatch_rows_kernel<8, QM_NONE><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, topk_w, wperm, dst, nullptr, nullptr, N);
+          dispatch_rows_kernel<8, QM_NONE><<<d.T, kRowThreads, 0, s>>>(src, d.T, d.K, d.D, pos, dst, nullptr, nullptr, N);
         return 0;
       }
     }
     dispatch_kernel<IO, ACT, QM_NONE><<<row_blocks(d), kRowThreads, 0, s>>>(
-        src, d.T, d.K, d.D, pos, topk_w, wperm, dst, nullptr, nullptr, N);
+        src, d.T, d.K, d.D, pos, dst, nullptr, nullptr, N);
     return 0;
   });
   prof_end(s);
@@ -555,18 +547,28 @@ int launch_unpermute(const moe_desc& d, const Layout& L, void* dx, bool out_f32,
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
-// dtopk_w[p] = sum over j of part[pos[p] * J + j], j ascending (pairs without a
-// row: 0).  One thread per pair.
+// dtopk_w[src[q]] = sum over j of part[q * J + j], j ascending, for every
+// permuted row q (thread q: a wave reads 64 consecutive rows of partials), and
+// dtopk_w[p] = 0 for the pairs without a row (thread p).
 __global__ void __launch_bounds__(256) dprob_reduce_kernel(const int32_t* __restrict__ pos,
+                                                           const int32_t* __restrict__ src,
+                                                           const int32_t* __restrict__ nrows,
                                                            const float* __restrict__ part, int J,
                                                            float* __restrict__ dtopk_w, int N) {
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= N) return;
-  const int q = pos[p];
-  float s = 0.f;
-  if (q >= 0)
-    for (int j = 0; j < J; ++j) s += part[size_t(q) * J + j];
-  dtopk_w[p] = s;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= N) return;
+  if (i < *nrows) {  // J is even (F % 128 == 0): the row's pairs of partials, loads first
+    const float2* r = reinterpret_cast<const float2*>(part + size_t(i) * J);
+    float s = 0.f;
+#pragma unroll 6
+    for (int j = 0; j < J / 2; ++j) {
+      const float2 v = r[j];
+      s += v.x;
+      s += v.y;
+    }
+    dtopk_w[src[i]] = s;
+  }
+  if (pos[i] < 0) dtopk_w[i] = 0.f;
 }
 
 int launch_dprob_reduce(const moe_desc& d, const Layout& L, float* dtopk_w, const char* scratch,
@@ -576,6 +578,8 @@ int launch_dprob_reduce(const moe_desc& d, const Layout& L, float* dtopk_w, cons
   prof_begin("dprob_reduce", s);
   dprob_reduce_kernel<<<unsigned((N + 255) / 256), 256, 0, s>>>(
       reinterpret_cast<const int32_t*>(scratch + L.pos),
+      reinterpret_cast<const int32_t*>(scratch + L.src),
+      reinterpret_cast<const int32_t*>(scratch + L.offsets) + d.E,
       reinterpret_cast<const float*>(scratch + L.dpart), dprob_parts(d), dtopk_w, N);
   prof_end(s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
