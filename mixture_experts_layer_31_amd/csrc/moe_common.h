@@ -30,7 +30,8 @@ enum : uint32_t { kErrIndex = 1u, kErrTimeout = 2u };
 
 // Routing processes the flat pair list in chunks of this many pairs per block.
 constexpr int kRouteChunk = 2048;
-constexpr int kRouteThreads = 256;
+constexpr int kRouteThreads = 1024;  // 256 measured 9.1 + 16.4 us for count + scatter
+                                     // at 30B against 6.4 + 12.2
 
 // Byte offsets of the regions of the caller's scratch buffer.  Every region
 // starts on a 256-byte boundary.  The layout depends only on the descriptor.

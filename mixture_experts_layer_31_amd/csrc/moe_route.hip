@@ -66,8 +66,8 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(
   if (e == 0) err[0] = bad ? kErrIndex : 0u;
   int total = 0;
   if (e < E) {
-    // the chunk counts of expert e, 16 independent loads at a time
-    constexpr int kB = 16;
+    // the chunk counts of expert e, 32 independent loads at a time
+    constexpr int kB = 32;
     for (int b0 = 0; b0 < nchunks; b0 += kB) {
       int c[kB];
 #pragma unroll
@@ -94,7 +94,7 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(
     for (int f = 0; f < E; ++f) rank += (cnt[f] > total || (cnt[f] == total && f < e)) ? 1 : 0;
     eorder[rank] = e;
   }
-  for (int step = 1; step < 1024; step <<= 1) {
+  for (int step = 1; step < E; step <<= 1) {
     int add[4];
     for (int q = 0; q < 4; ++q) add[q] = e >= step ? sc[q][e - step] : 0;
     __syncthreads();
