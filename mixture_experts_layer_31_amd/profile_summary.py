@@ -45,7 +45,11 @@ _GROUPED = {("false", "1"): "gemm_w1_swiglu", ("false", "0"): "gemm_w2",
 _PLAIN = [("clear_err_kernel", "clear_err"), ("route_count_kernel", "route_count"),
           ("route_scan_kernel", "route_scan"), ("route_scatter_kernel", "route_scatter"),
           ("dispatch_dy_kernel", "dispatch_dy"), ("dispatch_kernel", "dispatch"),
+          ("dprob_reduce_kernel", "dprob_reduce"), ("zero16_kernel", "zero"),
           ("convert_bf16_kernel", "convert_bf16"), ("__amd_rocclr_copyBuffer", "copyBuffer")]
+# Where the GEMMs carry the routing weights (bf16 at the Qwen3 shapes) the row
+# dispatch kernel runs once per step, on dy (the forward's dispatch is inside W1).
+DY_DISPATCH = {"flag": False}
 
 
 def sources_hash() -> str:
@@ -73,7 +77,7 @@ def step_name(kernel: str) -> str | None:
     if m:
         return "combine" if m.group(1) == "true" else "unpermute"
     if "dispatch_rows_kernel" in kernel:  # whole rows per wave (D = 2048, 4096; K >= 4)
-        return "dispatch"
+        return "dispatch_dy" if DY_DISPATCH["flag"] else "dispatch"
     for key, name in _PLAIN:
         if key in kernel:
             return name
@@ -209,7 +213,10 @@ def main():
     ap.add_argument("--workload", default="")
     ap.add_argument("--skip", type=int, default=0,
                     help="warm-up launches per kernel left out of the 'timed avg' column")
+    ap.add_argument("--dy-dispatch", action="store_true",
+                    help="the row dispatch kernel moves dy (no forward dispatch kernel runs)")
     args = ap.parse_args()
+    DY_DISPATCH["flag"] = args.dy_dispatch
     if args.stats_only:
         return stats_summary(args)
     if args.clock:
@@ -255,7 +262,7 @@ def main():
     for n, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
         if n == "copyBuffer":
             continue
-        per_step = len(v) // (len(dur["dispatch"]) if dur.get("dispatch") else len(v)) or 1
+        per_step = len(v) // (len(dur["combine"]) if dur.get("combine") else len(v)) or 1
         timed = v[args.skip * per_step:] or v
         lines.append(f"| {n} | {len(v)} | {sum(v) / len(v):.1f} | {sum(timed) / len(timed):.1f} | "
                      f"{min(v):.1f} | {max(v):.1f} | {100 * sum(v) / total:.1f} |")
