@@ -295,7 +295,7 @@ int moe::forward(const moe_desc* d, const void* x, const int32_t* topk_idx, cons
         return rc;
     }
     if ((rc = fp8_x_tokens(*d, L, x, rows_in_pass, sc, s))) return rc;
-  } else if (!bf16_wide(*d) && (rc = launch_dispatch(*d, L, x, io_f32, sc, L.xperm, s))) {
+  } else if (!w1_gathers(*d) && (rc = launch_dispatch(*d, L, x, io_f32, sc, L.xperm, s))) {
     return rc;
   }
   if (d->mode == MOE_FP32)
@@ -305,7 +305,7 @@ int moe::forward(const moe_desc* d, const void* x, const int32_t* topk_idx, cons
     rc = fp8_fwd_gemms(*d, L, static_cast<const char*>(wprep), sc, s, true);
   else
     rc = launch_fwd_gemms(*d, L, g1, g2, sc, s,
-                          bf16_wide(*d) ? static_cast<const uint16_t*>(x) : nullptr, topk_w);
+                          w1_gathers(*d) ? static_cast<const uint16_t*>(x) : nullptr);
   if (rc) return rc;
   return launch_combine(*d, L, topk_w, y, io_f32, sc, s, !bf16_wide(*d));
 }

@@ -45,18 +45,20 @@ struct Layout {
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// bf16 at the shapes whose W1 GEMM takes the 128-byte-row loop (2F % 256 == 0,
-// D % 64 == 0).  There the GEMMs carry the routing weights and the dispatch:
-// - the W1 GEMM gathers x's rows itself (no dispatch kernel) and writes x_perm
-//   and w_perm for the backward;
-// - its SwiGLU epilogue stores A_w = w * A, so W2 yields O_w = w * O and the
-//   combine is an unweighted sum;
+// A bf16 forward (MOE_BF16, MOE_FP8_BWD) at the shapes whose W1 GEMM takes the
+// 128-byte-row loop (2F % 256 == 0, D % 64 == 0): the W1 GEMM gathers x's rows
+// itself (no dispatch kernel) and writes x_perm for the backward.
+inline bool w1_gathers(const moe_desc& d) {
+  return (d.mode == MOE_BF16 || d.mode == MOE_FP8_BWD) && (2 * d.F) % 256 == 0 &&
+         d.D % 64 == 0;
+}
+// MOE_BF16 at those shapes: the GEMMs also carry the routing weights.
+// - the W1 GEMM's SwiGLU epilogue stores A_w = w * A, so W2 yields O_w = w * O
+//   and the combine is an unweighted sum;
 // - the backward dispatches dy unscaled, the W2 dgrad's epilogue applies w and
 //   writes dProb partials (its accumulators G = dy W2^T against the SwiGLU
 //   output recomputed from H), and the W2 weight gradient pairs dy with A_w.
-inline bool bf16_wide(const moe_desc& d) {
-  return d.mode == MOE_BF16 && (2 * d.F) % 256 == 0 && d.D % 64 == 0;
-}
+inline bool bf16_wide(const moe_desc& d) { return d.mode == MOE_BF16 && w1_gathers(d); }
 // dProb partials per routed row: one per 64 columns of F
 inline int dprob_parts(const moe_desc& d) { return d.F / 64; }
 
@@ -169,10 +171,9 @@ bool pair_capable(const moe_desc& d);
 bool queue_capable(const moe_desc& d);
 int launch_fwd_queue(const moe_desc& d, const Layout& L, const void* x, bool in_f32,
                      const uint16_t* w1, const uint16_t* w2, char* scratch, hipStream_t s);
-// x and topk_w: the token rows and routing weights when bf16_wide(d), else null.
+// x: the token rows when w1_gathers(d), else null.
 int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
-                     char* scratch, hipStream_t s, const uint16_t* x = nullptr,
-                     const float* topk_w = nullptr);
+                     char* scratch, hipStream_t s, const uint16_t* x = nullptr);
 // MOE_FLAG_RECOMPUTE: the forward's W1 GEMM again, storing only H (into L.h,
 // the dH region), with the same kernels and operands as the forward.
 int launch_recompute_h(const moe_desc& d, const Layout& L, const uint16_t* w1, char* scratch,

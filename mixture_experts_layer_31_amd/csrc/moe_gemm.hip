@@ -277,19 +277,20 @@ int run_pair(const moe_desc& d, const Layout& L, GroupedArgs a, int N, WgradArgs
 // backward's recompute skips A).
 int run_w1_swiglu(const moe_desc& d, const Layout& L, const uint16_t* w1, uint16_t* h,
                   uint16_t* act, const char* name, char* scratch, hipStream_t s,
-                  const uint16_t* x = nullptr, const float* topk_w = nullptr) {
+                  const uint16_t* x = nullptr) {
   GroupedArgs a{};
   a.K = d.D;
   a.F = d.F;
   a.A = reinterpret_cast<const uint16_t*>(scratch + L.xperm);
   if (x != nullptr) {
-    if (!bf16_wide(d) || topk_w == nullptr) return MOE_EINVAL;
+    if (!w1_gathers(d)) return MOE_EINVAL;
     a.A = x;
     a.gather = reinterpret_cast<const int32_t*>(scratch + L.src);
     a.gK = d.K;
     a.gT = d.T;
     a.xcopy = reinterpret_cast<uint16_t*>(scratch + L.xperm);
-    a.rw = reinterpret_cast<const float*>(scratch + L.wperm);  // A_w = w A (routing wrote w_perm)
+    if (bf16_wide(d))  // A_w = w A (the routing wrote w_perm)
+      a.rw = reinterpret_cast<const float*>(scratch + L.wperm);
   }
   a.lda = d.D;
   a.B = w1;
@@ -310,11 +311,10 @@ int launch_recompute_h(const moe_desc& d, const Layout& L, const uint16_t* w1, c
 }
 
 int launch_fwd_gemms(const moe_desc& d, const Layout& L, const uint16_t* w1, const uint16_t* w2,
-                     char* scratch, hipStream_t s, const uint16_t* x, const float* topk_w) {
+                     char* scratch, hipStream_t s, const uint16_t* x) {
   const int D = d.D, F = d.F;
   int rc = run_w1_swiglu(d, L, w1, L.recompute ? nullptr : reinterpret_cast<uint16_t*>(scratch + L.h),
-                         reinterpret_cast<uint16_t*>(scratch + L.a), "gemm_w1_swiglu", scratch, s, x,
-                         topk_w);
+                         reinterpret_cast<uint16_t*>(scratch + L.a), "gemm_w1_swiglu", scratch, s, x);
   if (rc) return rc;
   {  // expert linear 2: O.  W2[e] is [D, F].
     GroupedArgs a{};
