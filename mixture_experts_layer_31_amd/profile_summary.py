@@ -46,6 +46,7 @@ _PLAIN = [("clear_err_kernel", "clear_err"), ("route_count_kernel", "route_count
           ("route_scan_kernel", "route_scan"), ("route_scatter_kernel", "route_scatter"),
           ("dispatch_dy_kernel", "dispatch_dy"), ("dispatch_kernel", "dispatch"),
           ("dprob_reduce_kernel", "dprob_reduce"), ("zero16_kernel", "zero"),
+          ("fwd_queue_kernel", "fwd_queue"), ("queue_build_kernel", "queue_build"),
           ("convert_bf16_kernel", "convert_bf16"), ("__amd_rocclr_copyBuffer", "copyBuffer")]
 # Where the GEMMs carry the routing weights (bf16 at the Qwen3 shapes) the row
 # dispatch kernel runs once per step, on dy (the forward's dispatch is inside W1).
@@ -101,14 +102,22 @@ def _wgrad_split(rows):
 
 
 def name_rows(rows):
+    """(step name, row) for every named launch, in dispatch order.  Where the
+    rows carry their routing weights (--dy-dispatch) the combine and the
+    un-permute are the same unweighted gather-reduce kernel: a launch after W2
+    (or the persistent forward) is the combine, any other the un-permute."""
     split = _wgrad_split(rows)
     out = []
-    for r in rows:
+    prev = None
+    for r in sorted(rows, key=lambda r: int(r.get("Dispatch_Id") or 0)):
         n = step_name(r["Kernel_Name"])
         if n == "wgrad":
             n = split.get(_grid(r), "gemm_wgrad")
+        if n == "unpermute" and DY_DISPATCH["flag"] and prev in ("gemm_w2", "fwd_queue"):
+            n = "combine"
         if n:
             out.append((n, r))
+            prev = n
     return out
 
 
