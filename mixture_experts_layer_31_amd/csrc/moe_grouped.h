@@ -142,7 +142,7 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoo
     with_active<WMT>(act, [&](auto a) {
       if constexpr (TL::WIDE) {
         bool copy = false;
-        if constexpr (CAN_GATHER) copy = gathered;
+        if constexpr (CAN_GATHER) copy = gathered && p.xcopy != nullptr;
         if (copy) {
           if constexpr (CAN_GATHER) {
             // k-step kt's 128-byte row segments of A, from LDS to the permuted rows, by the
