@@ -244,9 +244,12 @@ int moe_scratch_view(const moe_desc* d, const void* scratch, size_t scratch_byte
  * (x -> expert-contiguous rows), expert linear 1 with SwiGLU fused into its
  * epilogue, expert linear 2,
  * and the weighted combine y_t = sum_k w[t,k] o_{t,k} (an fp32 gather-reduce in
- * ascending k, rounded once).  Writes `y`; leaves the routing metadata and the
- * intermediates needed by moe_bwd in `scratch`.  `wprep` is ignored in the
- * bf16/fp32 modes. */
+ * ascending k, rounded once).  In MOE_BF16 and MOE_FP8_BWD at D % 64 == 0 and
+ * 2F % 256 == 0 the dispatch is part of expert linear 1 (its loader gathers x's
+ * rows); in MOE_BF16 there the weights also enter in that GEMM's epilogue
+ * (w * silu(g) * u), so the combine sums w * o rows.  Writes `y`; leaves the
+ * routing metadata and the intermediates needed by moe_bwd in `scratch`.
+ * `wprep` is ignored in the bf16/fp32 modes. */
 int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const float* topk_w,
             const void* w1, const void* w2, const void* wprep, void* y,
             void* scratch, size_t scratch_bytes, void* stream);
@@ -263,7 +266,11 @@ int moe_fwd(const moe_desc* d, const void* x, const int32_t* topk_idx, const flo
  * output, an fp32 dot product), the W2 dgrad with SwiGLU-backward fused into
  * its epilogue, the W2 and W1 wgrads (per-expert reductions over that expert's
  * tokens, no atomics), the W1 dgrad and the un-permute reduction of dx (fp32
- * sum over k).  Overwrites dx, dw1, dw2 (experts with no tokens get zeros) and
+ * sum over k).  In MOE_BF16 at D % 64 == 0 and 2F % 256 == 0, dy is
+ * dispatched unscaled and the W2 dgrad's epilogue applies w and forms
+ * dtopk_w[t,k] as sum_f (dy_t W2^T)[f] a_{t,k}[f] (the same value in exact
+ * arithmetic, a_{t,k} recomputed from the saved H), summed over 64-column
+ * partials in column order.  Overwrites dx, dw1, dw2 (experts with no tokens get zeros) and
  * dtopk_w (0 for a slot whose expert id is out of range). */
 int moe_bwd(const moe_desc* d, const void* dy, const float* topk_w,
             const void* w1, const void* w2, const void* wprep,
