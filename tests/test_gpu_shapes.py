@@ -45,7 +45,12 @@ def _cases(n=20, seed=4242):
     return out
 
 
-CASES = _cases()
+# and the expert counts past the paired backward's limit (256) up to the
+# descriptor's (1024), where the routing blocks loop over experts
+CASES = _cases() + [
+    (mi.LayerConfig("many_experts", T=200, D=128, F=128, E=300, K=8, seed=5100), 0),
+    (mi.LayerConfig("max_experts", T=500, D=64, F=64, E=1024, K=4, routing="dead100", seed=5101), 0),
+]
 
 
 @pytest.fixture(scope="module", autouse=True)
