@@ -95,7 +95,9 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs& p, int l, char* smem
   constexpr int WMT = TL::WMT, WNT = TL::WNT, WAVES = TL::WAVES;
 
   const ExpertTile et = expert_tile(p.eorder, l, p.tm * p.tn);
-  const int e = et.e, mt = et.rem / p.tn, nt = et.rem - mt * p.tn;
+  const int e = et.e;
+  int mt, nt;
+  wgrad_mn(et.rem, p.tm, p.tn, mt, nt);
   const int off = p.offsets[e];
   const int ne = p.offsets[e + 1] - off;
 

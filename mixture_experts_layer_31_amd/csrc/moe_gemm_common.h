@@ -59,6 +59,19 @@ __device__ __forceinline__ ExpertTile expert_tile(const int32_t* eorder, int l, 
   return {eorder[rank], l - rank * per};
 }
 
+// Output tile (mt, nt) of the rem-th of one expert's tm x tn weight-gradient
+// tiles: blocks of up to 4 m-tiles x 8 n-tiles, m-tiles fastest, so the run of
+// 32 consecutive tiles an XCD holds at once reads 4 + 8 operand slices (with
+// n-tiles fastest and tn = 16 it read 2 + 16, the whole second operand).
+__device__ __forceinline__ void wgrad_mn(int rem, int tm, int tn, int& mt, int& nt) {
+  constexpr int GM = 4, GN = 8;
+  const int sr = rem / (GM * tn), gm = min(GM, tm - sr * GM);
+  const int in_sr = rem - sr * GM * tn;
+  const int nb = in_sr / (gm * GN), in_nb = in_sr - nb * gm * GN;
+  mt = sr * GM + in_nb % gm;
+  nt = nb * GN + in_nb / gm;
+}
+
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
