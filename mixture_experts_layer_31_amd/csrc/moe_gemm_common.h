@@ -61,8 +61,11 @@ __device__ __forceinline__ ExpertTile expert_tile(const int32_t* eorder, int l, 
 
 // Output tile (mt, nt) of the rem-th of one expert's tm x tn weight-gradient
 // tiles: blocks of up to 4 m-tiles x 8 n-tiles, m-tiles fastest, so the run of
-// 32 consecutive tiles an XCD holds at once reads 4 + 8 operand slices (with
-// n-tiles fastest and tn = 16 it read 2 + 16, the whole second operand).
+// 32 consecutive tiles an XCD holds at once reads 4 + 8 operand slices (in row
+// order with tn = 16 it read 2 + 16, the whole second operand: the 235B W1
+// wgrad fetched 7.45 GB, now 4.83 GB, and runs 1.8% faster in bf16 and 3.7% in
+// blockwise FP8; row order for rows of at most 8 tiles made the 30B MXFP8 W2
+// wgrad 7% slower).
 __device__ __forceinline__ void wgrad_mn(int rem, int tm, int tn, int& mt, int& nt) {
   constexpr int GM = 4, GN = 8;
   const int sr = rem / (GM * tn), gm = min(GM, tm - sr * GM);
@@ -482,6 +485,12 @@ __device__ __forceinline__ void zero(f32x16 (&acc)[A][B]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
 
+// The logistic function with the hardware reciprocal (v_rcp_f32, within 1 ulp):
+// an IEEE division here compiles to about ten instructions (scale, reciprocal,
+// Newton steps, fix-up) per value, in epilogues that run while the matrix
+// cores wait.  exp(-x) = inf gives 0 and exp(-x) = 0 gives 1, as the division.
+__device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   return make_uint2(uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16),
                     uint32_t(f2bf(c)) | (uint32_t(f2bf(d)) << 16));
@@ -705,7 +714,7 @@ __device__ __forceinline__ void dswiglu_epilogue(const EpiArgs& p,
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float G = acc[i][j][4 * g + q];
-          const float sg = 1.f / (1.f + __expf(-gv[q]));
+          const float sg = sigmoid(gv[q]);
           if constexpr (WS) {
             const float s = gv[q] * sg, dA = G * wr[i];
             part += G * (s * uv[q]);
@@ -814,7 +823,7 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
           for (int q = 0; q < 4; ++q) {
             gv[q] = acc[i][j][4 * g + q];
             uv[q] = acc[i][j + WNT / 2][4 * g + q];
-            av[q] = gv[q] / (1.f + __expf(-gv[q])) * uv[q];
+            av[q] = gv[q] * sigmoid(gv[q]) * uv[q];
             if constexpr (WS) if (p.wscale) av[q] *= p.wrow[i];
           }
           *reinterpret_cast<uint2*>(tg.at(rr, c)) = pack4(gv[0], gv[1], gv[2], gv[3]);
