@@ -25,6 +25,15 @@ __device__ __forceinline__ void store16_nt(void* p, const uint4& a) {
   __builtin_nontemporal_store(v, static_cast<nt_u32x4*>(p));
 }
 
+// Two floats rounded to bf16 (nearest, ties to even) in one packed word, low
+// half first: one v_cvt_pk_bf16_f32.  Converting each value on its own took
+// two conversions, a shift and an OR per pair.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 // Bits of the device error word kept in scratch.
 enum : uint32_t { kErrIndex = 1u, kErrTimeout = 2u };
 

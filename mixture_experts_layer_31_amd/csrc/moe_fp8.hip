@@ -253,8 +253,7 @@ __device__ __forceinline__ uint4 scale_bf16x8(const uint4& v, float w) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const float lo = w * __uint_as_float(in[k] << 16), hi = w * __uint_as_float(in[k] & 0xffff0000u);
-    out[k] = uint32_t(__builtin_bit_cast(uint16_t, (__bf16)lo)) |
-             (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)hi)) << 16);
+    out[k] = pack_bf16x2(lo, hi);
   }
   return make_uint4(out[0], out[1], out[2], out[3]);
 }

@@ -76,7 +76,6 @@ __device__ __forceinline__ void wgrad_mn(int rem, int tm, int tn, int& mt, int& 
 }
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
-__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // The expert of flat tile l is the last e in [0, E) with tile_start[e] * u <= key
 // (u = ntn, key = l for n-tiles outer; u = 1, key = the m-tile otherwise):
@@ -492,8 +491,7 @@ __device__ __forceinline__ void zero(f32x16 (&acc)[A][B]) {
 __device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-  return make_uint2(uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16),
-                    uint32_t(f2bf(c)) | (uint32_t(f2bf(d)) << 16));
+  return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
 __device__ __forceinline__ void unpack4(uint2 v, float (&f)[4]) {

@@ -214,12 +214,6 @@ __device__ __forceinline__ void wait_at_least(const int* p, int target, uint64_t
   atomicOr(err, kErrTimeout);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
-  const uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
-  return a | (b << 16);
-}
-
 // Gathers x_perm rows [r0, r1): row r is token src[r] / K.
 template <int THREADS>
 __device__ __forceinline__ void dispatch_rows(const QueueArgs& q, int r0, int r1) {

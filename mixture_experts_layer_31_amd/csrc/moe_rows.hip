@@ -32,11 +32,7 @@ __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
   }
 }
 
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
-  const uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
-  return a | (b << 16);
-}
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
 __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
   return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));

@@ -34,6 +34,7 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 GEMM_SOURCES = [
+    "mixture_experts_layer_31_amd/csrc/moe_common.h",
     "mixture_experts_layer_31_amd/csrc/moe_gemm.hip",
     "mixture_experts_layer_31_amd/csrc/moe_gemm_common.h",
     "mixture_experts_layer_31_amd/csrc/moe_fp8_codec.h",
