@@ -526,10 +526,9 @@ struct EpiArgs {
   int F;
   // Routing weights carried by the GEMMs (epilogues instantiated with WS):
   // SWIGLU stores A_w = w * A, with wrow[i] the weight of the lane's row in
-  // 32-row block i of its wave's share (loaded ahead of the main loop); DSWIGLU
-  // takes dA = w * G, loading row r's weight wp[r] itself, and writes dProb
-  // partials.  Null wp / wscale false: no weights.
-  bool wscale;
+  // 32-row block i of its wave's share (loaded ahead of the main loop; 1
+  // without weights); DSWIGLU takes dA = w * G, loading row r's weight wp[r]
+  // itself, and writes dProb partials.  Null wp: no weights.
   float wrow[4];
   const float* wp;        // DSWIGLU: [rows] routing weight of each permuted row
   float* dpart;           // DSWIGLU: dProb partials [rows, F / 64], the wave's 64 columns of
@@ -621,10 +620,11 @@ template <int THREADS, int CH>
 __device__ __forceinline__ void slice_store(const BandTile<2>& t, int n, size_t row0, int col0,
                                             uint16_t* out, int ld, int tid) {
   static_assert(CH <= 32, "one swizzle period per row");
+  uint16_t* o = out + row0 * ld + col0;  // wave-uniform: scalar 64-bit arithmetic once
   for (int k = tid; k < 32 * CH; k += THREADS) {
     const int r = k / CH, c = k - r * CH;
     const uint4 v = *reinterpret_cast<const uint4*>(t.base + r * CH * 16 + ((c ^ (r & (CH - 1))) << 4));
-    if (r < n) *reinterpret_cast<uint4*>(out + (row0 + r) * ld + col0 + 8 * c) = v;
+    if (r < n) *reinterpret_cast<uint4*>(o + r * ld + 8 * c) = v;
   }
 }
 
@@ -781,9 +781,10 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
               pack4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
         }
     __syncthreads();
-    tile_store<TL::THREADS, TL::BM, BN * 2 / 16>(smem, rows_valid, [&](int r) {
-      return reinterpret_cast<char*>(p.out + (grow0 + r) * p.ldo + nt * BN);
-    });
+    // the tile's first row once in 64 bits (wave-uniform), each row's offset in 32
+    char* ob = reinterpret_cast<char*>(p.out + grow0 * p.ldo + nt * BN);
+    const int ldb = p.ldo * 2;
+    tile_store<TL::THREADS, TL::BM, BN * 2 / 16>(smem, rows_valid, [&](int r) { return ob + r * ldb; });
     return;
   }
 #pragma unroll
@@ -804,9 +805,9 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
         const int first = w * WM + i * 32, n = min(32, rows_valid - first);
         if (n <= 0) continue;
         BandTile<2> sub{smem + w * 32 * BN * 2, BN};
-        band_store<TL::THREADS>(sub, 32, n, tid, [&](int r) {
-          return reinterpret_cast<char*>(p.out + (grow0 + first + r) * p.ldo + nt * BN);
-        });
+        char* ob = reinterpret_cast<char*>(p.out + (grow0 + first) * p.ldo + nt * BN);
+        const int ldb = p.ldo * 2;
+        band_store<TL::THREADS>(sub, 32, n, tid, [&](int r) { return ob + r * ldb; });
       }
     } else if constexpr (EPI == EPI_SWIGLU) {
       const int F = p.F;
@@ -822,7 +823,7 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
             gv[q] = acc[i][j][4 * g + q];
             uv[q] = acc[i][j + WNT / 2][4 * g + q];
             av[q] = gv[q] * sigmoid(gv[q]) * uv[q];
-            if constexpr (WS) if (p.wscale) av[q] *= p.wrow[i];
+            if constexpr (WS) av[q] *= p.wrow[i];  // 1 without routing weights
           }
           *reinterpret_cast<uint2*>(tg.at(rr, c)) = pack4(gv[0], gv[1], gv[2], gv[3]);
           *reinterpret_cast<uint2*>(tu.at(rr, c)) = pack4(uv[0], uv[1], uv[2], uv[3]);
@@ -835,19 +836,18 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
         const int off = w * 32 * BN;  // bytes of 32 rows of BN/2 bf16
         const int f0 = nt * (BN / 2);
         if (p.out != nullptr) {  // H (not kept under activation recompute)
-          band_store<TL::THREADS>(BandTile<2>{smem + off, BN / 2}, 32, n, tid, [&](int r) {
-            return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + f0);
-          });
-          band_store<TL::THREADS>(BandTile<2>{smem + RB * BN + off, BN / 2}, 32, n, tid, [&](int r) {
-            return reinterpret_cast<char*>(p.out + (grow0 + first + r) * 2 * F + F + f0);
-          });
+          char* hb = reinterpret_cast<char*>(p.out + (grow0 + first) * 2 * F + f0);
+          band_store<TL::THREADS>(BandTile<2>{smem + off, BN / 2}, 32, n, tid,
+                                  [&](int r) { return hb + r * (4 * F); });
+          band_store<TL::THREADS>(BandTile<2>{smem + RB * BN + off, BN / 2}, 32, n, tid,
+                                  [&](int r) { return hb + r * (4 * F) + 2 * F; });
         }
         if (p.out2 != nullptr) {  // A (not needed when H is recomputed in the backward)
-          if constexpr (COH2)
+          if constexpr (COH2) {
+            char* ab = reinterpret_cast<char*>(p.out2 + (grow0 + first) * F + f0);
             band_store<TL::THREADS, 2, true>(BandTile<2>{smem + 2 * RB * BN + off, BN / 2}, 32, n,
-                                             tid, [&](int r) {
-              return reinterpret_cast<char*>(p.out2 + (grow0 + first + r) * F + f0);
-            });
+                                             tid, [&](int r) { return ab + r * (2 * F); });
+          }
           else
             slice_store<TL::THREADS, BN / 16>(BandTile<2>{smem + 2 * RB * BN + off, BN / 2}, n,
                                               grow0 + first, f0, p.out2, F, tid);

@@ -99,14 +99,12 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoo
   EpiArgs ea{p.out, p.ldo, p.out2, p.hsave, p.F};
   if constexpr (EPI == EPI_SWIGLU) {  // the routing weights of the lane's rows, ahead of the main loop
     static_assert(WMT <= 4, "one routing weight per 32-row block");
-    if (p.rw != nullptr) {
-      ea.wscale = true;
 #pragma unroll
-      for (int i = 0; i < WMT; ++i) {
-        const int trow = wm * TL::WM + i * 32 + (lane & 31);
-        const int r = e0 + m0 + trow;
-        ea.wrow[i] = trow < rows_valid ? p.rw[p.rsrc != nullptr ? p.rsrc[r] : r] : 0.f;
-      }
+    for (int i = 0; i < WMT; ++i) {
+      const int trow = wm * TL::WM + i * 32 + (lane & 31);
+      const int r = e0 + m0 + trow;
+      ea.wrow[i] = p.rw == nullptr ? 1.f  // no routing weights: A itself
+                   : trow < rows_valid ? p.rw[p.rsrc != nullptr ? p.rsrc[r] : r] : 0.f;
     }
   } else if constexpr (EPI == EPI_DSWIGLU) {  // loaded by the epilogue (rsrc unused)
     ea.wp = p.rw;
