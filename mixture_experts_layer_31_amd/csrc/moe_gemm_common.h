@@ -581,7 +581,7 @@ __device__ __forceinline__ void band_store(const BandTile<ES>& t, int rows, int 
 // rows dst(row), the first `valid` of them.  Every thread reads all of its
 // chunks from LDS before it issues any store, so its stores leave back to back
 // instead of each behind its own LDS round trip.
-template <int THREADS, int ROWS, int CH, class Dst>
+template <int THREADS, int ROWS, int CH, bool NT = false, class Dst>
 __device__ __forceinline__ void tile_store(const char* base, int valid, Dst dst) {
   constexpr int N = ROWS * CH / THREADS;
   constexpr int SW = (CH < 32 ? CH : 32) - 1;
@@ -597,7 +597,10 @@ __device__ __forceinline__ void tile_store(const char* base, int valid, Dst dst)
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     const int i = tid + k * THREADS, r = i / CH, c = i % CH;
-    if (r < valid) *reinterpret_cast<uint4*>(dst(r) + c * 16) = v[k];
+    if (r < valid) {
+      if constexpr (NT) store16_nt(dst(r) + c * 16, v[k]);
+      else *reinterpret_cast<uint4*>(dst(r) + c * 16) = v[k];
+    }
   }
 }
 
@@ -754,8 +757,9 @@ __device__ __forceinline__ void dswiglu_epilogue(const EpiArgs& p,
 // at acc_col(g).  grow0 is the tile's first row in the permuted buffers; smem is
 // the (now free) pipeline LDS, AVAIL bytes of it.  A plain store stages the
 // whole bf16 tile at once when AVAIL holds it (one barrier, every store of a
-// thread issued back to back), else one band at a time.
-template <class TL, int EPI, bool COH2 = false, int AVAIL = 0, bool WS = false>
+// thread issued back to back; NT: with streaming stores), else one band at a
+// time.
+template <class TL, int EPI, bool COH2 = false, int AVAIL = 0, bool WS = false, bool NT = false>
 __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
                                                  f32x16 (&acc)[TL::WMT][TL::WNT], size_t grow0,
                                                  int rows_valid, int nt, int wm, int wn, int lane,
@@ -784,7 +788,7 @@ __device__ __forceinline__ void grouped_epilogue(const EpiArgs& p,
     // the tile's first row once in 64 bits (wave-uniform), each row's offset in 32
     char* ob = reinterpret_cast<char*>(p.out + grow0 * p.ldo + nt * BN);
     const int ldb = p.ldo * 2;
-    tile_store<TL::THREADS, TL::BM, BN * 2 / 16>(smem, rows_valid, [&](int r) { return ob + r * ldb; });
+    tile_store<TL::THREADS, TL::BM, BN * 2 / 16, NT>(smem, rows_valid, [&](int r) { return ob + r * ldb; });
     return;
   }
 #pragma unroll

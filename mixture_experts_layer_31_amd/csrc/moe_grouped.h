@@ -172,8 +172,10 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& p, const TileCoo
     });
   }
 
-  grouped_epilogue<TL, EPI, COH2, TL::LDS, true>(ea, acc, size_t(e0) + m0, rows_valid, nt, wm, wn, lane,
-                                           smem, tid);
+  // the dgrads' plain stores (dX_perm, read once by the un-permute after the launch) stream
+  // past the caches, which keep the operands of the tiles still running
+  grouped_epilogue<TL, EPI, COH2, TL::LDS, true, B_T>(ea, acc, size_t(e0) + m0, rows_valid, nt, wm,
+                                                     wn, lane, smem, tid);
 }
 
 }  // namespace gemm
