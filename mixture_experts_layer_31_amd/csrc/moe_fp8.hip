@@ -531,9 +531,8 @@ __device__ __forceinline__ void mainloop8(char* smem, const SA& sa, const SB& sb
 // both operands are scaled per 128-token block along an output axis, so each
 // of the lane's 16 columns has its own s_b, read from LDS right before the
 // promotion (16 products and 16 FMAs).  The step's B fragments stay in
-// registers while the A fragments stream one 32-row block at a time (in the
-// token-grouped GEMMs the next block's are read while the current one
-// multiplies), which keeps the loop inside 256 registers.
+// registers while the A fragments stream one 32-row block at a time, which
+// keeps the loop inside 256 registers.
 template <class TL, bool SB_COL, class SA, class SB>
 __device__ __forceinline__ void block8(char* smem, const SA& sa, const SB& sb,
                                        const ScaleStager& ssa, const ScaleStager& ssb, int ktiles,
@@ -572,26 +571,33 @@ __device__ __forceinline__ void block8(char* smem, const SA& sa, const SB& sb,
     const int r0 = wm * WM + (lane & 31);
     i32x8 a0 = frag8(ta, r0, 0, lane), a1 = frag8(ta, r0, 1, lane);
     float sav = __uint_as_float(sca[r0]);
-    if constexpr (SB_COL) {
+    {
       // Software-pipelined over the wave's 32x32 blocks u = 2i + j: block u's two
-      // MFMAs are issued before block u-1 is promoted, so that promotion's 32
-      // VALU operations per lane can run while the matrix core works on block u
-      // (2% faster than promoting each block behind its own MFMAs; a timing
-      // probe that skipped the promotion put its cost at 0.6 ms of the 235B W1
-      // wgrad's 2.8 ms, but at 256 registers the block's A fragments are read
-      // at its start instead of one block ahead).
+      // MFMAs are issued before block u-1 is promoted, so that promotion's VALU
+      // work can run while the matrix core works on block u.  Against promoting
+      // each block behind its own MFMAs: the weight gradients 2% faster (a timing
+      // probe that skipped their promotion put its cost at 0.6 ms of the 235B W1
+      // wgrad's 2.8 ms), the 30B token-grouped GEMMs 2-8% (their register spills
+      // gone).  At 256 registers a block's A fragments are read at its start
+      // instead of one block ahead.
       static_assert(WNT == 2, "two column blocks per wave");
       f32x16 P[2];
       float savp = 0.f;
       auto promote = [&](int i, int j, const f32x16& part, float s) {
-        float sbc[16];
+        if constexpr (SB_COL) {
+          float sbc[16];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 v4 = *reinterpret_cast<const float4*>(scb + wn * WN + j * 32 + acc_col(g, lane));
-          sbc[4 * g] = v4.x; sbc[4 * g + 1] = v4.y; sbc[4 * g + 2] = v4.z; sbc[4 * g + 3] = v4.w;
+          for (int g = 0; g < 4; ++g) {
+            const float4 v4 = *reinterpret_cast<const float4*>(scb + wn * WN + j * 32 + acc_col(g, lane));
+            sbc[4 * g] = v4.x; sbc[4 * g + 1] = v4.y; sbc[4 * g + 2] = v4.z; sbc[4 * g + 3] = v4.w;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[r], s * sbc[r], acc[i][j][r]);
+        } else {
+          const float sc = s * sbv[j];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[r], sc, acc[i][j][r]);
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[r], s * sbc[r], acc[i][j][r]);
       };
 #pragma unroll
       for (int u = 0; u < 2 * WMT; ++u) {
@@ -614,46 +620,6 @@ __device__ __forceinline__ void block8(char* smem, const SA& sa, const SB& sb,
         __builtin_amdgcn_sched_barrier(0);
       }
       promote(WMT - 1, 1, P[1], sav);
-      continue;
-    }
-#pragma unroll
-    for (int i = 0; i < WMT; ++i) {
-      i32x8 n0, n1;
-      float nsa = 0.f;
-      if (i + 1 < WMT) {
-        n0 = frag8(ta, r0 + (i + 1) * 32, 0, lane);
-        n1 = frag8(ta, r0 + (i + 1) * 32, 1, lane);
-        nsa = __uint_as_float(sca[r0 + (i + 1) * 32]);
-      }
-      f32x16 part[WNT];
-#pragma unroll
-      for (int j = 0; j < WNT; ++j) part[j] = mfma8<0>(b0[j], a0, f32x16{}, 127, 127);
-#pragma unroll
-      for (int j = 0; j < WNT; ++j) part[j] = mfma8<0>(b1[j], a1, part[j], 127, 127);
-#pragma unroll
-      for (int j = 0; j < WNT; ++j) {
-        if constexpr (SB_COL) {  // one scale per output column: the lane's 16 columns
-          float sbc[16];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const float4 v4 = *reinterpret_cast<const float4*>(scb + wn * WN + j * 32 + acc_col(g, lane));
-            sbc[4 * g] = v4.x; sbc[4 * g + 1] = v4.y; sbc[4 * g + 2] = v4.z; sbc[4 * g + 3] = v4.w;
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            acc[i][j][r] = __builtin_fmaf(part[j][r], sav * sbc[r], acc[i][j][r]);
-        } else {
-          const float sc = sav * sbv[j];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[j][r], sc, acc[i][j][r]);
-        }
-      }
-      if (i + 1 < WMT) {
-        a0 = n0;
-        a1 = n1;
-        sav = nsa;
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
