@@ -1,7 +1,7 @@
 """A seeded sweep of small layer shapes against the CPU oracle, through the C ABI.
 
 The named parity shapes pick particular cases; this sweep draws twenty more
-from fixed ranges (D and F multiples of 64, one to 33 experts, top-1 to top-8,
+(plus four fixed edge cases listed with them) from fixed ranges (D and F multiples of 64, one to 33 experts, top-1 to top-8,
 one to 700 tokens, uniform, dead-expert and skewed routing, bf16 and fp32-I/O
 modes, each backward schedule and activation recompute), so that both the
 path where the bf16 GEMMs carry the routing weights and the dispatch (2F a
@@ -46,10 +46,14 @@ def _cases(n=20, seed=4242):
 
 
 # and the expert counts past the paired backward's limit (256) up to the
-# descriptor's (1024), where the routing blocks loop over experts
+# descriptor's (1024), where the routing blocks loop over experts; and weight-
+# gradient tile grids that end in partial blocks of the 4 x 8 tile order (W1:
+# 2 x 9 tiles of 256, W2: 9 x 1), one kernel per GEMM and paired
 CASES = _cases() + [
     (mi.LayerConfig("many_experts", T=200, D=128, F=128, E=300, K=8, seed=5100), 0),
     (mi.LayerConfig("max_experts", T=500, D=64, F=64, E=1024, K=4, routing="dead100", seed=5101), 0),
+    (mi.LayerConfig("wgrad_grid", T=96, D=2304, F=256, E=3, K=2, seed=5102), moe.MOE_FLAG_SERIAL_BWD),
+    (mi.LayerConfig("wgrad_grid_pair", T=96, D=2304, F=256, E=3, K=2, seed=5103), 0),
 ]
 
 
