@@ -715,17 +715,18 @@ __device__ __forceinline__ void dswiglu_epilogue(const EpiArgs& p,
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float G = acc[i][j][4 * g + q];
+          // silu(g) = g sg and silu'(g) = sg + silu(g) (1 - sg), with sg the logistic
+          // function: dH_gate = dA u silu'(g), dH_up = dA silu(g)
           const float sg = sigmoid(gv[q]);
-          if constexpr (WS) {
-            const float s = gv[q] * sg, dA = G * wr[i];
-            part += G * (s * uv[q]);
+          const float s = gv[q] * sg, ds = __builtin_fmaf(s, 1.f - sg, sg), Gu = G * uv[q];
+          if constexpr (WS) {  // dA = w G; the dProb partial takes G A = G u silu(g)
+            part = __builtin_fmaf(Gu, s, part);
             asm volatile("" : "+v"(part));  // keeps the compiler from spilling here
-            dg[q] = dA * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
-            du[q] = dA * s;
+            dg[q] = Gu * wr[i] * ds;
+            du[q] = G * wr[i] * s;
           } else {
-            const float dA = G;
-            dg[q] = dA * uv[q] * sg * (1.f + gv[q] * (1.f - sg));
-            du[q] = dA * gv[q] * sg;
+            dg[q] = Gu * ds;
+            du[q] = G * s;
           }
         }
         *pg = pack4(dg[0], dg[1], dg[2], dg[3]);
