@@ -62,11 +62,10 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(
   const int e = threadIdx.x;
   int bad = 0;
   for (int b = e; b < nchunks; b += blockDim.x) bad |= chunk_bad[b];
-  bad = __syncthreads_or(bad);
-  if (e == 0) err[0] = bad ? kErrIndex : 0u;
   int total = 0;
   if (e < E) {
-    // the chunk counts of expert e, 32 independent loads at a time
+    // the chunk counts of expert e, 32 independent loads at a time, the first batch in
+    // flight together with the bad-index flags above
     constexpr int kB = 32;
     for (int b0 = 0; b0 < nchunks; b0 += kB) {
       int c[kB];
@@ -80,6 +79,8 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(
     }
     counts[e] = total;
   }
+  bad = __syncthreads_or(bad);
+  if (e == 0) err[0] = bad ? kErrIndex : 0u;
   // inclusive scans over experts of: count, tiles of 64, 128 and 256 rows
   int v[4];
   v[0] = e < E ? total : 0;
@@ -89,9 +90,14 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(
   for (int q = 0; q < 4; ++q) sc[q][e] = v[q];
   cnt[e] = v[0];
   __syncthreads();
+  int mx = 0;  // the largest count (every thread, in the ranking loop)
   if (e < E) {
     int rank = 0;
-    for (int f = 0; f < E; ++f) rank += (cnt[f] > total || (cnt[f] == total && f < e)) ? 1 : 0;
+    for (int f = 0; f < E; ++f) {
+      const int cf = cnt[f];
+      rank += (cf > total || (cf == total && f < e)) ? 1 : 0;
+      mx = max(mx, cf);
+    }
     eorder[rank] = e;
   }
   for (int step = 1; step < E; step <<= 1) {
@@ -108,8 +114,6 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(
     tiles128[e] = sc[2][e] - v[2];
     tiles256[e] = sc[3][e] - v[3];
     if (e == E - 1) {
-      int mx = 0;
-      for (int f = 0; f < E; ++f) mx = max(mx, cnt[f]);
       eorder[E] = (long long)mx * E > 2LL * sc[0][e] ? 1 : 0;
       offsets[E] = sc[0][e];
       tiles64[E] = sc[1][e];
