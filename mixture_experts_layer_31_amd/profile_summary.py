@@ -18,8 +18,8 @@ size (the W1 one has twice the output tiles of the W2 one).  The calibration
 scales each counter so that the device copy of M MiB reads and writes M MiB.
 
     python -m mixture_experts_layer_31_amd.profile_summary --config 30b \\
-        --trace gpurun_out/prof/trace --fetch gpurun_out/prof/fetch \\
-        --write gpurun_out/prof/write --calib-mib 512 --commands "..."
+        --trace <dir>/trace --fetch <dir>/fetch \\
+        --write <dir>/write --calib-mib 512 --commands "..."
 """
 from __future__ import annotations
 
