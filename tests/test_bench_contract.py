@@ -1,6 +1,7 @@
 """Host-side checks of bench.py's contract that need no GPU: the refusal of more
 than one GPU (the layer's expert-parallel exchange is not part of this library),
-and the algorithmic byte counts behind the reported HBM rates."""
+the algorithmic byte counts behind the reported HBM rates, and the source hash
+that keeps a stale traffic summary out of the roofline entry."""
 import os
 import subprocess
 import sys
@@ -65,3 +66,45 @@ def test_row_mover_bytes_follow_the_definitions():
                                     mode=mi.MODE_FP32_BF16GEMM))
     assert b.row_bytes(fb)["dispatch"] == io["dispatch"]
     assert b.row_bytes(fb)["dispatch_dy"] - io["dispatch_dy"] == fcodes - 2 * fb.N * fb.D
+
+
+def _local_includes(path, seen):
+    """The csrc headers a source pulls in, directly or through other csrc headers."""
+    import re
+    csrc = os.path.dirname(path)
+    for line in open(path):
+        m = re.match(r'\s*#include "([^"]+)"', line)
+        if m and os.path.exists(os.path.join(csrc, m.group(1))) and m.group(1) not in seen:
+            seen.add(m.group(1))
+            _local_includes(os.path.join(csrc, m.group(1)), seen)
+    return seen
+
+
+def test_traffic_summaries_cover_every_gemm_source_and_go_stale_on_change(tmp_path):
+    """The roofline's traffic comes from a committed FETCH/WRITE summary keyed to a hash of
+    the GEMM sources: the hashed list must hold every csrc header the GEMM kernels include,
+    and changing any of them must make bench.py report no traffic rather than a stale one."""
+    import json
+    import shutil
+    b = _bench_module()
+    from mixture_experts_layer_31_amd import profile_summary as ps
+    gemm = os.path.join(ROOT, "mixture_experts_layer_31_amd", "csrc", "moe_gemm.hip")
+    needed = {"mixture_experts_layer_31_amd/csrc/" + h for h in _local_includes(gemm, set())}
+    needed.add("mixture_experts_layer_31_amd/csrc/moe_gemm.hip")
+    assert needed <= set(ps.GEMM_SOURCES), needed - set(ps.GEMM_SOURCES)
+    cfg = mi.CONFIGS["30b"]
+    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_30b_bf16.json")))
+    assert rec["sources"] == ps.GEMM_SOURCES
+    k = "pair_w1"
+    assert b.measured_traffic(cfg, k) == rec["kernels"][k]["fetch_bytes"] + rec["kernels"][k]["write_bytes"]
+    # a copy of the tree with one hashed source changed by a byte
+    shutil.copytree(os.path.join(ROOT, "profiles"), tmp_path / "profiles")
+    for src in rec["sources"]:
+        dst = tmp_path / src
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(ROOT, src), dst)
+    b.ROOT = str(tmp_path)
+    assert b.measured_traffic(cfg, k) is not None
+    with open(tmp_path / rec["sources"][-1], "a") as f:
+        f.write("\n")
+    assert b.measured_traffic(cfg, k) is None
