@@ -135,6 +135,24 @@ def test_all_pairs_on_two_experts():
         assert np.all(out["dw1"][e] == 0) and np.all(out["dw2"][e] == 0)
 
 
+@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16"])
+def test_saturated_gates(name):
+    # W1 scaled by 200: about one gate value in ten lies beyond +-88, where exp(-g) is 0 or
+    # overflows to inf and the logistic function is exactly 1 or 0 in fp32; the SwiGLU and
+    # SwiGLU-backward epilogues must give the oracle's values there, without NaN or inf
+    cfg = mi.CONFIGS[name]
+    inp = mi.make_inputs(cfg)
+    w1 = inp["w1"] * np.float32(200.0)
+    mi.bf16_round(w1)
+    f = orc.forward(inp["x"], inp["topk_idx"], inp["topk_w"], w1, inp["w2"])
+    g = f["h"][..., :cfg.F]
+    assert (g < -88).mean() > 0.02 and (g > 88).mean() > 0.02
+    print(f"[case] {name} with W1 x 200", flush=True)
+    L, out, b = layer_vs_oracle(cfg, dict(inp, w1=w1))
+    for k, v in out.items():
+        assert np.all(np.isfinite(v)), k
+
+
 @pytest.mark.parametrize("mode", [moe.MOE_FP32, moe.MOE_FP32_BF16GEMM, moe.MOE_BF16,
                                   moe.MOE_FP8_BWD, moe.MOE_MXFP8, moe.MOE_FP8])
 def test_empty_layer(mode):
