@@ -135,6 +135,20 @@ def test_all_pairs_on_two_experts():
         assert np.all(out["dw1"][e] == 0) and np.all(out["dw2"][e] == 0)
 
 
+@pytest.mark.parametrize("name", ["mid_bf16", "mid_f32io"])
+def test_zero_routing_weights(name):
+    # a third of the tokens give their second expert weight 0: those pairs add nothing to y,
+    # dx or the weight gradients, yet their routing-weight gradient <dy, o> is not zero (with
+    # the weights in the GEMMs, dProb's partials use the unweighted A, never dividing by w)
+    cfg = mi.CONFIGS[name]
+    inp = mi.make_inputs(cfg)
+    w = inp["topk_w"].copy()
+    w[::3, 1] = 0.0
+    print(f"[case] {name} with zero routing weights", flush=True)
+    L, out, b = layer_vs_oracle(cfg, dict(inp, topk_w=w))
+    assert np.all(out["dprob"][::3, 1] != 0)
+
+
 @pytest.mark.parametrize("name", ["small_bf16", "mid_bf16"])
 def test_saturated_gates(name):
     # W1 scaled by 200: about one gate value in ten lies beyond +-88, where exp(-g) is 0 or
