@@ -8,10 +8,12 @@
 // running in lock-step phases, and one tail replaces two.
 //
 // Schedule.  The items form one list in the experts' longest-first order
-// (routing's eorder): for each expert its A tiles, then its B tiles (spreading
-// the A tiles evenly among the B tiles measured 1-2% slower: it splits the
-// expert's A tiles, which share the weight slices, over more of the XCD's
-// workgroup slots).  The list
+// (routing's eorder): for each expert its B tiles, then its A tiles (the dgrad
+// then finds the token rows both read, dY or dH, in the caches: W2 pair -1.5%
+// and W1 pair -0.4% at the 30B shape, both -0.4% at 235B, against A tiles
+// first; spreading the A tiles evenly among the B tiles measured 1-2% slower:
+// it splits the expert's A tiles, which share the weight slices, over more of
+// the XCD's workgroup slots).  The list
 // is cut into 8 contiguous ranges of about equal estimated cost (an A tile
 // costs its contraction length, a B tile its expert's token count, both plus
 // an epilogue share), one per XCD queue; workgroup b takes tickets from queue
@@ -132,13 +134,12 @@ __device__ __forceinline__ void pair_setup(const PairSched& s, PairLds& L) {
         if (L.cost[mid] <= target) lo = mid; else hi = mid;
       }
       const int e = s.eorder[lo];
-      const int na = (s.tstart[e + 1] - s.tstart[e]) * s.ntn;
       const int ne = s.offsets[e + 1] - s.offsets[e];
       const float ca = float(s.cost_a + kPairEpilogueCost), cb = float(ne + kPairEpilogueCost);
       const float rem = target - L.cost[lo];
       int i;
-      if (rem <= float(na) * ca) i = int(ceilf(rem / ca));
-      else i = na + int(ceilf((rem - float(na) * ca) / cb));
+      if (rem <= float(s.per_b) * cb) i = int(ceilf(rem / cb));
+      else i = s.per_b + int(ceilf((rem - float(s.per_b) * cb) / ca));
       b = min(L.items[lo] + max(i, 0), L.items[lo + 1]);
     }
     L.bound[t] = b;
@@ -174,10 +175,10 @@ __device__ __forceinline__ int pair_next(const PairSched& s, PairLds& L, int* q)
   return item;
 }
 
-// Which GEMM and which of its flat tile indices item g is: A tiles of the
-// expert of rank r are flat tiles tstart[e] * ntn + i of the token-grouped
-// GEMM; B tiles are r * per_b + (i - na) of the weight gradient (which maps
-// rank r back to its expert through eorder).
+// Which GEMM and which of its flat tile indices item g is: item i of the
+// expert of rank r is, for i < per_b, tile r * per_b + i of the weight gradient
+// (which maps rank r back to its expert through eorder), else flat tile
+// tstart[e] * ntn + (i - per_b) of the token-grouped GEMM.
 struct PairItem { bool is_a; int l; };
 __device__ __forceinline__ PairItem pair_decode(const PairSched& s, const PairLds& L, int g) {
   int lo = 0, hi = s.E;  // last rank whose first item is <= g
@@ -187,10 +188,9 @@ __device__ __forceinline__ PairItem pair_decode(const PairSched& s, const PairLd
   }
   const int e = s.eorder[lo];
   const int i = g - L.items[lo];
-  const int na = (s.tstart[e + 1] - s.tstart[e]) * s.ntn;
   PairItem it;
-  it.is_a = i < na;
-  it.l = it.is_a ? s.tstart[e] * s.ntn + i : lo * s.per_b + (i - na);
+  it.is_a = i >= s.per_b;
+  it.l = it.is_a ? s.tstart[e] * s.ntn + (i - s.per_b) : lo * s.per_b + i;
   it.is_a = __builtin_amdgcn_readfirstlane(it.is_a ? 1 : 0) != 0;
   it.l = __builtin_amdgcn_readfirstlane(it.l);
   return it;
